@@ -1,0 +1,182 @@
+"""Benchmark: DeepSeek-V3-shape MoE-layer forward on one MI355X.
+
+One step = the whole hot path over one batch: 1x128 quantisation of x, routing
+(sigmoid affinities, bias, group limit, top-k, gates, load), permutation, routed FP8
+SwiGLU experts, shared expert, combine, bias update. Inputs and weights are seeded
+synthetic values already resident in HBM when the timed region starts.
+
+Prints one JSON line. Per-stage HIP events are recorded on the launch stream inside
+the timed region; the roofline entry is for the dominant call, the routed grouped FFN.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at V3 shape (T=4096); FP8 TFLOP/s as % MFMA peak"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ffn_algorithmic_bytes(cfg, counts, n_experts_rows_tokens):
+    """Minimum HBM bytes of one routed grouped-FFN call: codes and scales of every expert
+    that received a row, the unique token rows of xq/xs, the FP8 intermediate written and
+    read once, and the bf16 expert outputs written once."""
+    H, I = cfg.hidden_size, cfg.moe_intermediate_size
+    rows, tokens = n_experts_rows_tokens
+    touched = int((counts > 0).sum())
+    w = touched * (3 * I * H + 3 * (I // 128) * (H // 128) * 4)
+    act = tokens * (H + (H // 128) * 4)
+    inter = 2 * rows * (I + (I // 128) * 4)
+    out = rows * H * 2
+    return w + act + inter + out, touched
+
+
+def cpu_baseline(cfg, n_tokens: int):
+    """Times the CPU oracle on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    x = synth.hidden_states(cfg)[:n_tokens]
+    wr = synth.router_weight(cfg)
+    b = synth.expert_bias(cfg)
+    r = oracle.route(x, wr, b, cfg.num_experts_per_tok, cfg.n_group, cfg.topk_group,
+                     cfg.group_score_topn, cfg.routed_scaling_factor)
+    experts = sorted(set(r["idx"].ravel().tolist()))
+    cache, sh = {}, {}
+
+    def q3(w):
+        return (*oracle.quantize_128x128(w[0]), *oracle.quantize_128x128(w[1]),
+                *oracle.quantize_128x128(w[2]))
+    synth.map_experts(cfg, lambda e, w: cache.__setitem__(e, q3(w)), experts)
+    synth.map_experts(cfg, lambda s, w: sh.__setitem__(s, q3(w)), range(cfg.num_shared_experts),
+                      shared=True)
+    t0 = time.perf_counter()
+    oracle.layer_forward(x, wr, b, cfg, lambda e: cache[e], lambda s: sh[s])
+    dt = time.perf_counter() - t0
+    cores = max(blas, min(16, os.cpu_count() or 1))
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{n_tokens} tokens of {cfg.name} through the FP64 oracle layer forward "
+                       f"(1x128 quantisation, routing against all {cfg.num_experts} experts, "
+                       f"{len(experts)} routed + {cfg.num_shared_experts} shared expert FFNs, "
+                       f"combine); weight quantisation of those experts excluded; {dt:.1f} s"),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_prefill")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the multi-GPU (expert-parallel) path is not "
+              "built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from deepseekmoe_routing_fp8_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    from deepseekmoe_routing_fp8_amd import MoELayer
+
+    cfg = synth.PRESETS[args.workload]
+    T, H, I, k, S = (cfg.tokens, cfg.hidden_size, cfg.moe_intermediate_size,
+                     cfg.num_experts_per_tok, cfg.num_shared_experts)
+    log(f"[bench] {cfg.name}: generating and quantising weights on the device")
+    t0 = time.time()
+    layer = MoELayer(cfg)
+    layer.load_from_synth()
+    x = torch.from_numpy(synth.hidden_states(cfg)).to(
+        torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32).cuda()
+    log(f"[bench] weights ready in {time.time() - t0:.1f} s; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+
+    nst = len(MoELayer.STAGES)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        layer.forward(x, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nst)]
+                         for i in range(args.steps)])
+    step_ms = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in range(args.steps)])
+    ms_per_step = wall * 1e3 / args.steps
+    value = T * args.steps / wall
+
+    counts = layer.counts.cpu().numpy()
+    flops_layer = 6.0 * H * I * T * (k + S)
+    tflops = flops_layer / (ms_per_step * 1e-3) / 1e12
+    ffn_ms = float(stage_ms[:, MoELayer.STAGES.index("ffn_routed")].mean())
+    ffn_bytes, touched = ffn_algorithmic_bytes(cfg, counts, (T * k, T))
+    ffn_flops = 6.0 * H * I * T * k
+    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) weights quantised to E4M3 128x128)",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "routed_experts": cfg.num_experts,
+                   "shared_experts": S, "top_k": k, "expert_intermediate": I,
+                   "groups": f"{cfg.n_group}x{cfg.num_experts // cfg.n_group} keep {cfg.topk_group} "
+                             f"(top-{cfg.group_score_topn} sum)" if cfg.n_group > 1 else "none",
+                   "parallelism": "single GPU"},
+        "tflops_fp8": round(tflops, 1),
+        "frac_fp8_mfma_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+        "roofline": {
+            "kernel": "moe_grouped_ffn_fp8 routed call (ffn_gate_up_kernel + ffn_down_kernel + plan)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes": ffn_bytes, "experts_touched": touched,
+            "avg_ms": round(ffn_ms, 4),
+            "mfma_tflops": round(ffn_flops / (ffn_ms * 1e-3) / 1e12, 1),
+        },
+        "stage_ms": {s: round(float(stage_ms[:, j].mean()), 4) for j, s in enumerate(MoELayer.STAGES)},
+        "event_ms_per_step": round(float(step_ms.mean()), 4),
+        "max_over_mean_load": round(float(counts.max() / counts.mean()), 3),
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

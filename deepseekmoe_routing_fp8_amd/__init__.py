@@ -1,0 +1,239 @@
+"""Python binding of libmoe_fp8.so, the gfx950 DeepSeekMoE layer-forward library.
+
+Argument marshalling only: every function below checks tensor placement, dtype and
+shape, then calls the C entry point of the same name (declared in include/moe_fp8.h)
+on the current HIP stream. All arithmetic happens in the library's HIP kernels; torch
+only provides device memory and streams. A missing or unloadable library raises at
+import time — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m deepseekmoe_routing_fp8_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_F32, MOE_BF16 = 0, 1
+
+ENTRY_POINTS = (
+    "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_route",
+    "moe_permute", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8", "moe_combine",
+    "moe_update_bias",
+)
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+        ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("n_group", ctypes.c_int32),
+        ("topk_group", ctypes.c_int32), ("group_topn", ctypes.c_int32),
+        ("routed_scaling", ctypes.c_float), ("bias_gamma", ctypes.c_float),
+    ]
+
+
+def make_config(cfg) -> moe_config:
+    """moe_config from any object with the synth.MoEConfig field names."""
+    return moe_config(cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts,
+                      cfg.num_shared_experts, cfg.num_experts_per_tok, cfg.n_group,
+                      cfg.topk_group, cfg.group_score_topn, cfg.routed_scaling_factor,
+                      cfg.expert_bias_update_rate)
+
+
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_CFG = ctypes.POINTER(moe_config)
+_sig = {
+    "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_quantize_1x128": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "moe_quantize_128x128": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "moe_route": ([_CFG, _P, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_permute": ([_CFG, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_grouped_ffn_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
+    "moe_grouped_ffn_fp8": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             _P, ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
+    "moe_combine": ([_CFG, _I64, _P, ctypes.c_int, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_update_bias": ([_CFG, _I64, _P, _P, _P], ctypes.c_int),
+}
+for _name, (_args, _res) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MoEError(f"{what}: {_lib.moe_status_string(status).decode()} (status {status})")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoEError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise MoEError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoEError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MoEError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _xdtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return MOE_BF16
+    if x.dtype == torch.float32:
+        return MOE_F32
+    raise MoEError(f"unsupported activation dtype {x.dtype}")
+
+
+def moe_quantize_1x128(x: torch.Tensor, q: torch.Tensor = None, scales: torch.Tensor = None,
+                       stream=None):
+    """1x128 E4M3 quantisation of x [rows, cols] -> (q uint8 [rows, cols], scales f32)."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    if scales is None:
+        scales = torch.empty((rows, max(cols // 128, 0)), dtype=torch.float32, device=x.device)
+    _check(_lib.moe_quantize_1x128(_dev(x, x.dtype, "x"), _xdtype(x), rows, cols,
+                                   _dev(q, torch.uint8, "q", (rows, cols)),
+                                   _dev(scales, torch.float32, "scales"), _stream(stream)),
+           "moe_quantize_1x128")
+    return q, scales
+
+
+def moe_quantize_128x128(w: torch.Tensor, q: torch.Tensor = None, scales: torch.Tensor = None,
+                         stream=None):
+    """128x128-block E4M3 quantisation of w [mats, rows, cols] (or [rows, cols]) float32."""
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    mats, rows, cols = w3.shape
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        sshape = (rows // 128, cols // 128) if squeeze else (mats, rows // 128, cols // 128)
+        scales = torch.empty(sshape, dtype=torch.float32, device=w.device)
+    _check(_lib.moe_quantize_128x128(_dev(w, torch.float32, "w"), mats, rows, cols,
+                                     _dev(q, torch.uint8, "q", w.shape),
+                                     _dev(scales, torch.float32, "scales"), _stream(stream)),
+           "moe_quantize_128x128")
+    return q, scales
+
+
+def moe_route(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+              scores: torch.Tensor = None, topk_idx: torch.Tensor = None,
+              topk_gate: torch.Tensor = None, counts: torch.Tensor = None, stream=None):
+    """Router: -> (scores [T,N_r] f32, topk_idx [T,k] i32, topk_gate [T,k] f32, counts i32)."""
+    T = x.shape[0]
+    N, k = cfg.n_routed, cfg.top_k
+    dev = x.device
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev) if scores is None else scores
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
+    counts = torch.empty((N,), dtype=torch.int32, device=dev) if counts is None else counts
+    _check(_lib.moe_route(ctypes.byref(cfg), _dev(x, x.dtype, "x", (T, cfg.hidden)), _xdtype(x), T,
+                          _dev(w_router, torch.float32, "w_router", (N, cfg.hidden)),
+                          _dev(bias, torch.float32, "bias", (N,)),
+                          _dev(scores, torch.float32, "scores", (T, N)),
+                          _dev(topk_idx, torch.int32, "topk_idx", (T, k)),
+                          _dev(topk_gate, torch.float32, "topk_gate", (T, k)),
+                          _dev(counts, torch.int32, "counts", (N,)), _stream(stream)),
+           "moe_route")
+    return scores, topk_idx, topk_gate, counts
+
+
+def moe_permute(cfg: moe_config, topk_idx: torch.Tensor, offsets: torch.Tensor = None,
+                row_token: torch.Tensor = None, row_of: torch.Tensor = None, stream=None):
+    """-> (offsets [N_r+1], row_token [T*k], row_of [T,k]), all int32."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    offsets = torch.empty((cfg.n_routed + 1,), dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_token = torch.empty((T * k,), dtype=torch.int32, device=dev) if row_token is None else row_token
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
+    _check(_lib.moe_permute(ctypes.byref(cfg), T, _dev(topk_idx, torch.int32, "topk_idx", (T, cfg.top_k)),
+                            _dev(offsets, torch.int32, "offsets", (cfg.n_routed + 1,)),
+                            _dev(row_token, torch.int32, "row_token", (T * k,)),
+                            _dev(row_of, torch.int32, "row_of", (T, k)), _stream(stream)),
+           "moe_permute")
+    return offsets, row_token, row_of
+
+
+def moe_grouped_ffn_workspace_bytes(cfg: moe_config, n_experts: int, n_rows: int) -> int:
+    return int(_lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(cfg), n_experts, n_rows))
+
+
+def moe_grouped_ffn_fp8(cfg: moe_config, n_experts: int, n_rows: int, xq: torch.Tensor,
+                        xs: torch.Tensor, row_token: Optional[torch.Tensor], offsets: torch.Tensor,
+                        w1, w1s, w3, w3s, w2, w2s, y: torch.Tensor = None,
+                        ws: torch.Tensor = None, y_dtype=torch.bfloat16, stream=None):
+    """Grouped SwiGLU FP8 experts -> y [n_rows, H] (bf16 or f32)."""
+    H, I = cfg.hidden, cfg.inter
+    n_tokens = xq.shape[0]
+    dev = xq.device
+    if y is None:
+        y = torch.empty((n_rows, H), dtype=y_dtype, device=dev)
+    yt = MOE_BF16 if y.dtype == torch.bfloat16 else MOE_F32
+    need = moe_grouped_ffn_workspace_bytes(cfg, n_experts, n_rows)
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    rt = ctypes.c_void_p(0) if row_token is None else _dev(row_token, torch.int32, "row_token")
+    E = n_experts
+    _check(_lib.moe_grouped_ffn_fp8(
+        ctypes.byref(cfg), E, n_rows, n_tokens, _dev(xq, torch.uint8, "xq", (n_tokens, H)),
+        _dev(xs, torch.float32, "xs", (n_tokens, H // 128)), rt,
+        _dev(offsets, torch.int32, "offsets", (E + 1,)),
+        _dev(w1, torch.uint8, "w1", (E, I, H)), _dev(w1s, torch.float32, "w1s", (E, I // 128, H // 128)),
+        _dev(w3, torch.uint8, "w3", (E, I, H)), _dev(w3s, torch.float32, "w3s", (E, I // 128, H // 128)),
+        _dev(w2, torch.uint8, "w2", (E, H, I)), _dev(w2s, torch.float32, "w2s", (E, H // 128, I // 128)),
+        _dev(y, y.dtype, "y", (n_rows, H)), yt, _dev(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "moe_grouped_ffn_fp8")
+    return y
+
+
+def moe_combine(cfg: moe_config, y_rows: torch.Tensor, row_of: torch.Tensor,
+                topk_gate: torch.Tensor, y_shared: Optional[torch.Tensor],
+                out: torch.Tensor = None, stream=None):
+    """-> out [T, H] bf16 = sum of shared outputs + sum_j gate_j * y_rows[row_of[:, j]]."""
+    T, k = row_of.shape
+    H = cfg.hidden
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=row_of.device) if out is None else out
+    yt = MOE_BF16 if y_rows.dtype == torch.bfloat16 else MOE_F32
+    ys = ctypes.c_void_p(0)
+    if y_shared is not None:
+        ys = _dev(y_shared, y_rows.dtype, "y_shared")
+        if y_shared.numel() != cfg.n_shared * T * H:
+            raise MoEError("y_shared must hold [N_s, T, H]")
+    _check(_lib.moe_combine(ctypes.byref(cfg), T, _dev(y_rows, y_rows.dtype, "y_rows"), yt,
+                            _dev(row_of, torch.int32, "row_of", (T, cfg.top_k)),
+                            _dev(topk_gate, torch.float32, "topk_gate", (T, cfg.top_k)), ys,
+                            _dev(out, torch.bfloat16, "out", (T, H)), _stream(stream)),
+           "moe_combine")
+    return out
+
+
+def moe_update_bias(cfg: moe_config, T: int, counts: torch.Tensor, bias: torch.Tensor, stream=None):
+    """In-place sign-based update of bias [N_r] from counts [N_r]."""
+    _check(_lib.moe_update_bias(ctypes.byref(cfg), T,
+                                _dev(counts, torch.int32, "counts", (cfg.n_routed,)),
+                                _dev(bias, torch.float32, "bias", (cfg.n_routed,)), _stream(stream)),
+           "moe_update_bias")
+    return bias
+
+
+from .layer import MoELayer  # noqa: E402,F401

@@ -1,0 +1,94 @@
+// Shared helpers of the gfx950 MoE library: status plumbing, config validation,
+// E4M3 encoding, bf16 conversion and wavefront reductions. gfx950 only (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_fp8.h"
+
+#define MOE_TRY_HIP(expr)                         \
+  do {                                            \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kTile = 128;            // 1x128 activation tiles, 128x128 weight blocks
+constexpr float kE4M3Max = 448.0f;
+constexpr int kMaxRouted = 512;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxGroups = 64;
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline moe_status launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Host-side validation of a layer configuration (the ranges stated in moe_fp8.h).
+inline moe_status check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_NULL;
+  if (c->hidden <= 0 || c->hidden % kTile) return MOE_ERR_SHAPE;
+  if (c->inter <= 0 || c->inter % kTile) return MOE_ERR_SHAPE;
+  if (c->n_routed < 1 || c->n_routed > kMaxRouted) return MOE_ERR_SHAPE;
+  if (c->n_shared < 0) return MOE_ERR_SHAPE;
+  if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_routed) return MOE_ERR_SHAPE;
+  if (c->n_group < 1 || c->n_group > kMaxGroups || c->n_routed % c->n_group) return MOE_ERR_SHAPE;
+  if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_ERR_SHAPE;
+  const int gsz = c->n_routed / c->n_group;
+  if (c->group_topn < 1 || c->group_topn > gsz) return MOE_ERR_SHAPE;
+  if ((int64_t)c->topk_group * gsz < c->top_k) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------------
+
+// OCP E4M3FN encoding of a float32 value: nearest finite value, ties to even mantissa,
+// saturating at +-448, sign kept (-0 -> 0x80), NaN -> 0x7F | sign. Exact: the scalings
+// are by powers of two and rintf rounds half to even.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fabsf(v);
+  if (!(a == a)) return sign | 0x7Fu;
+  a = fminf(a, kE4M3Max);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8 (8 is the smallest normal)
+  } else {
+    const int e = __builtin_amdgcn_frexp_expf(a) - 1;   // a in [2^e, 2^(e+1)), e in [-6, 8]
+    const float m = __builtin_rintf(__builtin_ldexpf(a, 3 - e));  // in [8, 16]
+    code = ((uint32_t)(e + 7) << 3) + ((uint32_t)m - 8u);        // 16 carries into e+1
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// float32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Scale of a quantisation group from its amax: fl32(amax / 448), or 1 when that is 0.
+__device__ __forceinline__ float group_scale(float amax) {
+  const float s = __fdiv_rn(amax, kE4M3Max);
+  return s == 0.0f ? 1.0f : s;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
+  return v;
+}
+
+}  // namespace moe

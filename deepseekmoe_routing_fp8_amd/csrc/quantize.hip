@@ -1,0 +1,134 @@
+// Fine-grained E4M3 quantisers: 1x128 activation tiles and 128x128 weight blocks
+// (lpnh.cn guide section 3 [fp8] block; 2kiu.com digest section 4.3; zhihu infra
+// commentary, per-tile 1x128 / per-group 128x128). HBM-bound: one read of the
+// source, one write of codes and scales.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// 16 lanes per 128-element tile, 8 consecutive elements per lane; a 256-thread block
+// covers 16 tiles. Tiles are numbered row-major over [rows, cols/128].
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_1x128_kernel(const T* __restrict__ x,
+                                                             int64_t n_tiles, int64_t tiles_per_row,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ scales) {
+  const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool live = tile < n_tiles;
+  const int64_t base = tile * kTile + sub * 8;  // tiles are contiguous in row-major order
+  float v[8];
+  if (live) {
+    if constexpr (sizeof(T) == 2) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(x + base);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(x + base);
+      const float4 b = *reinterpret_cast<const float4*>(x + base + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = group_max<16>(amax);
+  const float s = group_scale(amax);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= e4m3_encode(__fdiv_rn(v[i], s)) << (8 * i);
+    hi |= e4m3_encode(__fdiv_rn(v[i + 4], s)) << (8 * i);
+  }
+  if (live) {
+    *reinterpret_cast<uint2*>(q + base) = make_uint2(lo, hi);
+    if (sub == 0) scales[tile] = s;
+  }
+  (void)tiles_per_row;
+}
+
+// One 256-thread block per 128x128 block. Thread t covers rows (t/32) + 8*i, i < 16,
+// and the 4 columns 4*(t%32)..+3 of each: 64 values kept in registers.
+__global__ __launch_bounds__(256) void quantize_128x128_kernel(const float* __restrict__ w,
+                                                               int64_t rows, int64_t cols,
+                                                               uint8_t* __restrict__ q,
+                                                               float* __restrict__ scales) {
+  const int64_t br = rows / kTile, bc = cols / kTile;
+  const int64_t blk = blockIdx.x;             // (mat, block row, block col) flattened
+  const int64_t mat = blk / (br * bc);
+  const int64_t rem = blk % (br * bc);
+  const int64_t r0 = (rem / bc) * kTile, c0 = (rem % bc) * kTile;
+  const float* src = w + mat * rows * cols;
+  uint8_t* dst = q + mat * rows * cols;
+  const int t = threadIdx.x;
+  const int rsub = t >> 5, col = (t & 31) * 4;
+  float4 v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + rsub + 8 * i;
+    v[i] = *reinterpret_cast<const float4*>(src + r * cols + c0 + col);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  }
+  amax = group_max<kWave>(amax);
+  __shared__ float red[4];
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = group_scale(amax);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + rsub + 8 * i;
+    const uint32_t packed = e4m3_encode(__fdiv_rn(v[i].x, s)) | (e4m3_encode(__fdiv_rn(v[i].y, s)) << 8) |
+                            (e4m3_encode(__fdiv_rn(v[i].z, s)) << 16) |
+                            (e4m3_encode(__fdiv_rn(v[i].w, s)) << 24);
+    *reinterpret_cast<uint32_t*>(dst + r * cols + c0 + col) = packed;
+  }
+  if (t == 0) scales[blk] = s;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_quantize_1x128(const void* x, moe_dtype xt, int64_t rows, int64_t cols,
+                                         uint8_t* q, float* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % kTile) return MOE_ERR_SHAPE;
+  if (xt != MOE_F32 && xt != MOE_BF16) return MOE_ERR_DTYPE;
+  const int64_t tiles = rows * (cols / kTile);
+  if (tiles == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_NULL;
+  const int64_t blocks = (tiles + 15) / 16;
+  if (blocks > 0x7fffffff) return MOE_ERR_SHAPE;
+  if (xt == MOE_BF16)
+    hipLaunchKernelGGL(quantize_1x128_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0,
+                       as_stream(stream), static_cast<const uint16_t*>(x), tiles, cols / kTile, q,
+                       scales);
+  else
+    hipLaunchKernelGGL(quantize_1x128_kernel<float>, dim3((unsigned)blocks), dim3(256), 0,
+                       as_stream(stream), static_cast<const float*>(x), tiles, cols / kTile, q,
+                       scales);
+  return launch_status();
+}
+
+extern "C" moe_status moe_quantize_128x128(const float* w, int64_t mats, int64_t rows, int64_t cols,
+                                           uint8_t* q, float* scales, void* stream) {
+  if (mats < 0 || rows <= 0 || cols <= 0 || rows % kTile || cols % kTile) return MOE_ERR_SHAPE;
+  const int64_t blocks = mats * (rows / kTile) * (cols / kTile);
+  if (blocks == 0) return MOE_OK;
+  if (!w || !q || !scales) return MOE_ERR_NULL;
+  if (blocks > 0x7fffffff) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(quantize_128x128_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     as_stream(stream), w, rows, cols, q, scales);
+  return launch_status();
+}

@@ -1,0 +1,150 @@
+"""MoE layer driver: device-resident weights and buffers, and the call sequence of one
+forward step through the C entry points (quantise -> route -> permute -> routed experts
+-> shared experts -> combine -> bias update).
+
+Weights arrive as float32 host arrays (from the seeded generators) and are quantised to
+E4M3 128x128 blocks on the device by moe_quantize_128x128.
+"""
+from __future__ import annotations
+
+from typing import Callable, Iterable, Optional
+
+import numpy as np
+import torch
+
+from . import (make_config, moe_combine, moe_grouped_ffn_fp8, moe_grouped_ffn_workspace_bytes,
+               moe_permute, moe_quantize_1x128, moe_quantize_128x128, moe_route, moe_update_bias)
+
+
+class MoELayer:
+    """One DeepSeekMoE layer on one GPU.
+
+    ``cfg`` carries the synth.MoEConfig field names. Call ``load_weights`` (or
+    ``load_from_synth``) once, then ``forward(x)`` per step.
+    """
+
+    def __init__(self, cfg, device="cuda", y_dtype=torch.bfloat16):
+        self.cfg = cfg
+        self.c = make_config(cfg)
+        self.dev = torch.device(device)
+        self.y_dtype = y_dtype
+        H, I, E, S = cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts, cfg.num_shared_experts
+        u8, f32 = torch.uint8, torch.float32
+        d = self.dev
+        self.w1 = torch.empty((E, I, H), dtype=u8, device=d)
+        self.w3 = torch.empty((E, I, H), dtype=u8, device=d)
+        self.w2 = torch.empty((E, H, I), dtype=u8, device=d)
+        self.w1s = torch.empty((E, I // 128, H // 128), dtype=f32, device=d)
+        self.w3s = torch.empty((E, I // 128, H // 128), dtype=f32, device=d)
+        self.w2s = torch.empty((E, H // 128, I // 128), dtype=f32, device=d)
+        Sx = max(S, 1)
+        self.sw1 = torch.empty((Sx, I, H), dtype=u8, device=d)
+        self.sw3 = torch.empty((Sx, I, H), dtype=u8, device=d)
+        self.sw2 = torch.empty((Sx, H, I), dtype=u8, device=d)
+        self.sw1s = torch.empty((Sx, I // 128, H // 128), dtype=f32, device=d)
+        self.sw3s = torch.empty((Sx, I // 128, H // 128), dtype=f32, device=d)
+        self.sw2s = torch.empty((Sx, H // 128, I // 128), dtype=f32, device=d)
+        self.w_router = None
+        self.bias = None
+        self._T = None
+
+    # -- weights -------------------------------------------------------------------
+    def _quant_into(self, w: np.ndarray, q: torch.Tensor, s: torch.Tensor):
+        t = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(self.dev)
+        moe_quantize_128x128(t, q, s)
+
+    def load_weights(self, w_router: np.ndarray, bias: np.ndarray,
+                     routed: Callable[[Callable], None], shared: Callable[[Callable], None]):
+        """``routed(put)`` / ``shared(put)`` call put(e, (w1, w3, w2)) for every expert."""
+        self.w_router = torch.from_numpy(np.ascontiguousarray(w_router, np.float32)).to(self.dev)
+        self.bias = torch.from_numpy(np.ascontiguousarray(bias, np.float32)).to(self.dev)
+
+        def put_routed(e, w):
+            self._quant_into(w[0], self.w1[e], self.w1s[e])
+            self._quant_into(w[1], self.w3[e], self.w3s[e])
+            self._quant_into(w[2], self.w2[e], self.w2s[e])
+
+        def put_shared(e, w):
+            self._quant_into(w[0], self.sw1[e], self.sw1s[e])
+            self._quant_into(w[1], self.sw3[e], self.sw3s[e])
+            self._quant_into(w[2], self.sw2[e], self.sw2s[e])
+        routed(put_routed)
+        shared(put_shared)
+        torch.cuda.synchronize(self.dev)
+
+    def load_from_synth(self, threads: Optional[int] = None):
+        import synth
+        cfg = self.cfg
+        self.load_weights(
+            synth.router_weight(cfg), synth.expert_bias(cfg),
+            lambda put: synth.map_experts(cfg, put, range(cfg.num_experts), threads=threads),
+            lambda put: synth.map_experts(cfg, put, range(cfg.num_shared_experts), shared=True,
+                                          threads=threads))
+
+    # -- buffers -------------------------------------------------------------------
+    def _buffers(self, T: int):
+        if self._T == T:
+            return
+        cfg, d = self.cfg, self.dev
+        H, I, N, k, S = (cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts,
+                         cfg.num_experts_per_tok, cfg.num_shared_experts)
+        i32, f32 = torch.int32, torch.float32
+        self.xq = torch.empty((T, H), dtype=torch.uint8, device=d)
+        self.xs = torch.empty((T, H // 128), dtype=f32, device=d)
+        self.scores = torch.empty((T, N), dtype=f32, device=d)
+        self.topk_idx = torch.empty((T, k), dtype=i32, device=d)
+        self.topk_gate = torch.empty((T, k), dtype=f32, device=d)
+        self.counts = torch.empty((N,), dtype=i32, device=d)
+        self.offsets = torch.empty((N + 1,), dtype=i32, device=d)
+        self.row_token = torch.empty((T * k,), dtype=i32, device=d)
+        self.row_of = torch.empty((T, k), dtype=i32, device=d)
+        self.y_rows = torch.empty((T * k, H), dtype=self.y_dtype, device=d)
+        self.ws = torch.empty((max(moe_grouped_ffn_workspace_bytes(self.c, N, T * k), 1),),
+                              dtype=torch.uint8, device=d)
+        if S > 0:
+            self.y_shared = torch.empty((S * T, H), dtype=self.y_dtype, device=d)
+            self.sh_offsets = torch.arange(0, S + 1, dtype=i32, device=d) * T
+            self.ws_sh = torch.empty((max(moe_grouped_ffn_workspace_bytes(self.c, S, S * T), 1),),
+                                     dtype=torch.uint8, device=d)
+        else:
+            self.y_shared = None
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+        self._T = T
+
+    # -- forward -------------------------------------------------------------------
+    STAGES = ("quantize", "route", "permute", "ffn_routed", "ffn_shared", "combine", "bias_update")
+
+    def forward(self, x: torch.Tensor, update_bias: bool = True, events=None) -> torch.Tensor:
+        """One layer step on x [T, H] (bf16 or f32, on the device). Returns out [T, H] bf16
+        (a buffer reused by the next call); routing results stay in the attributes.
+
+        ``events``: optional list of len(STAGES)+1 torch.cuda.Event recorded on the current
+        stream around each stage (per-stage timing without extra synchronisation)."""
+        cfg, c = self.cfg, self.c
+        T = x.shape[0]
+        self._buffers(T)
+        k, N, S = cfg.num_experts_per_tok, cfg.num_experts, cfg.num_shared_experts
+        mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        mark(0)
+        moe_quantize_1x128(x, self.xq, self.xs)
+        mark(1)
+        moe_route(c, x, self.w_router, self.bias, self.scores, self.topk_idx, self.topk_gate,
+                  self.counts)
+        mark(2)
+        moe_permute(c, self.topk_idx, self.offsets, self.row_token, self.row_of)
+        mark(3)
+        moe_grouped_ffn_fp8(c, N, T * k, self.xq, self.xs, self.row_token, self.offsets,
+                            self.w1, self.w1s, self.w3, self.w3s, self.w2, self.w2s,
+                            y=self.y_rows, ws=self.ws)
+        mark(4)
+        if S > 0:
+            moe_grouped_ffn_fp8(c, S, S * T, self.xq, self.xs, None, self.sh_offsets,
+                                self.sw1[:S], self.sw1s[:S], self.sw3[:S], self.sw3s[:S],
+                                self.sw2[:S], self.sw2s[:S], y=self.y_shared, ws=self.ws_sh)
+        mark(5)
+        moe_combine(c, self.y_rows, self.row_of, self.topk_gate, self.y_shared, self.out)
+        mark(6)
+        if update_bias:
+            moe_update_bias(c, T, self.counts, self.bias)
+        mark(7)
+        return self.out

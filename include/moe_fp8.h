@@ -1,0 +1,207 @@
+/*
+ * moe_fp8.h — C ABI of a gfx950 (MI355X) library for the forward pass of a
+ * DeepSeek-V3-style DeepSeekMoE layer: sigmoid routing with the auxiliary-loss-free
+ * expert bias and an optional group limit, FP8 E4M3 SwiGLU experts with 1x128
+ * activation tiles and 128x128 weight blocks, a shared expert, the weighted combine
+ * and the sign-based bias update.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [guide]  lpnh.cn, "从技术报告到可跑配置：DeepSeek-V3 的 MoE、MLA、FP8 到底难在哪",
+ *            section 3 (model JSON; [fp8] block: e4m3, tile_wise_1x128 inputs,
+ *            block_wise_128x128 weights, moe_gating kept out of FP8).
+ *   [digest] 2kiu.com DeepSeek-V3 technical-report digest: section 3.2 (sigmoid
+ *            affinities, bias used only for ranking, normalised gates, load bincount,
+ *            +-gamma update after each step), section 3.4 (group/node-limited routing,
+ *            no token dropping), section 4.3 (per-group scales, higher-precision
+ *            accumulation), section 5.2 (batch-level load statistics).
+ *   [zhihu]  zhihu infra commentary on the report, training part (E4M3 throughout,
+ *            1x128 / 128x128 groups, GEMM by partial-sum promotion; SwiGLU recompute).
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers owned by the caller unless stated otherwise; a
+ *     pointer to an array with zero elements may be NULL. The
+ *     library never allocates, frees or keeps a pointer; scratch memory comes in
+ *     through an explicit workspace whose size is queried first.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is
+ *     enqueued asynchronously; results are valid after the caller synchronises.
+ *   - Arguments are validated on the host before any launch. A failed check returns
+ *     the status and launches nothing. A failed launch returns MOE_ERR_HIP. No C++
+ *     exception crosses this interface.
+ *   - All matrices are row-major and densely packed. E4M3 codes are OCP E4M3FN bytes
+ *     (the bit patterns of torch.float8_e4m3fn). bf16 is passed as uint16 bits.
+ *   - NaN/Inf in inputs give unspecified values but never out-of-bounds accesses.
+ *   - No global mutable state: calls are thread-safe; results are deterministic.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  MOE_ERR_SHAPE = 2,       /* a size or config field is out of range            */
+  MOE_ERR_DTYPE = 3,       /* unsupported dtype for this argument               */
+  MOE_ERR_UNSUPPORTED = 4, /* valid request this build does not implement       */
+  MOE_ERR_HIP = 5,         /* a HIP launch or runtime call failed               */
+  MOE_ERR_WORKSPACE = 6    /* workspace NULL or smaller than the queried size   */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer configuration; field meanings follow the model JSON of [guide] section 3. */
+typedef struct moe_config {
+  int32_t hidden;          /* H: hidden size, multiple of 128                         */
+  int32_t inter;           /* I: expert intermediate size, multiple of 128            */
+  int32_t n_routed;        /* N_r: routed experts, 1..512                             */
+  int32_t n_shared;        /* N_s: shared experts, >= 0                               */
+  int32_t top_k;           /* k: experts per token, 1..16                             */
+  int32_t n_group;         /* G: expert groups (1 disables the limit); N_r % G == 0,
+                              G <= 64                                                 */
+  int32_t topk_group;      /* G_k: groups a token may use, 1..G; k <= G_k * N_r / G   */
+  int32_t group_topn;      /* affinities summed into a group score, 1..N_r/G          */
+  float routed_scaling;    /* rho: gates of a token sum to rho ([guide] routed_scaling_factor) */
+  float bias_gamma;        /* gamma: bias step ([guide] expert_bias_update_rate)      */
+} moe_config;
+
+/* Human-readable text for a status (static storage). */
+const char* moe_status_string(moe_status s);
+
+/*
+ * moe_quantize_1x128 — fine-grained activation quantisation ([guide] section 3
+ * tile_wise_1x128, e4m3; [digest] section 4.3; [zhihu] per-tile 1x128).
+ * For each row and each 128-wide column tile: amax = max|x|, scale s = fl32(amax/448)
+ * (s = 1 when that is 0), code = E4M3 round-to-nearest-even of fl32(x/s), saturating
+ * at +-448, sign kept.
+ *   x       [rows, cols] of dtype xt (MOE_F32 or MOE_BF16)
+ *   q       [rows, cols] uint8 E4M3 codes (output)
+ *   scales  [rows, cols/128] float (output)
+ * Errors: NULL pointers; rows < 0; cols <= 0 or cols % 128 != 0.
+ */
+moe_status moe_quantize_1x128(const void* x, moe_dtype xt, int64_t rows, int64_t cols,
+                              uint8_t* q, float* scales, void* stream);
+
+/*
+ * moe_quantize_128x128 — weight-block quantisation, the preparation of the GEMM
+ * weight operand ([guide] section 3 block_wise_128x128; [zhihu] per-group 128x128).
+ * Same rule as moe_quantize_1x128 over each 128x128 block of each matrix.
+ *   w       [mats, rows, cols] float
+ *   q       [mats, rows, cols] uint8 (output)
+ *   scales  [mats, rows/128, cols/128] float (output)
+ * Errors: NULL pointers; mats < 0; rows or cols not positive multiples of 128.
+ */
+moe_status moe_quantize_128x128(const float* w, int64_t mats, int64_t rows, int64_t cols,
+                                uint8_t* q, float* scales, void* stream);
+
+/*
+ * moe_route — router ([digest] section 3.2 pseudocode and prose; section 3.4 group
+ * limit; [guide] section 3 norm_topk_prob, routed_scaling_factor, gating kept in
+ * high precision).
+ *   s = sigmoid(x . W_r^T) from unquantised x, FP32 products with FP32 partial sums
+ *   over 128-wide K chunks promoted into an FP64 accumulator; ranking score s + b.
+ *   With G > 1: a group's score is the FP32 sum of its group_topn best ranking scores;
+ *   the G_k best groups are kept (ties: lower group index); experts elsewhere are
+ *   excluded. Top-k by ranking score, descending, ties to the lower expert index.
+ *   Gates: s[idx_j] / sum_j s[idx_j] * rho (unbiased s). counts[e] = selections of e.
+ *   x          [T, H] of dtype xt
+ *   w_router   [N_r, H] float
+ *   bias       [N_r] float
+ *   scores     [T, N_r] float, output: the sigmoid affinities s
+ *   topk_idx   [T, k] int32, output, slot order = descending ranking score
+ *   topk_gate  [T, k] float, output
+ *   counts     [N_r] int32, output (overwritten, not accumulated)
+ * Errors: NULL pointers; invalid config (see moe_config); T < 0.
+ */
+moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype xt, int64_t T,
+                     const float* w_router, const float* bias, float* scores,
+                     int32_t* topk_idx, float* topk_gate, int32_t* counts, void* stream);
+
+/*
+ * moe_permute — group the (token, slot) pairs by expert ([digest] section 3.2: the
+ * output sums ffn_expert[idx[j]] over the slots; section 3.4: every token reaches its
+ * experts, none is dropped). The expert histogram is recomputed from topk_idx, so the
+ * outputs are consistent with it by construction.
+ *   offsets   [N_r+1] int32, output: exclusive prefix sum of the per-expert loads
+ *   row_token [T*k] int32, output: token of each permuted row; rows of expert e are
+ *             offsets[e]..offsets[e+1]-1, in ascending token order
+ *   row_of    [T, k] int32, output: permuted row of (t, j)
+ * topk_idx entries outside [0, N_r) are skipped (their row_of is -1). Experts must be
+ * distinct within a token (moe_route guarantees it); otherwise rows are unspecified
+ * but all accesses stay in bounds.
+ * Errors: NULL pointers; invalid config; T < 0 or T*k >= 2^31.
+ */
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,
+                       int32_t* offsets, int32_t* row_token, int32_t* row_of, void* stream);
+
+/* Workspace bytes moe_grouped_ffn_fp8 needs for n_experts experts and n_rows rows. */
+size_t moe_grouped_ffn_workspace_bytes(const moe_config* cfg, int32_t n_experts,
+                                       int64_t n_rows);
+
+/*
+ * moe_grouped_ffn_fp8 — SwiGLU experts as FP8 grouped GEMMs ([zhihu] training part:
+ * E4M3 operands with 1x128 / 128x128 scales, GEMM by partial-sum promotion; SwiGLU;
+ * [digest] section 4.3: higher-precision accumulation; [guide] section 3: all GEMM
+ * inputs 1x128-quantised).
+ * For permuted row r of expert e (offsets[e] <= r < offsets[e+1]) with token
+ * t = row_token[r] (or t = r - offsets[e] when row_token is NULL):
+ *   G = DQ(xq_t) . DQ(W1_e)^T, U = DQ(xq_t) . DQ(W3_e)^T — every 128-wide K chunk is one
+ *   FP8 MFMA partial sum, promoted into an FP32 accumulator times a_scale * w_scale;
+ *   h = fl32(silu(G) * U), re-quantised 1x128 (rule of moe_quantize_1x128);
+ *   y_r = DQ(hq) . DQ(W2_e)^T with the same promotion, stored as yt.
+ *   n_tokens  rows of xq / xs
+ *   xq, xs    [n_tokens, H] uint8, [n_tokens, H/128] float
+ *   row_token [n_rows] int32 or NULL
+ *   offsets   [n_experts+1] int32, device; read on the device (no host sync).
+ *             Values are clamped to [0, n_rows].
+ *   w1, w3    [n_experts, I, H] uint8; w1s, w3s [n_experts, I/128, H/128] float
+ *   w2        [n_experts, H, I] uint8; w2s [n_experts, H/128, I/128] float
+ *   y         [n_rows, H] of dtype yt (MOE_BF16 or MOE_F32), output
+ *   ws        workspace of at least moe_grouped_ffn_workspace_bytes(...) bytes
+ * Rows whose token index falls outside [0, n_tokens) produce y = 0.
+ * Errors: NULL pointers; invalid config; n_experts < 1; n_rows < 0; workspace.
+ */
+moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
+                               int64_t n_tokens, const uint8_t* xq, const float* xs,
+                               const int32_t* row_token, const int32_t* offsets,
+                               const uint8_t* w1, const float* w1s, const uint8_t* w3,
+                               const float* w3s, const uint8_t* w2, const float* w2s,
+                               void* y, moe_dtype yt, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * moe_combine — weighted combine ([digest] section 3.2: y = sum_j gate[j] *
+ * ffn_expert[idx[j]](h)) plus the shared experts with gate 1 ([guide] section 3
+ * num_shared_experts). FP32 accumulation in fixed order (shared experts 0..N_s-1,
+ * then slots 0..k-1), rounded once to bf16.
+ *   y_rows    [T*k, H] of dtype yt
+ *   row_of    [T, k] int32 (entries < 0 are skipped)
+ *   topk_gate [T, k] float
+ *   y_shared  [N_s, T, H] of dtype yt, or NULL when N_s == 0
+ *   out       [T, H] bf16 bits, output
+ * Errors: NULL pointers; invalid config; T < 0.
+ */
+moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, moe_dtype yt,
+                       const int32_t* row_of, const float* topk_gate, const void* y_shared,
+                       uint16_t* out, void* stream);
+
+/*
+ * moe_update_bias — sign-based bias update ([digest] section 3.2 pseudocode: after a
+ * step, experts above the mean load T*k/N_r lose gamma, those below gain gamma;
+ * section 5.2: statistics over the whole batch). Dead band 0: the comparison is the
+ * integer T*k vs N_r*counts[e]; equal load leaves b unchanged. One FP32 rounding.
+ *   counts [N_r] int32 (from moe_route over the same T tokens); bias [N_r] float, in/out
+ * Errors: NULL pointers; invalid config; T < 0.
+ */
+moe_status moe_update_bias(const moe_config* cfg, int64_t T, const int32_t* counts,
+                           float* bias, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H */

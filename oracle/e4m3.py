@@ -12,6 +12,9 @@ and negative values that round to zero give 0x80), NaN -> 0x7F with its sign.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 E4M3_MAX = 448.0
@@ -44,25 +47,36 @@ def decode(codes: np.ndarray) -> np.ndarray:
     return _TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
-def encode(v: np.ndarray, chunk: int = 1 << 22) -> np.ndarray:
-    """float32 values -> E4M3 codes (uint8): nearest value, ties to even, saturating."""
+def _encode_chunk(x: np.ndarray) -> np.ndarray:
+    pos = _POS
+    nan = np.isnan(x)
+    neg = np.signbit(x)
+    a = np.abs(x.astype(np.float64))
+    a = np.where(nan, 0.0, np.minimum(a, E4M3_MAX))
+    hi = np.searchsorted(pos, a, side="left")      # pos[hi-1] < a <= pos[hi]
+    hi = np.minimum(hi, 126)
+    lo_i = np.maximum(hi - 1, 0)
+    d_lo = a - pos[lo_i]
+    d_hi = pos[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo_i).astype(np.uint8)
+    code = np.where(nan, np.uint8(0x7F), code)
+    return code | (neg.astype(np.uint8) << 7)
+
+
+def encode(v: np.ndarray, chunk: int = 1 << 20) -> np.ndarray:
+    """float32 values -> E4M3 codes (uint8): nearest value, ties to even, saturating.
+
+    Large inputs are cut into chunks encoded on a thread pool (same arithmetic)."""
     v = np.asarray(v, dtype=np.float32)
     flat = v.reshape(-1)
+    if flat.size <= chunk:
+        return _encode_chunk(flat).reshape(v.shape)
     out = np.empty(flat.shape, dtype=np.uint8)
-    pos = _POS
-    for lo in range(0, flat.size, chunk):
-        x = flat[lo:lo + chunk]
-        nan = np.isnan(x)
-        neg = np.signbit(x)
-        a = np.abs(x.astype(np.float64))
-        a = np.where(nan, 0.0, np.minimum(a, E4M3_MAX))
-        hi = np.searchsorted(pos, a, side="left")      # pos[hi-1] < a <= pos[hi]
-        hi = np.minimum(hi, 126)
-        lo_i = np.maximum(hi - 1, 0)
-        d_lo = a - pos[lo_i]
-        d_hi = pos[hi] - a
-        pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-        code = np.where(pick_hi, hi, lo_i).astype(np.uint8)
-        code = np.where(nan, np.uint8(0x7F), code)
-        out[lo:lo + chunk] = code | (neg.astype(np.uint8) << 7)
+    starts = range(0, flat.size, chunk)
+
+    def job(lo):
+        out[lo:lo + chunk] = _encode_chunk(flat[lo:lo + chunk])
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(job, starts))
     return out.reshape(v.shape)

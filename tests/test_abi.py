@@ -1,0 +1,104 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/moe_fp8.h declares, and rejects invalid arguments on the host with the
+documented status codes before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
+
+
+def _lib():
+    from deepseekmoe_routing_fp8_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    import deepseekmoe_routing_fp8_amd as m
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_six_calls():
+    names = _declared()
+    for n in ("moe_quantize_1x128", "moe_route", "moe_permute", "moe_grouped_ffn_fp8",
+              "moe_combine", "moe_update_bias"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    m = _lib()
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(m.ENTRY_POINTS)
+
+
+def test_status_strings():
+    m = _lib()
+    for s in range(7):
+        assert m._lib.moe_status_string(s).decode()
+    assert m._lib.moe_status_string(0).decode() == "ok"
+
+
+def _cfg(m, **kw):
+    base = dict(hidden=256, inter=128, n_routed=16, n_shared=1, top_k=4, n_group=1, topk_group=1,
+                group_topn=2, routed_scaling=2.5, bias_gamma=0.001)
+    base.update(kw)
+    return m.moe_config(*[base[f] for f, _ in m.moe_config._fields_])
+
+
+def test_host_validation_status_codes():
+    m = _lib()
+    L = m._lib
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: every call below fails validation first
+    # NULL pointers
+    assert L.moe_quantize_1x128(None, 0, 4, 128, fake, fake, None) == 1
+    # shapes
+    assert L.moe_quantize_1x128(fake, 0, 4, 100, fake, fake, None) == 2
+    assert L.moe_quantize_1x128(fake, 0, -1, 128, fake, fake, None) == 2
+    assert L.moe_quantize_128x128(fake, 1, 128, 130, fake, fake, None) == 2
+    # dtype
+    assert L.moe_quantize_1x128(fake, 7, 4, 128, fake, fake, None) == 3
+    # config checks
+    bad = [dict(hidden=200), dict(inter=0), dict(n_routed=0), dict(n_routed=1024),
+           dict(top_k=17), dict(top_k=20, n_routed=16), dict(n_group=3),
+           dict(n_group=4, topk_group=5), dict(n_group=4, topk_group=1, top_k=5),
+           dict(n_group=4, topk_group=2, group_topn=5)]
+    for b in bad:
+        c = _cfg(m, **b)
+        assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, None) == 2, b
+        assert L.moe_permute(ctypes.byref(c), 4, fake, fake, fake, fake, None) == 2, b
+    c = _cfg(m)
+    assert L.moe_route(None, fake, 1, 4, fake, fake, fake, fake, fake, fake, None) == 1
+    assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, None, fake, fake, fake, fake, None) == 1
+    assert L.moe_route(ctypes.byref(c), fake, 5, 4, fake, fake, fake, fake, fake, fake, None) == 3
+    assert L.moe_permute(ctypes.byref(c), -2, fake, fake, fake, fake, None) == 2
+    assert L.moe_combine(ctypes.byref(c), 4, fake, 1, fake, fake, None, fake, None) == 1  # N_s=1 needs y_shared
+    assert L.moe_update_bias(ctypes.byref(c), 4, None, fake, None) == 1
+    # grouped FFN: workspace too small, bad expert count
+    need = L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 16, 256)
+    assert need > 256 * 128
+    args = [fake] * 10
+    assert L.moe_grouped_ffn_fp8(ctypes.byref(c), 16, 256, 64, fake, fake, None, *args[:7], fake, 1,
+                                 fake, need - 1, None) == 6
+    assert L.moe_grouped_ffn_fp8(ctypes.byref(c), 0, 256, 64, fake, fake, None, *args[:7], fake, 1,
+                                 fake, need, None) == 2
+    assert L.moe_grouped_ffn_fp8(ctypes.byref(c), 16, 256, 64, fake, fake, None, *args[:7], fake, 9,
+                                 fake, need, None) == 3
+
+
+def test_workspace_size_grows_with_rows():
+    m = _lib()
+    c = _cfg(m)
+    a = m._lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 16, 256)
+    b = m._lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 16, 4096)
+    assert 0 < a < b
+    assert m._lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 0, 256) == 0

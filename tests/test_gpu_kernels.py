@@ -1,0 +1,386 @@
+"""Per-kernel parity of the HIP library against the CPU oracle (needs an MI355X).
+
+Both sides see identical seeded inputs; integer and byte outputs must match exactly,
+floating outputs within the stated tolerances.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import e4m3
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import deepseekmoe_routing_fp8_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+DEV = "cuda"
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------------------
+# 1x128 activation quantisation: bit-exact codes and scales
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("reduced", None), ("v3_prefill", None),
+                                       ("v3_prefill", 1), ("reduced", 3)])
+def test_quantize_1x128_matches_oracle(lib, name, rows):
+    cfg = synth.PRESETS[name]
+    if rows is not None:
+        cfg = cfg.with_tokens(rows)
+    say(f"quantize_1x128 {name} T={cfg.tokens} H={cfg.hidden_size} {cfg.x_dtype}")
+    x = synth.hidden_states(cfg)
+    xd = dev(x, torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32)
+    q, s = lib.moe_quantize_1x128(xd)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_1x128(x)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(q), rq)
+
+
+def _edge_tiles():
+    rng = np.random.default_rng(7)
+    tiles = []
+    tiles.append(np.zeros(128))                                   # all zero -> s = 1
+    t = rng.standard_normal(128); t[5] = 1e4; tiles.append(t)      # one outlier
+    tiles.append(np.full(128, -3.25))                              # constant
+    t = np.zeros(128); t[0] = -0.0; t[1] = 1e-30; tiles.append(t)  # -0 and a tiny value
+    tiles.append(rng.standard_normal(128) * 1e-38)                 # float32 subnormal range
+    tiles.append(rng.standard_normal(128) * 5e37)                  # near float32 max
+    # amax 448 -> s = 1 exactly: every E4M3 value, midpoint and +-1 ulp neighbour
+    pos = e4m3.finite_values()
+    mids = (pos[:-1] + pos[1:]) / 2
+    pts = np.concatenate([pos, mids]).astype(np.float32)
+    nb = np.concatenate([pts, np.nextafter(pts, np.float32(0)), np.nextafter(pts, np.float32(1e9))])
+    nb = np.concatenate([nb, -nb])
+    nb = nb[np.abs(nb) <= 448]
+    n = (len(nb) + 126) // 127
+    for i in range(n):
+        chunk = nb[i * 127:(i + 1) * 127]
+        t = np.zeros(128, np.float32)
+        t[:len(chunk)] = chunk
+        t[127] = 448.0
+        tiles.append(t)
+    return np.stack(tiles).astype(np.float32)
+
+
+def test_quantize_1x128_edge_cases(lib):
+    x = _edge_tiles()
+    say(f"quantize_1x128 edge tiles {x.shape}")
+    q, s = lib.moe_quantize_1x128(dev(x))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_1x128(x)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(q), rq)
+
+
+def test_quantize_1x128_bf16_sweep(lib):
+    """Every finite bf16 bit pattern, 127 per tile next to a fixed amax of 448."""
+    b = np.arange(0, 1 << 16, dtype=np.uint32)
+    v = (b << 16).view(np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) <= 448)]
+    n = (len(v) + 126) // 127
+    x = np.zeros((n, 128), np.float32)
+    x[:, 127] = 448.0
+    flat = x[:, :127].reshape(-1)
+    flat[:len(v)] = v
+    x[:, :127] = flat.reshape(n, 127)
+    say(f"quantize_1x128 bf16 sweep {x.shape}")
+    xd = dev(x, torch.bfloat16)
+    q, s = lib.moe_quantize_1x128(xd)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_1x128(x)
+    assert np.all(host(s) == 1.0) and np.array_equal(host(s), rs)
+    assert np.array_equal(host(q), rq)
+
+
+# ---------------------------------------------------------------------------------------
+# 128x128 weight quantisation: bit-exact
+# ---------------------------------------------------------------------------------------
+def test_quantize_128x128_matches_oracle(lib):
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((3, 256, 384)) * np.exp2(rng.integers(-8, 8, (3, 1, 1)))).astype(np.float32)
+    w[1, :128, :128] = 0.0
+    w[2, 5, 300] = 1e6
+    say("quantize_128x128 random [3,256,384]")
+    q, s = lib.moe_quantize_128x128(dev(w))
+    torch.cuda.synchronize()
+    for i in range(3):
+        rq, rs = oracle.quantize_128x128(w[i])
+        assert np.array_equal(host(s[i]).view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(host(q[i]), rq)
+    cfg = synth.PRESETS["reduced"]
+    for e in (0, 63):
+        say(f"quantize_128x128 reduced expert {e}")
+        for wm in synth.routed_expert_weights(cfg, e):
+            q, s = lib.moe_quantize_128x128(dev(wm))
+            torch.cuda.synchronize()
+            rq, rs = oracle.quantize_128x128(wm)
+            assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+            assert np.array_equal(host(q), rq)
+
+
+# ---------------------------------------------------------------------------------------
+# Router
+# ---------------------------------------------------------------------------------------
+NEAR_TIE = 1e-6
+
+
+def check_routing(cfg, x, wr, b, g_scores, g_idx, g_gate, g_counts):
+    """Indices exact outside declared near-ties; gates and scores within tolerance."""
+    r = oracle.route(x, wr, b, cfg.num_experts_per_tok, cfg.n_group, cfg.topk_group,
+                     cfg.group_score_topn, cfg.routed_scaling_factor)
+    assert np.max(np.abs(g_scores - r["s"])) < 5e-7
+    tie = (r["kth_gap"] < NEAR_TIE) | (r["group_gap"] < NEAR_TIE)
+    diff = np.any(g_idx != r["idx"], axis=1)
+    assert not np.any(diff & ~tie), f"routing differs outside near-ties at tokens {np.where(diff & ~tie)[0][:10]}"
+    # the GPU's own selections: distinct experts, counts consistent
+    k = cfg.num_experts_per_tok
+    assert np.all(np.sort(g_idx, 1)[:, 1:] != np.sort(g_idx, 1)[:, :-1]) if k > 1 else True
+    assert np.array_equal(g_counts, np.bincount(g_idx.ravel(), minlength=cfg.num_experts))
+    if not np.any(tie):
+        assert np.array_equal(g_counts, r["counts"])
+    # gates from the oracle's affinities at the GPU's selection
+    rf = oracle.route(x, wr, b, k, cfg.n_group, cfg.topk_group, cfg.group_score_topn,
+                      cfg.routed_scaling_factor, force_idx=g_idx)
+    assert np.allclose(g_gate, rf["gate"], rtol=2e-6, atol=0)
+    assert np.allclose(g_gate.sum(1), cfg.routed_scaling_factor, rtol=1e-5)
+    return int(tie.sum())
+
+
+@pytest.mark.parametrize("name", ["tiny", "reduced", "v3_prefill", "v3_decode"])
+def test_route_matches_oracle(lib, name):
+    cfg = synth.PRESETS[name]
+    say(f"route {name} T={cfg.tokens}")
+    x = synth.hidden_states(cfg)
+    wr = synth.router_weight(cfg)
+    b = synth.expert_bias(cfg)
+    xd = dev(x, torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32)
+    c = lib.make_config(cfg)
+    s, idx, gate, counts = lib.moe_route(c, xd, dev(wr), dev(b))
+    torch.cuda.synchronize()
+    nt = check_routing(cfg, x, wr, b, host(s), host(idx), host(gate), host(counts))
+    say(f"  near-tie tokens: {nt}")
+
+
+def test_route_group_limit_binds_with_bias(lib):
+    """V3 grouping with a large random bias, so that the group choice decides."""
+    cfg = synth.PRESETS["v3_decode"]
+    x = synth.hidden_states(cfg)
+    wr = synth.router_weight(cfg)
+    b = np.random.default_rng(9).uniform(-0.3, 0.3, cfg.num_experts).astype(np.float32)
+    say("route v3_decode shapes, large bias")
+    c = lib.make_config(cfg)
+    s, idx, gate, counts = lib.moe_route(c, dev(x, torch.bfloat16), dev(wr), dev(b))
+    torch.cuda.synchronize()
+    check_routing(cfg, x, wr, b, host(s), host(idx), host(gate), host(counts))
+    free = oracle.route(x, wr, b, 8)
+    assert np.any(free["idx"] != host(idx))  # the limit changed some selection
+
+
+def test_route_general_shapes(lib):
+    """Groups of uneven use, k = 1, N_r not a multiple of 64, fp32 input."""
+    import dataclasses
+    base = synth.PRESETS["tiny"]
+    for kw in [dict(num_experts=48, num_experts_per_tok=1, n_group=4, topk_group=2, group_score_topn=3),
+               dict(num_experts=96, num_experts_per_tok=5, n_group=6, topk_group=3),
+               dict(num_experts=16, num_experts_per_tok=16),
+               dict(tokens=1), dict(tokens=130, num_experts=32, num_experts_per_tok=3)]:
+        cfg = dataclasses.replace(base, **kw)
+        say(f"route general {kw}")
+        x = synth.hidden_states(cfg)
+        rng = np.random.default_rng(11)
+        wr = (rng.standard_normal((cfg.num_experts, cfg.hidden_size)) / 16).astype(np.float32)
+        b = rng.uniform(-0.05, 0.05, cfg.num_experts).astype(np.float32)
+        s, idx, gate, counts = lib.moe_route(lib.make_config(cfg), dev(x), dev(wr), dev(b))
+        torch.cuda.synchronize()
+        check_routing(cfg, x, wr, b, host(s), host(idx), host(gate), host(counts))
+
+
+# ---------------------------------------------------------------------------------------
+# Permutation: bit-exact
+# ---------------------------------------------------------------------------------------
+def _idx(rng, T, N, k, skew=None):
+    if skew is None:
+        return np.stack([rng.permutation(N)[:k] for _ in range(T)]).astype(np.int32)
+    p = np.arange(1, N + 1) ** (-skew)
+    p /= p.sum()
+    return np.stack([rng.choice(N, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,N,k,skew", [(64, 16, 4, None), (4096, 256, 8, None),
+                                        (16384, 256, 8, 1.1), (1, 256, 8, None), (1500, 512, 16, None),
+                                        (3000, 64, 6, 2.0)])
+def test_permute_matches_oracle(lib, T, N, k, skew):
+    import dataclasses
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], num_experts=N, num_experts_per_tok=k, tokens=T)
+    rng = np.random.default_rng(T + N)
+    idx = _idx(rng, T, N, k, skew)
+    say(f"permute T={T} N={N} k={k} skew={skew}")
+    off, rt, ro = lib.moe_permute(lib.make_config(cfg), dev(idx))
+    torch.cuda.synchronize()
+    r_off, r_rt, r_ro = oracle.permute(idx, N)
+    assert np.array_equal(host(off), r_off)
+    assert np.array_equal(host(rt), r_rt)
+    assert np.array_equal(host(ro), r_ro)
+
+
+def test_permute_collapse_and_empty(lib):
+    import dataclasses
+    cfg = dataclasses.replace(synth.PRESETS["v3_prefill"], tokens=2048)
+    c = lib.make_config(cfg)
+    idx = np.tile(np.arange(200, 208, dtype=np.int32), (2048, 1))
+    say("permute collapse")
+    off, rt, ro = lib.moe_permute(c, dev(idx))
+    torch.cuda.synchronize()
+    r = oracle.permute(idx, 256)
+    assert np.array_equal(host(off), r[0]) and np.array_equal(host(rt), r[1]) and np.array_equal(host(ro), r[2])
+    say("permute T=0")
+    off, rt, ro = lib.moe_permute(c, torch.empty((0, 8), dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert np.all(host(off) == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# Grouped FP8 SwiGLU experts
+# ---------------------------------------------------------------------------------------
+def _rand_codes(rng, shape):
+    c = rng.integers(0, 0x7F, shape).astype(np.uint8)
+    return c | (rng.integers(0, 2, shape).astype(np.uint8) << 7)
+
+
+def _expert_set(rng, E, H, I):
+    f = lambda n, k: rng.uniform(0.5, 2.0, (E, n // 128, k // 128)).astype(np.float32) / 448
+    w1 = _rand_codes(rng, (E, I, H)); w3 = _rand_codes(rng, (E, I, H)); w2 = _rand_codes(rng, (E, H, I))
+    return w1, f(I, H), w3, f(I, H), w2, f(H, I)
+
+
+def _relerr(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+@pytest.mark.parametrize("H,I,E,loads,identity", [
+    (256, 128, 4, [0, 17, 64, 3], False),
+    (512, 256, 3, [193, 1, 400], False),          # several M tiles, tiny tail
+    (384, 256, 2, [16, 33], True),                 # identity token map, H % 256 == 128
+    (1024, 512, 5, [130, 0, 0, 7, 250], False),
+])
+def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity):
+    import dataclasses
+    rng = np.random.default_rng(H + I + E)
+    rows = int(sum(loads))
+    T = rows if identity else 300
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], hidden_size=H, moe_intermediate_size=I,
+                              num_experts=max(E, 4), num_experts_per_tok=1, tokens=T)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    xq, xs = oracle.quantize_1x128(x)
+    offsets = np.concatenate([[0], np.cumsum(loads)]).astype(np.int32)
+    row_token = (np.arange(rows) - np.repeat(offsets[:-1], loads)).astype(np.int32) if identity \
+        else rng.integers(0, T, rows).astype(np.int32)
+    w = _expert_set(rng, E, H, I)
+    say(f"grouped_ffn H={H} I={I} E={E} loads={loads} identity={identity}")
+    y = lib.moe_grouped_ffn_fp8(lib.make_config(cfg), E, rows, dev(xq), dev(xs),
+                                None if identity else dev(row_token), dev(offsets),
+                                *[dev(a) for a in w], y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y = host(y)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi == lo:
+            continue
+        toks = row_token[lo:hi]
+        ref = oracle.expert_ffn(xq[toks], xs[toks], w[0][e], w[1][e], w[2][e], w[3][e], w[4][e], w[5][e])[0]
+        err = _relerr(y[lo:hi], ref)
+        assert err < 5e-3, (e, err)
+
+
+def test_grouped_ffn_bf16_output_and_bad_tokens(lib):
+    import dataclasses
+    rng = np.random.default_rng(21)
+    H, I, E = 256, 256, 2
+    loads = [40, 24]
+    rows, T = 64, 50
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], hidden_size=H, moe_intermediate_size=I,
+                              num_experts=4, num_experts_per_tok=1, tokens=T)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    xq, xs = oracle.quantize_1x128(x)
+    offsets = np.array([0, 40, 64], np.int32)
+    row_token = rng.integers(0, T, rows).astype(np.int32)
+    row_token[3] = -1
+    row_token[50] = T + 5        # out of range -> y row is 0
+    w = _expert_set(rng, E, H, I)
+    say("grouped_ffn bf16 output, invalid tokens")
+    y = lib.moe_grouped_ffn_fp8(lib.make_config(cfg), E, rows, dev(xq), dev(xs), dev(row_token),
+                                dev(offsets), *[dev(a) for a in w], y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    assert np.all(y[3] == 0) and np.all(y[50] == 0)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        ok = [r for r in range(lo, hi) if 0 <= row_token[r] < T]
+        ref = oracle.expert_ffn(xq[row_token[ok]], xs[row_token[ok]], *[a[e] for a in w])[0]
+        assert _relerr(y[ok], ref) < 5e-3
+
+
+# ---------------------------------------------------------------------------------------
+# Combine and bias update
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,k,S", [(64, 256, 4, 1), (300, 2048, 6, 2), (17, 7168, 8, 1), (5, 128, 2, 0)])
+def test_combine_matches_oracle(lib, T, H, k, S):
+    import dataclasses
+    rng = np.random.default_rng(T * H)
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], hidden_size=H, num_experts=max(16, k),
+                              num_experts_per_tok=k, num_shared_experts=S, tokens=T)
+    y_rows = synth.to_bf16_exact(rng.standard_normal((T * k, H)).astype(np.float32))
+    y_sh = synth.to_bf16_exact(rng.standard_normal((max(S, 1) * T, H)).astype(np.float32))
+    row_of = rng.permutation(T * k).reshape(T, k).astype(np.int32)
+    gate = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    say(f"combine T={T} H={H} k={k} S={S}")
+    out = lib.moe_combine(lib.make_config(cfg), dev(y_rows, torch.bfloat16), dev(row_of), dev(gate),
+                          dev(y_sh[:S * T], torch.bfloat16) if S else None)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = oracle.combine(y_rows, row_of, gate, [y_sh[s * T:(s + 1) * T] for s in range(S)])
+    # one bf16 rounding of an FP32 sum: |err| <= 2^-8 |ref| + FP32 summation error
+    bound = np.abs(ref) * 2.0 ** -8 + 1e-5 * (np.abs(y_rows[row_of]).sum(1) + S * 4)
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_update_bias_matches_oracle_over_trajectory(lib):
+    cfg = synth.PRESETS["v3_prefill"]
+    c = lib.make_config(cfg)
+    N, T, k = cfg.num_experts, cfg.tokens, cfg.num_experts_per_tok
+    rng = np.random.default_rng(12)
+    b = np.zeros(N, np.float32)
+    bd = dev(b)
+    say("update_bias 100 steps")
+    for step in range(100):
+        counts = rng.multinomial(T * k, np.ones(N) / N).astype(np.int32)
+        counts[step % N] = T * k // N   # exactly on target -> unchanged
+        lib.moe_update_bias(c, T, dev(counts), bd)
+        b = oracle.bias_update(b, counts, T, k, cfg.expert_bias_update_rate)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(bd).view(np.uint32), b.view(np.uint32))

@@ -1,0 +1,169 @@
+"""Whole-layer parity of the HIP path against the CPU oracle (needs an MI355X).
+
+tiny and reduced run in full. The DeepSeek-V3 shapes (prefill T=4096, decode T=128,
+skewed T=16384) run the full layer on the GPU in the configuration the benchmark times;
+the oracle checks the routing of every token and the outputs of a few sampled tokens
+(it quantises only the experts those tokens reach, and those codes must equal the GPU's).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+NEAR_TIE = 1e-6
+TOL = 5e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def relerr(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def q3(w):
+    w1, w3, w2 = w
+    return (*oracle.quantize_128x128(w1), *oracle.quantize_128x128(w3), *oracle.quantize_128x128(w2))
+
+
+def x_device(cfg, x):
+    dt = torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32
+    return torch.from_numpy(x).to(dt).cuda()
+
+
+def routing_ties(r):
+    return (r["kth_gap"] < NEAR_TIE) | (r["group_gap"] < NEAR_TIE)
+
+
+@pytest.mark.parametrize("name", ["tiny", "reduced"])
+def test_layer_matches_oracle(name):
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    cfg = synth.PRESETS[name]
+    say(f"layer {name}: loading weights")
+    layer = MoELayer(cfg)
+    layer.load_from_synth()
+    x = synth.hidden_states(cfg)
+    b0 = synth.expert_bias(cfg)
+    say(f"layer {name}: forward T={cfg.tokens}")
+    out = layer.forward(x_device(cfg, x)).float().cpu().numpy()
+    g_idx = layer.topk_idx.cpu().numpy()
+    g_counts = layer.counts.cpu().numpy()
+    g_bias = layer.bias.cpu().numpy()
+    wr = synth.router_weight(cfg)
+    routed = [q3(synth.routed_expert_weights(cfg, e)) for e in range(cfg.num_experts)]
+    shared = [q3(synth.shared_expert_weights(cfg, s)) for s in range(cfg.num_shared_experts)]
+    # the device-quantised weights equal the oracle's codes and scales
+    for e in (0, cfg.num_experts - 1):
+        assert np.array_equal(layer.w1[e].cpu().numpy(), routed[e][0])
+        assert np.array_equal(layer.w2s[e].cpu().numpy(), routed[e][5])
+    ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s])
+    r = ref["route"]
+    tie = routing_ties(r)
+    diff = np.any(g_idx != r["idx"], axis=1)
+    assert not np.any(diff & ~tie)
+    if np.any(diff):   # re-evaluate the oracle on the GPU's (equally valid) near-tie choice
+        ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s],
+                                   force_idx=g_idx)
+    err = relerr(out, ref["out"])
+    say(f"layer {name}: normwise error {err:.3e}, near-tie tokens {int(tie.sum())}")
+    assert err < TOL
+    assert np.array_equal(g_counts, ref["route"]["counts"])
+    nb = oracle.bias_update(b0, g_counts, cfg.tokens, cfg.num_experts_per_tok, cfg.expert_bias_update_rate)
+    assert np.array_equal(g_bias.view(np.uint32), nb.view(np.uint32))
+
+
+@pytest.fixture(scope="module")
+def v3_layer():
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    cfg = synth.PRESETS["v3_prefill"]
+    say("V3 layer: generating and quantising 257 experts on the device")
+    layer = MoELayer(cfg)
+    layer.load_from_synth()
+    return layer
+
+
+def _sampled_parity(layer, cfg, x, bias, n_sample, seed):
+    wr = synth.router_weight(cfg)
+    g_idx = layer.topk_idx.cpu().numpy()
+    # routing of every token
+    r = oracle.route(x, wr, bias, cfg.num_experts_per_tok, cfg.n_group, cfg.topk_group,
+                     cfg.group_score_topn, cfg.routed_scaling_factor)
+    tie = routing_ties(r)
+    diff = np.any(g_idx != r["idx"], axis=1)
+    assert not np.any(diff & ~tie), np.where(diff & ~tie)[0][:10]
+    say(f"  routing ok, near-tie tokens {int(tie.sum())}")
+    # outputs of sampled tokens
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(cfg.tokens, n_sample, replace=False))
+    experts = sorted(set(g_idx[toks].ravel().tolist()))
+    say(f"  sampled tokens {toks.tolist()} reach {len(experts)} experts")
+    cache = {}
+
+    def put(e, w):
+        cache[e] = q3(w)
+    synth.map_experts(cfg, put, experts)
+    for e in experts[:3]:
+        assert np.array_equal(layer.w3[e].cpu().numpy(), cache[e][2])
+        assert np.array_equal(layer.w1s[e].cpu().numpy(), cache[e][1])
+    sh = {}
+    synth.map_experts(cfg, lambda s, w: sh.__setitem__(s, q3(w)), range(cfg.num_shared_experts), shared=True)
+    ref = oracle.layer_forward(x[toks], wr, bias, cfg, lambda e: cache[e], lambda s: sh[s],
+                               force_idx=g_idx[toks])
+    out = layer.out[torch.from_numpy(toks).cuda()].float().cpu().numpy()
+    err = relerr(out, ref["out"])
+    say(f"  sampled normwise error {err:.3e}")
+    assert err < TOL
+    return g_idx
+
+
+@pytest.mark.timeout(900)
+def test_v3_prefill_sampled(v3_layer):
+    cfg = synth.PRESETS["v3_prefill"]
+    x = synth.hidden_states(cfg)
+    bias = v3_layer.bias.cpu().numpy()
+    say("V3 prefill forward T=4096")
+    v3_layer.forward(x_device(cfg, x), update_bias=False)
+    torch.cuda.synchronize()
+    g_idx = _sampled_parity(v3_layer, cfg, x, bias, 3, 0)
+    assert np.array_equal(v3_layer.counts.cpu().numpy(), np.bincount(g_idx.ravel(), minlength=256))
+
+
+@pytest.mark.timeout(900)
+def test_v3_decode_sampled(v3_layer):
+    cfg = synth.PRESETS["v3_decode"]
+    x = synth.hidden_states(cfg)
+    bias = v3_layer.bias.cpu().numpy()
+    say("V3 decode forward T=128")
+    v3_layer.forward(x_device(cfg, x), update_bias=False)
+    torch.cuda.synchronize()
+    _sampled_parity(v3_layer, cfg, x, bias, 3, 1)
+
+
+@pytest.mark.timeout(900)
+def test_v3_skewed_steps(v3_layer):
+    """Forward + bias update on the skewed workload: every step's bias follows the
+    oracle's update of the GPU's own counts, and its routing matches the oracle."""
+    cfg = synth.PRESETS["v3_skewed"]
+    b = np.zeros(cfg.num_experts, np.float32)
+    v3_layer.bias.copy_(torch.from_numpy(b))
+    loads = []
+    for step in range(3):
+        x = synth.hidden_states(cfg, step=step)
+        say(f"V3 skewed step {step} T={cfg.tokens}")
+        v3_layer.forward(x_device(cfg, x), update_bias=True)
+        torch.cuda.synchronize()
+        counts = v3_layer.counts.cpu().numpy()
+        loads.append(counts.max() / counts.mean())
+        if step == 0:
+            _sampled_parity(v3_layer, cfg, x, b, 2, 2)
+        b = oracle.bias_update(b, counts, cfg.tokens, cfg.num_experts_per_tok, cfg.expert_bias_update_rate)
+        assert np.array_equal(v3_layer.bias.cpu().numpy().view(np.uint32), b.view(np.uint32))
+    say(f"  max/mean load per step: {[round(float(v), 2) for v in loads]}")
+    assert loads[0] > 2.0   # the clustered input is skewed
