@@ -99,7 +99,8 @@ def main():
     import torch
 
     import synth
-    from deepseekmoe_routing_fp8_amd import build as b
+    import __graft_entry__
+    b = __graft_entry__._builder()
     if not os.path.exists(b.LIB):
         b.build()
     from deepseekmoe_routing_fp8_amd import MoELayer

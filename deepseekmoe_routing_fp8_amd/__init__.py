@@ -19,13 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m deepseekmoe_routing_fp8_amd.build`")
+        f"{LIB_PATH} is missing: build it with `python deepseekmoe_routing_fp8_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_F32, MOE_BF16 = 0, 1
 
 ENTRY_POINTS = (
-    "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_route",
+    "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_pack_fp8_weights",
+    "moe_route",
     "moe_permute", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8", "moe_combine",
     "moe_update_bias",
 )
@@ -55,6 +56,7 @@ _sig = {
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_quantize_1x128": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "moe_quantize_128x128": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "moe_pack_fp8_weights": ([_P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
     "moe_route": ([_CFG, _P, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_permute": ([_CFG, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_grouped_ffn_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
@@ -134,6 +136,18 @@ def moe_quantize_128x128(w: torch.Tensor, q: torch.Tensor = None, scales: torch.
                                      _dev(scales, torch.float32, "scales"), _stream(stream)),
            "moe_quantize_128x128")
     return q, scales
+
+
+def moe_pack_fp8_weights(q: torch.Tensor, packed: torch.Tensor = None, stream=None):
+    """Re-lay E4M3 codes q [mats, rows, cols] (or [rows, cols]) into the fragment-packed
+    layout the grouped FFN reads; returns a tensor of q's shape holding the packed bytes."""
+    q3 = q.unsqueeze(0) if q.dim() == 2 else q
+    mats, rows, cols = q3.shape
+    packed = torch.empty_like(q) if packed is None else packed
+    _check(_lib.moe_pack_fp8_weights(_dev(q, torch.uint8, "q"), mats, rows, cols,
+                                     _dev(packed, torch.uint8, "packed", q.shape), _stream(stream)),
+           "moe_pack_fp8_weights")
+    return packed
 
 
 def moe_route(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,

@@ -1,6 +1,7 @@
 """Build libmoe_fp8.so (gfx950 only) from csrc/*.hip with hipcc.
 
-Usage: python -m deepseekmoe_routing_fp8_amd.build   (or build() from Python).
+Usage: python deepseekmoe_routing_fp8_amd/build.py  (run as a file: importing the
+package would first load the library this builds).
 Objects go to <repo>/_build/, the library next to this file.
 """
 from __future__ import annotations

@@ -29,12 +29,12 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kMT = 192;              // max rows of one expert per tile (multiple of 16)
 constexpr int kNTS = kMT / 16;        // MFMA column tiles per M tile
 constexpr int kThreads = 512;         // 8 waves
 constexpr int kWaves = kThreads / kWave;
-constexpr int kPD = 2;                // weight prefetch distance, in K chunks
 constexpr int kMaxExperts = 1024;
 
 struct Tile {
@@ -94,305 +94,301 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
   }
 }
 
-// Stage the 128-byte K chunk `kc` of the tile's activation rows: each thread moves 16 B.
-// LDS row r holds its 8 segments at positions seg ^ (r & 7).
-struct ActStage {
-  uint4 v[(kMT * 8 + kThreads - 1) / kThreads];
-  float s[(kMT + kThreads - 1) / kThreads];
-};
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding and for all LDS operations (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0070; }
 
-__device__ __forceinline__ void act_load(ActStage& st, const uint8_t* __restrict__ aq,
-                                         const float* __restrict__ as, const int* tok_s,
-                                         int rows, int64_t K, int kc, int tid) {
-  const int64_t nkc = K / kTile;
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(st.v) / sizeof(uint4)); ++i) {
-    const int slot = tid + i * kThreads;
-    const int r = slot >> 3, seg = slot & 7;
-    st.v[i] = make_uint4(0, 0, 0, 0);
-    if (r < rows) {
-      const int t = tok_s[r];
-      if (t >= 0) st.v[i] = *reinterpret_cast<const uint4*>(aq + (int64_t)t * K + kc * kTile + seg * 16);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(st.s) / sizeof(float)); ++i) {
-    const int r = tid + i * kThreads;
-    st.s[i] = 0.0f;
-    if (r < rows) {
-      const int t = tok_s[r];
-      if (t >= 0) st.s[i] = as[(int64_t)t * nkc + kc];
-    }
-  }
+// Wait for this wave's operations of one pipeline stage, then a workgroup barrier. The
+// empty asm statements keep the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void act_store(const ActStage& st, uint8_t* act, float* scl, int rows,
-                                          int tid) {
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(st.v) / sizeof(uint4)); ++i) {
-    const int slot = tid + i * kThreads;
-    const int r = slot >> 3, seg = slot & 7;
-    if (r < ((rows + 15) & ~15))
-      *reinterpret_cast<uint4*>(act + r * kTile + ((seg ^ (r & 7)) << 4)) = st.v[i];
-  }
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(st.s) / sizeof(float)); ++i) {
-    const int r = tid + i * kThreads;
-    if (r < kMT) scl[r] = st.s[i];
-  }
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copies: lane i of the wave writes its bytes at lds + i * size.
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave, 4, 0, 0);
 }
 
-// Column operand (16 tokens x 128 K) for lane `lane` from the staged chunk: lane group g
-// holds K bytes [16g, 16g+16) and [64+16g, 64+16g+16) of token (lane % 16) — the same
-// K map as the weight operand, which is all the MFMA needs.
+constexpr int kStages = 3;                          // 1 chunk consumed + 2 in flight
+constexpr int kActBytes = kMT * kTile;              // one K chunk of the tile's rows
+constexpr int kDma = kActBytes / (16 * kThreads);   // 16-byte copies per thread per chunk
+static_assert(kActBytes % (16 * kThreads) == 0, "tile rows must split evenly over threads");
+constexpr int kVmPerChunk = 4 + kDma + 1;           // weight loads + row copies + scale copy
+constexpr int kStageBytes = kActBytes + kThreads * 4;
+constexpr int kXcds = 8;
+constexpr int kMaxChunks = 128;                     // K <= 16384
+
+// Column operand (16 tokens x 128 K) for lane `lane` from a staged chunk. Lane group g
+// holds K bytes [16g, 16g+16) and [64+16g, 64+16g+16) of token (lane % 16); the weight
+// operand uses the same K map, which is all the MFMA needs. Row r keeps its eight
+// 16-byte segments at positions seg ^ (r & 7), so eight consecutive rows hit all banks.
 __device__ __forceinline__ v8i act_frag(const uint8_t* act, int ts, int lane) {
   const int r = ts * 16 + (lane & 15), g = lane >> 4;
-  const uint4 lo = *reinterpret_cast<const uint4*>(act + r * kTile + ((g ^ (r & 7)) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(act + r * kTile + (((g + 4) ^ (r & 7)) << 4));
-  return join(lo, hi);
+  const v4i lo = *reinterpret_cast<const v4i*>(act + r * kTile + ((g ^ (r & 7)) << 4));
+  const v4i hi = *reinterpret_cast<const v4i*>(act + r * kTile + (((g + 4) ^ (r & 7)) << 4));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Row operand: 16 weight rows x 128 K starting at `w` (row stride K), same K map.
-__device__ __forceinline__ void w_load(const uint8_t* __restrict__ w, int64_t K, int kc, int lane,
-                                       uint4& lo, uint4& hi) {
-  const uint8_t* p = w + (int64_t)(lane & 15) * K + kc * kTile + (lane >> 4) * 16;
-  const v4u a = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-  const v4u b = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p + 64));
-  lo = make_uint4(a[0], a[1], a[2], a[3]);
-  hi = make_uint4(b[0], b[1], b[2], b[3]);
+// Row operand fragment: 16 weight rows x 128 K from the packed layout, where lane l's
+// two 16-byte pieces sit at l*16 and 1024 + l*16 of the fragment's 2 KB (same K map as
+// the column operand).
+constexpr int kFragBytes = 16 * kTile;
+__device__ __forceinline__ v8i w_load(const uint8_t* p) {
+  const v4i lo = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+  const v4i hi = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p + kFragBytes / 2));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ void load_tokens(int* tok_s, const Tile& tl, const int32_t* row_token,
-                                            int64_t n_tokens, int tid) {
+struct FfnArgs {
+  const Tile* tiles;
+  const int32_t* n_tiles;
+  const uint8_t* aq;     // activation codes: xq (phase 1) or hq (phase 2)
+  const float* as;       // their 1x128 scales
+  int64_t n_tokens;
+  const int32_t* row_token;
+  const uint8_t* wa;     // W1 (phase 1) or W2 (phase 2)
+  const float* wsa;
+  const uint8_t* wb;     // W3 (phase 1)
+  const float* wsb;
+  int H, I, n_nb;
+  uint8_t* hq;           // phase 1 outputs
+  float* hs;
+  void* y;               // phase 2 output
+};
+
+// ------------------------------------------------------------------------------------
+// One grouped-FFN GEMM phase over tiles (expert, M tile) x n-blocks.
+//   PHASE 1: h = silu(x W1^T) * (x W3^T) on 128 intermediate columns per workgroup
+//            (wave w: 16 rows of W1 and the same 16 of W3), re-quantised 1x128.
+//   PHASE 2: y = hq W2^T on 256 output features per workgroup (wave w: 32 rows of W2).
+// Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD
+// so the tile's activation rows are fetched into that XCD's L2 once.
+// Pipeline: stage c of the K loop holds chunk c's weight fragments in registers and its
+// activation rows + scales in LDS (copied directly, no register staging). Every lane
+// issues the same kVmPerChunk vector-memory operations per chunk, in chunk order, so
+// "chunk c has landed" is the immediate wait vmcnt <= kVmPerChunk * (chunks issued
+// after c); one barrier per chunk then publishes it to all waves.
+// ------------------------------------------------------------------------------------
+template <int PHASE, typename YT>
+__global__ __launch_bounds__(kThreads) void ffn_kernel(const FfnArgs a) {
+  // one array per pipeline stage: the chunk's activation rows, then one scale per row
+  __shared__ __attribute__((aligned(16))) uint8_t stg0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stg1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stg2[kStageBytes];
+  __shared__ int tok_s[kMT];
+  __shared__ float red[PHASE == 1 ? kWaves : 1][kMT];
+  __shared__ float wsc[kWaves][2][kMaxChunks];   // this wave's weight-block scales per K chunk
+
+  const int L = blockIdx.x;
+  const int xcd = L % kXcds, slot = L / kXcds;
+  const int tile = (slot / a.n_nb) * kXcds + xcd;
+  const int nb = slot % a.n_nb;
+  if (tile >= *a.n_tiles) return;
+  const Tile tl = a.tiles[tile];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = PHASE == 1 ? a.H : a.I;
+  const int nkc = K / kTile;
+  const int nts = (tl.mlen + 15) >> 4;
+
+  // source row of every tile row: a token (phase 1) or a permuted row (phase 2)
   for (int r = tid; r < kMT; r += kThreads) {
     int t = -1;
     if (r < tl.mlen) {
-      const int64_t v = row_token ? (int64_t)row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
-      t = (v >= 0 && v < n_tokens) ? (int)v : -1;
+      if (PHASE == 1) {
+        const int64_t v = a.row_token ? (int64_t)a.row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
+        t = (v >= 0 && v < a.n_tokens) ? (int)v : -1;
+      } else {
+        t = tl.m0 + r;
+      }
     }
     tok_s[r] = t;
   }
-}
-
-// ------------------------------------------------------------------------------------
-// Phase 1: h = silu(x W1^T) * (x W3^T), re-quantised 1x128 into hq / hs.
-// grid = (max tiles, I / 128); block = 512.
-// ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void ffn_gate_up_kernel(
-    const Tile* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    const uint8_t* __restrict__ xq, const float* __restrict__ xs, int64_t n_tokens,
-    const int32_t* __restrict__ row_token, const uint8_t* __restrict__ w1,
-    const float* __restrict__ w1s, const uint8_t* __restrict__ w3, const float* __restrict__ w3s,
-    int H, int I, uint8_t* __restrict__ hq, float* __restrict__ hs) {
-  __shared__ __attribute__((aligned(16))) uint8_t act[2][kMT * kTile];
-  __shared__ float ascl[2][kMT];
-  __shared__ int tok_s[kMT];
-  __shared__ float red[kWaves][kMT];
-  if ((int)blockIdx.x >= *n_tiles) return;
-  const Tile tl = tiles[blockIdx.x];
-  const int nb = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nts = (tl.mlen + 15) >> 4;
-  const int nkc = H / kTile;
-  const int64_t wrow = (int64_t)nb * kTile + wave * 16;  // first W1/W3 row of this wave
-  const uint8_t* wg = w1 + ((int64_t)tl.e * I + wrow) * H;
-  const uint8_t* wu = w3 + ((int64_t)tl.e * I + wrow) * H;
-  const float* sg_row = w1s + ((int64_t)tl.e * (I / kTile) + nb) * nkc;
-  const float* su_row = w3s + ((int64_t)tl.e * (I / kTile) + nb) * nkc;
-
-  load_tokens(tok_s, tl, row_token, n_tokens, tid);
   __syncthreads();
 
-  uint4 wbuf[kPD + 1][4];
+  // per-thread copy sources as 32-bit offsets from the operand base; rows past the tile
+  // (or with an invalid token) read a valid row whose results are discarded
+  uint32_t aoff[kDma];
 #pragma unroll
-  for (int p = 0; p < kPD; ++p)
-    if (p < nkc) {
-      w_load(wg, H, p, lane, wbuf[p][0], wbuf[p][1]);
-      w_load(wu, H, p, lane, wbuf[p][2], wbuf[p][3]);
-    }
-  ActStage st;
-  act_load(st, xq, xs, tok_s, tl.mlen, H, 0, tid);
-  act_store(st, act[0], ascl[0], tl.mlen, tid);
-  __syncthreads();
-
-  v4f accg[kNTS], accu[kNTS];
-#pragma unroll
-  for (int ts = 0; ts < kNTS; ++ts) accg[ts] = accu[ts] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int kc0 = 0; kc0 < nkc; kc0 += kPD + 1) {
-#pragma unroll
-    for (int s = 0; s <= kPD; ++s) {
-      const int kc = kc0 + s;
-      if (kc < nkc) {
-        const int pf = kc + kPD;                    // refill the buffer freed last step
-        const int pslot = (s + kPD) % (kPD + 1);
-        if (pf < nkc) {
-          w_load(wg, H, pf, lane, wbuf[pslot][0], wbuf[pslot][1]);
-          w_load(wu, H, pf, lane, wbuf[pslot][2], wbuf[pslot][3]);
-        }
-        const bool more = kc + 1 < nkc;
-        if (more) act_load(st, xq, xs, tok_s, tl.mlen, H, kc + 1, tid);
-        const float sbg = sg_row[kc], sbu = su_row[kc];
-        const v8i ag = join(wbuf[s][0], wbuf[s][1]);
-        const v8i au = join(wbuf[s][2], wbuf[s][3]);
-        const uint8_t* a_lds = act[kc & 1];
-        const float* s_lds = ascl[kc & 1];
-#pragma unroll
-        for (int ts = 0; ts < kNTS; ++ts) {
-          if (ts < nts) {
-            const v8i b = act_frag(a_lds, ts, lane);
-            const v4f pg = mfma_fp8(ag, b);
-            const v4f pu = mfma_fp8(au, b);
-            const float sa = s_lds[ts * 16 + (lane & 15)];
-            const float cg = sa * sbg, cu = sa * sbu;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              accg[ts][i] = fmaf(pg[i], cg, accg[ts][i]);
-              accu[ts][i] = fmaf(pu[i], cu, accu[ts][i]);
-            }
-          }
-        }
-        if (more) act_store(st, act[(kc + 1) & 1], ascl[(kc + 1) & 1], tl.mlen, tid);
-        __syncthreads();
-      }
-    }
+  for (int j = 0; j < kDma; ++j) {
+    const int sidx = j * kThreads + tid;
+    const int r = sidx >> 3, seg = (sidx & 7) ^ (r & 7);
+    const int src = max(tok_s[min(r, tl.mlen - 1)], 0);
+    aoff[j] = (uint32_t)src * (uint32_t)K + seg * 16;
   }
+  const uint32_t soff = (uint32_t)max(tok_s[min(tid, tl.mlen - 1)], 0) * (uint32_t)nkc * 4u;
 
-  // Epilogue: SwiGLU, amax over the 128 columns of the group, E4M3 codes.
-  float h[kNTS][4];
-#pragma unroll
-  for (int ts = 0; ts < kNTS; ++ts) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float g = accg[ts][i];
-      h[ts][i] = (g / (1.0f + expf(-g))) * accu[ts][i];
-      m = fmaxf(m, fabsf(h[ts][i]));
-    }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if (ts < nts && lane < 16) red[wave][ts * 16 + lane] = m;
+  // weight fragments of this wave (packed layout: fragment (n16, kc) at (n16*nkc + kc)*2 KB)
+  int64_t wrow;
+  const uint8_t *pa, *pb;
+  const float *psa, *psb;
+  bool live = true;
+  if (PHASE == 1) {
+    wrow = (int64_t)nb * kTile + wave * 16;
+    const int64_t frag0 = (wrow / 16) * nkc * kFragBytes;
+    pa = a.wa + (int64_t)tl.e * a.I * K + frag0;
+    pb = a.wb + (int64_t)tl.e * a.I * K + frag0;
+    psa = a.wsa + ((int64_t)tl.e * (a.I / kTile) + nb) * nkc;
+    psb = a.wsb + ((int64_t)tl.e * (a.I / kTile) + nb) * nkc;
+  } else {
+    wrow = (int64_t)nb * 256 + wave * 32;
+    live = wrow < a.H;                       // H % 256 == 128: the last block is half used
+    const int64_t wr = live ? wrow : 0;
+    pa = a.wa + (int64_t)tl.e * a.H * K + (wr / 16) * nkc * kFragBytes;
+    pb = pa + (int64_t)nkc * kFragBytes;
+    psa = a.wsa + ((int64_t)tl.e * (a.H / kTile) + wr / kTile) * nkc;
+    psb = psa;
+  }
+  const uint32_t woff = (uint32_t)lane * 16;
+  // the K loop reads weight scales from LDS only, so that its vector-memory operations
+  // are exactly the pipelined copies
+  for (int c = lane; c < nkc; c += kWave) {
+    wsc[wave][0][c] = psa[c];
+    wsc[wave][1][c] = psb[c];
   }
   __syncthreads();
-  const int nkh = I / kTile;
-#pragma unroll
-  for (int ts = 0; ts < kNTS; ++ts) {
-    if (ts < nts) {
-      const int r = ts * 16 + (lane & 15);
-      float m = red[0][r];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][r]);
-      const float s = group_scale(m);
-      uint32_t packed = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__fdiv_rn(h[ts][i], s)) << (8 * i);
-      if (r < tl.mlen) {
-        const int64_t row = tl.m0 + r;
-        *reinterpret_cast<uint32_t*>(hq + row * I + wrow + 4 * (lane >> 4)) = packed;
-        if (wave == 0 && lane < 16) hs[row * nkh + nb] = s;
-      }
-    }
-  }
-}
 
-// ------------------------------------------------------------------------------------
-// Phase 2: y = DQ(hq) . DQ(W2)^T. grid = (max tiles, ceil(H / 256)); block = 512.
-// ------------------------------------------------------------------------------------
-template <typename YT>
-__global__ __launch_bounds__(kThreads) void ffn_down_kernel(
-    const Tile* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    const uint8_t* __restrict__ hq, const float* __restrict__ hs, const uint8_t* __restrict__ w2,
-    const float* __restrict__ w2s, int H, int I, YT* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint8_t act[2][kMT * kTile];
-  __shared__ float ascl[2][kMT];
-  __shared__ int tok_s[kMT];
-  if ((int)blockIdx.x >= *n_tiles) return;
-  const Tile tl = tiles[blockIdx.x];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nts = (tl.mlen + 15) >> 4;
-  const int nkc = I / kTile;
-  const int64_t wrow = (int64_t)blockIdx.y * 256 + wave * 32;  // first W2 row of this wave
-  const bool wave_live = wrow < H;                              // H % 256 == 128 tail
-  const int64_t wr_c = wave_live ? wrow : 0;
-  const uint8_t* wa = w2 + ((int64_t)tl.e * H + wr_c) * I;
-  const uint8_t* wb = wa + (int64_t)16 * I;
-  const float* sb_row = w2s + ((int64_t)tl.e * (H / kTile) + wr_c / kTile) * nkc;
-
-  // the hq rows of the tile are contiguous permuted rows
-  for (int r = tid; r < kMT; r += kThreads) tok_s[r] = r < tl.mlen ? tl.m0 + r : -1;
-  __syncthreads();
-
-  uint4 wbuf[kPD + 1][4];
+  // stage layout: [0, kActBytes) rows, then kThreads floats (row scales)
+  auto issue = [&](int c, v8i (&w)[2], uint8_t* stg) {
+    w[0] = w_load(pa + c * kFragBytes + woff);
+    w[1] = w_load(pb + c * kFragBytes + woff);
+    const uint8_t* ab = a.aq + c * kTile;
 #pragma unroll
-  for (int p = 0; p < kPD; ++p)
-    if (p < nkc) {
-      w_load(wa, I, p, lane, wbuf[p][0], wbuf[p][1]);
-      w_load(wb, I, p, lane, wbuf[p][2], wbuf[p][3]);
-    }
-  ActStage st;
-  act_load(st, hq, hs, tok_s, tl.mlen, I, 0, tid);
-  act_store(st, act[0], ascl[0], tl.mlen, tid);
-  __syncthreads();
+    for (int j = 0; j < kDma; ++j) dma16(ab + aoff[j], stg + j * (16 * kThreads) + wave * 1024);
+    dma4(reinterpret_cast<const uint8_t*>(a.as) + c * 4 + soff, stg + kActBytes + wave * 256);
+  };
 
   v4f acc0[kNTS], acc1[kNTS];
 #pragma unroll
   for (int ts = 0; ts < kNTS; ++ts) acc0[ts] = acc1[ts] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc0 = 0; kc0 < nkc; kc0 += kPD + 1) {
+  // one K chunk: for each 16-token column tile, two MFMAs (one per weight fragment) and
+  // the promotion acc += partial * (a_scale * w_scale); the next tile's operand is read
+  // from LDS while the current one is in the matrix core
+  auto compute = [&](int c, const v8i (&w)[2], const uint8_t* stg) {
+    const float s0 = wsc[wave][0][c], s1 = wsc[wave][1][c];
+    const float* sc = reinterpret_cast<const float*>(stg + kActBytes);
+    v8i b = act_frag(stg, 0, lane);
+    float sa = sc[lane & 15];
 #pragma unroll
-    for (int s = 0; s <= kPD; ++s) {
-      const int kc = kc0 + s;
-      if (kc < nkc) {
-        const int pf = kc + kPD;
-        const int pslot = (s + kPD) % (kPD + 1);
-        if (pf < nkc) {
-          w_load(wa, I, pf, lane, wbuf[pslot][0], wbuf[pslot][1]);
-          w_load(wb, I, pf, lane, wbuf[pslot][2], wbuf[pslot][3]);
+    for (int ts = 0; ts < kNTS; ++ts) {
+      if (ts < nts) {
+        v8i bn = b;
+        float san = sa;
+        if (ts + 1 < nts) {
+          bn = act_frag(stg, ts + 1, lane);
+          san = sc[(ts + 1) * 16 + (lane & 15)];
         }
-        const bool more = kc + 1 < nkc;
-        if (more) act_load(st, hq, hs, tok_s, tl.mlen, I, kc + 1, tid);
-        const float sb = sb_row[kc];
-        const v8i a0 = join(wbuf[s][0], wbuf[s][1]);
-        const v8i a1 = join(wbuf[s][2], wbuf[s][3]);
-        const uint8_t* a_lds = act[kc & 1];
-        const float* s_lds = ascl[kc & 1];
+        const v4f p0 = mfma_fp8(w[0], b);
+        const v4f p1 = mfma_fp8(w[1], b);
+        const float c0 = sa * s0, c1 = sa * s1;
 #pragma unroll
-        for (int ts = 0; ts < kNTS; ++ts) {
-          if (ts < nts) {
-            const v8i b = act_frag(a_lds, ts, lane);
-            const v4f p0 = mfma_fp8(a0, b);
-            const v4f p1 = mfma_fp8(a1, b);
-            const float c = s_lds[ts * 16 + (lane & 15)] * sb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              acc0[ts][i] = fmaf(p0[i], c, acc0[ts][i]);
-              acc1[ts][i] = fmaf(p1[i], c, acc1[ts][i]);
-            }
-          }
+        for (int i = 0; i < 4; ++i) {
+          acc0[ts][i] = fmaf(p0[i], c0, acc0[ts][i]);
+          acc1[ts][i] = fmaf(p1[i], c1, acc1[ts][i]);
         }
-        if (more) act_store(st, act[(kc + 1) & 1], ascl[(kc + 1) & 1], tl.mlen, tid);
-        __syncthreads();
+        b = bn;
+        sa = san;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
+  };
 
-  if (!wave_live) return;
+  // Every step issues one chunk (past the end: the last chunk again, an L2 hit whose
+  // data is never used) so the number of operations in flight is the same at every
+  // wait: at step c, chunks c and c+1 are outstanding and vmcnt <= kVmPerChunk means
+  // chunk c has landed.
+  const int last = nkc - 1;
+  v8i w0[2], w1[2], w2[2];
+  issue(0, w0, stg0);
+  issue(min(1, last), w1, stg1);
+#define FFN_STEP(S, WC, SC, WN, SN)                \
+  {                                                \
+    const int c = kc0 + S;                         \
+    stage_barrier<kVmPerChunk>();                  \
+    issue(min(c + 2, last), WN, SN);               \
+    compute(c, WC, SC);                            \
+  }
+  int kc0 = 0;
+  for (; kc0 + kStages <= nkc; kc0 += kStages) {
+    FFN_STEP(0, w0, stg0, w2, stg2)
+    FFN_STEP(1, w1, stg1, w0, stg0)
+    FFN_STEP(2, w2, stg2, w1, stg1)
+  }
+  if (kc0 < nkc) FFN_STEP(0, w0, stg0, w2, stg2)
+  if (kc0 + 1 < nkc) FFN_STEP(1, w1, stg1, w0, stg0)
+#undef FFN_STEP
+  // drain the copies still in flight before this workgroup's LDS can be reused
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  asm volatile("" ::: "memory");
+
+  if (PHASE == 1) {
+    // SwiGLU, amax over the 128 columns of the group (4 per lane, 4 lane groups, 8 waves)
+    float h[kNTS][4];
 #pragma unroll
-  for (int ts = 0; ts < kNTS; ++ts) {
-    const int r = ts * 16 + (lane & 15);
-    if (ts < nts && r < tl.mlen) {
-      YT* dst = y + (int64_t)(tl.m0 + r) * H + wrow + 4 * (lane >> 4);
-      if constexpr (sizeof(YT) == 2) {
-        uint2 a, b;
-        a.x = f32_to_bf16(acc0[ts][0]) | ((uint32_t)f32_to_bf16(acc0[ts][1]) << 16);
-        a.y = f32_to_bf16(acc0[ts][2]) | ((uint32_t)f32_to_bf16(acc0[ts][3]) << 16);
-        b.x = f32_to_bf16(acc1[ts][0]) | ((uint32_t)f32_to_bf16(acc1[ts][1]) << 16);
-        b.y = f32_to_bf16(acc1[ts][2]) | ((uint32_t)f32_to_bf16(acc1[ts][3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = a;
-        *reinterpret_cast<uint2*>(dst + 16) = b;
-      } else {
-        *reinterpret_cast<float4*>(dst) = make_float4(acc0[ts][0], acc0[ts][1], acc0[ts][2], acc0[ts][3]);
-        *reinterpret_cast<float4*>(dst + 16) = make_float4(acc1[ts][0], acc1[ts][1], acc1[ts][2], acc1[ts][3]);
+    for (int ts = 0; ts < kNTS; ++ts) {
+      const int r = ts * 16 + (lane & 15);
+      const bool valid = ts < nts && tok_s[r] >= 0;
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = acc0[ts][i];
+        h[ts][i] = valid ? (g / (1.0f + expf(-g))) * acc1[ts][i] : 0.0f;
+        m = fmaxf(m, fabsf(h[ts][i]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (ts < nts && lane < 16) red[wave][r] = m;
+    }
+    __syncthreads();
+    const int nkh = a.I / kTile;
+#pragma unroll
+    for (int ts = 0; ts < kNTS; ++ts) {
+      const int r = ts * 16 + (lane & 15);
+      if (ts < nts && r < tl.mlen) {
+        float m = red[0][r];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][r]);
+        const float s = group_scale(m);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__fdiv_rn(h[ts][i], s)) << (8 * i);
+        const int64_t row = tl.m0 + r;
+        *reinterpret_cast<uint32_t*>(a.hq + row * a.I + wrow + 4 * (lane >> 4)) = packed;
+        if (wave == 0 && lane < 16) a.hs[row * nkh + nb] = s;
+      }
+    }
+  } else {
+    if (!live) return;
+    YT* y = static_cast<YT*>(a.y);
+#pragma unroll
+    for (int ts = 0; ts < kNTS; ++ts) {
+      const int r = ts * 16 + (lane & 15);
+      if (ts < nts && r < tl.mlen) {
+        YT* dst = y + (int64_t)(tl.m0 + r) * a.H + wrow + 4 * (lane >> 4);
+        if constexpr (sizeof(YT) == 2) {
+          uint2 u, v;
+          u.x = f32_to_bf16(acc0[ts][0]) | ((uint32_t)f32_to_bf16(acc0[ts][1]) << 16);
+          u.y = f32_to_bf16(acc0[ts][2]) | ((uint32_t)f32_to_bf16(acc0[ts][3]) << 16);
+          v.x = f32_to_bf16(acc1[ts][0]) | ((uint32_t)f32_to_bf16(acc1[ts][1]) << 16);
+          v.y = f32_to_bf16(acc1[ts][2]) | ((uint32_t)f32_to_bf16(acc1[ts][3]) << 16);
+          *reinterpret_cast<uint2*>(dst) = u;
+          *reinterpret_cast<uint2*>(dst + 16) = v;
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc0[ts][0], acc0[ts][1], acc0[ts][2], acc0[ts][3]);
+          *reinterpret_cast<float4*>(dst + 16) = make_float4(acc1[ts][0], acc1[ts][1], acc1[ts][2], acc1[ts][3]);
+        }
       }
     }
   }
@@ -445,6 +441,11 @@ extern "C" moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_exper
       n_tokens < 0 || n_tokens >= ((int64_t)1 << 31))
     return MOE_ERR_SHAPE;
   if (yt != MOE_BF16 && yt != MOE_F32) return MOE_ERR_DTYPE;
+  if (cfg->hidden > kMaxChunks * kTile || cfg->inter > kMaxChunks * kTile) return MOE_ERR_UNSUPPORTED;
+  // per-lane operand offsets are 32-bit
+  if (n_tokens * (int64_t)cfg->hidden >= ((int64_t)1 << 32) ||
+      n_rows * (int64_t)cfg->inter >= ((int64_t)1 << 32))
+    return MOE_ERR_UNSUPPORTED;
   if (n_rows == 0) return MOE_OK;
   if (!offsets || !w1 || !w1s || !w3 || !w3s || !w2 || !w2s || !y) return MOE_ERR_NULL;
   if (n_tokens > 0 && (!xq || !xs)) return MOE_ERR_NULL;
@@ -461,14 +462,18 @@ extern "C" moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_exper
 
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, n_experts, (int)n_rows,
                      (int)L.max_tiles, tiles, ntiles);
-  hipLaunchKernelGGL(ffn_gate_up_kernel, dim3((unsigned)L.max_tiles, I / kTile), dim3(kThreads), 0, s,
-                     tiles, ntiles, xq, xs, n_tokens, row_token, w1, w1s, w3, w3s, H, I, hq, hs);
-  const dim3 g2((unsigned)L.max_tiles, (unsigned)((H + 255) / 256));
+  const int64_t tiles_padded = (L.max_tiles + kXcds - 1) / kXcds * kXcds;
+  FfnArgs a1{tiles, ntiles, xq, xs, n_tokens, row_token, w1, w1s, w3, w3s, H, I, I / kTile,
+             hq, hs, nullptr};
+  hipLaunchKernelGGL((ffn_kernel<1, uint16_t>), dim3((unsigned)(tiles_padded * a1.n_nb)),
+                     dim3(kThreads), 0, s, a1);
+  FfnArgs a2{tiles, ntiles, hq, hs, n_rows, nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256,
+             nullptr, nullptr, y};
   if (yt == MOE_BF16)
-    hipLaunchKernelGGL(ffn_down_kernel<uint16_t>, g2, dim3(kThreads), 0, s, tiles, ntiles, hq, hs,
-                       w2, w2s, H, I, static_cast<uint16_t*>(y));
+    hipLaunchKernelGGL((ffn_kernel<2, uint16_t>), dim3((unsigned)(tiles_padded * a2.n_nb)),
+                       dim3(kThreads), 0, s, a2);
   else
-    hipLaunchKernelGGL(ffn_down_kernel<float>, g2, dim3(kThreads), 0, s, tiles, ntiles, hq, hs, w2,
-                       w2s, H, I, static_cast<float*>(y));
+    hipLaunchKernelGGL((ffn_kernel<2, float>), dim3((unsigned)(tiles_padded * a2.n_nb)),
+                       dim3(kThreads), 0, s, a2);
   return launch_status();
 }

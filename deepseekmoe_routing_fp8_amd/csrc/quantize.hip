@@ -96,10 +96,44 @@ __global__ __launch_bounds__(256) void quantize_128x128_kernel(const float* __re
   if (t == 0) scales[blk] = s;
 }
 
+// Fragment-packed weight layout read by the grouped FFN: for a [rows, cols] matrix,
+// fragment (n16, kc) = rows 16*n16..+15 x cols 128*kc..+127 occupies 2 KB at
+// ((n16 * cols/128) + kc) * 2048, as two 1 KB halves; byte b of lane l in half h is
+// W[16*n16 + l % 16][128*kc + 64*h + 16*(l / 16) + b]. One thread moves 16 bytes.
+__global__ __launch_bounds__(256) void pack_fp8_kernel(const uint8_t* __restrict__ q, int64_t mats,
+                                                       int64_t rows, int64_t cols,
+                                                       uint8_t* __restrict__ out) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-byte unit of the output
+  const int64_t per_mat = rows * cols / 16;
+  if (o >= mats * per_mat) return;
+  const int64_t mat = o / per_mat, r = o % per_mat;
+  const int lane = (int)(r & 63), half = (int)((r >> 6) & 1);
+  const int64_t frag = r >> 7, nkc = cols / kTile;
+  const int64_t n16 = frag / nkc, kc = frag % nkc;
+  const int64_t row = n16 * 16 + (lane & 15);
+  const int64_t col = kc * kTile + half * 64 + (lane >> 4) * 16;
+  const uint4 v = *reinterpret_cast<const uint4*>(q + mat * rows * cols + row * cols + col);
+  *reinterpret_cast<uint4*>(out + o * 16) = v;
+}
+
 }  // namespace
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" moe_status moe_pack_fp8_weights(const uint8_t* q, int64_t mats, int64_t rows, int64_t cols,
+                                           uint8_t* packed, void* stream) {
+  if (mats < 0 || rows <= 0 || cols <= 0 || rows % 16 || cols % kTile) return MOE_ERR_SHAPE;
+  const int64_t units = mats * rows * cols / 16;
+  if (units == 0) return MOE_OK;
+  if (!q || !packed) return MOE_ERR_NULL;
+  if (q == packed) return MOE_ERR_UNSUPPORTED;
+  const int64_t blocks = (units + 255) / 256;
+  if (blocks > 0x7fffffff) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream), q, mats,
+                     rows, cols, packed);
+  return launch_status();
+}
 
 extern "C" moe_status moe_quantize_1x128(const void* x, moe_dtype xt, int64_t rows, int64_t cols,
                                          uint8_t* q, float* scales, void* stream) {

@@ -2,8 +2,10 @@
 forward step through the C entry points (quantise -> route -> permute -> routed experts
 -> shared experts -> combine -> bias update).
 
-Weights arrive as float32 host arrays (from the seeded generators) and are quantised to
-E4M3 128x128 blocks on the device by moe_quantize_128x128.
+Weights arrive as float32 host arrays (from the seeded generators), are quantised to
+E4M3 128x128 blocks on the device by moe_quantize_128x128 and re-laid by
+moe_pack_fp8_weights into the layout the grouped FFN streams. ``w1``/``w3``/``w2`` hold
+the packed codes; ``unpacked_codes`` recovers the row-major codes of one expert.
 """
 from __future__ import annotations
 
@@ -13,7 +15,8 @@ import numpy as np
 import torch
 
 from . import (make_config, moe_combine, moe_grouped_ffn_fp8, moe_grouped_ffn_workspace_bytes,
-               moe_permute, moe_quantize_1x128, moe_quantize_128x128, moe_route, moe_update_bias)
+               moe_pack_fp8_weights, moe_permute, moe_quantize_1x128, moe_quantize_128x128,
+               moe_route, moe_update_bias)
 
 
 class MoELayer:
@@ -51,7 +54,16 @@ class MoELayer:
     # -- weights -------------------------------------------------------------------
     def _quant_into(self, w: np.ndarray, q: torch.Tensor, s: torch.Tensor):
         t = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(self.dev)
-        moe_quantize_128x128(t, q, s)
+        rowmajor, _ = moe_quantize_128x128(t, scales=s)
+        moe_pack_fp8_weights(rowmajor, q)
+
+    @staticmethod
+    def unpack(packed: np.ndarray) -> np.ndarray:
+        """Row-major codes of one packed [rows, cols] matrix (inverse of the packing)."""
+        rows, cols = packed.shape
+        nkc = cols // 128
+        f = packed.reshape(rows // 16, nkc, 2, 4, 16, 16)      # n16, kc, half, lane/16, lane%16, byte
+        return np.ascontiguousarray(f.transpose(0, 4, 1, 2, 3, 5)).reshape(rows, cols)
 
     def load_weights(self, w_router: np.ndarray, bias: np.ndarray,
                      routed: Callable[[Callable], None], shared: Callable[[Callable], None]):

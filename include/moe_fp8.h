@@ -99,6 +99,20 @@ moe_status moe_quantize_128x128(const float* w, int64_t mats, int64_t rows, int6
                                 uint8_t* q, float* scales, void* stream);
 
 /*
+ * moe_pack_fp8_weights — re-lays E4M3 weight codes for the grouped FFN (a byte
+ * permutation, no arithmetic). The FFN streams each 16-row x 128-column fragment of a
+ * weight matrix as 2 KB of contiguous memory in MFMA operand order, which HBM serves at
+ * close to its sequential bandwidth. For a [rows, cols] matrix, fragment (n16, kc) sits
+ * at byte ((n16 * cols/128) + kc) * 2048, as two 1 KB halves h = 0, 1; byte b of lane l
+ * (0..63) in half h holds code [16*n16 + l%16][128*kc + 64*h + 16*(l/16) + b].
+ *   q       [mats, rows, cols] uint8 row-major codes (e.g. from moe_quantize_128x128)
+ *   packed  [mats, rows*cols] uint8, output; must not overlap q
+ * Errors: NULL pointers; rows % 16 or cols % 128 != 0; q == packed (UNSUPPORTED).
+ */
+moe_status moe_pack_fp8_weights(const uint8_t* q, int64_t mats, int64_t rows, int64_t cols,
+                                uint8_t* packed, void* stream);
+
+/*
  * moe_route — router ([digest] section 3.2 pseudocode and prose; section 3.4 group
  * limit; [guide] section 3 norm_topk_prob, routed_scaling_factor, gating kept in
  * high precision).
@@ -158,8 +172,9 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_config* cfg, int32_t n_experts,
  *   row_token [n_rows] int32 or NULL
  *   offsets   [n_experts+1] int32, device; read on the device (no host sync).
  *             Values are clamped to [0, n_rows].
- *   w1, w3    [n_experts, I, H] uint8; w1s, w3s [n_experts, I/128, H/128] float
- *   w2        [n_experts, H, I] uint8; w2s [n_experts, H/128, I/128] float
+ *   w1, w3    [n_experts, I, H] E4M3 codes in the layout of moe_pack_fp8_weights;
+ *             w1s, w3s [n_experts, I/128, H/128] float (row-major block scales)
+ *   w2        [n_experts, H, I] codes, packed likewise; w2s [n_experts, H/128, I/128] float
  *   y         [n_rows, H] of dtype yt (MOE_BF16 or MOE_F32), output
  *   ws        workspace of at least moe_grouped_ffn_workspace_bytes(...) bytes
  * Rows whose token index falls outside [0, n_tokens) produce y = 0.

@@ -12,7 +12,8 @@ HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
 
 
 def _lib():
-    from deepseekmoe_routing_fp8_amd import build as b
+    import __graft_entry__
+    b = __graft_entry__._builder()
     if not os.path.exists(b.LIB):
         b.build()
     import deepseekmoe_routing_fp8_amd as m

@@ -278,6 +278,37 @@ def _expert_set(rng, E, H, I):
     return w1, f(I, H), w3, f(I, H), w2, f(H, I)
 
 
+def _device_weights(lib, w):
+    """Row-major codes and scales -> device tensors, codes in the packed FFN layout."""
+    out = []
+    for i, a in enumerate(w):
+        t = dev(a)
+        out.append(lib.moe_pack_fp8_weights(t) if i % 2 == 0 else t)
+    return out
+
+
+def _pack_reference(W):
+    """The packed layout by its documented index map (pure re-indexing, no arithmetic)."""
+    rows, cols = W.shape
+    nkc = cols // 128
+    n16, kc, h, l, b = np.meshgrid(np.arange(rows // 16), np.arange(nkc), np.arange(2),
+                                   np.arange(64), np.arange(16), indexing="ij")
+    src = W[16 * n16 + l % 16, 128 * kc + 64 * h + 16 * (l // 16) + b]
+    return src.reshape(-1)
+
+
+@pytest.mark.parametrize("mats,rows,cols", [(1, 16, 128), (3, 48, 384), (2, 2048, 1024)])
+def test_pack_fp8_weights_layout(lib, mats, rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    W = rng.integers(0, 256, (mats, rows, cols)).astype(np.uint8)
+    say(f"pack {mats}x{rows}x{cols}")
+    got = host(lib.moe_pack_fp8_weights(dev(W))).reshape(mats, -1)
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    for i in range(mats):
+        assert np.array_equal(got[i], _pack_reference(W[i]))
+        assert np.array_equal(MoELayer.unpack(got[i].reshape(rows, cols)), W[i])
+
+
 def _relerr(a, b):
     return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
@@ -304,7 +335,7 @@ def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity):
     say(f"grouped_ffn H={H} I={I} E={E} loads={loads} identity={identity}")
     y = lib.moe_grouped_ffn_fp8(lib.make_config(cfg), E, rows, dev(xq), dev(xs),
                                 None if identity else dev(row_token), dev(offsets),
-                                *[dev(a) for a in w], y_dtype=torch.float32)
+                                *_device_weights(lib, w), y_dtype=torch.float32)
     torch.cuda.synchronize()
     y = host(y)
     for e in range(E):
@@ -334,7 +365,7 @@ def test_grouped_ffn_bf16_output_and_bad_tokens(lib):
     w = _expert_set(rng, E, H, I)
     say("grouped_ffn bf16 output, invalid tokens")
     y = lib.moe_grouped_ffn_fp8(lib.make_config(cfg), E, rows, dev(xq), dev(xs), dev(row_token),
-                                dev(offsets), *[dev(a) for a in w], y_dtype=torch.bfloat16)
+                                dev(offsets), *_device_weights(lib, w), y_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     y = y.float().cpu().numpy()
     assert np.all(y[3] == 0) and np.all(y[50] == 0)

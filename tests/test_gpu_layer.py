@@ -61,7 +61,8 @@ def test_layer_matches_oracle(name):
     shared = [q3(synth.shared_expert_weights(cfg, s)) for s in range(cfg.num_shared_experts)]
     # the device-quantised weights equal the oracle's codes and scales
     for e in (0, cfg.num_experts - 1):
-        assert np.array_equal(layer.w1[e].cpu().numpy(), routed[e][0])
+        assert np.array_equal(MoELayer.unpack(layer.w1[e].cpu().numpy()), routed[e][0])
+        assert np.array_equal(MoELayer.unpack(layer.w2[e].cpu().numpy()), routed[e][4])
         assert np.array_equal(layer.w2s[e].cpu().numpy(), routed[e][5])
     ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s])
     r = ref["route"]
@@ -109,8 +110,9 @@ def _sampled_parity(layer, cfg, x, bias, n_sample, seed):
     def put(e, w):
         cache[e] = q3(w)
     synth.map_experts(cfg, put, experts)
+    from deepseekmoe_routing_fp8_amd import MoELayer
     for e in experts[:3]:
-        assert np.array_equal(layer.w3[e].cpu().numpy(), cache[e][2])
+        assert np.array_equal(MoELayer.unpack(layer.w3[e].cpu().numpy()), cache[e][2])
         assert np.array_equal(layer.w1s[e].cpu().numpy(), cache[e][1])
     sh = {}
     synth.map_experts(cfg, lambda s, w: sh.__setitem__(s, q3(w)), range(cfg.num_shared_experts), shared=True)
