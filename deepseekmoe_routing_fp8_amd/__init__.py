@@ -26,7 +26,7 @@ MOE_F32, MOE_BF16 = 0, 1
 
 ENTRY_POINTS = (
     "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_pack_fp8_weights",
-    "moe_route",
+    "moe_pack_router_weights", "moe_route",
     "moe_permute", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8", "moe_combine",
     "moe_update_bias",
 )
@@ -57,6 +57,7 @@ _sig = {
     "moe_quantize_1x128": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "moe_quantize_128x128": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "moe_pack_fp8_weights": ([_P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
+    "moe_pack_router_weights": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "moe_route": ([_CFG, _P, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_permute": ([_CFG, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_grouped_ffn_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
@@ -150,10 +151,22 @@ def moe_pack_fp8_weights(q: torch.Tensor, packed: torch.Tensor = None, stream=No
     return packed
 
 
+def moe_pack_router_weights(w_router: torch.Tensor, out: torch.Tensor = None, stream=None):
+    """FP32 router weight [N_r, H] -> [3, N_r, H] bfloat16 planes with hi + mid + lo == W_r."""
+    N, H = w_router.shape
+    out = torch.empty((3, N, H), dtype=torch.bfloat16, device=w_router.device) if out is None else out
+    _check(_lib.moe_pack_router_weights(_dev(w_router, torch.float32, "w_router", (N, H)), N, H,
+                                        _dev(out, torch.bfloat16, "w_split", (3, N, H)),
+                                        _stream(stream)), "moe_pack_router_weights")
+    return out
+
+
 def moe_route(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
               scores: torch.Tensor = None, topk_idx: torch.Tensor = None,
               topk_gate: torch.Tensor = None, counts: torch.Tensor = None, stream=None):
-    """Router: -> (scores [T,N_r] f32, topk_idx [T,k] i32, topk_gate [T,k] f32, counts i32)."""
+    """Router: -> (scores [T,N_r] f32, topk_idx [T,k] i32, topk_gate [T,k] f32, counts i32).
+
+    ``w_router`` is the [3, N_r, H] bf16 split from moe_pack_router_weights."""
     T = x.shape[0]
     N, k = cfg.n_routed, cfg.top_k
     dev = x.device
@@ -162,7 +175,7 @@ def moe_route(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, bias: to
     topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
     counts = torch.empty((N,), dtype=torch.int32, device=dev) if counts is None else counts
     _check(_lib.moe_route(ctypes.byref(cfg), _dev(x, x.dtype, "x", (T, cfg.hidden)), _xdtype(x), T,
-                          _dev(w_router, torch.float32, "w_router", (N, cfg.hidden)),
+                          _dev(w_router, torch.bfloat16, "w_router_split", (3, N, cfg.hidden)),
                           _dev(bias, torch.float32, "bias", (N,)),
                           _dev(scores, torch.float32, "scores", (T, N)),
                           _dev(topk_idx, torch.int32, "topk_idx", (T, k)),

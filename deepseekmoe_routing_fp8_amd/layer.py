@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import (make_config, moe_combine, moe_grouped_ffn_fp8, moe_grouped_ffn_workspace_bytes,
-               moe_pack_fp8_weights, moe_permute, moe_quantize_1x128, moe_quantize_128x128,
+               moe_pack_fp8_weights, moe_pack_router_weights, moe_permute, moe_quantize_1x128, moe_quantize_128x128,
                moe_route, moe_update_bias)
 
 
@@ -68,7 +68,8 @@ class MoELayer:
     def load_weights(self, w_router: np.ndarray, bias: np.ndarray,
                      routed: Callable[[Callable], None], shared: Callable[[Callable], None]):
         """``routed(put)`` / ``shared(put)`` call put(e, (w1, w3, w2)) for every expert."""
-        self.w_router = torch.from_numpy(np.ascontiguousarray(w_router, np.float32)).to(self.dev)
+        self.w_router = moe_pack_router_weights(
+            torch.from_numpy(np.ascontiguousarray(w_router, np.float32)).to(self.dev))
         self.bias = torch.from_numpy(np.ascontiguousarray(bias, np.float32)).to(self.dev)
 
         def put_routed(e, w):

@@ -113,26 +113,40 @@ moe_status moe_pack_fp8_weights(const uint8_t* q, int64_t mats, int64_t rows, in
                                 uint8_t* packed, void* stream);
 
 /*
+ * moe_pack_router_weights — stores the FP32 router weight W_r as three bf16 planes
+ * (hi, mid, lo) with W_r == hi + mid + lo exactly, the form moe_route reads. Done once
+ * per weight load; lets the router run its FP32-exact products on bf16 MFMAs.
+ * Exact for every |W_r| >= 2^-110 and 0; below that the last piece is rounded to
+ * bf16's subnormal grid (error <= 2^-133).
+ *   w_router  [N_r, H] float
+ *   w_split   [3, N_r, H] bf16 bit patterns, output (plane 0 = RNE bf16 of W_r)
+ * Errors: NULL pointers; N_r < 0; H not a positive multiple of 128.
+ */
+moe_status moe_pack_router_weights(const float* w_router, int64_t n_routed, int64_t hidden,
+                                   uint16_t* w_split, void* stream);
+
+/*
  * moe_route — router ([digest] section 3.2 pseudocode and prose; section 3.4 group
  * limit; [guide] section 3 norm_topk_prob, routed_scaling_factor, gating kept in
  * high precision).
- *   s = sigmoid(x . W_r^T) from unquantised x, FP32 products with FP32 partial sums
- *   over 128-wide K chunks promoted into an FP64 accumulator; ranking score s + b.
+ *   s = sigmoid(x . W_r^T) from unquantised x. Every product is an exact product of the
+ *   FP32 operands (bf16-piece MFMAs), summed in FP32 within each 128-wide K chunk and
+ *   promoted into an FP64 accumulator; s is rounded to FP32. Ranking score s + b (FP32).
  *   With G > 1: a group's score is the FP32 sum of its group_topn best ranking scores;
  *   the G_k best groups are kept (ties: lower group index); experts elsewhere are
  *   excluded. Top-k by ranking score, descending, ties to the lower expert index.
  *   Gates: s[idx_j] / sum_j s[idx_j] * rho (unbiased s). counts[e] = selections of e.
- *   x          [T, H] of dtype xt
- *   w_router   [N_r, H] float
- *   bias       [N_r] float
- *   scores     [T, N_r] float, output: the sigmoid affinities s
- *   topk_idx   [T, k] int32, output, slot order = descending ranking score
- *   topk_gate  [T, k] float, output
- *   counts     [N_r] int32, output (overwritten, not accumulated)
+ *   x               [T, H] of dtype xt
+ *   w_router_split  [3, N_r, H] bf16 planes of W_r from moe_pack_router_weights
+ *   bias            [N_r] float
+ *   scores          [T, N_r] float, output: the sigmoid affinities s
+ *   topk_idx        [T, k] int32, output, slot order = descending ranking score
+ *   topk_gate       [T, k] float, output
+ *   counts          [N_r] int32, output (overwritten, not accumulated)
  * Errors: NULL pointers; invalid config (see moe_config); T < 0.
  */
 moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype xt, int64_t T,
-                     const float* w_router, const float* bias, float* scores,
+                     const uint16_t* w_router_split, const float* bias, float* scores,
                      int32_t* topk_idx, float* topk_gate, int32_t* counts, void* stream);
 
 /*

@@ -180,7 +180,7 @@ def test_route_matches_oracle(lib, name):
     b = synth.expert_bias(cfg)
     xd = dev(x, torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32)
     c = lib.make_config(cfg)
-    s, idx, gate, counts = lib.moe_route(c, xd, dev(wr), dev(b))
+    s, idx, gate, counts = lib.moe_route(c, xd, lib.moe_pack_router_weights(dev(wr)), dev(b))
     torch.cuda.synchronize()
     nt = check_routing(cfg, x, wr, b, host(s), host(idx), host(gate), host(counts))
     say(f"  near-tie tokens: {nt}")
@@ -194,7 +194,7 @@ def test_route_group_limit_binds_with_bias(lib):
     b = np.random.default_rng(9).uniform(-0.3, 0.3, cfg.num_experts).astype(np.float32)
     say("route v3_decode shapes, large bias")
     c = lib.make_config(cfg)
-    s, idx, gate, counts = lib.moe_route(c, dev(x, torch.bfloat16), dev(wr), dev(b))
+    s, idx, gate, counts = lib.moe_route(c, dev(x, torch.bfloat16), lib.moe_pack_router_weights(dev(wr)), dev(b))
     torch.cuda.synchronize()
     check_routing(cfg, x, wr, b, host(s), host(idx), host(gate), host(counts))
     free = oracle.route(x, wr, b, 8)
@@ -215,9 +215,25 @@ def test_route_general_shapes(lib):
         rng = np.random.default_rng(11)
         wr = (rng.standard_normal((cfg.num_experts, cfg.hidden_size)) / 16).astype(np.float32)
         b = rng.uniform(-0.05, 0.05, cfg.num_experts).astype(np.float32)
-        s, idx, gate, counts = lib.moe_route(lib.make_config(cfg), dev(x), dev(wr), dev(b))
+        s, idx, gate, counts = lib.moe_route(lib.make_config(cfg), dev(x), lib.moe_pack_router_weights(dev(wr)), dev(b))
         torch.cuda.synchronize()
         check_routing(cfg, x, wr, b, host(s), host(idx), host(gate), host(counts))
+
+
+def test_pack_router_weights_exact(lib):
+    """hi + mid + lo reproduces every FP32 weight exactly; hi is the RNE bf16 of W_r."""
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((64, 512)) * np.exp2(rng.integers(-30, 30, (64, 512)))).astype(np.float32)
+    w[0, :4] = [0.0, -0.0, 1.0, -3.0e-38]
+    say("pack router weights")
+    sp = lib.moe_pack_router_weights(dev(w)).float().cpu().numpy().astype(np.float64)
+    total = sp[0] + sp[1] + sp[2]
+    exact = (np.abs(w) >= 2.0 ** -110) | (w == 0)
+    assert np.array_equal(total[exact], w.astype(np.float64)[exact])
+    # below 2^-110 the last piece is limited by bf16's subnormal grid (2^-133)
+    assert np.all(np.abs(total - w.astype(np.float64))[~exact] <= 2.0 ** -133)
+    hi = torch.from_numpy(w).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(sp[0].astype(np.float32), hi)
 
 
 # ---------------------------------------------------------------------------------------
