@@ -32,7 +32,6 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kMT = 192;              // max rows of one expert per tile (multiple of 16)
-constexpr int kNTS = kMT / 16;        // MFMA column tiles per M tile
 constexpr int kThreads = 512;         // 8 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxExperts = 1024;
@@ -111,7 +110,7 @@ __device__ __forceinline__ void stage_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Direct global -> LDS copies: lane i of the wave writes its bytes at lds + i * size.
+// Direct global -> LDS copy: lane i of the wave writes its 16 bytes at lds + i * 16.
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave, 16, 0, 0);
 }
@@ -119,35 +118,30 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave, 4, 0, 0);
 }
 
-constexpr int kStages = 3;                          // 1 chunk consumed + 2 in flight
-constexpr int kActBytes = kMT * kTile;              // one K chunk of the tile's rows
-constexpr int kDma = kActBytes / (16 * kThreads);   // 16-byte copies per thread per chunk
-static_assert(kActBytes % (16 * kThreads) == 0, "tile rows must split evenly over threads");
-constexpr int kVmPerChunk = 4 + kDma + 1;           // weight loads + row copies + scale copy
-constexpr int kStageBytes = kActBytes + kThreads * 4;
+// Tile geometry. A workgroup computes 256 weight rows (16 fragments of 16 rows) against
+// up to kMT tokens, with 8 consumer waves and 4 producer waves.
+//   consumer wave w: fragments of 32 weight rows (phase 1: 16 rows of W1 and the same 16
+//     of W3; phase 2: 32 rows of W2) against all of the tile's tokens. It streams its own
+//     fragments into a private 3-slot LDS ring (its vector-memory counter tracks nothing
+//     else, so W(c+1) and W(c+2) stay in flight while it computes chunk c);
+//   producer waves copy the tile's activation rows and scales (L2-resident) into a
+//     2-slot LDS ring shared by all consumers; one workgroup barrier per K chunk
+//     publishes chunk c and frees chunk c-1's slot.
+constexpr int kConsumers = 8, kProducers = 4;
+constexpr int kFThreads = (kConsumers + kProducers) * kWave;   // 768
+constexpr int kNTS = kMT / 16;                   // 16-token tiles per M tile
+constexpr int kFragBytes = 16 * kTile;           // one 16 x 128 fragment: 2 KB
+constexpr int kWPriv = 2 * kFragBytes;           // one consumer's weights per K chunk
+constexpr int kWStage = kConsumers * kWPriv;     // 32 KB
+constexpr int kActBytes = kMT * kTile;           // 24 KB of activation codes per chunk
+constexpr int kAStage = kActBytes + kMT * 4;     // + one scale per row
+constexpr int kActUnits = kActBytes / 16;        // 16-byte copies per chunk
+constexpr int kProdLanes = kProducers * kWave;
+static_assert(kActUnits % kProdLanes == 0, "activation copies split evenly");
+constexpr int kActDma = kActUnits / kProdLanes;  // per producer lane per chunk (6)
 constexpr int kXcds = 8;
-constexpr int kMaxChunks = 128;                     // K <= 16384
-
-// Column operand (16 tokens x 128 K) for lane `lane` from a staged chunk. Lane group g
-// holds K bytes [16g, 16g+16) and [64+16g, 64+16g+16) of token (lane % 16); the weight
-// operand uses the same K map, which is all the MFMA needs. Row r keeps its eight
-// 16-byte segments at positions seg ^ (r & 7), so eight consecutive rows hit all banks.
-__device__ __forceinline__ v8i act_frag(const uint8_t* act, int ts, int lane) {
-  const int r = ts * 16 + (lane & 15), g = lane >> 4;
-  const v4i lo = *reinterpret_cast<const v4i*>(act + r * kTile + ((g ^ (r & 7)) << 4));
-  const v4i hi = *reinterpret_cast<const v4i*>(act + r * kTile + (((g + 4) ^ (r & 7)) << 4));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Row operand fragment: 16 weight rows x 128 K from the packed layout, where lane l's
-// two 16-byte pieces sit at l*16 and 1024 + l*16 of the fragment's 2 KB (same K map as
-// the column operand).
-constexpr int kFragBytes = 16 * kTile;
-__device__ __forceinline__ v8i w_load(const uint8_t* p) {
-  const v4i lo = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
-  const v4i hi = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p + kFragBytes / 2));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
+constexpr int kMaxChunks = 128;                  // K <= 16384
+constexpr int kUnroll = 6;                       // lcm(activation slots 2, weight slots 3)
 
 struct FfnArgs {
   const Tile* tiles;
@@ -156,9 +150,9 @@ struct FfnArgs {
   const float* as;       // their 1x128 scales
   int64_t n_tokens;
   const int32_t* row_token;
-  const uint8_t* wa;     // W1 (phase 1) or W2 (phase 2)
+  const uint8_t* wa;     // packed W1 (phase 1) or W2 (phase 2)
   const float* wsa;
-  const uint8_t* wb;     // W3 (phase 1)
+  const uint8_t* wb;     // packed W3 (phase 1)
   const float* wsb;
   int H, I, n_nb;
   uint8_t* hq;           // phase 1 outputs
@@ -166,28 +160,44 @@ struct FfnArgs {
   void* y;               // phase 2 output
 };
 
+// Column operand (16 tokens x 128 K) from a staged activation chunk: lane group g holds
+// K bytes [16g, 16g+16) and [64+16g, 64+16g+16) of token (lane % 16), the K map of the
+// packed weights. Row r keeps its 16-byte segments at positions seg ^ (r & 7).
+__device__ __forceinline__ v8i act_frag(const uint8_t* act, int ts, int lane) {
+  const int r = ts * 16 + (lane & 15), g = lane >> 4;
+  const v4i lo = *reinterpret_cast<const v4i*>(act + r * kTile + ((g ^ (r & 7)) << 4));
+  const v4i hi = *reinterpret_cast<const v4i*>(act + r * kTile + (((g + 4) ^ (r & 7)) << 4));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Row operand: fragment f of a consumer's private chunk (two 1 KB halves, lane*16 each).
+__device__ __forceinline__ v8i w_frag(const uint8_t* priv, int f, int lane) {
+  const v4i lo = *reinterpret_cast<const v4i*>(priv + f * kFragBytes + lane * 16);
+  const v4i hi = *reinterpret_cast<const v4i*>(priv + f * kFragBytes + kFragBytes / 2 + lane * 16);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // ------------------------------------------------------------------------------------
 // One grouped-FFN GEMM phase over tiles (expert, M tile) x n-blocks.
-//   PHASE 1: h = silu(x W1^T) * (x W3^T) on 128 intermediate columns per workgroup
-//            (wave w: 16 rows of W1 and the same 16 of W3), re-quantised 1x128.
-//   PHASE 2: y = hq W2^T on 256 output features per workgroup (wave w: 32 rows of W2).
-// Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD
+//   PHASE 1: 128 intermediate columns per workgroup; epilogue h = silu(G) * U,
+//            re-quantised 1x128 (amax over the 128 columns reduced across the 8
+//            consumers through LDS).
+//   PHASE 2: 256 output features per workgroup.
+// Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD,
 // so the tile's activation rows are fetched into that XCD's L2 once.
-// Pipeline: stage c of the K loop holds chunk c's weight fragments in registers and its
-// activation rows + scales in LDS (copied directly, no register staging). Every lane
-// issues the same kVmPerChunk vector-memory operations per chunk, in chunk order, so
-// "chunk c has landed" is the immediate wait vmcnt <= kVmPerChunk * (chunks issued
-// after c); one barrier per chunk then publishes it to all waves.
+// Steps are padded to a multiple of kUnroll (extra steps re-issue the last chunk and
+// skip compute) so that every wait is an immediate and never sits behind a branch.
 // ------------------------------------------------------------------------------------
 template <int PHASE, typename YT>
-__global__ __launch_bounds__(kThreads) void ffn_kernel(const FfnArgs a) {
-  // one array per pipeline stage: the chunk's activation rows, then one scale per row
-  __shared__ __attribute__((aligned(16))) uint8_t stg0[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t stg1[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t stg2[kStageBytes];
+__global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t wst0[kWStage];
+  __shared__ __attribute__((aligned(16))) uint8_t wst1[kWStage];
+  __shared__ __attribute__((aligned(16))) uint8_t wst2[kWStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ast0[kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ast1[kAStage];
   __shared__ int tok_s[kMT];
-  __shared__ float red[PHASE == 1 ? kWaves : 1][kMT];
-  __shared__ float wsc[kWaves][2][kMaxChunks];   // this wave's weight-block scales per K chunk
+  __shared__ float wsc[2][kMaxChunks];   // weight-block scales per K chunk (two row blocks)
+  __shared__ float red[PHASE == 1 ? kConsumers : 1][kMT];   // phase-1 amax partials
 
   const int L = blockIdx.x;
   const int xcd = L % kXcds, slot = L / kXcds;
@@ -197,12 +207,15 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const FfnArgs a) {
   const Tile tl = a.tiles[tile];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave >= kConsumers;
   const int K = PHASE == 1 ? a.H : a.I;
   const int nkc = K / kTile;
   const int nts = (tl.mlen + 15) >> 4;
+  const int nsteps = (nkc + kUnroll - 1) / kUnroll * kUnroll;
+  const int last = nkc - 1;
 
   // source row of every tile row: a token (phase 1) or a permuted row (phase 2)
-  for (int r = tid; r < kMT; r += kThreads) {
+  for (int r = tid; r < kMT; r += kFThreads) {
     int t = -1;
     if (r < tl.mlen) {
       if (PHASE == 1) {
@@ -214,71 +227,104 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const FfnArgs a) {
     }
     tok_s[r] = t;
   }
+  // weight-block scales for every K chunk: phase 1 (W1, W3) of row block nb; phase 2 the
+  // two W2 row blocks of this workgroup's 256 rows
+  const int64_t nrb = (PHASE == 1 ? a.I : a.H) / kTile;
+  for (int c = tid; c < 2 * nkc; c += kFThreads) {
+    const int which = c / nkc, kc = c % nkc;
+    float v;
+    if (PHASE == 1) {
+      v = (which == 0 ? a.wsa : a.wsb)[((int64_t)tl.e * nrb + nb) * nkc + kc];
+    } else {
+      const int64_t rb = min((int64_t)nb * 2 + which, nrb - 1);
+      v = a.wsa[((int64_t)tl.e * nrb + rb) * nkc + kc];
+    }
+    wsc[which][kc] = v;
+  }
   __syncthreads();
 
-  // per-thread copy sources as 32-bit offsets from the operand base; rows past the tile
-  // (or with an invalid token) read a valid row whose results are discarded
-  uint32_t aoff[kDma];
+  if (producer) {
+    // ---------------- producer waves: activation rows + scales ----------------
+    const int pl = (wave - kConsumers) * kWave + lane;          // 0..255
+    uint32_t aoff[kActDma];
 #pragma unroll
-  for (int j = 0; j < kDma; ++j) {
-    const int sidx = j * kThreads + tid;
-    const int r = sidx >> 3, seg = (sidx & 7) ^ (r & 7);
-    const int src = max(tok_s[min(r, tl.mlen - 1)], 0);
-    aoff[j] = (uint32_t)src * (uint32_t)K + seg * 16;
+    for (int j = 0; j < kActDma; ++j) {
+      const int sidx = j * kProdLanes + pl;
+      const int r = sidx >> 3, seg = (sidx & 7) ^ (r & 7);
+      const int src = max(tok_s[min(r, tl.mlen - 1)], 0);
+      aoff[j] = (uint32_t)src * (uint32_t)K + seg * 16;
+    }
+    const bool has_scale = pl < kMT;
+    const uint32_t soff = (uint32_t)max(tok_s[min(pl, tl.mlen - 1)], 0) * (uint32_t)nkc;
+    auto issue = [&](int c, uint8_t* st) {
+      const uint8_t* base = a.aq + (uint32_t)c * kTile;
+#pragma unroll
+      for (int j = 0; j < kActDma; ++j)
+        dma16(base + aoff[j], st + (j * kProdLanes + (wave - kConsumers) * kWave) * 16);
+      if (has_scale) dma4(a.as + soff + c, st + kActBytes + (wave - kConsumers) * kWave * 4);
+    };
+    issue(0, ast0);
+#define PROD_STEP(S)                                                   \
+    {                                                                  \
+      const int c = s0 + (S);                                          \
+      asm volatile("" ::: "memory");                                   \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                 \
+      __builtin_amdgcn_s_barrier();                                    \
+      asm volatile("" ::: "memory");                                   \
+      issue(min(c + 1, last), ((S) % 2) == 0 ? ast1 : ast0);           \
+    }
+    for (int s0 = 0; s0 < nsteps; s0 += kUnroll) {
+      PROD_STEP(0) PROD_STEP(1) PROD_STEP(2) PROD_STEP(3) PROD_STEP(4) PROD_STEP(5)
+    }
+#undef PROD_STEP
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    asm volatile("" ::: "memory");
+    // epilogue barrier partner (phase 1 amax exchange)
+    if (PHASE == 1) __syncthreads();
+    return;
   }
-  const uint32_t soff = (uint32_t)max(tok_s[min(tid, tl.mlen - 1)], 0) * (uint32_t)nkc * 4u;
 
-  // weight fragments of this wave (packed layout: fragment (n16, kc) at (n16*nkc + kc)*2 KB)
+  // ---------------- consumer waves: weights + MFMAs ----------------
+  // this wave's two fragments: unit j (1 KB) = fragment j/2, half j%2
+  const int64_t per_expert = (int64_t)a.H * a.I;
+  const uint8_t* fb[2];
   int64_t wrow;
-  const uint8_t *pa, *pb;
-  const float *psa, *psb;
   bool live = true;
   if (PHASE == 1) {
     wrow = (int64_t)nb * kTile + wave * 16;
-    const int64_t frag0 = (wrow / 16) * nkc * kFragBytes;
-    pa = a.wa + (int64_t)tl.e * a.I * K + frag0;
-    pb = a.wb + (int64_t)tl.e * a.I * K + frag0;
-    psa = a.wsa + ((int64_t)tl.e * (a.I / kTile) + nb) * nkc;
-    psb = a.wsb + ((int64_t)tl.e * (a.I / kTile) + nb) * nkc;
+    const int64_t off = (wrow / 16) * nkc * kFragBytes;
+    fb[0] = a.wa + (int64_t)tl.e * per_expert + off;
+    fb[1] = a.wb + (int64_t)tl.e * per_expert + off;
   } else {
     wrow = (int64_t)nb * 256 + wave * 32;
-    live = wrow < a.H;                       // H % 256 == 128: the last block is half used
-    const int64_t wr = live ? wrow : 0;
-    pa = a.wa + (int64_t)tl.e * a.H * K + (wr / 16) * nkc * kFragBytes;
-    pb = pa + (int64_t)nkc * kFragBytes;
-    psa = a.wsa + ((int64_t)tl.e * (a.H / kTile) + wr / kTile) * nkc;
-    psb = psa;
+    live = wrow < a.H;                        // H % 256 == 128: the last block is half used
+    const int64_t n16 = (live ? wrow : 0) / 16;
+    fb[0] = a.wa + (int64_t)tl.e * per_expert + n16 * nkc * kFragBytes;
+    fb[1] = fb[0] + (int64_t)nkc * kFragBytes;
   }
-  const uint32_t woff = (uint32_t)lane * 16;
-  // the K loop reads weight scales from LDS only, so that its vector-memory operations
-  // are exactly the pipelined copies
-  for (int c = lane; c < nkc; c += kWave) {
-    wsc[wave][0][c] = psa[c];
-    wsc[wave][1][c] = psb[c];
-  }
-  __syncthreads();
+  const int wsel0 = PHASE == 1 ? 0 : (wave >= 4 ? 1 : 0);   // scale row block of fragment 0
+  const int wsel1 = PHASE == 1 ? 1 : wsel0;
 
-  // stage layout: [0, kActBytes) rows, then kThreads floats (row scales)
-  auto issue = [&](int c, v8i (&w)[2], uint8_t* stg) {
-    w[0] = w_load(pa + c * kFragBytes + woff);
-    w[1] = w_load(pb + c * kFragBytes + woff);
-    const uint8_t* ab = a.aq + c * kTile;
+  auto issue_w = [&](int c, uint8_t* st) {
+    uint8_t* priv = st + wave * kWPriv;
 #pragma unroll
-    for (int j = 0; j < kDma; ++j) dma16(ab + aoff[j], stg + j * (16 * kThreads) + wave * 1024);
-    dma4(reinterpret_cast<const uint8_t*>(a.as) + c * 4 + soff, stg + kActBytes + wave * 256);
+    for (int j = 0; j < 4; ++j)
+      dma16(fb[j >> 1] + (uint32_t)c * kFragBytes + (j & 1) * (kFragBytes / 2) + lane * 16,
+            priv + j * (kFragBytes / 2));
   };
 
   v4f acc0[kNTS], acc1[kNTS];
 #pragma unroll
   for (int ts = 0; ts < kNTS; ++ts) acc0[ts] = acc1[ts] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // one K chunk: for each 16-token column tile, two MFMAs (one per weight fragment) and
-  // the promotion acc += partial * (a_scale * w_scale); the next tile's operand is read
-  // from LDS while the current one is in the matrix core
-  auto compute = [&](int c, const v8i (&w)[2], const uint8_t* stg) {
-    const float s0 = wsc[wave][0][c], s1 = wsc[wave][1][c];
-    const float* sc = reinterpret_cast<const float*>(stg + kActBytes);
-    v8i b = act_frag(stg, 0, lane);
+  auto compute = [&](int c, const uint8_t* wst, const uint8_t* act) {
+    const uint8_t* priv = wst + wave * kWPriv;
+    const v8i A0 = w_frag(priv, 0, lane);
+    const v8i A1 = w_frag(priv, 1, lane);
+    const float s0 = wsc[wsel0][c], s1 = wsc[wsel1][c];
+    const float* sc = reinterpret_cast<const float*>(act + kActBytes);
+    v8i b = act_frag(act, 0, lane);
     float sa = sc[lane & 15];
 #pragma unroll
     for (int ts = 0; ts < kNTS; ++ts) {
@@ -286,11 +332,11 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const FfnArgs a) {
         v8i bn = b;
         float san = sa;
         if (ts + 1 < nts) {
-          bn = act_frag(stg, ts + 1, lane);
+          bn = act_frag(act, ts + 1, lane);
           san = sc[(ts + 1) * 16 + (lane & 15)];
         }
-        const v4f p0 = mfma_fp8(w[0], b);
-        const v4f p1 = mfma_fp8(w[1], b);
+        const v4f p0 = mfma_fp8(A0, b);
+        const v4f p1 = mfma_fp8(A1, b);
         const float c0 = sa * s0, c1 = sa * s1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -304,31 +350,26 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const FfnArgs a) {
     }
   };
 
-  // Every step issues one chunk (past the end: the last chunk again, an L2 hit whose
-  // data is never used) so the number of operations in flight is the same at every
-  // wait: at step c, chunks c and c+1 are outstanding and vmcnt <= kVmPerChunk means
-  // chunk c has landed.
-  const int last = nkc - 1;
-  v8i w0[2], w1[2], w2[2];
-  issue(0, w0, stg0);
-  issue(min(1, last), w1, stg1);
-#define FFN_STEP(S, WC, SC, WN, SN)                \
-  {                                                \
-    const int c = kc0 + S;                         \
-    stage_barrier<kVmPerChunk>();                  \
-    issue(min(c + 2, last), WN, SN);               \
-    compute(c, WC, SC);                            \
+  issue_w(0, wst0);
+  issue_w(min(1, last), wst1);
+#define WST(S) (((S) % 3) == 0 ? wst0 : (((S) % 3) == 1 ? wst1 : wst2))
+#define CONS_STEP(S)                                                   \
+  {                                                                    \
+    const int c = s0 + (S);                                            \
+    asm volatile("" ::: "memory");                                     \
+    __builtin_amdgcn_s_barrier();                                      \
+    asm volatile("" ::: "memory");                                     \
+    issue_w(min(c + 2, last), WST((S) + 2));                           \
+    asm volatile("" ::: "memory");                                     \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));                   \
+    asm volatile("" ::: "memory");                                     \
+    if (c < nkc) compute(c, WST(S), ((S) % 2) == 0 ? ast0 : ast1);      \
   }
-  int kc0 = 0;
-  for (; kc0 + kStages <= nkc; kc0 += kStages) {
-    FFN_STEP(0, w0, stg0, w2, stg2)
-    FFN_STEP(1, w1, stg1, w0, stg0)
-    FFN_STEP(2, w2, stg2, w1, stg1)
+  for (int s0 = 0; s0 < nsteps; s0 += kUnroll) {
+    CONS_STEP(0) CONS_STEP(1) CONS_STEP(2) CONS_STEP(3) CONS_STEP(4) CONS_STEP(5)
   }
-  if (kc0 < nkc) FFN_STEP(0, w0, stg0, w2, stg2)
-  if (kc0 + 1 < nkc) FFN_STEP(1, w1, stg1, w0, stg0)
-#undef FFN_STEP
-  // drain the copies still in flight before this workgroup's LDS can be reused
+#undef CONS_STEP
+#undef WST
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   asm volatile("" ::: "memory");
@@ -359,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const FfnArgs a) {
       if (ts < nts && r < tl.mlen) {
         float m = red[0][r];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][r]);
+        for (int w = 1; w < kConsumers; ++w) m = fmaxf(m, red[w][r]);
         const float s = group_scale(m);
         uint32_t packed = 0;
 #pragma unroll
@@ -466,14 +507,14 @@ extern "C" moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_exper
   FfnArgs a1{tiles, ntiles, xq, xs, n_tokens, row_token, w1, w1s, w3, w3s, H, I, I / kTile,
              hq, hs, nullptr};
   hipLaunchKernelGGL((ffn_kernel<1, uint16_t>), dim3((unsigned)(tiles_padded * a1.n_nb)),
-                     dim3(kThreads), 0, s, a1);
+                     dim3(kFThreads), 0, s, a1);
   FfnArgs a2{tiles, ntiles, hq, hs, n_rows, nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256,
              nullptr, nullptr, y};
   if (yt == MOE_BF16)
     hipLaunchKernelGGL((ffn_kernel<2, uint16_t>), dim3((unsigned)(tiles_padded * a2.n_nb)),
-                       dim3(kThreads), 0, s, a2);
+                       dim3(kFThreads), 0, s, a2);
   else
     hipLaunchKernelGGL((ffn_kernel<2, float>), dim3((unsigned)(tiles_padded * a2.n_nb)),
-                       dim3(kThreads), 0, s, a2);
+                       dim3(kFThreads), 0, s, a2);
   return launch_status();
 }
