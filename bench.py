@@ -6,7 +6,8 @@ SwiGLU experts, shared expert, combine, bias update. Inputs and weights are seed
 synthetic values already resident in HBM when the timed region starts.
 
 Prints one JSON line. Per-stage HIP events are recorded on the launch stream inside
-the timed region; the roofline entry is for the dominant call, the routed grouped FFN.
+the timed region; the roofline entry is for the dominant kernel, the gate/up half of the
+grouped FFN (routed and shared experts in one launch).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_prefill]
 """
 from __future__ import annotations
@@ -29,18 +30,49 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def ffn_algorithmic_bytes(cfg, counts, n_experts_rows_tokens):
-    """Minimum HBM bytes of one routed grouped-FFN call: codes and scales of every expert
-    that received a row, the unique token rows of xq/xs, the FP8 intermediate written and
-    read once, and the bf16 expert outputs written once."""
-    H, I = cfg.hidden_size, cfg.moe_intermediate_size
-    rows, tokens = n_experts_rows_tokens
-    touched = int((counts > 0).sum())
-    w = touched * (3 * I * H + 3 * (I // 128) * (H // 128) * 4)
-    act = tokens * (H + (H // 128) * 4)
-    inter = 2 * rows * (I + (I // 128) * 4)
-    out = rows * H * 2
-    return w + act + inter + out, touched
+def ffn_algorithmic_bytes(cfg, counts):
+    """Minimum HBM bytes of the two grouped-FFN launches (routed + shared experts in one
+    grouped call). Per expert that received a row: its codes and 128x128 scales, read once.
+    Per token: its 1x128 codes and scales, read once. Per permuted row: the 1x128 FP8
+    intermediate written by gate/up and read by down, and the bf16 output row written by
+    down. Returns {"gate_up": bytes, "down": bytes, "experts": n}."""
+    H, I, S = cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_shared_experts
+    T, k = cfg.tokens, cfg.num_experts_per_tok
+    rows = T * (k + S)
+    experts = int((counts > 0).sum()) + S
+    mat = I * H + (I // 128) * (H // 128) * 4          # one weight matrix + its scales
+    act = T * (H + (H // 128) * 4)
+    inter = rows * (I + (I // 128) * 4)
+    return {"gate_up": experts * 2 * mat + act + inter,
+            "down": experts * mat + inter + rows * H * 2,
+            "experts": experts}
+
+
+COUNTER_FILE = os.path.join(ROOT, "profiles", "ffn_gate_up_v3_prefill_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "deepseekmoe_routing_fp8_amd", "csrc", f)
+                  for f in ("ffn.hip", "common.h")]
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, or None once the
+    kernel sources differ from the ones the counters were taken on."""
+    import hashlib
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTER_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    if kv.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, n_tokens: int):
@@ -86,7 +118,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -137,10 +169,10 @@ def main():
     counts = layer.counts.cpu().numpy()
     flops_layer = 6.0 * H * I * T * (k + S)
     tflops = flops_layer / (ms_per_step * 1e-3) / 1e12
-    ffn_ms = float(stage_ms[:, MoELayer.STAGES.index("ffn_routed")].mean())
-    ffn_bytes, touched = ffn_algorithmic_bytes(cfg, counts, (T * k, T))
-    ffn_flops = 6.0 * H * I * T * k
-    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    st = {s: float(stage_ms[:, j].mean()) for j, s in enumerate(MoELayer.STAGES)}
+    ab = ffn_algorithmic_bytes(cfg, counts)
+    gu_ms, dn_ms = st["ffn_gate_up"], st["ffn_down"]
+    achieved = ab["gate_up"] / (gu_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -162,14 +194,20 @@ def main():
         "tflops_fp8": round(tflops, 1),
         "frac_fp8_mfma_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
         "roofline": {
-            "kernel": "moe_grouped_ffn_fp8 routed call (ffn_gate_up_kernel + ffn_down_kernel + plan)",
+            "kernel": "ffn_kernel<1> (moe_grouped_ffn_fp8_gate_up: routed + shared experts, "
+                      "gate/up GEMMs, SwiGLU, 1x128 re-quantisation; includes the 1-block tile plan)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "algorithmic_bytes": ffn_bytes, "experts_touched": touched,
-            "avg_ms": round(ffn_ms, 4),
-            "mfma_tflops": round(ffn_flops / (ffn_ms * 1e-3) / 1e12, 1),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+            "algorithmic_bytes": ab["gate_up"], "experts_touched": ab["experts"],
+            "avg_ms": round(gu_ms, 4),
+            "mfma_tflops": round(4.0 * H * I * T * (k + S) / (gu_ms * 1e-3) / 1e12, 1),
         },
-        "stage_ms": {s: round(float(stage_ms[:, j].mean()), 4) for j, s in enumerate(MoELayer.STAGES)},
+        "down_kernel": {
+            "avg_ms": round(dn_ms, 4), "algorithmic_bytes": ab["down"],
+            "achieved_gbs": round(ab["down"] / (dn_ms * 1e-3) / 1e9, 1),
+            "mfma_tflops": round(2.0 * H * I * T * (k + S) / (dn_ms * 1e-3) / 1e12, 1),
+        },
+        "stage_ms": {s: round(v, 4) for s, v in st.items()},
         "event_ms_per_step": round(float(step_ms.mean()), 4),
         "max_over_mean_load": round(float(counts.max() / counts.mean()), 3),
     }

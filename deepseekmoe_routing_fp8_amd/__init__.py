@@ -27,7 +27,8 @@ MOE_F32, MOE_BF16 = 0, 1
 ENTRY_POINTS = (
     "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_pack_fp8_weights",
     "moe_pack_router_weights", "moe_route",
-    "moe_permute", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8", "moe_combine",
+    "moe_permute", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8",
+    "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
     "moe_update_bias",
 )
 
@@ -63,6 +64,10 @@ _sig = {
     "moe_grouped_ffn_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
     "moe_grouped_ffn_fp8": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _P, ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
+    "moe_grouped_ffn_fp8_gate_up": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _SZ, _P], ctypes.c_int),
+    "moe_grouped_ffn_fp8_down": ([_CFG, _I32, _I64, _P, _P, _P, ctypes.c_int, _P, _SZ, _P],
+                                 ctypes.c_int),
     "moe_combine": ([_CFG, _I64, _P, ctypes.c_int, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_update_bias": ([_CFG, _I64, _P, _P, _P], ctypes.c_int),
 }
@@ -187,15 +192,19 @@ def moe_route(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, bias: to
 
 def moe_permute(cfg: moe_config, topk_idx: torch.Tensor, offsets: torch.Tensor = None,
                 row_token: torch.Tensor = None, row_of: torch.Tensor = None, stream=None):
-    """-> (offsets [N_r+1], row_token [T*k], row_of [T,k]), all int32."""
+    """-> (offsets [N_r+N_s+1], row_token [T*(k+N_s)], row_of [T,k]), all int32. The
+    shared experts follow the routed ones as segments of T rows in token order."""
     T, k = topk_idx.shape
+    S = cfg.n_shared
     dev = topk_idx.device
-    offsets = torch.empty((cfg.n_routed + 1,), dtype=torch.int32, device=dev) if offsets is None else offsets
-    row_token = torch.empty((T * k,), dtype=torch.int32, device=dev) if row_token is None else row_token
+    if offsets is None:
+        offsets = torch.empty((cfg.n_routed + S + 1,), dtype=torch.int32, device=dev)
+    if row_token is None:
+        row_token = torch.empty((T * (k + S),), dtype=torch.int32, device=dev)
     row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
     _check(_lib.moe_permute(ctypes.byref(cfg), T, _dev(topk_idx, torch.int32, "topk_idx", (T, cfg.top_k)),
-                            _dev(offsets, torch.int32, "offsets", (cfg.n_routed + 1,)),
-                            _dev(row_token, torch.int32, "row_token", (T * k,)),
+                            _dev(offsets, torch.int32, "offsets", (cfg.n_routed + S + 1,)),
+                            _dev(row_token, torch.int32, "row_token", (T * (k + S),)),
                             _dev(row_of, torch.int32, "row_of", (T, k)), _stream(stream)),
            "moe_permute")
     return offsets, row_token, row_of
@@ -205,31 +214,71 @@ def moe_grouped_ffn_workspace_bytes(cfg: moe_config, n_experts: int, n_rows: int
     return int(_lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(cfg), n_experts, n_rows))
 
 
+def _ffn_ws(cfg, n_experts, n_rows, ws, dev):
+    need = moe_grouped_ffn_workspace_bytes(cfg, n_experts, n_rows)
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    return ws
+
+
+def _gate_up_args(cfg, n_experts, n_rows, xq, xs, row_token, offsets, w1, w1s, w3, w3s):
+    H, I, E = cfg.hidden, cfg.inter, n_experts
+    n_tokens = xq.shape[0]
+    rt = ctypes.c_void_p(0) if row_token is None else _dev(row_token, torch.int32, "row_token")
+    return (E, n_rows, n_tokens, _dev(xq, torch.uint8, "xq", (n_tokens, H)),
+            _dev(xs, torch.float32, "xs", (n_tokens, H // 128)), rt,
+            _dev(offsets, torch.int32, "offsets", (E + 1,)),
+            _dev(w1, torch.uint8, "w1", (E, I, H)), _dev(w1s, torch.float32, "w1s", (E, I // 128, H // 128)),
+            _dev(w3, torch.uint8, "w3", (E, I, H)), _dev(w3s, torch.float32, "w3s", (E, I // 128, H // 128)))
+
+
+def _down_args(cfg, n_experts, n_rows, w2, w2s, y):
+    H, I, E = cfg.hidden, cfg.inter, n_experts
+    yt = MOE_BF16 if y.dtype == torch.bfloat16 else MOE_F32
+    return (_dev(w2, torch.uint8, "w2", (E, H, I)), _dev(w2s, torch.float32, "w2s", (E, H // 128, I // 128)),
+            _dev(y, y.dtype, "y", (n_rows, H)), yt)
+
+
 def moe_grouped_ffn_fp8(cfg: moe_config, n_experts: int, n_rows: int, xq: torch.Tensor,
                         xs: torch.Tensor, row_token: Optional[torch.Tensor], offsets: torch.Tensor,
                         w1, w1s, w3, w3s, w2, w2s, y: torch.Tensor = None,
                         ws: torch.Tensor = None, y_dtype=torch.bfloat16, stream=None):
     """Grouped SwiGLU FP8 experts -> y [n_rows, H] (bf16 or f32)."""
-    H, I = cfg.hidden, cfg.inter
-    n_tokens = xq.shape[0]
     dev = xq.device
     if y is None:
-        y = torch.empty((n_rows, H), dtype=y_dtype, device=dev)
-    yt = MOE_BF16 if y.dtype == torch.bfloat16 else MOE_F32
-    need = moe_grouped_ffn_workspace_bytes(cfg, n_experts, n_rows)
-    if ws is None:
-        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    rt = ctypes.c_void_p(0) if row_token is None else _dev(row_token, torch.int32, "row_token")
-    E = n_experts
+        y = torch.empty((n_rows, cfg.hidden), dtype=y_dtype, device=dev)
+    ws = _ffn_ws(cfg, n_experts, n_rows, ws, dev)
     _check(_lib.moe_grouped_ffn_fp8(
-        ctypes.byref(cfg), E, n_rows, n_tokens, _dev(xq, torch.uint8, "xq", (n_tokens, H)),
-        _dev(xs, torch.float32, "xs", (n_tokens, H // 128)), rt,
-        _dev(offsets, torch.int32, "offsets", (E + 1,)),
-        _dev(w1, torch.uint8, "w1", (E, I, H)), _dev(w1s, torch.float32, "w1s", (E, I // 128, H // 128)),
-        _dev(w3, torch.uint8, "w3", (E, I, H)), _dev(w3s, torch.float32, "w3s", (E, I // 128, H // 128)),
-        _dev(w2, torch.uint8, "w2", (E, H, I)), _dev(w2s, torch.float32, "w2s", (E, H // 128, I // 128)),
-        _dev(y, y.dtype, "y", (n_rows, H)), yt, _dev(ws, torch.uint8, "ws"), ws.numel(),
+        ctypes.byref(cfg), *_gate_up_args(cfg, n_experts, n_rows, xq, xs, row_token, offsets,
+                                          w1, w1s, w3, w3s),
+        *_down_args(cfg, n_experts, n_rows, w2, w2s, y), _dev(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)), "moe_grouped_ffn_fp8")
+    return y
+
+
+def moe_grouped_ffn_fp8_gate_up(cfg: moe_config, n_experts: int, n_rows: int, xq: torch.Tensor,
+                                xs: torch.Tensor, row_token: Optional[torch.Tensor],
+                                offsets: torch.Tensor, w1, w1s, w3, w3s, ws: torch.Tensor = None,
+                                stream=None):
+    """First half of the grouped FFN; returns the workspace holding the tile plan and the
+    quantised intermediate for moe_grouped_ffn_fp8_down."""
+    ws = _ffn_ws(cfg, n_experts, n_rows, ws, xq.device)
+    _check(_lib.moe_grouped_ffn_fp8_gate_up(
+        ctypes.byref(cfg), *_gate_up_args(cfg, n_experts, n_rows, xq, xs, row_token, offsets,
+                                          w1, w1s, w3, w3s),
+        _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "moe_grouped_ffn_fp8_gate_up")
+    return ws
+
+
+def moe_grouped_ffn_fp8_down(cfg: moe_config, n_experts: int, n_rows: int, w2, w2s,
+                             ws: torch.Tensor, y: torch.Tensor = None, y_dtype=torch.bfloat16,
+                             stream=None):
+    """Second half of the grouped FFN, from the workspace of the gate_up call -> y."""
+    if y is None:
+        y = torch.empty((n_rows, cfg.hidden), dtype=y_dtype, device=w2.device)
+    _check(_lib.moe_grouped_ffn_fp8_down(
+        ctypes.byref(cfg), n_experts, n_rows, *_down_args(cfg, n_experts, n_rows, w2, w2s, y),
+        _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "moe_grouped_ffn_fp8_down")
     return y
 
 

@@ -2,7 +2,8 @@
 
 Usage: python deepseekmoe_routing_fp8_amd/build.py  (run as a file: importing the
 package would first load the library this builds).
-Objects go to <repo>/_build/, the library next to this file.
+Objects go to <repo>/_build/, the library next to this file. Also builds
+bench/ffn_counters, a native driver of the grouped FFN for profiler counter runs.
 """
 from __future__ import annotations
 
@@ -15,6 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoe_fp8.so")
+COUNTERS = os.path.join(PKG, "bench", "ffn_counters")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -47,6 +49,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    tmp = COUNTERS + ".tmp"
+    _run([HIPCC, *FLAGS, COUNTERS + ".hip", "-L" + PKG, "-lmoe_fp8", "-Wl,-rpath,$ORIGIN/..",
+          "-o", tmp])
+    os.replace(tmp, COUNTERS)
     return LIB
 
 

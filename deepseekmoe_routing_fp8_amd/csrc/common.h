@@ -18,6 +18,7 @@ constexpr int kWave = 64;
 constexpr int kTile = 128;            // 1x128 activation tiles, 128x128 weight blocks
 constexpr float kE4M3Max = 448.0f;
 constexpr int kMaxRouted = 512;
+constexpr int kMaxShared = 16;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxGroups = 64;
 
@@ -33,7 +34,7 @@ inline moe_status check_config(const moe_config* c) {
   if (c->hidden <= 0 || c->hidden % kTile) return MOE_ERR_SHAPE;
   if (c->inter <= 0 || c->inter % kTile) return MOE_ERR_SHAPE;
   if (c->n_routed < 1 || c->n_routed > kMaxRouted) return MOE_ERR_SHAPE;
-  if (c->n_shared < 0) return MOE_ERR_SHAPE;
+  if (c->n_shared < 0 || c->n_shared > kMaxShared) return MOE_ERR_SHAPE;
   if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_routed) return MOE_ERR_SHAPE;
   if (c->n_group < 1 || c->n_group > kMaxGroups || c->n_routed % c->n_group) return MOE_ERR_SHAPE;
   if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_ERR_SHAPE;

@@ -21,6 +21,8 @@
 // of W3); the workgroup covers 128 columns, i.e. whole 1x128 groups of h, so the SwiGLU
 // output is re-quantised in the epilogue (amax reduced across waves through LDS).
 // Phase 2 (down): wave w owns 32 rows of W2; the workgroup covers 256 output features.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -55,39 +57,63 @@ __device__ __forceinline__ v8i join(const uint4& lo, const uint4& hi) {
   return r;
 }
 
-// Tile plan: split every expert's rows into near-equal M tiles of at most kMT rows.
-__global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
-                                                        int n_experts, int n_rows, int max_tiles,
-                                                        Tile* __restrict__ tiles,
-                                                        int32_t* __restrict__ n_tiles) {
-  __shared__ int cnt[kMaxExperts];
-  __shared__ int start[kMaxExperts];
-  const int e = threadIdx.x;
+// Tile plan: split every expert's rows into near-equal M tiles of at most kMT rows and
+// order the experts by descending row count (ties: lower index first), so the longest
+// tiles start first and the short ones fill the end of the launch.
+__global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
+                                                               int n_experts, int n_rows,
+                                                               int max_tiles,
+                                                               Tile* __restrict__ tiles,
+                                                               int32_t* __restrict__ n_tiles) {
+  __shared__ int len_s[kMaxExperts];
+  __shared__ int nt_r[kMaxExperts];
+  __shared__ int start_r[kMaxExperts];
+  __shared__ int wsum[kMaxExperts / kWave];
+  const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
   int lo = 0, hi = 0, nt = 0;
   if (e < n_experts) {
     lo = min(max(offsets[e], 0), n_rows);
     hi = min(max(offsets[e + 1], lo), n_rows);
     nt = (hi - lo + kMT - 1) / kMT;
-    cnt[e] = nt;
+  }
+  const int m = hi - lo;
+  len_s[e] = m;
+  __syncthreads();
+  int rank = 0;
+  if (e < n_experts) {
+    for (int j = 0; j < n_experts; ++j) {
+      const int mj = len_s[j];
+      rank += (mj > m) || (mj == m && j < e);
+    }
+    nt_r[rank] = nt;   // ranks are a permutation of [0, n_experts)
   }
   __syncthreads();
-  if (e == 0) {
-    int run = 0;
-    for (int i = 0; i < n_experts; ++i) {
-      start[i] = run;
-      run += cnt[i];
-    }
-    *n_tiles = min(run, max_tiles);  // offsets that are not monotone cannot overflow the grid
+  // exclusive scan of the tile counts in rank order
+  const int v = e < n_experts ? nt_r[e] : 0;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int u = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += u;
+  }
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  start_r[e] = before + inc - v;
+  if (e == kMaxExperts - 1) {
+    // offsets that are not monotone cannot overflow the grid
+    *n_tiles = min(before + inc, max_tiles);
   }
   __syncthreads();
   if (e < n_experts && nt > 0) {
-    const int m = hi - lo;
     const int units = (m + 15) / 16;  // 16-row units, spread evenly over the tiles
+    const int start = start_r[rank];
     int row = lo;
     for (int i = 0; i < nt; ++i) {
       const int u = units / nt + (i < units % nt ? 1 : 0);
       const int len = min(u * 16, hi - row);
-      if (start[e] + i < max_tiles) tiles[start[e] + i] = Tile{e, row, len, lo};
+      if (start + i < max_tiles) tiles[start + i] = Tile{e, row, len, lo};
       row += len;
     }
   }
@@ -146,6 +172,7 @@ constexpr int kUnroll = 6;                       // lcm(activation slots 2, weig
 struct FfnArgs {
   const Tile* tiles;
   const int32_t* n_tiles;
+  int max_tiles, n_experts, n_rows;
   const uint8_t* aq;     // activation codes: xq (phase 1) or hq (phase 2)
   const float* as;       // their 1x128 scales
   int64_t n_tokens;
@@ -203,8 +230,12 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   const int xcd = L % kXcds, slot = L / kXcds;
   const int tile = (slot / a.n_nb) * kXcds + xcd;
   const int nb = slot % a.n_nb;
-  if (tile >= *a.n_tiles) return;
+  if (tile >= min(*a.n_tiles, a.max_tiles)) return;
   const Tile tl = a.tiles[tile];
+  // a workspace that does not hold this call's plan must not lead out of bounds
+  if (tl.e < 0 || tl.e >= a.n_experts || tl.mlen < 1 || tl.mlen > kMT || tl.m0 < 0 ||
+      tl.m0 > a.n_rows - tl.mlen)
+    return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = wave >= kConsumers;
@@ -469,6 +500,109 @@ extern "C" size_t moe_grouped_ffn_workspace_bytes(const moe_config* cfg, int32_t
   return ws_layout(cfg, n_experts, n_rows).total;
 }
 
+namespace {
+
+// Checks shared by the three entry points; fills the workspace pointers.
+struct FfnCall {
+  WsLayout L;
+  Tile* tiles;
+  int32_t* ntiles;
+  uint8_t* hq;
+  float* hs;
+  unsigned grid_tiles;   // M-tile slots, padded to a multiple of the XCD count
+};
+
+moe_status ffn_check(const moe_config* cfg, int32_t n_experts, int64_t n_rows, void* ws,
+                     size_t ws_bytes, FfnCall* f) {
+  const moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 0 || n_rows >= ((int64_t)1 << 31))
+    return MOE_ERR_SHAPE;
+  if (cfg->hidden > kMaxChunks * kTile || cfg->inter > kMaxChunks * kTile) return MOE_ERR_UNSUPPORTED;
+  // per-lane operand offsets into hq are 32-bit
+  if (n_rows * (int64_t)cfg->inter >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  f->L = ws_layout(cfg, n_experts, n_rows);
+  if (n_rows == 0) return MOE_OK;
+  if (!ws || ws_bytes < f->L.total) return MOE_ERR_WORKSPACE;
+  // total work-items of the larger launch must fit the 32-bit grid size
+  const int64_t grid_tiles = (f->L.max_tiles + kXcds - 1) / kXcds * kXcds;
+  const int64_t nb_max = std::max<int64_t>(cfg->inter / kTile, (cfg->hidden + 255) / 256);
+  if (grid_tiles * nb_max * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  f->tiles = reinterpret_cast<Tile*>(base + f->L.tiles);
+  f->ntiles = reinterpret_cast<int32_t*>(base + f->L.ntiles);
+  f->hq = base + f->L.hq;
+  f->hs = reinterpret_cast<float*>(base + f->L.hs);
+  f->grid_tiles = (unsigned)grid_tiles;
+  return MOE_OK;
+}
+
+moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows, int64_t n_tokens,
+                       const uint8_t* xq, const float* xs, const int32_t* row_token,
+                       const int32_t* offsets, const uint8_t* w1, const float* w1s,
+                       const uint8_t* w3, const float* w3s, void* ws, size_t ws_bytes,
+                       void* stream) {
+  FfnCall f;
+  const moe_status st = ffn_check(cfg, n_experts, n_rows, ws, ws_bytes, &f);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0 || n_tokens * (int64_t)cfg->hidden >= ((int64_t)1 << 32))
+    return n_tokens < 0 ? MOE_ERR_SHAPE : MOE_ERR_UNSUPPORTED;
+  if (n_rows == 0) return MOE_OK;
+  if (!offsets || !w1 || !w1s || !w3 || !w3s) return MOE_ERR_NULL;
+  if (n_tokens > 0 && (!xq || !xs)) return MOE_ERR_NULL;
+  hipStream_t s = as_stream(stream);
+  const int H = cfg->hidden, I = cfg->inter;
+  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
+                     (int)n_rows, (int)f.L.max_tiles, f.tiles, f.ntiles);
+  FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, xs, n_tokens,
+             row_token, w1, w1s, w3, w3s, H, I, I / kTile, f.hq, f.hs, nullptr};
+  hipLaunchKernelGGL((ffn_kernel<1, uint16_t>), dim3(f.grid_tiles * a1.n_nb), dim3(kFThreads), 0,
+                     s, a1);
+  return launch_status();
+}
+
+moe_status ffn_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows, const uint8_t* w2,
+                    const float* w2s, void* y, moe_dtype yt, void* ws, size_t ws_bytes,
+                    void* stream) {
+  FfnCall f;
+  const moe_status st = ffn_check(cfg, n_experts, n_rows, ws, ws_bytes, &f);
+  if (st != MOE_OK) return st;
+  if (yt != MOE_BF16 && yt != MOE_F32) return MOE_ERR_DTYPE;
+  if (n_rows == 0) return MOE_OK;
+  if (!w2 || !w2s || !y) return MOE_ERR_NULL;
+  hipStream_t s = as_stream(stream);
+  const int H = cfg->hidden, I = cfg->inter;
+  FfnArgs a2{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, f.hq, f.hs, n_rows,
+             nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256, nullptr, nullptr, y};
+  const dim3 grid(f.grid_tiles * a2.n_nb);
+  if (yt == MOE_BF16)
+    hipLaunchKernelGGL((ffn_kernel<2, uint16_t>), grid, dim3(kFThreads), 0, s, a2);
+  else
+    hipLaunchKernelGGL((ffn_kernel<2, float>), grid, dim3(kFThreads), 0, s, a2);
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" moe_status moe_grouped_ffn_fp8_gate_up(const moe_config* cfg, int32_t n_experts,
+                                                  int64_t n_rows, int64_t n_tokens,
+                                                  const uint8_t* xq, const float* xs,
+                                                  const int32_t* row_token,
+                                                  const int32_t* offsets, const uint8_t* w1,
+                                                  const float* w1s, const uint8_t* w3,
+                                                  const float* w3s, void* ws, size_t ws_bytes,
+                                                  void* stream) {
+  return ffn_gate_up(cfg, n_experts, n_rows, n_tokens, xq, xs, row_token, offsets, w1, w1s, w3,
+                     w3s, ws, ws_bytes, stream);
+}
+
+extern "C" moe_status moe_grouped_ffn_fp8_down(const moe_config* cfg, int32_t n_experts,
+                                               int64_t n_rows, const uint8_t* w2, const float* w2s,
+                                               void* y, moe_dtype yt, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  return ffn_down(cfg, n_experts, n_rows, w2, w2s, y, yt, ws, ws_bytes, stream);
+}
+
 extern "C" moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
                                           int64_t n_tokens, const uint8_t* xq, const float* xs,
                                           const int32_t* row_token, const int32_t* offsets,
@@ -476,45 +610,14 @@ extern "C" moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_exper
                                           const float* w3s, const uint8_t* w2, const float* w2s,
                                           void* y, moe_dtype yt, void* ws, size_t ws_bytes,
                                           void* stream) {
-  const moe_status st = check_config(cfg);
+  // validate both halves before launching either
+  FfnCall f;
+  moe_status st = ffn_check(cfg, n_experts, n_rows, ws, ws_bytes, &f);
   if (st != MOE_OK) return st;
-  if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 0 || n_rows >= ((int64_t)1 << 31) ||
-      n_tokens < 0 || n_tokens >= ((int64_t)1 << 31))
-    return MOE_ERR_SHAPE;
   if (yt != MOE_BF16 && yt != MOE_F32) return MOE_ERR_DTYPE;
-  if (cfg->hidden > kMaxChunks * kTile || cfg->inter > kMaxChunks * kTile) return MOE_ERR_UNSUPPORTED;
-  // per-lane operand offsets are 32-bit
-  if (n_tokens * (int64_t)cfg->hidden >= ((int64_t)1 << 32) ||
-      n_rows * (int64_t)cfg->inter >= ((int64_t)1 << 32))
-    return MOE_ERR_UNSUPPORTED;
-  if (n_rows == 0) return MOE_OK;
-  if (!offsets || !w1 || !w1s || !w3 || !w3s || !w2 || !w2s || !y) return MOE_ERR_NULL;
-  if (n_tokens > 0 && (!xq || !xs)) return MOE_ERR_NULL;
-  const WsLayout L = ws_layout(cfg, n_experts, n_rows);
-  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  if (L.max_tiles > 0x7fffffff) return MOE_ERR_SHAPE;
-  hipStream_t s = as_stream(stream);
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  Tile* tiles = reinterpret_cast<Tile*>(base + L.tiles);
-  int32_t* ntiles = reinterpret_cast<int32_t*>(base + L.ntiles);
-  uint8_t* hq = base + L.hq;
-  float* hs = reinterpret_cast<float*>(base + L.hs);
-  const int H = cfg->hidden, I = cfg->inter;
-
-  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, n_experts, (int)n_rows,
-                     (int)L.max_tiles, tiles, ntiles);
-  const int64_t tiles_padded = (L.max_tiles + kXcds - 1) / kXcds * kXcds;
-  FfnArgs a1{tiles, ntiles, xq, xs, n_tokens, row_token, w1, w1s, w3, w3s, H, I, I / kTile,
-             hq, hs, nullptr};
-  hipLaunchKernelGGL((ffn_kernel<1, uint16_t>), dim3((unsigned)(tiles_padded * a1.n_nb)),
-                     dim3(kFThreads), 0, s, a1);
-  FfnArgs a2{tiles, ntiles, hq, hs, n_rows, nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256,
-             nullptr, nullptr, y};
-  if (yt == MOE_BF16)
-    hipLaunchKernelGGL((ffn_kernel<2, uint16_t>), dim3((unsigned)(tiles_padded * a2.n_nb)),
-                       dim3(kFThreads), 0, s, a2);
-  else
-    hipLaunchKernelGGL((ffn_kernel<2, float>), dim3((unsigned)(tiles_padded * a2.n_nb)),
-                       dim3(kFThreads), 0, s, a2);
-  return launch_status();
+  if (n_rows > 0 && (!w2 || !w2s || !y)) return MOE_ERR_NULL;
+  st = ffn_gate_up(cfg, n_experts, n_rows, n_tokens, xq, xs, row_token, offsets, w1, w1s, w3, w3s,
+                   ws, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  return ffn_down(cfg, n_experts, n_rows, w2, w2s, y, yt, ws, ws_bytes, stream);
 }

@@ -9,6 +9,12 @@
 // a token's rank inside its expert is the running base + the popcounts of earlier
 // waves' masks + the popcount of its own wave's mask below its lane. Experts are
 // distinct within a token, so each mask bit stands for exactly one row.
+//
+// Shared experts (2kiu.com digest section 3.2 and lpnh.cn guide section 3: one shared
+// expert that every token passes through) become extra segments after the routed ones,
+// so one grouped-FFN launch serves both: shared expert s owns rows T*k + s*T + t, in
+// token order. Rows between the last routed row and T*k (left by topk_idx entries that
+// name no routed expert) belong to the first shared segment and carry token -1.
 #include "common.h"
 
 namespace moe {
@@ -18,7 +24,7 @@ constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ idx,
-                                                               int64_t T, int k, int N,
+                                                               int64_t T, int k, int N, int S,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ row_token,
                                                                int32_t* __restrict__ row_of) {
@@ -46,6 +52,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
   }
   __syncthreads();
   for (int i = tid; i <= N; i += kPermThreads) offsets[i] = base[i];
+  for (int s = tid; s < S; s += kPermThreads) offsets[N + 1 + s] = (int32_t)(pairs + (s + 1) * T);
+  for (int64_t r = base[N] + tid; r < pairs; r += kPermThreads) row_token[r] = -1;
+  for (int64_t r = tid; r < S * T; r += kPermThreads) row_token[pairs + r] = (int32_t)(r % T);
 
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t t0 = 0; t0 < T; t0 += kPermThreads) {
@@ -105,10 +114,10 @@ extern "C" moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_
                                   void* stream) {
   const moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (T < 0 || T * cfg->top_k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (T < 0 || T * (cfg->top_k + cfg->n_shared) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if (!offsets) return MOE_ERR_NULL;
   if (T > 0 && (!topk_idx || !row_token || !row_of)) return MOE_ERR_NULL;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, as_stream(stream), topk_idx,
-                     T, cfg->top_k, cfg->n_routed, offsets, row_token, row_of);
+                     T, cfg->top_k, cfg->n_routed, cfg->n_shared, offsets, row_token, row_of);
   return launch_status();
 }

@@ -5,7 +5,9 @@ forward step through the C entry points (quantise -> route -> permute -> routed 
 Weights arrive as float32 host arrays (from the seeded generators), are quantised to
 E4M3 128x128 blocks on the device by moe_quantize_128x128 and re-laid by
 moe_pack_fp8_weights into the layout the grouped FFN streams. ``w1``/``w3``/``w2`` hold
-the packed codes; ``unpacked_codes`` recovers the row-major codes of one expert.
+the packed codes of the N_r routed experts followed by the N_s shared experts (index
+N_r + s), so that one grouped-FFN call over N_r + N_s segments (moe_permute appends the
+shared segments) evaluates both; ``unpack`` recovers the row-major codes of one matrix.
 """
 from __future__ import annotations
 
@@ -14,8 +16,8 @@ from typing import Callable, Iterable, Optional
 import numpy as np
 import torch
 
-from . import (make_config, moe_combine, moe_grouped_ffn_fp8, moe_grouped_ffn_workspace_bytes,
-               moe_pack_fp8_weights, moe_pack_router_weights, moe_permute, moe_quantize_1x128, moe_quantize_128x128,
+from . import (make_config, moe_combine, moe_grouped_ffn_fp8_down, moe_grouped_ffn_fp8_gate_up,
+               moe_grouped_ffn_workspace_bytes, moe_pack_fp8_weights, moe_pack_router_weights, moe_permute, moe_quantize_1x128, moe_quantize_128x128,
                moe_route, moe_update_bias)
 
 
@@ -34,19 +36,13 @@ class MoELayer:
         H, I, E, S = cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts, cfg.num_shared_experts
         u8, f32 = torch.uint8, torch.float32
         d = self.dev
-        self.w1 = torch.empty((E, I, H), dtype=u8, device=d)
-        self.w3 = torch.empty((E, I, H), dtype=u8, device=d)
-        self.w2 = torch.empty((E, H, I), dtype=u8, device=d)
-        self.w1s = torch.empty((E, I // 128, H // 128), dtype=f32, device=d)
-        self.w3s = torch.empty((E, I // 128, H // 128), dtype=f32, device=d)
-        self.w2s = torch.empty((E, H // 128, I // 128), dtype=f32, device=d)
-        Sx = max(S, 1)
-        self.sw1 = torch.empty((Sx, I, H), dtype=u8, device=d)
-        self.sw3 = torch.empty((Sx, I, H), dtype=u8, device=d)
-        self.sw2 = torch.empty((Sx, H, I), dtype=u8, device=d)
-        self.sw1s = torch.empty((Sx, I // 128, H // 128), dtype=f32, device=d)
-        self.sw3s = torch.empty((Sx, I // 128, H // 128), dtype=f32, device=d)
-        self.sw2s = torch.empty((Sx, H // 128, I // 128), dtype=f32, device=d)
+        EA = E + S   # routed experts, then shared experts
+        self.w1 = torch.empty((EA, I, H), dtype=u8, device=d)
+        self.w3 = torch.empty((EA, I, H), dtype=u8, device=d)
+        self.w2 = torch.empty((EA, H, I), dtype=u8, device=d)
+        self.w1s = torch.empty((EA, I // 128, H // 128), dtype=f32, device=d)
+        self.w3s = torch.empty((EA, I // 128, H // 128), dtype=f32, device=d)
+        self.w2s = torch.empty((EA, H // 128, I // 128), dtype=f32, device=d)
         self.w_router = None
         self.bias = None
         self._T = None
@@ -77,10 +73,8 @@ class MoELayer:
             self._quant_into(w[1], self.w3[e], self.w3s[e])
             self._quant_into(w[2], self.w2[e], self.w2s[e])
 
-        def put_shared(e, w):
-            self._quant_into(w[0], self.sw1[e], self.sw1s[e])
-            self._quant_into(w[1], self.sw3[e], self.sw3s[e])
-            self._quant_into(w[2], self.sw2[e], self.sw2s[e])
+        def put_shared(s, w):
+            put_routed(self.cfg.num_experts + s, w)
         routed(put_routed)
         shared(put_shared)
         torch.cuda.synchronize(self.dev)
@@ -108,24 +102,18 @@ class MoELayer:
         self.topk_idx = torch.empty((T, k), dtype=i32, device=d)
         self.topk_gate = torch.empty((T, k), dtype=f32, device=d)
         self.counts = torch.empty((N,), dtype=i32, device=d)
-        self.offsets = torch.empty((N + 1,), dtype=i32, device=d)
-        self.row_token = torch.empty((T * k,), dtype=i32, device=d)
+        self.offsets = torch.empty((N + S + 1,), dtype=i32, device=d)
+        self.row_token = torch.empty((T * (k + S),), dtype=i32, device=d)
         self.row_of = torch.empty((T, k), dtype=i32, device=d)
-        self.y_rows = torch.empty((T * k, H), dtype=self.y_dtype, device=d)
-        self.ws = torch.empty((max(moe_grouped_ffn_workspace_bytes(self.c, N, T * k), 1),),
+        self.y_rows = torch.empty((T * (k + S), H), dtype=self.y_dtype, device=d)
+        self.ws = torch.empty((max(moe_grouped_ffn_workspace_bytes(self.c, N + S, T * (k + S)), 1),),
                               dtype=torch.uint8, device=d)
-        if S > 0:
-            self.y_shared = torch.empty((S * T, H), dtype=self.y_dtype, device=d)
-            self.sh_offsets = torch.arange(0, S + 1, dtype=i32, device=d) * T
-            self.ws_sh = torch.empty((max(moe_grouped_ffn_workspace_bytes(self.c, S, S * T), 1),),
-                                     dtype=torch.uint8, device=d)
-        else:
-            self.y_shared = None
+        self.y_shared = self.y_rows[T * k:] if S > 0 else None
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
         self._T = T
 
     # -- forward -------------------------------------------------------------------
-    STAGES = ("quantize", "route", "permute", "ffn_routed", "ffn_shared", "combine", "bias_update")
+    STAGES = ("quantize", "route", "permute", "ffn_gate_up", "ffn_down", "combine", "bias_update")
 
     def forward(self, x: torch.Tensor, update_bias: bool = True, events=None) -> torch.Tensor:
         """One layer step on x [T, H] (bf16 or f32, on the device). Returns out [T, H] bf16
@@ -137,6 +125,7 @@ class MoELayer:
         T = x.shape[0]
         self._buffers(T)
         k, N, S = cfg.num_experts_per_tok, cfg.num_experts, cfg.num_shared_experts
+        EA, rows = N + S, T * (k + S)
         mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
         mark(0)
         moe_quantize_1x128(x, self.xq, self.xs)
@@ -146,14 +135,10 @@ class MoELayer:
         mark(2)
         moe_permute(c, self.topk_idx, self.offsets, self.row_token, self.row_of)
         mark(3)
-        moe_grouped_ffn_fp8(c, N, T * k, self.xq, self.xs, self.row_token, self.offsets,
-                            self.w1, self.w1s, self.w3, self.w3s, self.w2, self.w2s,
-                            y=self.y_rows, ws=self.ws)
+        moe_grouped_ffn_fp8_gate_up(c, EA, rows, self.xq, self.xs, self.row_token, self.offsets,
+                                    self.w1, self.w1s, self.w3, self.w3s, ws=self.ws)
         mark(4)
-        if S > 0:
-            moe_grouped_ffn_fp8(c, S, S * T, self.xq, self.xs, None, self.sh_offsets,
-                                self.sw1[:S], self.sw1s[:S], self.sw3[:S], self.sw3s[:S],
-                                self.sw2[:S], self.sw2s[:S], y=self.y_shared, ws=self.ws_sh)
+        moe_grouped_ffn_fp8_down(c, EA, rows, self.w2, self.w2s, self.ws, y=self.y_rows)
         mark(5)
         moe_combine(c, self.y_rows, self.row_of, self.topk_gate, self.y_shared, self.out)
         mark(6)

@@ -59,7 +59,7 @@ typedef struct moe_config {
   int32_t hidden;          /* H: hidden size, multiple of 128                         */
   int32_t inter;           /* I: expert intermediate size, multiple of 128            */
   int32_t n_routed;        /* N_r: routed experts, 1..512                             */
-  int32_t n_shared;        /* N_s: shared experts, >= 0                               */
+  int32_t n_shared;        /* N_s: shared experts, 0..16                              */
   int32_t top_k;           /* k: experts per token, 1..16                             */
   int32_t n_group;         /* G: expert groups (1 disables the limit); N_r % G == 0,
                               G <= 64                                                 */
@@ -152,21 +152,29 @@ moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype xt, int64_t
 /*
  * moe_permute — group the (token, slot) pairs by expert ([digest] section 3.2: the
  * output sums ffn_expert[idx[j]] over the slots; section 3.4: every token reaches its
- * experts, none is dropped). The expert histogram is recomputed from topk_idx, so the
- * outputs are consistent with it by construction.
- *   offsets   [N_r+1] int32, output: exclusive prefix sum of the per-expert loads
- *   row_token [T*k] int32, output: token of each permuted row; rows of expert e are
- *             offsets[e]..offsets[e+1]-1, in ascending token order
+ * experts, none is dropped), followed by one segment per shared expert that every token
+ * passes ([guide] section 3: num_shared_experts; [digest] section 3.2: shared plus
+ * routed experts), so a single moe_grouped_ffn_fp8 call over N_r + N_s experts serves
+ * both. The expert histogram is recomputed from topk_idx, so the outputs are consistent
+ * with it by construction.
+ *   offsets   [N_r+N_s+1] int32, output. offsets[0..N_r] is the exclusive prefix sum of
+ *             the routed loads; offsets[N_r+1+s] = T*k + (s+1)*T.
+ *   row_token [T*(k+N_s)] int32, output: token of each permuted row. Rows of routed
+ *             expert e are offsets[e]..offsets[e+1]-1 in ascending token order; shared
+ *             expert s owns rows T*k + s*T + t (token t). Rows offsets[N_r]..T*k-1 exist
+ *             only when topk_idx holds entries outside [0, N_r); they carry -1 (a row the
+ *             grouped FFN turns into zeros) and belong to the first shared segment.
  *   row_of    [T, k] int32, output: permuted row of (t, j)
  * topk_idx entries outside [0, N_r) are skipped (their row_of is -1). Experts must be
  * distinct within a token (moe_route guarantees it); otherwise rows are unspecified
  * but all accesses stay in bounds.
- * Errors: NULL pointers; invalid config; T < 0 or T*k >= 2^31.
+ * Errors: NULL pointers; invalid config; T < 0 or T*(k+N_s) >= 2^31.
  */
 moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,
                        int32_t* offsets, int32_t* row_token, int32_t* row_of, void* stream);
 
-/* Workspace bytes moe_grouped_ffn_fp8 needs for n_experts experts and n_rows rows. */
+/* Workspace bytes the grouped FFN needs for n_experts experts and n_rows rows (the same
+ * figure serves moe_grouped_ffn_fp8 and the gate_up / down pair). */
 size_t moe_grouped_ffn_workspace_bytes(const moe_config* cfg, int32_t n_experts,
                                        int64_t n_rows);
 
@@ -190,9 +198,13 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_config* cfg, int32_t n_experts,
  *             w1s, w3s [n_experts, I/128, H/128] float (row-major block scales)
  *   w2        [n_experts, H, I] codes, packed likewise; w2s [n_experts, H/128, I/128] float
  *   y         [n_rows, H] of dtype yt (MOE_BF16 or MOE_F32), output
- *   ws        workspace of at least moe_grouped_ffn_workspace_bytes(...) bytes
- * Rows whose token index falls outside [0, n_tokens) produce y = 0.
- * Errors: NULL pointers; invalid config; n_experts < 1; n_rows < 0; workspace.
+ *   ws        workspace of at least moe_grouped_ffn_workspace_bytes(...) bytes; holds
+ *             the tile plan and the quantised intermediate (hq, hs) between the halves
+ * Rows whose token index falls outside [0, n_tokens) produce y = 0. Rows outside every
+ * expert segment are not written.
+ * Errors: NULL pointers; invalid config; n_experts < 1 or > 1024; n_rows < 0;
+ * workspace; MOE_ERR_UNSUPPORTED for H or I > 16384, n_tokens*H or n_rows*I >= 2^32.
+ * Equivalent to moe_grouped_ffn_fp8_gate_up followed by moe_grouped_ffn_fp8_down.
  */
 moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
                                int64_t n_tokens, const uint8_t* xq, const float* xs,
@@ -203,14 +215,37 @@ moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_experts, int64_t
                                void* stream);
 
 /*
+ * moe_grouped_ffn_fp8_gate_up — first half of moe_grouped_ffn_fp8 (same passages):
+ * plans the tiles from offsets, computes G, U, h and stores its 1x128 re-quantisation
+ * (hq, hs) in ws. Arguments as in moe_grouped_ffn_fp8.
+ */
+moe_status moe_grouped_ffn_fp8_gate_up(const moe_config* cfg, int32_t n_experts,
+                                       int64_t n_rows, int64_t n_tokens, const uint8_t* xq,
+                                       const float* xs, const int32_t* row_token,
+                                       const int32_t* offsets, const uint8_t* w1,
+                                       const float* w1s, const uint8_t* w3, const float* w3s,
+                                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn_fp8_down — second half: y = DQ(hq) . DQ(W2_e)^T for every row, from
+ * the plan and intermediate that the preceding moe_grouped_ffn_fp8_gate_up call with the
+ * same cfg, n_experts and n_rows left in ws (stream-ordered after it). If ws holds no
+ * such result, y is unspecified but every access stays in bounds.
+ */
+moe_status moe_grouped_ffn_fp8_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
+                                    const uint8_t* w2, const float* w2s, void* y, moe_dtype yt,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_combine — weighted combine ([digest] section 3.2: y = sum_j gate[j] *
  * ffn_expert[idx[j]](h)) plus the shared experts with gate 1 ([guide] section 3
  * num_shared_experts). FP32 accumulation in fixed order (shared experts 0..N_s-1,
  * then slots 0..k-1), rounded once to bf16.
- *   y_rows    [T*k, H] of dtype yt
+ *   y_rows    [T*k, H] of dtype yt (rows past T*k, if any, are not read)
  *   row_of    [T, k] int32 (entries < 0 are skipped)
  *   topk_gate [T, k] float
- *   y_shared  [N_s, T, H] of dtype yt, or NULL when N_s == 0
+ *   y_shared  [N_s, T, H] of dtype yt, or NULL when N_s == 0 (after moe_permute and one
+ *             grouped FFN call over N_r + N_s experts this is y_rows + T*k rows)
  *   out       [T, H] bf16 bits, output
  * Errors: NULL pointers; invalid config; T < 0.
  */

@@ -29,7 +29,8 @@ def _declared():
 def test_header_declares_the_six_calls():
     names = _declared()
     for n in ("moe_quantize_1x128", "moe_route", "moe_permute", "moe_grouped_ffn_fp8",
-              "moe_combine", "moe_update_bias"):
+              "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
+              "moe_update_bias"):
         assert n in names
 
 
@@ -72,7 +73,7 @@ def test_host_validation_status_codes():
     bad = [dict(hidden=200), dict(inter=0), dict(n_routed=0), dict(n_routed=1024),
            dict(top_k=17), dict(top_k=20, n_routed=16), dict(n_group=3),
            dict(n_group=4, topk_group=5), dict(n_group=4, topk_group=1, top_k=5),
-           dict(n_group=4, topk_group=2, group_topn=5)]
+           dict(n_group=4, topk_group=2, group_topn=5), dict(n_shared=17), dict(n_shared=-1)]
     for b in bad:
         c = _cfg(m, **b)
         assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, None) == 2, b
@@ -94,6 +95,25 @@ def test_host_validation_status_codes():
                                  fake, need, None) == 2
     assert L.moe_grouped_ffn_fp8(ctypes.byref(c), 16, 256, 64, fake, fake, None, *args[:7], fake, 9,
                                  fake, need, None) == 3
+    # the two halves
+    assert L.moe_grouped_ffn_fp8_gate_up(ctypes.byref(c), 16, 256, 64, fake, fake, None, *args[:5],
+                                         fake, need - 1, None) == 6
+    assert L.moe_grouped_ffn_fp8_gate_up(ctypes.byref(c), 16, 256, 64, fake, fake, None, fake, None,
+                                         fake, fake, fake, fake, need, None) == 1
+    assert L.moe_grouped_ffn_fp8_gate_up(ctypes.byref(c), 2000, 256, 64, fake, fake, None, *args[:5],
+                                         fake, need, None) == 2
+    assert L.moe_grouped_ffn_fp8_down(ctypes.byref(c), 16, 256, fake, fake, fake, 1, fake, need - 1,
+                                      None) == 6
+    assert L.moe_grouped_ffn_fp8_down(ctypes.byref(c), 16, 256, fake, fake, fake, 4, fake, need,
+                                      None) == 3
+    assert L.moe_grouped_ffn_fp8_down(ctypes.byref(c), 16, 256, fake, None, fake, 1, fake, need,
+                                      None) == 1
+    # too large for 32-bit operand offsets
+    big = _cfg(m, hidden=16384, inter=16384)
+    assert L.moe_grouped_ffn_fp8_gate_up(ctypes.byref(big), 16, 1 << 18, 64, fake, fake, None,
+                                         *args[:5], fake, 1 << 62, None) == 4
+    assert L.moe_grouped_ffn_fp8_gate_up(ctypes.byref(c), 16, 256, 1 << 25, fake, fake, None,
+                                         *args[:5], fake, need, None) == 4
 
 
 def test_workspace_size_grows_with_rows():

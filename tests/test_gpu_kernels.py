@@ -247,21 +247,61 @@ def _idx(rng, T, N, k, skew=None):
     return np.stack([rng.choice(N, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
 
 
-@pytest.mark.parametrize("T,N,k,skew", [(64, 16, 4, None), (4096, 256, 8, None),
-                                        (16384, 256, 8, 1.1), (1, 256, 8, None), (1500, 512, 16, None),
-                                        (3000, 64, 6, 2.0)])
-def test_permute_matches_oracle(lib, T, N, k, skew):
+def _check_permute(idx, N, S, off, rt, ro):
+    """Routed part bit-exact against the oracle; shared segments by their closed form."""
+    T, k = idx.shape
+    off, rt, ro = host(off), host(rt), host(ro)
+    valid = (idx >= 0) & (idx < N)
+    if valid.all():
+        r_off, r_rt, r_ro = oracle.permute(idx, N)
+        assert np.array_equal(off[:N + 1], r_off)
+        assert np.array_equal(rt[:T * k], r_rt)
+        assert np.array_equal(ro, r_ro)
+    V = int(valid.sum())
+    assert off[N] == V
+    assert np.array_equal(off[N + 1:], T * k + T * np.arange(1, S + 1))
+    assert np.all(rt[V:T * k] == -1)
+    assert np.array_equal(rt[T * k:], np.tile(np.arange(T), S))
+    return off, rt, ro
+
+
+@pytest.mark.parametrize("T,N,k,skew,S", [(64, 16, 4, None, 1), (4096, 256, 8, None, 1),
+                                          (16384, 256, 8, 1.1, 1), (1, 256, 8, None, 1),
+                                          (1500, 512, 16, None, 0), (3000, 64, 6, 2.0, 2)])
+def test_permute_matches_oracle(lib, T, N, k, skew, S):
     import dataclasses
-    cfg = dataclasses.replace(synth.PRESETS["tiny"], num_experts=N, num_experts_per_tok=k, tokens=T)
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], num_experts=N, num_experts_per_tok=k, tokens=T,
+                              num_shared_experts=S)
     rng = np.random.default_rng(T + N)
     idx = _idx(rng, T, N, k, skew)
-    say(f"permute T={T} N={N} k={k} skew={skew}")
+    say(f"permute T={T} N={N} k={k} skew={skew} S={S}")
     off, rt, ro = lib.moe_permute(lib.make_config(cfg), dev(idx))
     torch.cuda.synchronize()
-    r_off, r_rt, r_ro = oracle.permute(idx, N)
-    assert np.array_equal(host(off), r_off)
-    assert np.array_equal(host(rt), r_rt)
-    assert np.array_equal(host(ro), r_ro)
+    _check_permute(idx, N, S, off, rt, ro)
+
+
+def test_permute_invalid_entries(lib):
+    """Entries naming no routed expert are skipped; the rows they leave free read token -1."""
+    import dataclasses
+    T, N, k, S = 500, 64, 6, 2
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], num_experts=N, num_experts_per_tok=k, tokens=T,
+                              num_shared_experts=S)
+    rng = np.random.default_rng(5)
+    idx = _idx(rng, T, N, k)
+    idx[rng.random((T, k)) < 0.05] = -1
+    idx[7, 2] = N + 3
+    say("permute with invalid entries")
+    off, rt, ro = lib.moe_permute(lib.make_config(cfg), dev(idx))
+    torch.cuda.synchronize()
+    off, rt, ro = _check_permute(idx, N, S, off, rt, ro)
+    valid = (idx >= 0) & (idx < N)
+    assert np.all(ro[~valid] == -1)
+    # every valid pair has its own row, inside its expert's segment, naming its token
+    rows = ro[valid]
+    assert len(set(rows.tolist())) == rows.size
+    e = idx[valid]
+    assert np.all((off[e] <= rows) & (rows < off[e + 1]))
+    assert np.array_equal(rt[rows], np.nonzero(valid)[0])
 
 
 def test_permute_collapse_and_empty(lib):
@@ -272,8 +312,9 @@ def test_permute_collapse_and_empty(lib):
     say("permute collapse")
     off, rt, ro = lib.moe_permute(c, dev(idx))
     torch.cuda.synchronize()
-    r = oracle.permute(idx, 256)
-    assert np.array_equal(host(off), r[0]) and np.array_equal(host(rt), r[1]) and np.array_equal(host(ro), r[2])
+    off, _, _ = _check_permute(idx, 256, 1, off, rt, ro)
+    cnt = np.diff(off[:257])
+    assert np.all(cnt[200:208] == 2048) and cnt.sum() == 2048 * 8
     say("permute T=0")
     off, rt, ro = lib.moe_permute(c, torch.empty((0, 8), dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
@@ -362,6 +403,31 @@ def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity):
         ref = oracle.expert_ffn(xq[toks], xs[toks], w[0][e], w[1][e], w[2][e], w[3][e], w[4][e], w[5][e])[0]
         err = _relerr(y[lo:hi], ref)
         assert err < 5e-3, (e, err)
+
+
+def test_grouped_ffn_halves_equal_fused_call(lib):
+    """gate_up + down on one workspace gives the fused call's output bit for bit (a load
+    mix with several M tiles per expert, so the tile order differs from expert order)."""
+    import dataclasses
+    rng = np.random.default_rng(77)
+    H, I, E = 768, 384, 6
+    loads = [5, 400, 0, 193, 64, 250]
+    rows, T = int(sum(loads)), 333
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], hidden_size=H, moe_intermediate_size=I,
+                              num_experts=8, num_experts_per_tok=1, tokens=T)
+    c = lib.make_config(cfg)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    xq, xs = oracle.quantize_1x128(x)
+    offsets = np.concatenate([[0], np.cumsum(loads)]).astype(np.int32)
+    row_token = rng.integers(0, T, rows).astype(np.int32)
+    w = _device_weights(lib, _expert_set(rng, E, H, I))
+    args = (dev(xq), dev(xs), dev(row_token), dev(offsets))
+    say("grouped_ffn halves vs fused")
+    y_fused = lib.moe_grouped_ffn_fp8(c, E, rows, *args, *w, y_dtype=torch.float32)
+    ws = lib.moe_grouped_ffn_fp8_gate_up(c, E, rows, *args, *w[:4])
+    y_split = lib.moe_grouped_ffn_fp8_down(c, E, rows, w[4], w[5], ws, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y_fused).view(np.uint32), host(y_split).view(np.uint32))
 
 
 def test_grouped_ffn_bf16_output_and_bad_tokens(lib):

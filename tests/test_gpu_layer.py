@@ -64,6 +64,9 @@ def test_layer_matches_oracle(name):
         assert np.array_equal(MoELayer.unpack(layer.w1[e].cpu().numpy()), routed[e][0])
         assert np.array_equal(MoELayer.unpack(layer.w2[e].cpu().numpy()), routed[e][4])
         assert np.array_equal(layer.w2s[e].cpu().numpy(), routed[e][5])
+    for s_ in range(cfg.num_shared_experts):   # shared experts follow the routed ones
+        assert np.array_equal(MoELayer.unpack(layer.w1[cfg.num_experts + s_].cpu().numpy()), shared[s_][0])
+        assert np.array_equal(layer.w3s[cfg.num_experts + s_].cpu().numpy(), shared[s_][3])
     ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s])
     r = ref["route"]
     tie = routing_ties(r)
