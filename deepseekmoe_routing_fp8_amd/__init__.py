@@ -26,7 +26,7 @@ MOE_F32, MOE_BF16 = 0, 1
 
 ENTRY_POINTS = (
     "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_pack_fp8_weights",
-    "moe_pack_router_weights", "moe_route",
+    "moe_pack_router_weights", "moe_router_weights_elems", "moe_route", "moe_route_workspace_bytes",
     "moe_permute", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8",
     "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
     "moe_update_bias",
@@ -59,7 +59,9 @@ _sig = {
     "moe_quantize_128x128": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "moe_pack_fp8_weights": ([_P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
     "moe_pack_router_weights": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
-    "moe_route": ([_CFG, _P, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_router_weights_elems": ([_I64, _I64], _SZ),
+    "moe_route": ([_CFG, _P, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "moe_route_workspace_bytes": ([_CFG, _I64, ctypes.c_int], _SZ),
     "moe_permute": ([_CFG, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_grouped_ffn_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
     "moe_grouped_ffn_fp8": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -156,22 +158,36 @@ def moe_pack_fp8_weights(q: torch.Tensor, packed: torch.Tensor = None, stream=No
     return packed
 
 
+def moe_router_weights_elems(n_routed: int, hidden: int) -> int:
+    return int(_lib.moe_router_weights_elems(n_routed, hidden))
+
+
 def moe_pack_router_weights(w_router: torch.Tensor, out: torch.Tensor = None, stream=None):
-    """FP32 router weight [N_r, H] -> [3, N_r, H] bfloat16 planes with hi + mid + lo == W_r."""
+    """FP32 router weight [N_r, H] -> packed bf16 planes (hi + mid + lo == W_r) in the MFMA
+    fragment order moe_route reads (a flat tensor of moe_router_weights_elems elements)."""
     N, H = w_router.shape
-    out = torch.empty((3, N, H), dtype=torch.bfloat16, device=w_router.device) if out is None else out
+    n = moe_router_weights_elems(N, H)
+    if n == 0:
+        raise MoEError("moe_pack_router_weights: unsupported shape")
+    out = torch.empty((n,), dtype=torch.bfloat16, device=w_router.device) if out is None else out
     _check(_lib.moe_pack_router_weights(_dev(w_router, torch.float32, "w_router", (N, H)), N, H,
-                                        _dev(out, torch.bfloat16, "w_split", (3, N, H)),
+                                        _dev(out, torch.bfloat16, "w_split", (n,)),
                                         _stream(stream)), "moe_pack_router_weights")
     return out
 
 
+def moe_route_workspace_bytes(cfg: moe_config, T: int, xt: int) -> int:
+    return int(_lib.moe_route_workspace_bytes(ctypes.byref(cfg), T, xt))
+
+
 def moe_route(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
               scores: torch.Tensor = None, topk_idx: torch.Tensor = None,
-              topk_gate: torch.Tensor = None, counts: torch.Tensor = None, stream=None):
+              topk_gate: torch.Tensor = None, counts: torch.Tensor = None,
+              ws: torch.Tensor = None, stream=None):
     """Router: -> (scores [T,N_r] f32, topk_idx [T,k] i32, topk_gate [T,k] f32, counts i32).
 
-    ``w_router`` is the [3, N_r, H] bf16 split from moe_pack_router_weights."""
+    ``w_router`` is the packed split from moe_pack_router_weights; ``ws`` a workspace of
+    moe_route_workspace_bytes bytes (allocated here when None)."""
     T = x.shape[0]
     N, k = cfg.n_routed, cfg.top_k
     dev = x.device
@@ -179,13 +195,18 @@ def moe_route(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, bias: to
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
     topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
     counts = torch.empty((N,), dtype=torch.int32, device=dev) if counts is None else counts
+    need = moe_route_workspace_bytes(cfg, T, _xdtype(x))
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     _check(_lib.moe_route(ctypes.byref(cfg), _dev(x, x.dtype, "x", (T, cfg.hidden)), _xdtype(x), T,
-                          _dev(w_router, torch.bfloat16, "w_router_split", (3, N, cfg.hidden)),
+                          _dev(w_router, torch.bfloat16, "w_router_split",
+                               (moe_router_weights_elems(N, cfg.hidden),)),
                           _dev(bias, torch.float32, "bias", (N,)),
                           _dev(scores, torch.float32, "scores", (T, N)),
                           _dev(topk_idx, torch.int32, "topk_idx", (T, k)),
                           _dev(topk_gate, torch.float32, "topk_gate", (T, k)),
-                          _dev(counts, torch.int32, "counts", (N,)), _stream(stream)),
+                          _dev(counts, torch.int32, "counts", (N,)),
+                          _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
            "moe_route")
     return scores, topk_idx, topk_gate, counts
 

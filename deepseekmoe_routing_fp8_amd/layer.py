@@ -16,9 +16,9 @@ from typing import Callable, Iterable, Optional
 import numpy as np
 import torch
 
-from . import (make_config, moe_combine, moe_grouped_ffn_fp8_down, moe_grouped_ffn_fp8_gate_up,
+from . import (MOE_F32, make_config, moe_combine, moe_grouped_ffn_fp8_down, moe_grouped_ffn_fp8_gate_up,
                moe_grouped_ffn_workspace_bytes, moe_pack_fp8_weights, moe_pack_router_weights, moe_permute, moe_quantize_1x128, moe_quantize_128x128,
-               moe_route, moe_update_bias)
+               moe_route, moe_route_workspace_bytes, moe_update_bias)
 
 
 class MoELayer:
@@ -110,6 +110,9 @@ class MoELayer:
                               dtype=torch.uint8, device=d)
         self.y_shared = self.y_rows[T * k:] if S > 0 else None
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+        # sized for FP32 input, the larger of the two
+        self.route_ws = torch.empty((max(moe_route_workspace_bytes(self.c, T, MOE_F32), 1),),
+                                    dtype=torch.uint8, device=d)
         self._T = T
 
     # -- forward -------------------------------------------------------------------
@@ -131,7 +134,7 @@ class MoELayer:
         moe_quantize_1x128(x, self.xq, self.xs)
         mark(1)
         moe_route(c, x, self.w_router, self.bias, self.scores, self.topk_idx, self.topk_gate,
-                  self.counts)
+                  self.counts, ws=self.route_ws)
         mark(2)
         moe_permute(c, self.topk_idx, self.offsets, self.row_token, self.row_of)
         mark(3)

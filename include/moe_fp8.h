@@ -118,12 +118,20 @@ moe_status moe_pack_fp8_weights(const uint8_t* q, int64_t mats, int64_t rows, in
  * per weight load; lets the router run its FP32-exact products on bf16 MFMAs.
  * Exact for every |W_r| >= 2^-110 and 0; below that the last piece is rounded to
  * bf16's subnormal grid (error <= 2^-133).
+ * Layout (MFMA fragment order): with nb16 = ceil(N_r/16), plane q (0 = RNE bf16 of W_r,
+ * 1 = mid, 2 = lo), expert block b (16 experts) and K step ks (32 columns) form one
+ * 512-element fragment at element ((q*nb16 + b)*(H/32) + ks)*512; its elements
+ * 8*l .. 8*l+7 are plane q of W_r[16*b + l%16][32*ks + 8*(l/16) .. +8], l = 0..63.
+ * Rows past N_r are zero.
  *   w_router  [N_r, H] float
- *   w_split   [3, N_r, H] bf16 bit patterns, output (plane 0 = RNE bf16 of W_r)
- * Errors: NULL pointers; N_r < 0; H not a positive multiple of 128.
+ *   w_split   moe_router_weights_elems(N_r, H) bf16 bit patterns, output, 16-byte aligned
+ * Errors: NULL pointers; N_r outside 1..512; H not a positive multiple of 128.
  */
 moe_status moe_pack_router_weights(const float* w_router, int64_t n_routed, int64_t hidden,
                                    uint16_t* w_split, void* stream);
+
+/* Elements of moe_pack_router_weights' output: 3 * ceil(N_r/16)*16 * H (0 if invalid). */
+size_t moe_router_weights_elems(int64_t n_routed, int64_t hidden);
 
 /*
  * moe_route — router ([digest] section 3.2 pseudocode and prose; section 3.4 group
@@ -131,23 +139,31 @@ moe_status moe_pack_router_weights(const float* w_router, int64_t n_routed, int6
  * high precision).
  *   s = sigmoid(x . W_r^T) from unquantised x. Every product is an exact product of the
  *   FP32 operands (bf16-piece MFMAs), summed in FP32 within each 128-wide K chunk and
- *   promoted into an FP64 accumulator; s is rounded to FP32. Ranking score s + b (FP32).
+ *   promoted into FP64 accumulators (per contiguous range of chunks, then the ranges
+ *   in order); s is rounded to FP32. Ranking score s + b (FP32).
  *   With G > 1: a group's score is the FP32 sum of its group_topn best ranking scores;
  *   the G_k best groups are kept (ties: lower group index); experts elsewhere are
  *   excluded. Top-k by ranking score, descending, ties to the lower expert index.
  *   Gates: s[idx_j] / sum_j s[idx_j] * rho (unbiased s). counts[e] = selections of e.
- *   x               [T, H] of dtype xt
- *   w_router_split  [3, N_r, H] bf16 planes of W_r from moe_pack_router_weights
+ *   x               [T, H] of dtype xt, 16-byte aligned
+ *   w_router_split  packed planes of W_r from moe_pack_router_weights
  *   bias            [N_r] float
  *   scores          [T, N_r] float, output: the sigmoid affinities s
  *   topk_idx        [T, k] int32, output, slot order = descending ranking score
  *   topk_gate       [T, k] float, output
  *   counts          [N_r] int32, output (overwritten, not accumulated)
- * Errors: NULL pointers; invalid config (see moe_config); T < 0.
+ *   ws              workspace of moe_route_workspace_bytes(cfg, T, xt) bytes (partial
+ *                   logits; NULL allowed when that is 0)
+ * Errors: NULL pointers; invalid config (see moe_config); T < 0; workspace;
+ * MOE_ERR_UNSUPPORTED for misaligned x or w_router_split.
  */
 moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype xt, int64_t T,
                      const uint16_t* w_router_split, const float* bias, float* scores,
-                     int32_t* topk_idx, float* topk_gate, int32_t* counts, void* stream);
+                     int32_t* topk_idx, float* topk_gate, int32_t* counts, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Workspace bytes moe_route needs for T tokens of dtype xt (0 for T = 0 or invalid). */
+size_t moe_route_workspace_bytes(const moe_config* cfg, int64_t T, moe_dtype xt);
 
 /*
  * moe_permute — group the (token, slot) pairs by expert ([digest] section 3.2: the

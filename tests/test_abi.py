@@ -76,12 +76,25 @@ def test_host_validation_status_codes():
            dict(n_group=4, topk_group=2, group_topn=5), dict(n_shared=17), dict(n_shared=-1)]
     for b in bad:
         c = _cfg(m, **b)
-        assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, None) == 2, b
+        assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, fake,
+                           1 << 30, None) == 2, b
         assert L.moe_permute(ctypes.byref(c), 4, fake, fake, fake, fake, None) == 2, b
     c = _cfg(m)
-    assert L.moe_route(None, fake, 1, 4, fake, fake, fake, fake, fake, fake, None) == 1
-    assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, None, fake, fake, fake, fake, None) == 1
-    assert L.moe_route(ctypes.byref(c), fake, 5, 4, fake, fake, fake, fake, fake, fake, None) == 3
+    big = 1 << 30
+    assert L.moe_route(None, fake, 1, 4, fake, fake, fake, fake, fake, fake, fake, big, None) == 1
+    assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, None, fake, fake, fake, fake, fake, big, None) == 1
+    assert L.moe_route(ctypes.byref(c), fake, 5, 4, fake, fake, fake, fake, fake, fake, fake, big, None) == 3
+    need_r = L.moe_route_workspace_bytes(ctypes.byref(c), 4, 1)
+    assert need_r > 0
+    assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, None, 0, None) == 6
+    assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, fake,
+                       need_r - 1, None) == 6
+    assert L.moe_route(ctypes.byref(c), P(0x1008), 1, 4, fake, fake, fake, fake, fake, fake, fake,
+                       need_r, None) == 4   # misaligned x
+    # FP32 input needs room for its three bf16 planes
+    assert L.moe_route_workspace_bytes(ctypes.byref(c), 4, 0) > need_r
+    assert L.moe_router_weights_elems(20, 256) == 3 * 32 * 256
+    assert L.moe_router_weights_elems(20, 100) == 0
     assert L.moe_permute(ctypes.byref(c), -2, fake, fake, fake, fake, None) == 2
     assert L.moe_combine(ctypes.byref(c), 4, fake, 1, fake, fake, None, fake, None) == 1  # N_s=1 needs y_shared
     assert L.moe_update_bias(ctypes.byref(c), 4, None, fake, None) == 1

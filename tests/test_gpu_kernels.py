@@ -208,7 +208,10 @@ def test_route_general_shapes(lib):
     for kw in [dict(num_experts=48, num_experts_per_tok=1, n_group=4, topk_group=2, group_score_topn=3),
                dict(num_experts=96, num_experts_per_tok=5, n_group=6, topk_group=3),
                dict(num_experts=16, num_experts_per_tok=16),
-               dict(tokens=1), dict(tokens=130, num_experts=32, num_experts_per_tok=3)]:
+               dict(tokens=1), dict(tokens=130, num_experts=32, num_experts_per_tok=3),
+               dict(tokens=300, num_experts=20, num_experts_per_tok=3, n_group=4, topk_group=2),
+               dict(tokens=700, hidden_size=1024, num_experts=200, num_experts_per_tok=6, n_group=8,
+                    topk_group=3, group_score_topn=2)]:
         cfg = dataclasses.replace(base, **kw)
         say(f"route general {kw}")
         x = synth.hidden_states(cfg)
@@ -220,13 +223,26 @@ def test_route_general_shapes(lib):
         check_routing(cfg, x, wr, b, host(s), host(idx), host(gate), host(counts))
 
 
+def _unpack_router(flat, N, H):
+    """Packed router planes -> [3, N, H] by the documented index map (re-indexing only)."""
+    nb16 = (N + 15) // 16
+    f = flat.reshape(3, nb16, H // 32, 4, 16, 8)            # q, block, K step, lane/16, lane%16, j
+    full = f.transpose(0, 1, 4, 2, 3, 5).reshape(3, nb16 * 16, H)
+    return full[:, :N], full[:, N:]
+
+
 def test_pack_router_weights_exact(lib):
-    """hi + mid + lo reproduces every FP32 weight exactly; hi is the RNE bf16 of W_r."""
+    """hi + mid + lo reproduces every FP32 weight exactly; hi is the RNE bf16 of W_r; rows
+    past N_r are zero."""
     rng = np.random.default_rng(13)
-    w = (rng.standard_normal((64, 512)) * np.exp2(rng.integers(-30, 30, (64, 512)))).astype(np.float32)
+    N, H = 60, 512
+    w = (rng.standard_normal((N, H)) * np.exp2(rng.integers(-30, 30, (N, H)))).astype(np.float32)
     w[0, :4] = [0.0, -0.0, 1.0, -3.0e-38]
     say("pack router weights")
-    sp = lib.moe_pack_router_weights(dev(w)).float().cpu().numpy().astype(np.float64)
+    flat = lib.moe_pack_router_weights(dev(w))
+    assert flat.numel() == lib.moe_router_weights_elems(N, H) == 3 * 64 * H
+    sp, pad = _unpack_router(flat.float().cpu().numpy().astype(np.float64), N, H)
+    assert np.all(pad == 0)
     total = sp[0] + sp[1] + sp[2]
     exact = (np.abs(w) >= 2.0 ** -110) | (w == 0)
     assert np.array_equal(total[exact], w.astype(np.float64)[exact])
