@@ -33,7 +33,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kMT = 192;              // max rows of one expert per tile (multiple of 16)
+constexpr int kMT = 160;              // max rows of one expert per tile (multiple of 16)
 constexpr int kThreads = 512;         // 8 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxExperts = 1024;
@@ -144,30 +144,37 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave, 4, 0, 0);
 }
 
-// Tile geometry. A workgroup computes 256 weight rows (16 fragments of 16 rows) against
-// up to kMT tokens, with 8 consumer waves and 4 producer waves.
-//   consumer wave w: fragments of 32 weight rows (phase 1: 16 rows of W1 and the same 16
-//     of W3; phase 2: 32 rows of W2) against all of the tile's tokens. It streams its own
-//     fragments into a private 3-slot LDS ring (its vector-memory counter tracks nothing
-//     else, so W(c+1) and W(c+2) stay in flight while it computes chunk c);
-//   producer waves copy the tile's activation rows and scales (L2-resident) into a
-//     2-slot LDS ring shared by all consumers; one workgroup barrier per K chunk
-//     publishes chunk c and frees chunk c-1's slot.
-constexpr int kConsumers = 8, kProducers = 4;
-constexpr int kFThreads = (kConsumers + kProducers) * kWave;   // 768
-constexpr int kNTS = kMT / 16;                   // 16-token tiles per M tile
+// Tile geometry. A workgroup of 8 waves computes 256 weight rows (16 fragments of 16
+// rows) against up to kMT rows of one expert.
+//   wave w: two fragments, i.e. 32 weight rows (phase 1: 16 rows of W1 and the same 16
+//     of W3; phase 2: 32 rows of W2), against all of the tile's rows. Its fragments
+//     stream from HBM straight into a VGPR ring; no other wave needs them, so they never
+//     touch LDS.
+//   the tile's activation rows and scales (gathered rows, L2-resident) are copied by all
+//     8 waves into an LDS ring by direct buffer->LDS loads. One workgroup barrier per K
+//     chunk publishes chunk c and frees chunk c-1.
+// Both rings have RING slots and run RING-1 chunks ahead: a wave's loads complete in
+// issue order, so the activation copies, which every chunk waits for, must be as deep
+// as the weight stream or they would drain it. All global reads are buffer loads: an
+// SGPR descriptor plus a 32-bit lane offset, and reads past a descriptor's range return
+// zeros without touching memory.
+constexpr int kFWaves = 8;
+constexpr int kFThreads = kFWaves * kWave;       // 512
+constexpr int kNTS = kMT / 16;                   // 16-row tiles per M tile
 constexpr int kFragBytes = 16 * kTile;           // one 16 x 128 fragment: 2 KB
-constexpr int kWPriv = 2 * kFragBytes;           // one consumer's weights per K chunk
-constexpr int kWStage = kConsumers * kWPriv;     // 32 KB
-constexpr int kActBytes = kMT * kTile;           // 24 KB of activation codes per chunk
-constexpr int kAStage = kActBytes + kMT * 4;     // + one scale per row
-constexpr int kActUnits = kActBytes / 16;        // 16-byte copies per chunk
-constexpr int kProdLanes = kProducers * kWave;
-static_assert(kActUnits % kProdLanes == 0, "activation copies split evenly");
-constexpr int kActDma = kActUnits / kProdLanes;  // per producer lane per chunk (6)
+constexpr int kActBytes = kMT * kTile;           // activation codes per chunk (20 KB)
+constexpr int kActRound = kFThreads * 16;        // bytes one copy instruction per wave moves
+constexpr int kActDma = (kActBytes + kActRound - 1) / kActRound;   // copies per lane (3)
+constexpr int kScaleWaves = (kMT + kWave - 1) / kWave;             // waves copying scales
+constexpr int kScaleBytes = kScaleWaves * kWave * 4;
+constexpr int kAStage = kActBytes + kScaleBytes; // one ring slot, a multiple of 128 bytes
+constexpr int kJunk = 1024;                      // landing area of copies past the slot
+constexpr int kStepOps = 4 + kActDma + 1;        // vector-memory ops per wave per chunk
+constexpr int kMaxRing = 7;
 constexpr int kXcds = 8;
 constexpr int kMaxChunks = 128;                  // K <= 16384
-constexpr int kUnroll = 6;                       // lcm(activation slots 2, weight slots 3)
+static_assert(kAStage % 128 == 0, "slot bases keep bit 6 of the swizzled offsets");
+static_assert((kMaxRing - 2) * kStepOps + kStepOps <= 63, "vmcnt holds every copy in flight");
 
 struct FfnArgs {
   const Tile* tiles;
@@ -175,7 +182,7 @@ struct FfnArgs {
   int max_tiles, n_experts, n_rows;
   const uint8_t* aq;     // activation codes: xq (phase 1) or hq (phase 2)
   const float* as;       // their 1x128 scales
-  int64_t n_tokens;
+  int64_t n_tokens;      // rows of aq
   const int32_t* row_token;
   const uint8_t* wa;     // packed W1 (phase 1) or W2 (phase 2)
   const float* wsa;
@@ -187,231 +194,215 @@ struct FfnArgs {
   void* y;               // phase 2 output
 };
 
-// Column operand (16 tokens x 128 K) from a staged activation chunk: lane group g holds
-// K bytes [16g, 16g+16) and [64+16g, 64+16g+16) of token (lane % 16), the K map of the
-// packed weights. Row r keeps its 16-byte segments at positions seg ^ (r & 7).
-__device__ __forceinline__ v8i act_frag(const uint8_t* act, int ts, int lane) {
-  const int r = ts * 16 + (lane & 15), g = lane >> 4;
-  const v4i lo = *reinterpret_cast<const v4i*>(act + r * kTile + ((g ^ (r & 7)) << 4));
-  const v4i hi = *reinterpret_cast<const v4i*>(act + r * kTile + (((g + 4) ^ (r & 7)) << 4));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+// Activation rows in a slot: row r keeps its 16-byte segment seg at position seg ^ (r&7).
+// A column operand (16 rows x 128 K) gives lane l row l%16 and K bytes [16g, 16g+16)
+// (g = l/16) and [64+16g, 64+16g+16), the K map of the packed weights. Tiles start at
+// multiples of 16 rows, so r & 7 == l & 7: the lane's first half sits at byte
+// act_lane_offset(l) of every tile and the second half at that offset ^ 64.
+__device__ __forceinline__ uint32_t act_lane_offset(int lane) {
+  return (lane & 15) * kTile + (((lane >> 4) ^ (lane & 7)) << 4);
 }
 
-// Row operand: fragment f of a consumer's private chunk (two 1 KB halves, lane*16 each).
-__device__ __forceinline__ v8i w_frag(const uint8_t* priv, int f, int lane) {
-  const v4i lo = *reinterpret_cast<const v4i*>(priv + f * kFragBytes + lane * 16);
-  const v4i hi = *reinterpret_cast<const v4i*>(priv + f * kFragBytes + kFragBytes / 2 + lane * 16);
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+typedef __attribute__((address_space(3))) const float lds_f32;
+
+struct FfnLds {
+  uint8_t* ast[kMaxRing];   // ring slots (kAStage bytes each, 128-byte aligned)
+  uint8_t* junk;            // kJunk bytes
+  const int* tok_s;         // source row of every tile row (-1: none)
+  const float* wsc;         // [2][kMaxChunks + kMaxRing] weight-block scales
+};
+
+// A wave-uniform pointer in scalar registers (buffer descriptors must be uniform; the
+// compiler cannot always prove it for values loaded from memory).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
+// Weight fragment of one lane. The whole offset is in the VGPR operand: the descriptor's
+// range check covers it (not an SGPR offset), so chunks past the range read zeros.
+__device__ __forceinline__ v8i buf_wfrag(__amdgpu_buffer_rsrc_t d, int voff) {
+  const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(d, voff, 0, 0));
+  const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(d, voff + kFragBytes / 2, 0, 0));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // ------------------------------------------------------------------------------------
-// One grouped-FFN GEMM phase over tiles (expert, M tile) x n-blocks.
-//   PHASE 1: 128 intermediate columns per workgroup; epilogue h = silu(G) * U,
-//            re-quantised 1x128 (amax over the 128 columns reduced across the 8
-//            consumers through LDS).
-//   PHASE 2: 256 output features per workgroup.
-// Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD,
-// so the tile's activation rows are fetched into that XCD's L2 once.
-// Steps are padded to a multiple of kUnroll (extra steps re-issue the last chunk and
-// skip compute) so that every wait is an immediate and never sits behind a branch.
+// Main loop and epilogue of one workgroup, for NT 16-row tiles (a compile-time count:
+// the tile's rows rounded up to 16 or more; rows past the tile are computed on a clamped
+// row and dropped) and a RING-slot pipeline. The K loop runs over the chunk count rounded
+// up to RING and is unrolled by RING, so ring slots are static, no step computes
+// conditionally and every wait is the same immediate; chunks past the last one read
+// zero weights (and carry weight scales 0), adding exact zeros.
 // ------------------------------------------------------------------------------------
-template <int PHASE, typename YT>
-__global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t wst0[kWStage];
-  __shared__ __attribute__((aligned(16))) uint8_t wst1[kWStage];
-  __shared__ __attribute__((aligned(16))) uint8_t wst2[kWStage];
-  __shared__ __attribute__((aligned(16))) uint8_t ast0[kAStage];
-  __shared__ __attribute__((aligned(16))) uint8_t ast1[kAStage];
-  __shared__ int tok_s[kMT];
-  __shared__ float wsc[2][kMaxChunks];   // weight-block scales per K chunk (two row blocks)
-  __shared__ float red[PHASE == 1 ? kConsumers : 1][kMT];   // phase-1 amax partials
-
-  const int L = blockIdx.x;
-  const int xcd = L % kXcds, slot = L / kXcds;
-  const int tile = (slot / a.n_nb) * kXcds + xcd;
-  const int nb = slot % a.n_nb;
-  if (tile >= min(*a.n_tiles, a.max_tiles)) return;
-  const Tile tl = a.tiles[tile];
-  // a workspace that does not hold this call's plan must not lead out of bounds
-  if (tl.e < 0 || tl.e >= a.n_experts || tl.mlen < 1 || tl.mlen > kMT || tl.m0 < 0 ||
-      tl.m0 > a.n_rows - tl.mlen)
-    return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool producer = wave >= kConsumers;
+template <int PHASE, typename YT, int NT, int RING>
+__device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int nb, int wave,
+                                         int lane, const FfnLds& sh) {
+  static_assert(RING >= 3 && RING <= kMaxRing, "ring depth");
+  static_assert(NT * 16 <= kMT, "tile rows");
+  const int tid = wave * kWave + lane;
   const int K = PHASE == 1 ? a.H : a.I;
   const int nkc = K / kTile;
-  const int nts = (tl.mlen + 15) >> 4;
-  const int nsteps = (nkc + kUnroll - 1) / kUnroll * kUnroll;
   const int last = nkc - 1;
+  const int nsteps = (nkc + RING - 1) / RING * RING;
 
-  // source row of every tile row: a token (phase 1) or a permuted row (phase 2)
-  for (int r = tid; r < kMT; r += kFThreads) {
-    int t = -1;
-    if (r < tl.mlen) {
-      if (PHASE == 1) {
-        const int64_t v = a.row_token ? (int64_t)a.row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
-        t = (v >= 0 && v < a.n_tokens) ? (int)v : -1;
-      } else {
-        t = tl.m0 + r;
-      }
-    }
-    tok_s[r] = t;
-  }
-  // weight-block scales for every K chunk: phase 1 (W1, W3) of row block nb; phase 2 the
-  // two W2 row blocks of this workgroup's 256 rows
-  const int64_t nrb = (PHASE == 1 ? a.I : a.H) / kTile;
-  for (int c = tid; c < 2 * nkc; c += kFThreads) {
-    const int which = c / nkc, kc = c % nkc;
-    float v;
-    if (PHASE == 1) {
-      v = (which == 0 ? a.wsa : a.wsb)[((int64_t)tl.e * nrb + nb) * nkc + kc];
-    } else {
-      const int64_t rb = min((int64_t)nb * 2 + which, nrb - 1);
-      v = a.wsa[((int64_t)tl.e * nrb + rb) * nkc + kc];
-    }
-    wsc[which][kc] = v;
-  }
-  __syncthreads();
-
-  if (producer) {
-    // ---------------- producer waves: activation rows + scales ----------------
-    const int pl = (wave - kConsumers) * kWave + lane;          // 0..255
-    uint32_t aoff[kActDma];
+  // activation copies of this lane: kActDma 16-byte units and one scale
+  const __amdgpu_buffer_rsrc_t adesc =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.aq), 0, (int)(uint32_t)(a.n_tokens * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sdesc =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.as), 0, (int)(uint32_t)(a.n_tokens * nkc * 4), 0x00020000);
+  int aoff[kActDma];
 #pragma unroll
-    for (int j = 0; j < kActDma; ++j) {
-      const int sidx = j * kProdLanes + pl;
-      const int r = sidx >> 3, seg = (sidx & 7) ^ (r & 7);
-      const int src = max(tok_s[min(r, tl.mlen - 1)], 0);
-      aoff[j] = (uint32_t)src * (uint32_t)K + seg * 16;
-    }
-    const bool has_scale = pl < kMT;
-    const uint32_t soff = (uint32_t)max(tok_s[min(pl, tl.mlen - 1)], 0) * (uint32_t)nkc;
-    auto issue = [&](int c, uint8_t* st) {
-      const uint8_t* base = a.aq + (uint32_t)c * kTile;
-#pragma unroll
-      for (int j = 0; j < kActDma; ++j)
-        dma16(base + aoff[j], st + (j * kProdLanes + (wave - kConsumers) * kWave) * 16);
-      if (has_scale) dma4(a.as + soff + c, st + kActBytes + (wave - kConsumers) * kWave * 4);
-    };
-    issue(0, ast0);
-#define PROD_STEP(S)                                                   \
-    {                                                                  \
-      const int c = s0 + (S);                                          \
-      asm volatile("" ::: "memory");                                   \
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                 \
-      __builtin_amdgcn_s_barrier();                                    \
-      asm volatile("" ::: "memory");                                   \
-      issue(min(c + 1, last), ((S) % 2) == 0 ? ast1 : ast0);           \
-    }
-    for (int s0 = 0; s0 < nsteps; s0 += kUnroll) {
-      PROD_STEP(0) PROD_STEP(1) PROD_STEP(2) PROD_STEP(3) PROD_STEP(4) PROD_STEP(5)
-    }
-#undef PROD_STEP
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    asm volatile("" ::: "memory");
-    // epilogue barrier partner (phase 1 amax exchange)
-    if (PHASE == 1) __syncthreads();
-    return;
+  for (int j = 0; j < kActDma; ++j) {
+    const int unit = min((j * kActRound + wave * 1024 + lane * 16) / 16, kActBytes / 16 - 1);
+    const int r = unit >> 3, seg = (unit & 7) ^ (r & 7);
+    const int src = max(sh.tok_s[min(r, tl.mlen - 1)], 0);
+    aoff[j] = src * K + seg * 16;
   }
+  const int soff = max(sh.tok_s[min(tid, tl.mlen - 1)], 0) * nkc * 4;
 
-  // ---------------- consumer waves: weights + MFMAs ----------------
-  // this wave's two fragments: unit j (1 KB) = fragment j/2, half j%2
+  // this wave's two fragments
   const int64_t per_expert = (int64_t)a.H * a.I;
-  const uint8_t* fb[2];
+  const uint8_t* fb0;
+  const uint8_t* fb1;
   int64_t wrow;
   bool live = true;
   if (PHASE == 1) {
     wrow = (int64_t)nb * kTile + wave * 16;
     const int64_t off = (wrow / 16) * nkc * kFragBytes;
-    fb[0] = a.wa + (int64_t)tl.e * per_expert + off;
-    fb[1] = a.wb + (int64_t)tl.e * per_expert + off;
+    fb0 = a.wa + (int64_t)tl.e * per_expert + off;
+    fb1 = a.wb + (int64_t)tl.e * per_expert + off;
   } else {
     wrow = (int64_t)nb * 256 + wave * 32;
     live = wrow < a.H;                        // H % 256 == 128: the last block is half used
     const int64_t n16 = (live ? wrow : 0) / 16;
-    fb[0] = a.wa + (int64_t)tl.e * per_expert + n16 * nkc * kFragBytes;
-    fb[1] = fb[0] + (int64_t)nkc * kFragBytes;
+    fb0 = a.wa + (int64_t)tl.e * per_expert + n16 * nkc * kFragBytes;
+    fb1 = fb0 + (int64_t)nkc * kFragBytes;
   }
-  const int wsel0 = PHASE == 1 ? 0 : (wave >= 4 ? 1 : 0);   // scale row block of fragment 0
-  const int wsel1 = PHASE == 1 ? 1 : wsel0;
+  const __amdgpu_buffer_rsrc_t wd0 =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(fb0), 0, nkc * kFragBytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wd1 =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(fb1), 0, nkc * kFragBytes, 0x00020000);
+  constexpr int kWscRow = kMaxChunks + kMaxRing;
+  const float* wsc0 = sh.wsc + (PHASE == 1 ? 0 : (wave >= 4 ? kWscRow : 0));
+  const float* wsc1 = sh.wsc + (PHASE == 1 ? kWscRow : (wave >= 4 ? kWscRow : 0));
 
-  auto issue_w = [&](int c, uint8_t* st) {
-    uint8_t* priv = st + wave * kWPriv;
+  // one chunk's loads, in a fixed order: 4 weight loads, kActDma activation copies, 1 scale
+  v8i W0[RING], W1[RING];
+  const int wlane = lane * 16;
+  auto issue = [&](int c, int ws, uint8_t* st) __attribute__((always_inline)) {
+    W0[ws] = buf_wfrag(wd0, wlane + c * kFragBytes);   // past the last chunk: zeros
+    W1[ws] = buf_wfrag(wd1, wlane + c * kFragBytes);
+    const int cc = min(c, last);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16(fb[j >> 1] + (uint32_t)c * kFragBytes + (j & 1) * (kFragBytes / 2) + lane * 16,
-            priv + j * (kFragBytes / 2));
+    for (int j = 0; j < kActDma; ++j) {
+      const int at = j * kActRound + wave * 1024;
+      uint8_t* dst = at < kActBytes ? st + at : sh.junk;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(adesc, (lds_u8*)dst, 16, aoff[j], cc * kTile, 0, 0);
+    }
+    uint8_t* sdst = wave < kScaleWaves ? st + kActBytes + wave * kWave * 4 : sh.junk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sdesc, (lds_u8*)sdst, 4, soff, cc * 4, 0, 0);
   };
 
-  v4f acc0[kNTS], acc1[kNTS];
+  v4f acc0[NT], acc1[NT];
 #pragma unroll
-  for (int ts = 0; ts < kNTS; ++ts) acc0[ts] = acc1[ts] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int ts = 0; ts < NT; ++ts) acc0[ts] = acc1[ts] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int c, const uint8_t* wst, const uint8_t* act) {
-    const uint8_t* priv = wst + wave * kWPriv;
-    const v8i A0 = w_frag(priv, 0, lane);
-    const v8i A1 = w_frag(priv, 1, lane);
-    const float s0 = wsc[wsel0][c], s1 = wsc[wsel1][c];
-    const float* sc = reinterpret_cast<const float*>(act + kActBytes);
-    v8i b = act_frag(act, 0, lane);
-    float sa = sc[lane & 15];
+  // One persistent register per slot holds the lane's operand address; the second half
+  // is that address ^ 64 and the scale address a per-lane constant away, both formed per
+  // step, and tile offsets (multiples of 2 KB and 64 B) stay in the immediates.
+  const uint32_t alo = act_lane_offset(lane);
+  const int sdelta = (int)(kActBytes + (lane & 15) * 4) - (int)alo;
+  lds_u8* pl[RING];
 #pragma unroll
-    for (int ts = 0; ts < kNTS; ++ts) {
-      if (ts < nts) {
-        v8i bn = b;
-        float san = sa;
-        if (ts + 1 < nts) {
-          bn = act_frag(act, ts + 1, lane);
-          san = sc[(ts + 1) * 16 + (lane & 15)];
-        }
-        const v4f p0 = mfma_fp8(A0, b);
-        const v4f p1 = mfma_fp8(A1, b);
-        const float c0 = sa * s0, c1 = sa * s1;
+  for (int r = 0; r < RING; ++r) {
+    pl[r] = (lds_u8*)sh.ast[r] + alo;
+    asm volatile("" : "+v"(pl[r]));   // a base register, not a folded constant
+  }
+  auto compute = [&](int c, int ws) __attribute__((always_inline)) {
+    const v8i A0 = W0[ws];
+    const v8i A1 = W1[ws];
+    const float s0 = wsc0[c], s1 = wsc1[c];
+    lds_u8* bl = pl[ws];
+    lds_u8* bh = (lds_u8*)((uintptr_t)bl ^ 64);
+    lds_u8* bs = bl + sdelta;
+    auto frag = [&](int ts) __attribute__((always_inline)) {
+      const v4i x = *reinterpret_cast<lds_v4i*>(bl + ts * 16 * kTile);
+      const v4i y = *reinterpret_cast<lds_v4i*>(bh + ts * 16 * kTile);
+      return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // operands of tile t+2 are read while tile t+1 multiplies and tile t is promoted
+    v8i bq[3];
+    float sa[3];
+    v4f p0[2], p1[2];
+    bq[0] = frag(0);
+    sa[0] = *reinterpret_cast<lds_f32*>(bs);
+    if (NT > 1) {
+      bq[1] = frag(1);
+      sa[1] = *reinterpret_cast<lds_f32*>(bs + 64);
+    }
+    p0[0] = mfma_fp8(A0, bq[0]);
+    p1[0] = mfma_fp8(A1, bq[0]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc0[ts][i] = fmaf(p0[i], c0, acc0[ts][i]);
-          acc1[ts][i] = fmaf(p1[i], c1, acc1[ts][i]);
-        }
-        b = bn;
-        sa = san;
-        __builtin_amdgcn_sched_barrier(0);
+    for (int ts = 0; ts < NT; ++ts) {
+      if (ts + 2 < NT) {
+        bq[(ts + 2) % 3] = frag(ts + 2);
+        sa[(ts + 2) % 3] = *reinterpret_cast<lds_f32*>(bs + (ts + 2) * 64);
       }
+      if (ts + 1 < NT) {
+        p0[(ts + 1) & 1] = mfma_fp8(A0, bq[(ts + 1) % 3]);
+        p1[(ts + 1) & 1] = mfma_fp8(A1, bq[(ts + 1) % 3]);
+      }
+      const float c0 = sa[ts % 3] * s0, c1 = sa[ts % 3] * s1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc0[ts][i] = fmaf(p0[ts & 1][i], c0, acc0[ts][i]);
+        acc1[ts][i] = fmaf(p1[ts & 1][i], c1, acc1[ts][i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // bound the live operands to three tiles
     }
   };
 
-  issue_w(0, wst0);
-  issue_w(min(1, last), wst1);
-#define WST(S) (((S) % 3) == 0 ? wst0 : (((S) % 3) == 1 ? wst1 : wst2))
-#define CONS_STEP(S)                                                   \
-  {                                                                    \
-    const int c = s0 + (S);                                            \
-    asm volatile("" ::: "memory");                                     \
-    __builtin_amdgcn_s_barrier();                                      \
-    asm volatile("" ::: "memory");                                     \
-    issue_w(min(c + 2, last), WST((S) + 2));                           \
-    asm volatile("" ::: "memory");                                     \
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));                   \
-    asm volatile("" ::: "memory");                                     \
-    if (c < nkc) compute(c, WST(S), ((S) % 2) == 0 ? ast0 : ast1);      \
+  // Chunks 0 .. RING-2 go out first; step c waits for chunk c, meets the barrier (every
+  // wave's copies of c are in LDS, every wave is done with c-1), issues chunk c+RING-1
+  // into the slots of c-1 and computes c.
+  // Every chunk's loads stay one group in the order of issue(): the compiler's own
+  // waits for the weight registers then see the same history on loop entry as on the
+  // back edge and never ask for more than the ring's own wait.
+#pragma unroll
+  for (int r = 0; r < RING - 1; ++r) {
+    issue(r, r, sh.ast[r]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  for (int s0 = 0; s0 < nsteps; s0 += kUnroll) {
-    CONS_STEP(0) CONS_STEP(1) CONS_STEP(2) CONS_STEP(3) CONS_STEP(4) CONS_STEP(5)
+  for (int s0 = 0; s0 < nsteps; s0 += RING) {
+#pragma unroll
+    for (int S = 0; S < RING; ++S) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((RING - 2) * kStepOps));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(s0 + S + RING - 1, (S + RING - 1) % RING, sh.ast[(S + RING - 1) % RING]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s0 + S, S);
+    }
   }
-#undef CONS_STEP
-#undef WST
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   asm volatile("" ::: "memory");
 
   if (PHASE == 1) {
     // SwiGLU, amax over the 128 columns of the group (4 per lane, 4 lane groups, 8 waves)
-    float h[kNTS][4];
+    __syncthreads();   // every wave is done with the activation ring: reuse slot 0
+    float(*red)[kMT] = reinterpret_cast<float(*)[kMT]>(sh.ast[0]);
+    float h[NT][4];
 #pragma unroll
-    for (int ts = 0; ts < kNTS; ++ts) {
+    for (int ts = 0; ts < NT; ++ts) {
       const int r = ts * 16 + (lane & 15);
-      const bool valid = ts < nts && tok_s[r] >= 0;
+      const bool valid = r < tl.mlen && sh.tok_s[r] >= 0;
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -421,17 +412,17 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
       }
       m = fmaxf(m, __shfl_xor(m, 16));
       m = fmaxf(m, __shfl_xor(m, 32));
-      if (ts < nts && lane < 16) red[wave][r] = m;
+      if (lane < 16) red[wave][r] = m;
     }
     __syncthreads();
     const int nkh = a.I / kTile;
 #pragma unroll
-    for (int ts = 0; ts < kNTS; ++ts) {
+    for (int ts = 0; ts < NT; ++ts) {
       const int r = ts * 16 + (lane & 15);
-      if (ts < nts && r < tl.mlen) {
+      if (r < tl.mlen) {
         float m = red[0][r];
 #pragma unroll
-        for (int w = 1; w < kConsumers; ++w) m = fmaxf(m, red[w][r]);
+        for (int w = 1; w < kFWaves; ++w) m = fmaxf(m, red[w][r]);
         const float s = group_scale(m);
         uint32_t packed = 0;
 #pragma unroll
@@ -445,9 +436,9 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
     if (!live) return;
     YT* y = static_cast<YT*>(a.y);
 #pragma unroll
-    for (int ts = 0; ts < kNTS; ++ts) {
+    for (int ts = 0; ts < NT; ++ts) {
       const int r = ts * 16 + (lane & 15);
-      if (ts < nts && r < tl.mlen) {
+      if (r < tl.mlen) {
         YT* dst = y + (int64_t)(tl.m0 + r) * a.H + wrow + 4 * (lane >> 4);
         if constexpr (sizeof(YT) == 2) {
           uint2 u, v;
@@ -463,6 +454,87 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
         }
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// One grouped-FFN GEMM phase over tiles (expert, M tile) x n-blocks.
+//   PHASE 1: 128 intermediate columns per workgroup; epilogue h = silu(G) * U,
+//            re-quantised 1x128 (amax over the 128 columns reduced across the 8
+//            waves through LDS).
+//   PHASE 2: 256 output features per workgroup.
+// Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD,
+// so the tile's activation rows are fetched into that XCD's L2 once.
+// ------------------------------------------------------------------------------------
+template <int PHASE, typename YT>
+__global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
+  __shared__ __attribute__((aligned(128))) uint8_t ast0[kAStage];
+  __shared__ __attribute__((aligned(128))) uint8_t ast1[kAStage];
+  __shared__ __attribute__((aligned(128))) uint8_t ast2[kAStage];
+  __shared__ __attribute__((aligned(128))) uint8_t ast3[kAStage];
+  __shared__ __attribute__((aligned(128))) uint8_t ast4[kAStage];
+  __shared__ __attribute__((aligned(128))) uint8_t ast5[kAStage];
+  __shared__ __attribute__((aligned(128))) uint8_t ast6[kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t junk[kJunk];
+  __shared__ int tok_s[kMT];
+  __shared__ float wsc[2][kMaxChunks + kMaxRing];   // weight-block scales per K chunk (two
+                                                    // row blocks); 0 past the last chunk
+  const int L = blockIdx.x;
+  const int xcd = L % kXcds, slot = L / kXcds;
+  const int tile = (slot / a.n_nb) * kXcds + xcd;
+  const int nb = slot % a.n_nb;
+  if (tile >= min(*a.n_tiles, a.max_tiles)) return;
+  const Tile tl = a.tiles[tile];
+  // a workspace that does not hold this call's plan must not lead out of bounds
+  if (tl.e < 0 || tl.e >= a.n_experts || tl.mlen < 1 || tl.mlen > kMT || tl.m0 < 0 ||
+      tl.m0 > a.n_rows - tl.mlen)
+    return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = PHASE == 1 ? a.H : a.I;
+  const int nkc = K / kTile;
+
+  // source row of every tile row: a token (phase 1) or a permuted row (phase 2)
+  for (int r = tid; r < kMT; r += kFThreads) {
+    int t = -1;
+    if (r < tl.mlen) {
+      if (PHASE == 1) {
+        const int64_t v = a.row_token ? (int64_t)a.row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
+        t = (v >= 0 && v < a.n_tokens) ? (int)v : -1;
+      } else {
+        t = tl.m0 + r;
+      }
+    }
+    tok_s[r] = t;
+  }
+  // weight-block scales for every K chunk (0 past the last one): phase 1 (W1, W3) of row
+  // block nb; phase 2 the two W2 row blocks of this workgroup's 256 rows
+  const int64_t nrb = (PHASE == 1 ? a.I : a.H) / kTile;
+  constexpr int kWscRow = kMaxChunks + kMaxRing;
+  for (int c = tid; c < 2 * kWscRow; c += kFThreads) {
+    const int which = c / kWscRow, kc = c % kWscRow;
+    float v = 0.0f;
+    if (kc >= nkc) {
+    } else if (PHASE == 1) {
+      v = (which == 0 ? a.wsa : a.wsb)[((int64_t)tl.e * nrb + nb) * nkc + kc];
+    } else {
+      const int64_t rb = min((int64_t)nb * 2 + which, nrb - 1);
+      v = a.wsa[((int64_t)tl.e * nrb + rb) * nkc + kc];
+    }
+    wsc[which][kc] = v;
+  }
+  __syncthreads();
+
+  const FfnLds sh{{ast0, ast1, ast2, ast3, ast4, ast5, ast6}, junk, tok_s, &wsc[0][0]};
+  constexpr int R1 = PHASE == 1 ? 7 : 4;   // ring depth for tiles of up to 8 16-row tiles
+  constexpr int R2 = PHASE == 1 ? 6 : 4;   // and for taller tiles
+  switch ((tl.mlen + 15) >> 4) {
+    case 1: case 2: ffn_main<PHASE, YT, 2, R1>(a, tl, nb, wave, lane, sh); break;
+    case 3: case 4: ffn_main<PHASE, YT, 4, R1>(a, tl, nb, wave, lane, sh); break;
+    case 5: case 6: ffn_main<PHASE, YT, 6, R1>(a, tl, nb, wave, lane, sh); break;
+    case 7: case 8: ffn_main<PHASE, YT, 8, R1>(a, tl, nb, wave, lane, sh); break;
+    case 9: ffn_main<PHASE, YT, 9, R2>(a, tl, nb, wave, lane, sh); break;
+    default: ffn_main<PHASE, YT, 10, R2>(a, tl, nb, wave, lane, sh); break;
   }
 }
 
