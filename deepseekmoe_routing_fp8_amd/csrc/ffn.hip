@@ -171,6 +171,8 @@ constexpr int kAStage = kActBytes + kScaleBytes; // one ring slot, a multiple of
 constexpr int kJunk = 1024;                      // landing area of copies past the slot
 constexpr int kStepOps = 4 + kActDma + 1;        // vector-memory ops per wave per chunk
 constexpr int kMaxRing = 7;
+constexpr int kMaxNbPerWg = 4;                   // n-blocks one workgroup runs back to back
+constexpr int kNbPerWg1 = 2, kNbPerWg2 = 4;      // gate/up (16 blocks at I = 2048), down
 constexpr int kXcds = 8;
 constexpr int kMaxChunks = 128;                  // K <= 16384
 static_assert(kAStage % 128 == 0, "slot bases keep bit 6 of the swizzled offsets");
@@ -188,7 +190,8 @@ struct FfnArgs {
   const float* wsa;
   const uint8_t* wb;     // packed W3 (phase 1)
   const float* wsb;
-  int H, I, n_nb;
+  int H, I, n_nb;        // n-blocks per tile
+  int nb_per;            // n-blocks per workgroup (1..kMaxNbPerWg)
   uint8_t* hq;           // phase 1 outputs
   float* hs;
   void* y;               // phase 2 output
@@ -211,7 +214,8 @@ struct FfnLds {
   uint8_t* ast[kMaxRing];   // ring slots (kAStage bytes each, 128-byte aligned)
   uint8_t* junk;            // kJunk bytes
   const int* tok_s;         // source row of every tile row (-1: none)
-  const float* wsc;         // [2][kMaxChunks + kMaxRing] weight-block scales
+  const float* wsc;         // [n-block][2][kMaxChunks + kMaxRing] weight-block scales
+  float* red;               // [kFWaves][kMT] phase-1 amax partials
 };
 
 // A wave-uniform pointer in scalar registers (buffer descriptors must be uniform; the
@@ -240,15 +244,15 @@ __device__ __forceinline__ v8i buf_wfrag(__amdgpu_buffer_rsrc_t d, int voff) {
 // zero weights (and carry weight scales 0), adding exact zeros.
 // ------------------------------------------------------------------------------------
 template <int PHASE, typename YT, int NT, int RING>
-__device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int nb, int wave,
-                                         int lane, const FfnLds& sh) {
+__device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int nb0, int nbn,
+                                         int wave, int lane, const FfnLds& sh) {
   static_assert(RING >= 3 && RING <= kMaxRing, "ring depth");
   static_assert(NT * 16 <= kMT, "tile rows");
   const int tid = wave * kWave + lane;
   const int K = PHASE == 1 ? a.H : a.I;
   const int nkc = K / kTile;
   const int last = nkc - 1;
-  const int nsteps = (nkc + RING - 1) / RING * RING;
+  const int nsteps = (nkc + RING - 1) / RING * RING;   // steps per n-block
 
   // activation copies of this lane: kActDma 16-byte units and one scale
   const __amdgpu_buffer_rsrc_t adesc =
@@ -265,38 +269,39 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   }
   const int soff = max(sh.tok_s[min(tid, tl.mlen - 1)], 0) * nkc * 4;
 
-  // this wave's two fragments
+  // this wave's two fragments of n-block nb: the first fragment row and the row offset
   const int64_t per_expert = (int64_t)a.H * a.I;
-  const uint8_t* fb0;
-  const uint8_t* fb1;
-  int64_t wrow;
-  bool live = true;
-  if (PHASE == 1) {
-    wrow = (int64_t)nb * kTile + wave * 16;
-    const int64_t off = (wrow / 16) * nkc * kFragBytes;
-    fb0 = a.wa + (int64_t)tl.e * per_expert + off;
-    fb1 = a.wb + (int64_t)tl.e * per_expert + off;
-  } else {
-    wrow = (int64_t)nb * 256 + wave * 32;
-    live = wrow < a.H;                        // H % 256 == 128: the last block is half used
-    const int64_t n16 = (live ? wrow : 0) / 16;
-    fb0 = a.wa + (int64_t)tl.e * per_expert + n16 * nkc * kFragBytes;
-    fb1 = fb0 + (int64_t)nkc * kFragBytes;
-  }
-  const __amdgpu_buffer_rsrc_t wd0 =
-      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(fb0), 0, nkc * kFragBytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t wd1 =
-      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(fb1), 0, nkc * kFragBytes, 0x00020000);
+  const int64_t frow = (int64_t)nkc * kFragBytes;   // bytes of one 16-row fragment row
+  auto wrow_of = [&](int nb) -> int64_t {
+    return PHASE == 1 ? (int64_t)nb * kTile + wave * 16 : (int64_t)nb * 256 + wave * 32;
+  };
+  auto wdesc = [&](int nb, int f) __attribute__((always_inline)) {
+    const int64_t wrow = wrow_of(nb);
+    const uint8_t* fb;
+    if (PHASE == 1) {
+      fb = (f == 0 ? a.wa : a.wb) + (int64_t)tl.e * per_expert + (wrow / 16) * frow;
+    } else {
+      // H % 256 == 128: the last block is half used; its idle waves read block 0
+      const int64_t n16 = (wrow < a.H ? wrow : 0) / 16;
+      fb = a.wa + (int64_t)tl.e * per_expert + (n16 + f) * frow;
+    }
+    return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(fb), 0, (int)frow, 0x00020000);
+  };
   constexpr int kWscRow = kMaxChunks + kMaxRing;
-  const float* wsc0 = sh.wsc + (PHASE == 1 ? 0 : (wave >= 4 ? kWscRow : 0));
-  const float* wsc1 = sh.wsc + (PHASE == 1 ? kWscRow : (wave >= 4 ? kWscRow : 0));
+  const int wsel0 = PHASE == 1 ? 0 : (wave >= 4 ? 1 : 0);   // scale row block of fragment 0
+  const int wsel1 = PHASE == 1 ? 1 : wsel0;
 
-  // one chunk's loads, in a fixed order: 4 weight loads, kActDma activation copies, 1 scale
+  // one chunk's loads, in a fixed order: 4 weight loads, kActDma activation copies, 1 scale.
+  // Step g of n-block it loads chunk g of that block; chunks past the block's last one
+  // (and blocks past the workgroup's range) read zero weights.
   v8i W0[RING], W1[RING];
   const int wlane = lane * 16;
-  auto issue = [&](int c, int ws, uint8_t* st) __attribute__((always_inline)) {
-    W0[ws] = buf_wfrag(wd0, wlane + c * kFragBytes);   // past the last chunk: zeros
-    W1[ws] = buf_wfrag(wd1, wlane + c * kFragBytes);
+  auto issue = [&](int it, int c, int ws, uint8_t* st) __attribute__((always_inline)) {
+    const bool real = it < nbn && c < nkc;
+    const int nb = nb0 + min(it, nbn - 1);
+    const int off = wlane + (real ? c : nkc) * kFragBytes;
+    W0[ws] = buf_wfrag(wdesc(nb, 0), off);
+    W1[ws] = buf_wfrag(wdesc(nb, 1), off);
     const int cc = min(c, last);
 #pragma unroll
     for (int j = 0; j < kActDma; ++j) {
@@ -323,6 +328,8 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
     pl[r] = (lds_u8*)sh.ast[r] + alo;
     asm volatile("" : "+v"(pl[r]));   // a base register, not a folded constant
   }
+  const float* wsc0 = nullptr;
+  const float* wsc1 = nullptr;
   auto compute = [&](int c, int ws) __attribute__((always_inline)) {
     const v8i A0 = W0[ws];
     const v8i A1 = W1[ws];
@@ -375,86 +382,98 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   // back edge and never ask for more than the ring's own wait.
 #pragma unroll
   for (int r = 0; r < RING - 1; ++r) {
-    issue(r, r, sh.ast[r]);
+    issue(0, r, r, sh.ast[r]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int s0 = 0; s0 < nsteps; s0 += RING) {
+  const int nkh = a.I / kTile;
+  for (int it = 0; it < nbn; ++it) {
+    const int nb = nb0 + it;
+    wsc0 = sh.wsc + (it * 2 + wsel0) * kWscRow;
+    wsc1 = sh.wsc + (it * 2 + wsel1) * kWscRow;
 #pragma unroll
-    for (int S = 0; S < RING; ++S) {
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((RING - 2) * kStepOps));
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      issue(s0 + S + RING - 1, (S + RING - 1) % RING, sh.ast[(S + RING - 1) % RING]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(s0 + S, S);
+    for (int ts = 0; ts < NT; ++ts) acc0[ts] = acc1[ts] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsteps; s0 += RING) {
+#pragma unroll
+      for (int S = 0; S < RING; ++S) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((RING - 2) * kStepOps));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int g = s0 + S + RING - 1;   // step whose chunk is issued now
+        const int nx = g >= nsteps ? 1 : 0;  // it belongs to the next n-block
+        issue(it + nx, g - nx * nsteps, (S + RING - 1) % RING, sh.ast[(S + RING - 1) % RING]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s0 + S, S);
+      }
+    }
+
+    // epilogue of n-block nb; the next block's first chunks are already in flight
+    const int64_t wrow = wrow_of(nb);
+    if (PHASE == 1) {
+      // SwiGLU, amax over the 128 columns of the group (4 per lane, 4 lane groups, 8 waves)
+      // h = silu(G) * U replaces G in acc0
+      float(*red)[kMT] = reinterpret_cast<float(*)[kMT]>(sh.red);
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int r = ts * 16 + (lane & 15);
+        const bool valid = r < tl.mlen && sh.tok_s[r] >= 0;
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = acc0[ts][i];
+          acc0[ts][i] = valid ? (g / (1.0f + expf(-g))) * acc1[ts][i] : 0.0f;
+          m = fmaxf(m, fabsf(acc0[ts][i]));
+        }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lane < 16) red[wave][r] = m;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int r = ts * 16 + (lane & 15);
+        if (r < tl.mlen) {
+          float m = red[0][r];
+#pragma unroll
+          for (int w = 1; w < kFWaves; ++w) m = fmaxf(m, red[w][r]);
+          const float s = group_scale(m);
+          uint32_t packed = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__fdiv_rn(acc0[ts][i], s)) << (8 * i);
+          const int64_t row = tl.m0 + r;
+          *reinterpret_cast<uint32_t*>(a.hq + row * a.I + wrow + 4 * (lane >> 4)) = packed;
+          if (wave == 0 && lane < 16) a.hs[row * nkh + nb] = s;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one tile's temporaries at a time
+      }
+      __syncthreads();   // red is free for the next block
+    } else if (wrow < a.H) {
+      YT* y = static_cast<YT*>(a.y);
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int r = ts * 16 + (lane & 15);
+        if (r < tl.mlen) {
+          YT* dst = y + (int64_t)(tl.m0 + r) * a.H + wrow + 4 * (lane >> 4);
+          if constexpr (sizeof(YT) == 2) {
+            uint2 u, v;
+            u.x = f32_to_bf16(acc0[ts][0]) | ((uint32_t)f32_to_bf16(acc0[ts][1]) << 16);
+            u.y = f32_to_bf16(acc0[ts][2]) | ((uint32_t)f32_to_bf16(acc0[ts][3]) << 16);
+            v.x = f32_to_bf16(acc1[ts][0]) | ((uint32_t)f32_to_bf16(acc1[ts][1]) << 16);
+            v.y = f32_to_bf16(acc1[ts][2]) | ((uint32_t)f32_to_bf16(acc1[ts][3]) << 16);
+            *reinterpret_cast<uint2*>(dst) = u;
+            *reinterpret_cast<uint2*>(dst + 16) = v;
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(acc0[ts][0], acc0[ts][1], acc0[ts][2], acc0[ts][3]);
+            *reinterpret_cast<float4*>(dst + 16) = make_float4(acc1[ts][0], acc1[ts][1], acc1[ts][2], acc1[ts][3]);
+          }
+        }
+      }
     }
   }
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   asm volatile("" ::: "memory");
-
-  if (PHASE == 1) {
-    // SwiGLU, amax over the 128 columns of the group (4 per lane, 4 lane groups, 8 waves)
-    __syncthreads();   // every wave is done with the activation ring: reuse slot 0
-    float(*red)[kMT] = reinterpret_cast<float(*)[kMT]>(sh.ast[0]);
-    float h[NT][4];
-#pragma unroll
-    for (int ts = 0; ts < NT; ++ts) {
-      const int r = ts * 16 + (lane & 15);
-      const bool valid = r < tl.mlen && sh.tok_s[r] >= 0;
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float g = acc0[ts][i];
-        h[ts][i] = valid ? (g / (1.0f + expf(-g))) * acc1[ts][i] : 0.0f;
-        m = fmaxf(m, fabsf(h[ts][i]));
-      }
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      if (lane < 16) red[wave][r] = m;
-    }
-    __syncthreads();
-    const int nkh = a.I / kTile;
-#pragma unroll
-    for (int ts = 0; ts < NT; ++ts) {
-      const int r = ts * 16 + (lane & 15);
-      if (r < tl.mlen) {
-        float m = red[0][r];
-#pragma unroll
-        for (int w = 1; w < kFWaves; ++w) m = fmaxf(m, red[w][r]);
-        const float s = group_scale(m);
-        uint32_t packed = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__fdiv_rn(h[ts][i], s)) << (8 * i);
-        const int64_t row = tl.m0 + r;
-        *reinterpret_cast<uint32_t*>(a.hq + row * a.I + wrow + 4 * (lane >> 4)) = packed;
-        if (wave == 0 && lane < 16) a.hs[row * nkh + nb] = s;
-      }
-    }
-  } else {
-    if (!live) return;
-    YT* y = static_cast<YT*>(a.y);
-#pragma unroll
-    for (int ts = 0; ts < NT; ++ts) {
-      const int r = ts * 16 + (lane & 15);
-      if (r < tl.mlen) {
-        YT* dst = y + (int64_t)(tl.m0 + r) * a.H + wrow + 4 * (lane >> 4);
-        if constexpr (sizeof(YT) == 2) {
-          uint2 u, v;
-          u.x = f32_to_bf16(acc0[ts][0]) | ((uint32_t)f32_to_bf16(acc0[ts][1]) << 16);
-          u.y = f32_to_bf16(acc0[ts][2]) | ((uint32_t)f32_to_bf16(acc0[ts][3]) << 16);
-          v.x = f32_to_bf16(acc1[ts][0]) | ((uint32_t)f32_to_bf16(acc1[ts][1]) << 16);
-          v.y = f32_to_bf16(acc1[ts][2]) | ((uint32_t)f32_to_bf16(acc1[ts][3]) << 16);
-          *reinterpret_cast<uint2*>(dst) = u;
-          *reinterpret_cast<uint2*>(dst + 16) = v;
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(acc0[ts][0], acc0[ts][1], acc0[ts][2], acc0[ts][3]);
-          *reinterpret_cast<float4*>(dst + 16) = make_float4(acc1[ts][0], acc1[ts][1], acc1[ts][2], acc1[ts][3]);
-        }
-      }
-    }
-  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -477,12 +496,16 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   __shared__ __attribute__((aligned(128))) uint8_t ast6[kAStage];
   __shared__ __attribute__((aligned(16))) uint8_t junk[kJunk];
   __shared__ int tok_s[kMT];
-  __shared__ float wsc[2][kMaxChunks + kMaxRing];   // weight-block scales per K chunk (two
-                                                    // row blocks); 0 past the last chunk
+  constexpr int kWscRow = kMaxChunks + kMaxRing;
+  __shared__ float wsc[kMaxNbPerWg * 2][kWscRow];   // weight-block scales per n-block, row
+                                                     // block and K chunk; 0 past the last chunk
+  __shared__ float red[PHASE == 1 ? kFWaves * kMT : 1];
   const int L = blockIdx.x;
   const int xcd = L % kXcds, slot = L / kXcds;
-  const int tile = (slot / a.n_nb) * kXcds + xcd;
-  const int nb = slot % a.n_nb;
+  const int nwg = (a.n_nb + a.nb_per - 1) / a.nb_per;   // workgroups per tile
+  const int tile = (slot / nwg) * kXcds + xcd;
+  const int nb0 = (slot % nwg) * a.nb_per;
+  const int nbn = min(a.nb_per, a.n_nb - nb0);
   if (tile >= min(*a.n_tiles, a.max_tiles)) return;
   const Tile tl = a.tiles[tile];
   // a workspace that does not hold this call's plan must not lead out of bounds
@@ -507,12 +530,12 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
     }
     tok_s[r] = t;
   }
-  // weight-block scales for every K chunk (0 past the last one): phase 1 (W1, W3) of row
-  // block nb; phase 2 the two W2 row blocks of this workgroup's 256 rows
+  // weight-block scales for every K chunk (0 past the last one) of each n-block: phase 1
+  // (W1, W3) of row block nb; phase 2 the two W2 row blocks of the block's 256 rows
   const int64_t nrb = (PHASE == 1 ? a.I : a.H) / kTile;
-  constexpr int kWscRow = kMaxChunks + kMaxRing;
-  for (int c = tid; c < 2 * kWscRow; c += kFThreads) {
-    const int which = c / kWscRow, kc = c % kWscRow;
+  for (int c = tid; c < nbn * 2 * kWscRow; c += kFThreads) {
+    const int it = c / (2 * kWscRow), which = (c / kWscRow) & 1, kc = c % kWscRow;
+    const int nb = nb0 + it;
     float v = 0.0f;
     if (kc >= nkc) {
     } else if (PHASE == 1) {
@@ -521,20 +544,20 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
       const int64_t rb = min((int64_t)nb * 2 + which, nrb - 1);
       v = a.wsa[((int64_t)tl.e * nrb + rb) * nkc + kc];
     }
-    wsc[which][kc] = v;
+    wsc[it * 2 + which][kc] = v;
   }
   __syncthreads();
 
-  const FfnLds sh{{ast0, ast1, ast2, ast3, ast4, ast5, ast6}, junk, tok_s, &wsc[0][0]};
-  constexpr int R1 = PHASE == 1 ? 7 : 4;   // ring depth for tiles of up to 8 16-row tiles
-  constexpr int R2 = PHASE == 1 ? 6 : 4;   // and for taller tiles
+  const FfnLds sh{{ast0, ast1, ast2, ast3, ast4, ast5, ast6}, junk, tok_s, &wsc[0][0], red};
+  constexpr int R1 = PHASE == 1 ? 5 : 4;   // ring depth for tiles of up to 8 16-row tiles
+  constexpr int R2 = 4;                    // and for taller tiles
   switch ((tl.mlen + 15) >> 4) {
-    case 1: case 2: ffn_main<PHASE, YT, 2, R1>(a, tl, nb, wave, lane, sh); break;
-    case 3: case 4: ffn_main<PHASE, YT, 4, R1>(a, tl, nb, wave, lane, sh); break;
-    case 5: case 6: ffn_main<PHASE, YT, 6, R1>(a, tl, nb, wave, lane, sh); break;
-    case 7: case 8: ffn_main<PHASE, YT, 8, R1>(a, tl, nb, wave, lane, sh); break;
-    case 9: ffn_main<PHASE, YT, 9, R2>(a, tl, nb, wave, lane, sh); break;
-    default: ffn_main<PHASE, YT, 10, R2>(a, tl, nb, wave, lane, sh); break;
+    case 1: case 2: ffn_main<PHASE, YT, 2, R1>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 3: case 4: ffn_main<PHASE, YT, 4, R1>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 5: case 6: ffn_main<PHASE, YT, 6, R1>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 7: case 8: ffn_main<PHASE, YT, 8, R1>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 9: ffn_main<PHASE, YT, 9, R2>(a, tl, nb0, nbn, wave, lane, sh); break;
+    default: ffn_main<PHASE, YT, 10, R2>(a, tl, nb0, nbn, wave, lane, sh); break;
   }
 }
 
@@ -627,9 +650,10 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
                      (int)n_rows, (int)f.L.max_tiles, f.tiles, f.ntiles);
   FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, xs, n_tokens,
-             row_token, w1, w1s, w3, w3s, H, I, I / kTile, f.hq, f.hs, nullptr};
-  hipLaunchKernelGGL((ffn_kernel<1, uint16_t>), dim3(f.grid_tiles * a1.n_nb), dim3(kFThreads), 0,
-                     s, a1);
+             row_token, w1, w1s, w3, w3s, H, I, I / kTile, kNbPerWg1, f.hq, f.hs, nullptr};
+  const unsigned nwg = (unsigned)((a1.n_nb + a1.nb_per - 1) / a1.nb_per);
+  hipLaunchKernelGGL((ffn_kernel<1, uint16_t>), dim3(f.grid_tiles * nwg), dim3(kFThreads), 0, s,
+                     a1);
   return launch_status();
 }
 
@@ -645,8 +669,9 @@ moe_status ffn_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows, co
   hipStream_t s = as_stream(stream);
   const int H = cfg->hidden, I = cfg->inter;
   FfnArgs a2{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, f.hq, f.hs, n_rows,
-             nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256, nullptr, nullptr, y};
-  const dim3 grid(f.grid_tiles * a2.n_nb);
+             nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256, kNbPerWg2, nullptr,
+             nullptr, y};
+  const dim3 grid(f.grid_tiles * (unsigned)((a2.n_nb + a2.nb_per - 1) / a2.nb_per));
   if (yt == MOE_BF16)
     hipLaunchKernelGGL((ffn_kernel<2, uint16_t>), grid, dim3(kFThreads), 0, s, a2);
   else
