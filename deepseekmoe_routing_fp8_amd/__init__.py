@@ -27,7 +27,7 @@ MOE_F32, MOE_BF16 = 0, 1
 ENTRY_POINTS = (
     "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_pack_fp8_weights",
     "moe_pack_router_weights", "moe_router_weights_elems", "moe_route", "moe_route_workspace_bytes",
-    "moe_permute", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8",
+    "moe_permute", "moe_permute_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8",
     "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
     "moe_update_bias",
 )
@@ -62,7 +62,8 @@ _sig = {
     "moe_router_weights_elems": ([_I64, _I64], _SZ),
     "moe_route": ([_CFG, _P, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "moe_route_workspace_bytes": ([_CFG, _I64, ctypes.c_int], _SZ),
-    "moe_permute": ([_CFG, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_permute": ([_CFG, _I64, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "moe_permute_workspace_bytes": ([_CFG, _I64], _SZ),
     "moe_grouped_ffn_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
     "moe_grouped_ffn_fp8": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _P, ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
@@ -211,8 +212,13 @@ def moe_route(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, bias: to
     return scores, topk_idx, topk_gate, counts
 
 
+def moe_permute_workspace_bytes(cfg: moe_config, T: int) -> int:
+    return int(_lib.moe_permute_workspace_bytes(ctypes.byref(cfg), T))
+
+
 def moe_permute(cfg: moe_config, topk_idx: torch.Tensor, offsets: torch.Tensor = None,
-                row_token: torch.Tensor = None, row_of: torch.Tensor = None, stream=None):
+                row_token: torch.Tensor = None, row_of: torch.Tensor = None,
+                ws: torch.Tensor = None, stream=None):
     """-> (offsets [N_r+N_s+1], row_token [T*(k+N_s)], row_of [T,k]), all int32. The
     shared experts follow the routed ones as segments of T rows in token order."""
     T, k = topk_idx.shape
@@ -223,10 +229,13 @@ def moe_permute(cfg: moe_config, topk_idx: torch.Tensor, offsets: torch.Tensor =
     if row_token is None:
         row_token = torch.empty((T * (k + S),), dtype=torch.int32, device=dev)
     row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
+    if ws is None:
+        ws = torch.empty((max(moe_permute_workspace_bytes(cfg, T), 1),), dtype=torch.uint8, device=dev)
     _check(_lib.moe_permute(ctypes.byref(cfg), T, _dev(topk_idx, torch.int32, "topk_idx", (T, cfg.top_k)),
                             _dev(offsets, torch.int32, "offsets", (cfg.n_routed + S + 1,)),
                             _dev(row_token, torch.int32, "row_token", (T * (k + S),)),
-                            _dev(row_of, torch.int32, "row_of", (T, k)), _stream(stream)),
+                            _dev(row_of, torch.int32, "row_of", (T, k)),
+                            _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
            "moe_permute")
     return offsets, row_token, row_of
 

@@ -138,7 +138,10 @@ int main(int argc, char** argv) {
   CK(hipMalloc(&row_token, rows * 4));
   CK(hipMalloc(&row_of, (size_t)T * K * 4));
   CK(hipMemcpy(d_idx, idx.data(), idx.size() * 4, hipMemcpyHostToDevice));
-  CM(moe_permute(&c, T, d_idx, offsets, row_token, row_of, nullptr));
+  void* pws;
+  const size_t pwsn = moe_permute_workspace_bytes(&c, T);
+  CK(hipMalloc(&pws, pwsn));
+  CM(moe_permute(&c, T, d_idx, offsets, row_token, row_of, pws, pwsn, nullptr));
 
   uint16_t* y;
   CK(hipMalloc(&y, (size_t)rows * H * 2));

@@ -26,8 +26,27 @@ __device__ __forceinline__ void load8(const YT* p, float (&v)[8]) {
   }
 }
 
+template <typename YT>
+__device__ __forceinline__ void unpack8(const uint4 (&raw)[sizeof(YT) / 2], float (&v)[8]) {
+  if constexpr (sizeof(YT) == 2) {
+    const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(raw[0].x); v[1] = __uint_as_float(raw[0].y);
+    v[2] = __uint_as_float(raw[0].z); v[3] = __uint_as_float(raw[0].w);
+    v[4] = __uint_as_float(raw[1].x); v[5] = __uint_as_float(raw[1].y);
+    v[6] = __uint_as_float(raw[1].z); v[7] = __uint_as_float(raw[1].w);
+  }
+}
+
 // One block per token; each thread sums 8 consecutive features per step, in the fixed
 // order: shared experts 0..N_s-1, then slots 0..k-1 (FP32), then one rounding to bf16.
+// All slots' rows of a step are loaded before any is added (a skipped slot reads row 0
+// and contributes exactly zero), so the loads of one step are in flight together.
 template <typename YT>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y_rows,
                                                       const int32_t* __restrict__ row_of,
@@ -35,13 +54,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y_r
                                                       const YT* __restrict__ y_shared, int n_shared,
                                                       int64_t T, int H, int k, int64_t n_rows,
                                                       uint16_t* __restrict__ out) {
+  constexpr int U = sizeof(YT) / 2;   // 16-byte units per 8 values
   const int64_t t = blockIdx.x;
   __shared__ int32_t rows[kMaxTopK];
   __shared__ float g[kMaxTopK];
-  if (threadIdx.x < k) {
-    const int32_t r = row_of[t * k + threadIdx.x];
+  if (threadIdx.x < kMaxTopK) {
+    int32_t r = -1;
+    float gv = 0.0f;
+    if (threadIdx.x < k) {
+      r = row_of[t * k + threadIdx.x];
+      gv = gate[t * k + threadIdx.x];
+    }
     rows[threadIdx.x] = (r >= 0 && r < n_rows) ? r : -1;
-    g[threadIdx.x] = gate[t * k + threadIdx.x];
+    g[threadIdx.x] = gv;
   }
   __syncthreads();
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
@@ -52,12 +77,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y_r
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
-    for (int j = 0; j < k; ++j) {
-      if (rows[j] < 0) continue;
-      float v[8];
-      load8(y_rows + (int64_t)rows[j] * H + c, v);
+    uint4 raw[kMaxTopK][U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[i], acc[i]);
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        const YT* p = y_rows + (int64_t)max(rows[j], 0) * H + c;
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[j][u] = reinterpret_cast<const uint4*>(p)[u];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k && rows[j] >= 0) {
+        float v[8];
+        unpack8<YT>(raw[j], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[i], acc[i]);
+      }
     }
     uint4 o;
     o.x = f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);

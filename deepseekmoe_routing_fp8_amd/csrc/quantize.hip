@@ -8,52 +8,62 @@ namespace moe {
 namespace {
 
 // 16 lanes per 128-element tile, 8 consecutive elements per lane; a 256-thread block
-// covers 16 tiles. Tiles are numbered row-major over [rows, cols/128].
+// covers kQTiles tiles, kQTiles/16 per thread group, with every load of a thread issued
+// before the first tile is reduced. Tiles are numbered row-major over [rows, cols/128].
+constexpr int kQPer = 4;
+constexpr int kQTiles = 16 * kQPer;
+
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_1x128_kernel(const T* __restrict__ x,
-                                                             int64_t n_tiles, int64_t tiles_per_row,
+                                                             int64_t n_tiles,
                                                              uint8_t* __restrict__ q,
                                                              float* __restrict__ scales) {
-  const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
-  const bool live = tile < n_tiles;
-  const int64_t base = tile * kTile + sub * 8;  // tiles are contiguous in row-major order
-  float v[8];
-  if (live) {
-    if constexpr (sizeof(T) == 2) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(x + base);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[kQPer][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  for (int u = 0; u < kQPer; ++u) {
+    const int64_t tile = (int64_t)blockIdx.x * kQTiles + u * 16 + (threadIdx.x >> 4);
+    const int64_t base = tile * kTile + sub * 8;  // tiles are contiguous in row-major order
+    if (tile < n_tiles) {
+      if constexpr (sizeof(T) == 2) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(x + base);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[u][2 * i] = __uint_as_float(w[i] << 16);
+          v[u][2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(x + base);
+        const float4 b = *reinterpret_cast<const float4*>(x + base + 4);
+        v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+        v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
       }
     } else {
-      const float4 a = *reinterpret_cast<const float4*>(x + base);
-      const float4 b = *reinterpret_cast<const float4*>(x + base + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
   }
-  float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = group_max<16>(amax);
-  const float s = group_scale(amax);
-  uint32_t lo = 0, hi = 0;
+  for (int u = 0; u < kQPer; ++u) {
+    const int64_t tile = (int64_t)blockIdx.x * kQTiles + u * 16 + (threadIdx.x >> 4);
+    const int64_t base = tile * kTile + sub * 8;
+    float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo |= e4m3_encode(__fdiv_rn(v[i], s)) << (8 * i);
-    hi |= e4m3_encode(__fdiv_rn(v[i + 4], s)) << (8 * i);
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
+    amax = group_max<16>(amax);
+    const float s = group_scale(amax);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3_encode(__fdiv_rn(v[u][i], s)) << (8 * i);
+      hi |= e4m3_encode(__fdiv_rn(v[u][i + 4], s)) << (8 * i);
+    }
+    if (tile < n_tiles) {
+      *reinterpret_cast<uint2*>(q + base) = make_uint2(lo, hi);
+      if (sub == 0) scales[tile] = s;
+    }
   }
-  if (live) {
-    *reinterpret_cast<uint2*>(q + base) = make_uint2(lo, hi);
-    if (sub == 0) scales[tile] = s;
-  }
-  (void)tiles_per_row;
 }
 
 // One 256-thread block per 128x128 block. Thread t covers rows (t/32) + 8*i, i < 16,
@@ -142,16 +152,14 @@ extern "C" moe_status moe_quantize_1x128(const void* x, moe_dtype xt, int64_t ro
   const int64_t tiles = rows * (cols / kTile);
   if (tiles == 0) return MOE_OK;
   if (!x || !q || !scales) return MOE_ERR_NULL;
-  const int64_t blocks = (tiles + 15) / 16;
+  const int64_t blocks = (tiles + kQTiles - 1) / kQTiles;
   if (blocks > 0x7fffffff) return MOE_ERR_SHAPE;
   if (xt == MOE_BF16)
     hipLaunchKernelGGL(quantize_1x128_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0,
-                       as_stream(stream), static_cast<const uint16_t*>(x), tiles, cols / kTile, q,
-                       scales);
+                       as_stream(stream), static_cast<const uint16_t*>(x), tiles, q, scales);
   else
     hipLaunchKernelGGL(quantize_1x128_kernel<float>, dim3((unsigned)blocks), dim3(256), 0,
-                       as_stream(stream), static_cast<const float*>(x), tiles, cols / kTile, q,
-                       scales);
+                       as_stream(stream), static_cast<const float*>(x), tiles, q, scales);
   return launch_status();
 }
 

@@ -16,9 +16,11 @@ from typing import Callable, Iterable, Optional
 import numpy as np
 import torch
 
-from . import (MOE_F32, make_config, moe_combine, moe_grouped_ffn_fp8_down, moe_grouped_ffn_fp8_gate_up,
-               moe_grouped_ffn_workspace_bytes, moe_pack_fp8_weights, moe_pack_router_weights, moe_permute, moe_quantize_1x128, moe_quantize_128x128,
-               moe_route, moe_route_workspace_bytes, moe_update_bias)
+from . import (MOE_F32, make_config, moe_combine, moe_grouped_ffn_fp8_down,
+               moe_grouped_ffn_fp8_gate_up, moe_grouped_ffn_workspace_bytes, moe_pack_fp8_weights,
+               moe_pack_router_weights, moe_permute, moe_permute_workspace_bytes,
+               moe_quantize_1x128, moe_quantize_128x128, moe_route, moe_route_workspace_bytes,
+               moe_update_bias)
 
 
 class MoELayer:
@@ -109,6 +111,8 @@ class MoELayer:
         self.ws = torch.empty((max(moe_grouped_ffn_workspace_bytes(self.c, N + S, T * (k + S)), 1),),
                               dtype=torch.uint8, device=d)
         self.y_shared = self.y_rows[T * k:] if S > 0 else None
+        self.perm_ws = torch.empty((max(moe_permute_workspace_bytes(self.c, T), 1),),
+                                   dtype=torch.uint8, device=d)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
         # sized for FP32 input, the larger of the two
         self.route_ws = torch.empty((max(moe_route_workspace_bytes(self.c, T, MOE_F32), 1),),
@@ -136,7 +140,7 @@ class MoELayer:
         moe_route(c, x, self.w_router, self.bias, self.scores, self.topk_idx, self.topk_gate,
                   self.counts, ws=self.route_ws)
         mark(2)
-        moe_permute(c, self.topk_idx, self.offsets, self.row_token, self.row_of)
+        moe_permute(c, self.topk_idx, self.offsets, self.row_token, self.row_of, ws=self.perm_ws)
         mark(3)
         moe_grouped_ffn_fp8_gate_up(c, EA, rows, self.xq, self.xs, self.row_token, self.offsets,
                                     self.w1, self.w1s, self.w3, self.w3s, ws=self.ws)

@@ -181,13 +181,18 @@ size_t moe_route_workspace_bytes(const moe_config* cfg, int64_t T, moe_dtype xt)
  *             only when topk_idx holds entries outside [0, N_r); they carry -1 (a row the
  *             grouped FFN turns into zeros) and belong to the first shared segment.
  *   row_of    [T, k] int32, output: permuted row of (t, j)
+ *   ws        workspace of moe_permute_workspace_bytes(cfg, T) bytes (NULL when 0)
  * topk_idx entries outside [0, N_r) are skipped (their row_of is -1). Experts must be
  * distinct within a token (moe_route guarantees it); otherwise rows are unspecified
  * but all accesses stay in bounds.
- * Errors: NULL pointers; invalid config; T < 0 or T*(k+N_s) >= 2^31.
+ * Errors: NULL pointers; invalid config; T < 0 or T*(k+N_s) >= 2^31; workspace.
  */
 moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,
-                       int32_t* offsets, int32_t* row_token, int32_t* row_of, void* stream);
+                       int32_t* offsets, int32_t* row_token, int32_t* row_of, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Workspace bytes moe_permute needs for T tokens (per-block expert counts; 0 for T = 0). */
+size_t moe_permute_workspace_bytes(const moe_config* cfg, int64_t T);
 
 /* Workspace bytes the grouped FFN needs for n_experts experts and n_rows rows (the same
  * figure serves moe_grouped_ffn_fp8 and the gate_up / down pair). */

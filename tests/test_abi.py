@@ -78,7 +78,7 @@ def test_host_validation_status_codes():
         c = _cfg(m, **b)
         assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, fake,
                            1 << 30, None) == 2, b
-        assert L.moe_permute(ctypes.byref(c), 4, fake, fake, fake, fake, None) == 2, b
+        assert L.moe_permute(ctypes.byref(c), 4, fake, fake, fake, fake, fake, 1 << 30, None) == 2, b
     c = _cfg(m)
     big = 1 << 30
     assert L.moe_route(None, fake, 1, 4, fake, fake, fake, fake, fake, fake, fake, big, None) == 1
@@ -95,7 +95,11 @@ def test_host_validation_status_codes():
     assert L.moe_route_workspace_bytes(ctypes.byref(c), 4, 0) > need_r
     assert L.moe_router_weights_elems(20, 256) == 3 * 32 * 256
     assert L.moe_router_weights_elems(20, 100) == 0
-    assert L.moe_permute(ctypes.byref(c), -2, fake, fake, fake, fake, None) == 2
+    assert L.moe_permute(ctypes.byref(c), -2, fake, fake, fake, fake, fake, 1 << 30, None) == 2
+    need_p = L.moe_permute_workspace_bytes(ctypes.byref(c), 1000)
+    assert need_p == 4 * 16 * 4     # 4 blocks of 256 tokens x 16 experts
+    assert L.moe_permute(ctypes.byref(c), 1000, fake, fake, fake, fake, fake, need_p - 1, None) == 6
+    assert L.moe_permute(ctypes.byref(c), 1000, fake, fake, fake, fake, None, 0, None) == 6
     assert L.moe_combine(ctypes.byref(c), 4, fake, 1, fake, fake, None, fake, None) == 1  # N_s=1 needs y_shared
     assert L.moe_update_bias(ctypes.byref(c), 4, None, fake, None) == 1
     # grouped FFN: workspace too small, bad expert count
