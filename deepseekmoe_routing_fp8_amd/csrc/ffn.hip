@@ -119,6 +119,30 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __
   }
 }
 
+// Activation scales of the permuted rows, chunk-major ([H/128][n_rows]): the scales of one
+// K chunk for a tile's rows are then one contiguous run, copied per chunk as a few cache
+// lines instead of one line per row. Rows that name no token get scale 0 (their codes are
+// never used). One block per planned tile.
+__global__ __launch_bounds__(256) void ffn_gather_scales_kernel(const Tile* __restrict__ tiles,
+                                                                const int32_t* __restrict__ n_tiles,
+                                                                int max_tiles, int n_experts,
+                                                                int n_rows, const float* __restrict__ xs,
+                                                                int64_t n_tokens,
+                                                                const int32_t* __restrict__ row_token,
+                                                                int nkc, float* __restrict__ xsp) {
+  const int tile = blockIdx.x;
+  if (tile >= min(*n_tiles, max_tiles)) return;
+  const Tile tl = tiles[tile];
+  if (tl.e < 0 || tl.e >= n_experts || tl.mlen < 1 || tl.mlen > kMT || tl.m0 < 0 ||
+      tl.m0 > n_rows - tl.mlen)
+    return;
+  for (int i = threadIdx.x; i < tl.mlen * nkc; i += 256) {
+    const int r = i % tl.mlen, c = i / tl.mlen;
+    const int64_t t = row_token ? (int64_t)row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
+    xsp[(int64_t)c * n_rows + tl.m0 + r] = (t >= 0 && t < n_tokens) ? xs[t * nkc + c] : 0.0f;
+  }
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding and for all LDS operations (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
 // lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
@@ -183,7 +207,7 @@ struct FfnArgs {
   const int32_t* n_tiles;
   int max_tiles, n_experts, n_rows;
   const uint8_t* aq;     // activation codes: xq (phase 1) or hq (phase 2)
-  const float* as;       // their 1x128 scales
+  const float* as;       // their 1x128 scales, chunk-major per permuted row: [K/128][n_rows]
   int64_t n_tokens;      // rows of aq
   const int32_t* row_token;
   const uint8_t* wa;     // packed W1 (phase 1) or W2 (phase 2)
@@ -258,7 +282,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   const __amdgpu_buffer_rsrc_t adesc =
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.aq), 0, (int)(uint32_t)(a.n_tokens * K), 0x00020000);
   const __amdgpu_buffer_rsrc_t sdesc =
-      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.as), 0, (int)(uint32_t)(a.n_tokens * nkc * 4), 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.as), 0, (int)(uint32_t)((int64_t)a.n_rows * nkc * 4), 0x00020000);
   int aoff[kActDma];
 #pragma unroll
   for (int j = 0; j < kActDma; ++j) {
@@ -267,7 +291,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
     const int src = max(sh.tok_s[min(r, tl.mlen - 1)], 0);
     aoff[j] = src * K + seg * 16;
   }
-  const int soff = max(sh.tok_s[min(tid, tl.mlen - 1)], 0) * nkc * 4;
+  const int soff = (tl.m0 + min(tid, tl.mlen - 1)) * 4;   // permuted row of this lane's scale
 
   // this wave's two fragments of n-block nb: the first fragment row and the row offset
   const int64_t per_expert = (int64_t)a.H * a.I;
@@ -310,7 +334,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
       __builtin_amdgcn_raw_ptr_buffer_load_lds(adesc, (lds_u8*)dst, 16, aoff[j], cc * kTile, 0, 0);
     }
     uint8_t* sdst = wave < kScaleWaves ? st + kActBytes + wave * kWave * 4 : sh.junk;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sdesc, (lds_u8*)sdst, 4, soff, cc * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sdesc, (lds_u8*)sdst, 4, soff, cc * a.n_rows * 4, 0, 0);
   };
 
   v4f acc0[NT], acc1[NT];
@@ -385,7 +409,6 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
     issue(0, r, r, sh.ast[r]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const int nkh = a.I / kTile;
   for (int it = 0; it < nbn; ++it) {
     const int nb = nb0 + it;
     wsc0 = sh.wsc + (it * 2 + wsel0) * kWscRow;
@@ -443,7 +466,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
           for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__fdiv_rn(acc0[ts][i], s)) << (8 * i);
           const int64_t row = tl.m0 + r;
           *reinterpret_cast<uint32_t*>(a.hq + row * a.I + wrow + 4 * (lane >> 4)) = packed;
-          if (wave == 0 && lane < 16) a.hs[row * nkh + nb] = s;
+          if (wave == 0 && lane < 16) a.hs[(int64_t)nb * a.n_rows + row] = s;
         }
         __builtin_amdgcn_sched_barrier(0);   // one tile's temporaries at a time
       }
@@ -564,7 +587,7 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t tiles, ntiles, hq, hs, total;
+  size_t tiles, ntiles, hq, hs, xsp, total;
   int64_t max_tiles;
 };
 
@@ -580,6 +603,8 @@ inline WsLayout ws_layout(const moe_config* c, int32_t n_experts, int64_t n_rows
   off = align256(off + (size_t)n_rows * c->inter);
   L.hs = off;
   off = align256(off + (size_t)n_rows * (c->inter / kTile) * sizeof(float));
+  L.xsp = off;
+  off = align256(off + (size_t)n_rows * (c->hidden / kTile) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -604,6 +629,7 @@ struct FfnCall {
   int32_t* ntiles;
   uint8_t* hq;
   float* hs;
+  float* xsp;
   unsigned grid_tiles;   // M-tile slots, padded to a multiple of the XCD count
 };
 
@@ -614,8 +640,10 @@ moe_status ffn_check(const moe_config* cfg, int32_t n_experts, int64_t n_rows, v
   if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 0 || n_rows >= ((int64_t)1 << 31))
     return MOE_ERR_SHAPE;
   if (cfg->hidden > kMaxChunks * kTile || cfg->inter > kMaxChunks * kTile) return MOE_ERR_UNSUPPORTED;
-  // per-lane operand offsets into hq are 32-bit
-  if (n_rows * (int64_t)cfg->inter >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  // per-lane operand offsets into hq and the chunk-major scale arrays are 32-bit
+  if (n_rows * (int64_t)cfg->inter >= ((int64_t)1 << 32) ||
+      n_rows * (int64_t)(cfg->hidden / kTile) * 4 >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
   f->L = ws_layout(cfg, n_experts, n_rows);
   if (n_rows == 0) return MOE_OK;
   if (!ws || ws_bytes < f->L.total) return MOE_ERR_WORKSPACE;
@@ -628,6 +656,7 @@ moe_status ffn_check(const moe_config* cfg, int32_t n_experts, int64_t n_rows, v
   f->ntiles = reinterpret_cast<int32_t*>(base + f->L.ntiles);
   f->hq = base + f->L.hq;
   f->hs = reinterpret_cast<float*>(base + f->L.hs);
+  f->xsp = reinterpret_cast<float*>(base + f->L.xsp);
   f->grid_tiles = (unsigned)grid_tiles;
   return MOE_OK;
 }
@@ -649,7 +678,11 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
   const int H = cfg->hidden, I = cfg->inter;
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
                      (int)n_rows, (int)f.L.max_tiles, f.tiles, f.ntiles);
-  FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, xs, n_tokens,
+  if (n_tokens > 0)
+    hipLaunchKernelGGL(ffn_gather_scales_kernel, dim3((unsigned)f.L.max_tiles), dim3(256), 0, s,
+                       f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xs, n_tokens,
+                       row_token, H / kTile, f.xsp);
+  FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, f.xsp, n_tokens,
              row_token, w1, w1s, w3, w3s, H, I, I / kTile, kNbPerWg1, f.hq, f.hs, nullptr};
   const unsigned nwg = (unsigned)((a1.n_nb + a1.nb_per - 1) / a1.nb_per);
   hipLaunchKernelGGL((ffn_kernel<1, uint16_t>), dim3(f.grid_tiles * nwg), dim3(kFThreads), 0, s,
