@@ -49,22 +49,25 @@ inline moe_status check_config(const moe_config* c) {
 // ---------------------------------------------------------------------------------
 
 // OCP E4M3FN encoding of a float32 value: nearest finite value, ties to even mantissa,
-// saturating at +-448, sign kept (-0 -> 0x80), NaN -> 0x7F | sign. Exact: the scalings
-// are by powers of two and rintf rounds half to even.
+// saturating at +-448, sign kept (-0 -> 0x80), NaN -> 0x7F | sign. gfx950's
+// v_cvt_pk_fp8_f32 rounds to nearest even on this grid (subnormals included) but turns
+// magnitudes from 464 up into NaN, hence the clamp to +-448 first; NaN takes its own path
+// because the clamp would turn it into a number.
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  float a = fabsf(v);
-  if (!(a == a)) return sign | 0x7Fu;
-  a = fminf(a, kE4M3Max);
-  uint32_t code;
-  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8 (8 is the smallest normal)
-  } else {
-    const int e = __builtin_amdgcn_frexp_expf(a) - 1;   // a in [2^e, 2^(e+1)), e in [-6, 8]
-    const float m = __builtin_rintf(__builtin_ldexpf(a, 3 - e));  // in [8, 16]
-    code = ((uint32_t)(e + 7) << 3) + ((uint32_t)m - 8u);        // 16 carries into e+1
-  }
-  return sign | code;
+  const float c = fminf(fmaxf(v, -kE4M3Max), kE4M3Max);
+  const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false) & 0xFFu;
+  return v == v ? code : (((__float_as_uint(v) >> 24) & 0x80u) | 0x7Fu);
+}
+
+// Four values encoded as by e4m3_encode, packed little-endian (a in the low byte), two
+// per conversion instruction.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  const auto cl = [](float v) { return fminf(fmaxf(v, -kE4M3Max), kE4M3Max); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+  if (!(a == a && b == b && c == c && d == d))
+    return e4m3_encode(a) | (e4m3_encode(b) << 8) | (e4m3_encode(c) << 16) | (e4m3_encode(d) << 24);
+  return (uint32_t)w;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -77,6 +80,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Two float32 values -> packed bf16 (a in the low half), round to nearest even, through
+// gfx950's v_cvt_pk_bf16_f32. For outputs; exact splits use f32_to_bf16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Scale of a quantisation group from its amax: fl32(amax / 448), or 1 when that is 0.

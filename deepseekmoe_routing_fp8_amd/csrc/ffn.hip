@@ -22,6 +22,7 @@
 // output is re-quantised in the epilogue (amax reduced across waves through LDS).
 // Phase 2 (down): wave w owns 32 rows of W2; the workgroup covers 256 output features.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -32,6 +33,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kMT = 160;              // max rows of one expert per tile (multiple of 16)
 constexpr int kThreads = 512;         // 8 waves
@@ -154,6 +156,17 @@ template <int N>
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations but not for
+// its global loads in flight (__syncthreads() would add s_waitcnt vmcnt(0) and drain the
+// weight ring).
+constexpr int kWaitLgkm0 = 0x000F | 0x0070 | 0xC000;   // lgkmcnt(0); vmcnt, expcnt at max
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -409,32 +422,53 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
     issue(0, r, r, sh.ast[r]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // Every n-block ends with an epilogue that issues exactly kEpiStores stores per wave
+  // (lanes with nothing to store are dropped by the buffer range check, never skipped),
+  // behind the next block's first RING-1 chunks; the first block gets as many dummy
+  // stores behind the prologue. Loads and stores complete in issue order, so while those
+  // chunks are awaited (the first group of steps of a block) the wait allows for the
+  // stores behind them.
+  constexpr int kEpiStores = 2 * NT;
+  constexpr int kWaitRing = (RING - 2) * kStepOps;
+  static_assert(kWaitRing + kEpiStores <= 63, "vmcnt range");
+  {
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.as), 0, 0, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kEpiStores; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, lane * 4, 0, 0);
+  }
+  auto group = [&](int it, int s0, auto first) __attribute__((always_inline)) {
+#pragma unroll
+    for (int S = 0; S < RING; ++S) {
+      asm volatile("" ::: "memory");
+      if (decltype(first)::value && S <= RING - 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWaitRing + kEpiStores));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWaitRing));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int g = s0 + S + RING - 1;     // step whose chunk is issued now
+      const int nx = g >= nsteps ? 1 : 0;  // it belongs to the next n-block
+      issue(it + nx, g - nx * nsteps, (S + RING - 1) % RING, sh.ast[(S + RING - 1) % RING]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s0 + S, S);
+    }
+  };
   for (int it = 0; it < nbn; ++it) {
     const int nb = nb0 + it;
     wsc0 = sh.wsc + (it * 2 + wsel0) * kWscRow;
     wsc1 = sh.wsc + (it * 2 + wsel1) * kWscRow;
 #pragma unroll
     for (int ts = 0; ts < NT; ++ts) acc0[ts] = acc1[ts] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsteps; s0 += RING) {
-#pragma unroll
-      for (int S = 0; S < RING; ++S) {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((RING - 2) * kStepOps));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const int g = s0 + S + RING - 1;   // step whose chunk is issued now
-        const int nx = g >= nsteps ? 1 : 0;  // it belongs to the next n-block
-        issue(it + nx, g - nx * nsteps, (S + RING - 1) % RING, sh.ast[(S + RING - 1) % RING]);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(s0 + S, S);
-      }
-    }
+    group(it, 0, std::true_type{});
+    for (int s0 = RING; s0 < nsteps; s0 += RING) group(it, s0, std::false_type{});
 
     // epilogue of n-block nb; the next block's first chunks are already in flight
     const int64_t wrow = wrow_of(nb);
     if (PHASE == 1) {
       // SwiGLU, amax over the 128 columns of the group (4 per lane, 4 lane groups, 8 waves)
-      // h = silu(G) * U replaces G in acc0
+      // h = silu(G) * U replaces G in acc0. silu(g) = g / (1 + 2^(-g log2 e)) with the
+      // hardware exp2 and reciprocal: a relative error of a few 1e-7, far below the E4M3
+      // step that h is rounded to next.
       float(*red)[kMT] = reinterpret_cast<float(*)[kMT]>(sh.red);
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts) {
@@ -444,7 +478,9 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float g = acc0[ts][i];
-          acc0[ts][i] = valid ? (g / (1.0f + expf(-g))) * acc1[ts][i] : 0.0f;
+          const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+          const float h = g * __builtin_amdgcn_rcpf(1.0f + e) * acc1[ts][i];
+          acc0[ts][i] = valid ? h : 0.0f;
           m = fmaxf(m, fabsf(acc0[ts][i]));
         }
         m = fmaxf(m, __shfl_xor(m, 16));
@@ -452,44 +488,54 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
         if (lane < 16) red[wave][r] = m;
         __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();
+      lds_barrier();
+      // codes and scales of the tile's rows; rows past the tile fall outside the
+      // descriptors' ranges, and only wave 0's first 16 lanes write the scales
+      const __amdgpu_buffer_rsrc_t qdesc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(a.hq + (int64_t)tl.m0 * a.I), 0, tl.mlen * a.I, 0x00020000);
+      const __amdgpu_buffer_rsrc_t hdesc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(a.hs + (int64_t)nb * a.n_rows + tl.m0), 0, tl.mlen * 4, 0x00020000);
+      const bool hs_lane = wave == 0 && lane < 16;
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts) {
         const int r = ts * 16 + (lane & 15);
-        if (r < tl.mlen) {
+        {
           float m = red[0][r];
 #pragma unroll
           for (int w = 1; w < kFWaves; ++w) m = fmaxf(m, red[w][r]);
           const float s = group_scale(m);
-          uint32_t packed = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__fdiv_rn(acc0[ts][i], s)) << (8 * i);
-          const int64_t row = tl.m0 + r;
-          *reinterpret_cast<uint32_t*>(a.hq + row * a.I + wrow + 4 * (lane >> 4)) = packed;
-          if (wave == 0 && lane < 16) a.hs[(int64_t)nb * a.n_rows + row] = s;
+          // h / s as h * (1/s): within an ulp of the quotient, which the encoder rounds
+          // and clamps to +-448
+          const float inv = __builtin_amdgcn_rcpf(s);
+          const uint32_t packed = e4m3_pack4(acc0[ts][0] * inv, acc0[ts][1] * inv,
+                                             acc0[ts][2] * inv, acc0[ts][3] * inv);
+          __builtin_amdgcn_raw_buffer_store_b32(packed, qdesc, r * a.I + (int)wrow + 4 * (lane >> 4), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), hdesc, hs_lane ? r * 4 : (1 << 30), 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);   // one tile's temporaries at a time
       }
-      __syncthreads();   // red is free for the next block
-    } else if (wrow < a.H) {
-      YT* y = static_cast<YT*>(a.y);
+      lds_barrier();   // red is free for the next block
+    } else {
+      // rows past the tile fall outside the descriptor's range; the idle waves of a
+      // half-used last block (H % 256 == 128) store past it as well
+      const __amdgpu_buffer_rsrc_t ydesc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(static_cast<YT*>(a.y) + (int64_t)tl.m0 * a.H), 0,
+          tl.mlen * a.H * (int)sizeof(YT), 0x00020000);
+      const uint32_t cb =
+          (uint32_t)((wrow < a.H ? (int)wrow : (1 << 28)) + 4 * (lane >> 4)) * (uint32_t)sizeof(YT);
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts) {
         const int r = ts * 16 + (lane & 15);
-        if (r < tl.mlen) {
-          YT* dst = y + (int64_t)(tl.m0 + r) * a.H + wrow + 4 * (lane >> 4);
-          if constexpr (sizeof(YT) == 2) {
-            uint2 u, v;
-            u.x = f32_to_bf16(acc0[ts][0]) | ((uint32_t)f32_to_bf16(acc0[ts][1]) << 16);
-            u.y = f32_to_bf16(acc0[ts][2]) | ((uint32_t)f32_to_bf16(acc0[ts][3]) << 16);
-            v.x = f32_to_bf16(acc1[ts][0]) | ((uint32_t)f32_to_bf16(acc1[ts][1]) << 16);
-            v.y = f32_to_bf16(acc1[ts][2]) | ((uint32_t)f32_to_bf16(acc1[ts][3]) << 16);
-            *reinterpret_cast<uint2*>(dst) = u;
-            *reinterpret_cast<uint2*>(dst + 16) = v;
-          } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(acc0[ts][0], acc0[ts][1], acc0[ts][2], acc0[ts][3]);
-            *reinterpret_cast<float4*>(dst + 16) = make_float4(acc1[ts][0], acc1[ts][1], acc1[ts][2], acc1[ts][3]);
-          }
+        const uint32_t off = (uint32_t)(r * a.H) * (uint32_t)sizeof(YT) + cb;
+        if constexpr (sizeof(YT) == 2) {
+          const v2u u = {pack_bf16x2(acc0[ts][0], acc0[ts][1]), pack_bf16x2(acc0[ts][2], acc0[ts][3])};
+          const v2u v = {pack_bf16x2(acc1[ts][0], acc1[ts][1]), pack_bf16x2(acc1[ts][2], acc1[ts][3])};
+          __builtin_amdgcn_raw_buffer_store_b64(u, ydesc, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(v, ydesc, (int)(off + 16 * sizeof(YT)), 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc0[ts]), ydesc, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc1[ts]), ydesc,
+                                                 (int)(off + 16 * sizeof(YT)), 0, 0);
         }
       }
     }

@@ -53,12 +53,11 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(const T* __restrict
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
     amax = group_max<16>(amax);
     const float s = group_scale(amax);
-    uint32_t lo = 0, hi = 0;
+    float qv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= e4m3_encode(__fdiv_rn(v[u][i], s)) << (8 * i);
-      hi |= e4m3_encode(__fdiv_rn(v[u][i + 4], s)) << (8 * i);
-    }
+    for (int i = 0; i < 8; ++i) qv[i] = __fdiv_rn(v[u][i], s);
+    const uint32_t lo = e4m3_pack4(qv[0], qv[1], qv[2], qv[3]);
+    const uint32_t hi = e4m3_pack4(qv[4], qv[5], qv[6], qv[7]);
     if (tile < n_tiles) {
       *reinterpret_cast<uint2*>(q + base) = make_uint2(lo, hi);
       if (sub == 0) scales[tile] = s;
@@ -98,9 +97,8 @@ __global__ __launch_bounds__(256) void quantize_128x128_kernel(const float* __re
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + rsub + 8 * i;
-    const uint32_t packed = e4m3_encode(__fdiv_rn(v[i].x, s)) | (e4m3_encode(__fdiv_rn(v[i].y, s)) << 8) |
-                            (e4m3_encode(__fdiv_rn(v[i].z, s)) << 16) |
-                            (e4m3_encode(__fdiv_rn(v[i].w, s)) << 24);
+    const uint32_t packed = e4m3_pack4(__fdiv_rn(v[i].x, s), __fdiv_rn(v[i].y, s),
+                                       __fdiv_rn(v[i].z, s), __fdiv_rn(v[i].w, s));
     *reinterpret_cast<uint32_t*>(dst + r * cols + c0 + col) = packed;
   }
   if (t == 0) scales[blk] = s;
