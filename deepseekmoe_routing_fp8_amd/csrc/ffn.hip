@@ -434,7 +434,8 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   {
     const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.as), 0, 0, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < kEpiStores; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, lane * 4, 0, 0);
+    for (int i = 0; i < kEpiStores; ++i)   // distinct offsets: stores the compiler cannot merge
+      __builtin_amdgcn_raw_buffer_store_b32(0u, none, i * 256 + lane * 4, 0, 0);
   }
   auto group = [&](int it, int s0, auto first) __attribute__((always_inline)) {
 #pragma unroll
