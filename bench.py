@@ -112,6 +112,48 @@ def cpu_baseline(cfg, n_tokens: int):
             "seconds": dt}
 
 
+def decode_step(layer, steps: int, warmup: int):
+    """The T=128 decode step of the same layer (same weights): weight-streaming bound, so
+    it is reported as the grouped FFN's algorithmic HBM bytes per second."""
+    import numpy as np
+    import torch
+
+    import synth
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    cfg = synth.PRESETS["v3_decode"]
+    x = torch.from_numpy(synth.hidden_states(cfg)).to(
+        torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32).cuda()
+    for _ in range(warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    nst = len(MoELayer.STAGES)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+    log(f"[bench] decode: timing {steps} steps of T={cfg.tokens}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer.forward(x, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nst)]
+                         for i in range(steps)])
+    st = {s: float(stage_ms[:, j].mean()) for j, s in enumerate(MoELayer.STAGES)}
+    ab = ffn_algorithmic_bytes(cfg, layer.counts.cpu().numpy())
+    ffn_ms = st["ffn_gate_up"] + st["ffn_down"]
+    gbs = (ab["gate_up"] + ab["down"]) / (ffn_ms * 1e-3) / 1e9
+    gu = ab["gate_up"] / (st["ffn_gate_up"] * 1e-3) / 1e9
+    dn = ab["down"] / (st["ffn_down"] * 1e-3) / 1e9
+    return {"workload": cfg.name, "tokens": cfg.tokens, "steps": steps,
+            "ms_per_step": round(wall * 1e3 / steps, 4),
+            "tokens_per_s": round(cfg.tokens * steps / wall, 1),
+            "experts_touched": ab["experts"],
+            "ffn_algorithmic_bytes": ab["gate_up"] + ab["down"],
+            "ffn_ms": round(ffn_ms, 4),
+            "ffn_gbs": round(gbs, 1), "ffn_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "gate_up_gbs": round(gu, 1), "down_gbs": round(dn, 1),
+            "stage_ms": {s: round(v, 4) for s, v in st.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +162,8 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=50,
+                    help="steps of the T=128 decode workload timed after the main one (0: skip)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -211,6 +255,8 @@ def main():
         "event_ms_per_step": round(float(step_ms.mean()), 4),
         "max_over_mean_load": round(float(counts.max() / counts.mean()), 3),
     }
+    if args.decode_steps > 0 and args.workload != "v3_decode":
+        res["decode"] = decode_step(layer, args.decode_steps, args.warmup)
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)

@@ -124,25 +124,22 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __
 // Activation scales of the permuted rows, chunk-major ([H/128][n_rows]): the scales of one
 // K chunk for a tile's rows are then one contiguous run, copied per chunk as a few cache
 // lines instead of one line per row. Rows that name no token get scale 0 (their codes are
-// never used). One block per planned tile.
-__global__ __launch_bounds__(256) void ffn_gather_scales_kernel(const Tile* __restrict__ tiles,
+// never used). One block per (planned tile, K chunk), one thread per row.
+__global__ __launch_bounds__(kMT) void ffn_gather_scales_kernel(const Tile* __restrict__ tiles,
                                                                 const int32_t* __restrict__ n_tiles,
                                                                 int max_tiles, int n_experts,
                                                                 int n_rows, const float* __restrict__ xs,
                                                                 int64_t n_tokens,
                                                                 const int32_t* __restrict__ row_token,
                                                                 int nkc, float* __restrict__ xsp) {
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.x, c = blockIdx.y, r = threadIdx.x;
   if (tile >= min(*n_tiles, max_tiles)) return;
   const Tile tl = tiles[tile];
   if (tl.e < 0 || tl.e >= n_experts || tl.mlen < 1 || tl.mlen > kMT || tl.m0 < 0 ||
-      tl.m0 > n_rows - tl.mlen)
+      tl.m0 > n_rows - tl.mlen || r >= tl.mlen)
     return;
-  for (int i = threadIdx.x; i < tl.mlen * nkc; i += 256) {
-    const int r = i % tl.mlen, c = i / tl.mlen;
-    const int64_t t = row_token ? (int64_t)row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
-    xsp[(int64_t)c * n_rows + tl.m0 + r] = (t >= 0 && t < n_tokens) ? xs[t * nkc + c] : 0.0f;
-  }
+  const int64_t t = row_token ? (int64_t)row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
+  xsp[(int64_t)c * n_rows + tl.m0 + r] = (t >= 0 && t < n_tokens) ? xs[t * nkc + c] : 0.0f;
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
@@ -428,7 +425,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   // stores behind the prologue. Loads and stores complete in issue order, so while those
   // chunks are awaited (the first group of steps of a block) the wait allows for the
   // stores behind them.
-  constexpr int kEpiStores = 2 * NT;
+  constexpr int kEpiStores = PHASE == 1 ? NT + 1 : (sizeof(YT) == 2 ? NT : 2 * NT);
   constexpr int kWaitRing = (RING - 2) * kStepOps;
   static_assert(kWaitRing + kEpiStores <= 63, "vmcnt range");
   {
@@ -496,7 +493,11 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
           uniform_ptr(a.hq + (int64_t)tl.m0 * a.I), 0, tl.mlen * a.I, 0x00020000);
       const __amdgpu_buffer_rsrc_t hdesc = __builtin_amdgcn_make_buffer_rsrc(
           uniform_ptr(a.hs + (int64_t)nb * a.n_rows + tl.m0), 0, tl.mlen * 4, 0x00020000);
-      const bool hs_lane = wave == 0 && lane < 16;
+      // packed W1/W3 row order: this lane's four h values are columns col0 .. col0+3
+      const int col0 = nb * kTile + 32 * (wave >> 1) + 8 * (lane >> 4) + 4 * (wave & 1);
+      // the scales of tile 4*wave + lane/16 (waves 0..2 cover up to 12 tiles): one store
+      const int ts_mine = 4 * wave + (lane >> 4);
+      float s_mine = 0.0f;
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts) {
         const int r = ts * 16 + (lane & 15);
@@ -510,11 +511,13 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
           const float inv = __builtin_amdgcn_rcpf(s);
           const uint32_t packed = e4m3_pack4(acc0[ts][0] * inv, acc0[ts][1] * inv,
                                              acc0[ts][2] * inv, acc0[ts][3] * inv);
-          __builtin_amdgcn_raw_buffer_store_b32(packed, qdesc, r * a.I + (int)wrow + 4 * (lane >> 4), 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), hdesc, hs_lane ? r * 4 : (1 << 30), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(packed, qdesc, r * a.I + col0, 0, 0);
+          s_mine = ts == ts_mine ? s : s_mine;
         }
         __builtin_amdgcn_sched_barrier(0);   // one tile's temporaries at a time
       }
+      __builtin_amdgcn_raw_buffer_store_b32(
+          __float_as_uint(s_mine), hdesc, ts_mine < NT ? (ts_mine * 16 + (lane & 15)) * 4 : (1 << 30), 0, 0);
       lds_barrier();   // red is free for the next block
     } else {
       // rows past the tile fall outside the descriptor's range; the idle waves of a
@@ -522,21 +525,21 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
       const __amdgpu_buffer_rsrc_t ydesc = __builtin_amdgcn_make_buffer_rsrc(
           uniform_ptr(static_cast<YT*>(a.y) + (int64_t)tl.m0 * a.H), 0,
           tl.mlen * a.H * (int)sizeof(YT), 0x00020000);
+      // packed W2 row order: this lane's eight outputs are features wrow + 8*(lane/16) + 0..7
+      // (acc0 the first four, acc1 the next four)
       const uint32_t cb =
-          (uint32_t)((wrow < a.H ? (int)wrow : (1 << 28)) + 4 * (lane >> 4)) * (uint32_t)sizeof(YT);
+          (uint32_t)((wrow < a.H ? (int)wrow : (1 << 28)) + 8 * (lane >> 4)) * (uint32_t)sizeof(YT);
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts) {
         const int r = ts * 16 + (lane & 15);
         const uint32_t off = (uint32_t)(r * a.H) * (uint32_t)sizeof(YT) + cb;
         if constexpr (sizeof(YT) == 2) {
-          const v2u u = {pack_bf16x2(acc0[ts][0], acc0[ts][1]), pack_bf16x2(acc0[ts][2], acc0[ts][3])};
-          const v2u v = {pack_bf16x2(acc1[ts][0], acc1[ts][1]), pack_bf16x2(acc1[ts][2], acc1[ts][3])};
-          __builtin_amdgcn_raw_buffer_store_b64(u, ydesc, (int)off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(v, ydesc, (int)(off + 16 * sizeof(YT)), 0, 0);
+          const v4u u = {pack_bf16x2(acc0[ts][0], acc0[ts][1]), pack_bf16x2(acc0[ts][2], acc0[ts][3]),
+                         pack_bf16x2(acc1[ts][0], acc1[ts][1]), pack_bf16x2(acc1[ts][2], acc1[ts][3])};
+          __builtin_amdgcn_raw_buffer_store_b128(u, ydesc, (int)off, 0, 0);
         } else {
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc0[ts]), ydesc, (int)off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc1[ts]), ydesc,
-                                                 (int)(off + 16 * sizeof(YT)), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc1[ts]), ydesc, (int)(off + 16), 0, 0);
         }
       }
     }
@@ -726,7 +729,8 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
                      (int)n_rows, (int)f.L.max_tiles, f.tiles, f.ntiles);
   if (n_tokens > 0)
-    hipLaunchKernelGGL(ffn_gather_scales_kernel, dim3((unsigned)f.L.max_tiles), dim3(256), 0, s,
+    hipLaunchKernelGGL(ffn_gather_scales_kernel, dim3((unsigned)f.L.max_tiles, (unsigned)(H / kTile)),
+                       dim3(kMT), 0, s,
                        f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xs, n_tokens,
                        row_token, H / kTile, f.xsp);
   FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, f.xsp, n_tokens,

@@ -118,7 +118,11 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint8_t* __restrict
   const int lane = (int)(r & 63), half = (int)((r >> 6) & 1);
   const int64_t frag = r >> 7, nkc = cols / kTile;
   const int64_t n16 = frag / nkc, kc = frag % nkc;
-  const int64_t row = n16 * 16 + (lane & 15);
+  // rows of a 32-row pair of fragments interleave by 4: fragment 2m holds rows
+  // 32m + 8a + b and fragment 2m+1 rows 32m + 8a + 4 + b (a, b < 4), so that the four
+  // MFMA output rows a lane gets from each fragment of the pair are adjacent
+  const int j = lane & 15;
+  const int64_t row = 32 * (n16 >> 1) + 8 * (j >> 2) + 4 * (n16 & 1) + (j & 3);
   const int64_t col = kc * kTile + half * 64 + (lane >> 4) * 16;
   const uint4 v = *reinterpret_cast<const uint4*>(q + mat * rows * cols + row * cols + col);
   *reinterpret_cast<uint4*>(out + o * 16) = v;
@@ -131,7 +135,7 @@ using namespace moe;
 
 extern "C" moe_status moe_pack_fp8_weights(const uint8_t* q, int64_t mats, int64_t rows, int64_t cols,
                                            uint8_t* packed, void* stream) {
-  if (mats < 0 || rows <= 0 || cols <= 0 || rows % 16 || cols % kTile) return MOE_ERR_SHAPE;
+  if (mats < 0 || rows <= 0 || cols <= 0 || rows % 32 || cols % kTile) return MOE_ERR_SHAPE;
   const int64_t units = mats * rows * cols / 16;
   if (units == 0) return MOE_OK;
   if (!q || !packed) return MOE_ERR_NULL;

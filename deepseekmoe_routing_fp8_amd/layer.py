@@ -60,8 +60,9 @@ class MoELayer:
         """Row-major codes of one packed [rows, cols] matrix (inverse of the packing)."""
         rows, cols = packed.shape
         nkc = cols // 128
-        f = packed.reshape(rows // 16, nkc, 2, 4, 16, 16)      # n16, kc, half, lane/16, lane%16, byte
-        return np.ascontiguousarray(f.transpose(0, 4, 1, 2, 3, 5)).reshape(rows, cols)
+        # fragment n16 = 2m + p, lane = 16g + 4a + b holds row 32m + 8a + 4p + b
+        f = packed.reshape(rows // 32, 2, nkc, 2, 4, 4, 4, 16)   # m, p, kc, half, g, a, b, byte
+        return np.ascontiguousarray(f.transpose(0, 5, 1, 6, 2, 3, 4, 7)).reshape(rows, cols)
 
     def load_weights(self, w_router: np.ndarray, bias: np.ndarray,
                      routed: Callable[[Callable], None], shared: Callable[[Callable], None]):

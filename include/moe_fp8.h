@@ -104,10 +104,13 @@ moe_status moe_quantize_128x128(const float* w, int64_t mats, int64_t rows, int6
  * weight matrix as 2 KB of contiguous memory in MFMA operand order, which HBM serves at
  * close to its sequential bandwidth. For a [rows, cols] matrix, fragment (n16, kc) sits
  * at byte ((n16 * cols/128) + kc) * 2048, as two 1 KB halves h = 0, 1; byte b of lane l
- * (0..63) in half h holds code [16*n16 + l%16][128*kc + 64*h + 16*(l/16) + b].
+ * (0..63) in half h holds code [rho(n16, l%16)][128*kc + 64*h + 16*(l/16) + b] with
+ * rho(n16, j) = 32*(n16/2) + 8*(j/4) + 4*(n16%2) + j%4: the two fragments of a 32-row
+ * group interleave their rows by 4, so that the eight outputs a lane gets from the pair
+ * are adjacent columns of the result.
  *   q       [mats, rows, cols] uint8 row-major codes (e.g. from moe_quantize_128x128)
  *   packed  [mats, rows*cols] uint8, output; must not overlap q
- * Errors: NULL pointers; rows % 16 or cols % 128 != 0; q == packed (UNSUPPORTED).
+ * Errors: NULL pointers; rows % 32 or cols % 128 != 0; q == packed (UNSUPPORTED).
  */
 moe_status moe_pack_fp8_weights(const uint8_t* q, int64_t mats, int64_t rows, int64_t cols,
                                 uint8_t* packed, void* stream);

@@ -140,3 +140,30 @@ def test_workspace_size_grows_with_rows():
     b = m._lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 16, 4096)
     assert 0 < a < b
     assert m._lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 0, 256) == 0
+
+
+def test_unpack_inverts_documented_pack_map():
+    """MoELayer.unpack against the packed layout written out from its documented index
+    map (byte b of lane l, half h of fragment (n16, kc) holds code
+    [32*(n16/2) + 8*(j/4) + 4*(n16%2) + j%4][128*kc + 64*h + 16*(l/16) + b], j = l%16)."""
+    import numpy as np
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    rows, cols = 96, 384
+    W = np.random.default_rng(5).integers(0, 256, (rows, cols)).astype(np.uint8)
+    packed = np.empty(rows * cols, np.uint8)
+    nkc = cols // 128
+    for n16 in range(rows // 16):
+        for kc in range(nkc):
+            for h in range(2):
+                for l in range(64):
+                    j = l % 16
+                    r = 32 * (n16 // 2) + 8 * (j // 4) + 4 * (n16 % 2) + j % 4
+                    c = 128 * kc + 64 * h + 16 * (l // 16)
+                    o = ((n16 * nkc + kc) * 2 + h) * 1024 + l * 16
+                    packed[o:o + 16] = W[r, c:c + 16]
+    assert np.array_equal(MoELayer.unpack(packed.reshape(rows, cols)), W)
+    # every row of a 32-row group appears exactly once across its two fragments
+    js = np.arange(16)
+    for m in range(rows // 32):
+        got = sorted([32 * m + 8 * (j // 4) + 4 * p + j % 4 for p in range(2) for j in js])
+        assert got == list(range(32 * m, 32 * m + 32))

@@ -366,11 +366,12 @@ def _pack_reference(W):
     nkc = cols // 128
     n16, kc, h, l, b = np.meshgrid(np.arange(rows // 16), np.arange(nkc), np.arange(2),
                                    np.arange(64), np.arange(16), indexing="ij")
-    src = W[16 * n16 + l % 16, 128 * kc + 64 * h + 16 * (l // 16) + b]
+    j = l % 16
+    src = W[32 * (n16 // 2) + 8 * (j // 4) + 4 * (n16 % 2) + j % 4, 128 * kc + 64 * h + 16 * (l // 16) + b]
     return src.reshape(-1)
 
 
-@pytest.mark.parametrize("mats,rows,cols", [(1, 16, 128), (3, 48, 384), (2, 2048, 1024)])
+@pytest.mark.parametrize("mats,rows,cols", [(1, 32, 128), (3, 96, 384), (2, 2048, 1024)])
 def test_pack_fp8_weights_layout(lib, mats, rows, cols):
     rng = np.random.default_rng(rows + cols)
     W = rng.integers(0, 256, (mats, rows, cols)).astype(np.uint8)
