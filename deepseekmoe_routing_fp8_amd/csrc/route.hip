@@ -289,10 +289,32 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
+// Affinities: one thread per (token, expert) sums the S partial logits in split order in
+// FP64, applies the sigmoid and rounds to FP32. Eight partials are loaded before any is
+// added, so a long split (small T: many K ranges) is not one load latency per range.
+__global__ __launch_bounds__(256) void router_reduce_kernel(const double* __restrict__ part,
+                                                            int S, int64_t T, int N,
+                                                            float* __restrict__ scores) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * N) return;
+  const int64_t plane = T * N;
+  double z = 0.0;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = s0 + u < S ? part[(int64_t)(s0 + u) * plane + i] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) z += v[u];
+  }
+  scores[i] = (float)(1.0 / (1.0 + exp(-z)));
+}
+
 // ------------------------------------------------------------------------------------
 // Top-k
 // ------------------------------------------------------------------------------------
 constexpr int kTopkWaves = 4;
+constexpr int kFusedSplits = 8;   // up to this many K ranges the top-k waves sum them
 constexpr int kPerLane = kMaxRouted / kWave;  // 8 experts per lane at most
 
 // (value desc, index asc) order: is (v, i) ahead of (bv, bi)?
@@ -341,10 +363,13 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return m;
 }
 
+// FUSED: the wave also sums its token's partial logits (short splits, large T);
+// otherwise the affinities come from router_reduce_kernel.
+template <bool FUSED>
 __global__ __launch_bounds__(kTopkWaves * kWave) void router_topk_kernel(
-    const double* __restrict__ part, int S, const float* __restrict__ bias, int64_t T, int N,
-    int k, int G, int Gk, int topn, float rho, float* __restrict__ scores,
-    int32_t* __restrict__ idx_out, float* __restrict__ gate_out) {
+    const double* __restrict__ part, int S, float* __restrict__ scores,
+    const float* __restrict__ bias, int64_t T, int N, int k, int G, int Gk, int topn, float rho,
+    int32_t* __restrict__ idx_out, float* __restrict__ gate_out, int32_t* __restrict__ counts) {
   __shared__ float rbuf[kTopkWaves][kMaxRouted];
   __shared__ float gtop[kTopkWaves][kMaxRouted];
   __shared__ float gbuf[kTopkWaves][kMaxGroups];
@@ -353,7 +378,8 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void router_topk_kernel(
   if (t >= T) return;   // whole wave; no workgroup barrier below
   const int gsz = N / G;
 
-  // affinities: FP64 sum of the partial logits in split order, sigmoid, rounded to FP32
+  // affinities (FP64 sum of the partial logits in split order, sigmoid, rounded to FP32)
+  // and bias-adjusted selection scores
   float sv[kPerLane], rv[kPerLane];
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
@@ -361,10 +387,14 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void router_topk_kernel(
     sv[i] = 0.0f;
     rv[i] = -INFINITY;
     if (e < N) {
-      double z = 0.0;
-      for (int s = 0; s < S; ++s) z += part[((int64_t)s * T + t) * N + e];
-      sv[i] = (float)(1.0 / (1.0 + exp(-z)));
-      scores[t * N + e] = sv[i];
+      if (FUSED) {
+        double z = 0.0;
+        for (int s = 0; s < S; ++s) z += part[((int64_t)s * T + t) * N + e];
+        sv[i] = (float)(1.0 / (1.0 + exp(-z)));
+        scores[t * N + e] = sv[i];
+      } else {
+        sv[i] = scores[t * N + e];
+      }
       rv[i] = sv[i] + bias[e];
     }
   }
@@ -439,10 +469,12 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void router_topk_kernel(
   if (lane < k) {
     idx_out[t * k + lane] = my_e;
     gate_out[t * k + lane] = __fdiv_rn(my_s, sum) * rho;
+    if (counts) atomicAdd(&counts[my_e], 1);   // per-expert load (counts zeroed beforehand)
   }
 }
 
-// counts[e] += number of entries of idx equal to e (counts zeroed beforehand)
+// counts[e] += number of entries of idx equal to e (counts zeroed beforehand): per-block
+// LDS histograms, then one global add per expert and block
 __global__ __launch_bounds__(256) void router_counts_kernel(const int32_t* __restrict__ idx,
                                                             int64_t n, int N,
                                                             int32_t* __restrict__ counts) {
@@ -457,6 +489,10 @@ __global__ __launch_bounds__(256) void router_counts_kernel(const int32_t* __res
   for (int i = threadIdx.x; i < N; i += 256)
     if (hist[i]) atomicAdd(&counts[i], hist[i]);
 }
+
+// Up to this many selections the top-k waves count them with global atomics; beyond, the
+// contention on the N counters costs more than a histogram launch.
+constexpr int64_t kAtomicCountPairs = 4096;
 
 inline size_t align256r(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -523,7 +559,7 @@ extern "C" moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype 
   hipLaunchKernelGGL(fill_i32_kernel, dim3((N + 255) / 256), dim3(256), 0, s, counts, N, 0);
   if (T == 0) return launch_status();
   const RouteGeom g = route_geom(T, N, H);
-  if (g.grid > 0x7fffffff) return MOE_ERR_SHAPE;
+  if (g.grid > 0x7fffffff || (T * N + 255) / 256 > 0x7fffffff) return MOE_ERR_SHAPE;
   uint8_t* base = static_cast<uint8_t*>(ws);
   double* part = reinterpret_cast<double*>(base + W.part);
   const int nb16 = (N + 15) / 16;
@@ -538,13 +574,21 @@ extern "C" moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype 
     hipLaunchKernelGGL(router_logits_kernel<3>, dim3((unsigned)g.grid), dim3(kLThreads), 0, s,
                        xs3, T, H, w_router_split, N, nb16, g, part);
   }
-  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + kTopkWaves - 1) / kTopkWaves)),
-                     dim3(kTopkWaves * kWave), 0, s, part, g.S, bias, T, N, cfg->top_k,
-                     cfg->n_group, cfg->topk_group, cfg->group_topn, cfg->routed_scaling, scores,
-                     topk_idx, topk_gate);
+  // few tokens: many K ranges, summed by one thread per (token, expert) first
+  const bool fused = g.S <= kFusedSplits;
+  if (!fused)
+    hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((T * N + 255) / 256)), dim3(256), 0,
+                       s, part, g.S, T, N, scores);
+  hipLaunchKernelGGL(fused ? router_topk_kernel<true> : router_topk_kernel<false>,
+                     dim3((unsigned)((T + kTopkWaves - 1) / kTopkWaves)), dim3(kTopkWaves * kWave),
+                     0, s, part, g.S, scores, bias, T, N, cfg->top_k, cfg->n_group, cfg->topk_group,
+                     cfg->group_topn, cfg->routed_scaling, topk_idx, topk_gate,
+                     T * cfg->top_k <= kAtomicCountPairs ? counts : nullptr);
   const int64_t pairs = T * cfg->top_k;
-  const int cblocks = (int)std::min<int64_t>(64, (pairs + 8191) / 8192);
-  hipLaunchKernelGGL(router_counts_kernel, dim3(cblocks), dim3(256), 0, s, topk_idx, pairs, N,
-                     counts);
+  if (pairs > kAtomicCountPairs) {
+    const int cblocks = (int)std::min<int64_t>(64, (pairs + 8191) / 8192);
+    hipLaunchKernelGGL(router_counts_kernel, dim3(cblocks), dim3(256), 0, s, topk_idx, pairs, N,
+                       counts);
+  }
   return launch_status();
 }
