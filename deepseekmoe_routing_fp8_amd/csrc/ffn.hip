@@ -124,7 +124,10 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __
 // Activation scales of the permuted rows, chunk-major ([H/128][n_rows]): the scales of one
 // K chunk for a tile's rows are then one contiguous run, copied per chunk as a few cache
 // lines instead of one line per row. Rows that name no token get scale 0 (their codes are
-// never used). One block per (planned tile, K chunk), one thread per row.
+// never used). One block per (planned tile, group of kGatherChunks K chunks), one thread
+// per row; a thread's loads for the group are all issued before its stores.
+constexpr int kGatherChunks = 8;
+
 __global__ __launch_bounds__(kMT) void ffn_gather_scales_kernel(const Tile* __restrict__ tiles,
                                                                 const int32_t* __restrict__ n_tiles,
                                                                 int max_tiles, int n_experts,
@@ -132,14 +135,20 @@ __global__ __launch_bounds__(kMT) void ffn_gather_scales_kernel(const Tile* __re
                                                                 int64_t n_tokens,
                                                                 const int32_t* __restrict__ row_token,
                                                                 int nkc, float* __restrict__ xsp) {
-  const int tile = blockIdx.x, c = blockIdx.y, r = threadIdx.x;
+  const int tile = blockIdx.x, c0 = blockIdx.y * kGatherChunks, r = threadIdx.x;
   if (tile >= min(*n_tiles, max_tiles)) return;
   const Tile tl = tiles[tile];
   if (tl.e < 0 || tl.e >= n_experts || tl.mlen < 1 || tl.mlen > kMT || tl.m0 < 0 ||
       tl.m0 > n_rows - tl.mlen || r >= tl.mlen)
     return;
   const int64_t t = row_token ? (int64_t)row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
-  xsp[(int64_t)c * n_rows + tl.m0 + r] = (t >= 0 && t < n_tokens) ? xs[t * nkc + c] : 0.0f;
+  const bool ok = t >= 0 && t < n_tokens;
+  float v[kGatherChunks];
+#pragma unroll
+  for (int u = 0; u < kGatherChunks; ++u) v[u] = (ok && c0 + u < nkc) ? xs[t * nkc + c0 + u] : 0.0f;
+#pragma unroll
+  for (int u = 0; u < kGatherChunks; ++u)
+    if (c0 + u < nkc) xsp[(int64_t)(c0 + u) * n_rows + tl.m0 + r] = v[u];
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
@@ -729,7 +738,8 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
                      (int)n_rows, (int)f.L.max_tiles, f.tiles, f.ntiles);
   if (n_tokens > 0)
-    hipLaunchKernelGGL(ffn_gather_scales_kernel, dim3((unsigned)f.L.max_tiles, (unsigned)(H / kTile)),
+    hipLaunchKernelGGL(ffn_gather_scales_kernel,
+                       dim3((unsigned)f.L.max_tiles, (unsigned)((H / kTile + kGatherChunks - 1) / kGatherChunks)),
                        dim3(kMT), 0, s,
                        f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xs, n_tokens,
                        row_token, H / kTile, f.xsp);

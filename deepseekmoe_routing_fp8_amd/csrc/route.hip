@@ -586,7 +586,7 @@ extern "C" moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype 
                      T * cfg->top_k <= kAtomicCountPairs ? counts : nullptr);
   const int64_t pairs = T * cfg->top_k;
   if (pairs > kAtomicCountPairs) {
-    const int cblocks = (int)std::min<int64_t>(64, (pairs + 8191) / 8192);
+    const int cblocks = (int)std::min<int64_t>(256, (pairs + 1023) / 1024);
     hipLaunchKernelGGL(router_counts_kernel, dim3(cblocks), dim3(256), 0, s, topk_idx, pairs, N,
                        counts);
   }
