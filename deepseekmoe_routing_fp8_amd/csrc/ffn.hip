@@ -254,7 +254,8 @@ typedef __attribute__((address_space(3))) const v4i lds_v4i;
 typedef __attribute__((address_space(3))) const float lds_f32;
 
 struct FfnLds {
-  uint8_t* ast[kMaxRing];   // ring slots (kAStage bytes each, 128-byte aligned)
+  uint8_t* ast[kMaxRing];   // ring slots (kAStage bytes each, 128-byte aligned); the
+                            // last one, never a ring slot, stages phase-1 h codes
   uint8_t* junk;            // kJunk bytes
   const int* tok_s;         // source row of every tile row (-1: none)
   const float* wsc;         // [n-block][2][kMaxChunks + kMaxRing] weight-block scales
@@ -434,7 +435,9 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   // stores behind the prologue. Loads and stores complete in issue order, so while those
   // chunks are awaited (the first group of steps of a block) the wait allows for the
   // stores behind them.
-  constexpr int kEpiStores = PHASE == 1 ? NT + 1 : (sizeof(YT) == 2 ? NT : 2 * NT);
+  constexpr int kStageStores = (kMT * 8 + kFThreads - 1) / kFThreads;   // 16-byte units
+  constexpr int kEpiStores = PHASE == 1 ? kStageStores + 1 : (sizeof(YT) == 2 ? NT : 2 * NT);
+  static_assert(RING < kMaxRing, "the last LDS slot stages the epilogue");
   constexpr int kWaitRing = (RING - 2) * kStepOps;
   static_assert(kWaitRing + kEpiStores <= 63, "vmcnt range");
   {
@@ -496,14 +499,17 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
         __builtin_amdgcn_sched_barrier(0);
       }
       lds_barrier();
-      // codes and scales of the tile's rows; rows past the tile fall outside the
-      // descriptors' ranges, and only wave 0's first 16 lanes write the scales
+      // codes of the tile's rows go through the staging slot (row r: 128 bytes, 16-byte
+      // segment s at s ^ (r & 7)) and out as whole rows; rows past the tile fall outside
+      // the descriptors' ranges
       const __amdgpu_buffer_rsrc_t qdesc = __builtin_amdgcn_make_buffer_rsrc(
-          uniform_ptr(a.hq + (int64_t)tl.m0 * a.I), 0, tl.mlen * a.I, 0x00020000);
+          uniform_ptr(a.hq + (int64_t)tl.m0 * a.I + (int64_t)nb * kTile), 0, tl.mlen * a.I, 0x00020000);
       const __amdgpu_buffer_rsrc_t hdesc = __builtin_amdgcn_make_buffer_rsrc(
           uniform_ptr(a.hs + (int64_t)nb * a.n_rows + tl.m0), 0, tl.mlen * 4, 0x00020000);
-      // packed W1/W3 row order: this lane's four h values are columns col0 .. col0+3
-      const int col0 = nb * kTile + 32 * (wave >> 1) + 8 * (lane >> 4) + 4 * (wave & 1);
+      uint8_t* stage = sh.ast[kMaxRing - 1];
+      // packed W1/W3 row order: this lane's four h values are columns col .. col+3 of the
+      // block's 128
+      const int col = 32 * (wave >> 1) + 8 * (lane >> 4) + 4 * (wave & 1);
       // the scales of tile 4*wave + lane/16 (waves 0..2 cover up to 12 tiles): one store
       const int ts_mine = 4 * wave + (lane >> 4);
       float s_mine = 0.0f;
@@ -520,14 +526,22 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
           const float inv = __builtin_amdgcn_rcpf(s);
           const uint32_t packed = e4m3_pack4(acc0[ts][0] * inv, acc0[ts][1] * inv,
                                              acc0[ts][2] * inv, acc0[ts][3] * inv);
-          __builtin_amdgcn_raw_buffer_store_b32(packed, qdesc, r * a.I + col0, 0, 0);
+          *reinterpret_cast<uint32_t*>(stage + r * kTile + ((((col >> 4) ^ (r & 7))) << 4) + (col & 15)) =
+              packed;
           s_mine = ts == ts_mine ? s : s_mine;
         }
         __builtin_amdgcn_sched_barrier(0);   // one tile's temporaries at a time
       }
       __builtin_amdgcn_raw_buffer_store_b32(
           __float_as_uint(s_mine), hdesc, ts_mine < NT ? (ts_mine * 16 + (lane & 15)) * 4 : (1 << 30), 0, 0);
-      lds_barrier();   // red is free for the next block
+      lds_barrier();   // the staged codes are complete; red is free for the next block
+#pragma unroll
+      for (int q = 0; q < kStageStores; ++q) {
+        const int u = (q * kFWaves + wave) * kWave + lane;   // 16-byte unit: row u/8, segment u%8
+        const int row = u >> 3, seg = u & 7, rr = min(row, kMT - 1);
+        const v4u v = *reinterpret_cast<const v4u*>(stage + rr * kTile + ((seg ^ (rr & 7)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(v, qdesc, row * a.I + seg * 16, 0, 0);
+      }
     } else {
       // rows past the tile fall outside the descriptor's range; the idle waves of a
       // half-used last block (H % 256 == 128) store past it as well
