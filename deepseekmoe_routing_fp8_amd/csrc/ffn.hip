@@ -308,8 +308,12 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   for (int j = 0; j < kActDma; ++j) {
     const int unit = min((j * kActRound + wave * 1024 + lane * 16) / 16, kActBytes / 16 - 1);
     const int r = unit >> 3, seg = (unit & 7) ^ (r & 7);
-    const int src = max(sh.tok_s[min(r, tl.mlen - 1)], 0);
-    aoff[j] = src * K + seg * 16;
+    // rows past the tile and rows without a token read zeros (an offset at the end of
+    // the range), so the padding of the last 16-row tile costs the matrix cores no
+    // switching power
+    const int src = sh.tok_s[r];
+    aoff[j] = (int)(src >= 0 ? (uint32_t)src * (uint32_t)K + (uint32_t)(seg * 16)
+                             : (uint32_t)(a.n_tokens * K));
   }
   const int soff = (tl.m0 + min(tid, tl.mlen - 1)) * 4;   // permuted row of this lane's scale
 
