@@ -16,11 +16,14 @@
 //   bytes per lane. A 4-deep ring of 32-wide K steps keeps three steps in flight.
 //   Workgroups with the same (K range, expert block) run on one XCD, so their W_r
 //   slice (1.4 MB at the V3 shape) stays in that XCD's L2.
-// router_topk: one wavefront per token: sums the S partials in a fixed order, sigmoid,
+// router_reduce (long splits only, i.e. few tokens): one thread per (token, expert) sums
+//   the S partials in a fixed order and applies the sigmoid.
+// router_topk: one wavefront per token: for short splits sums the S partials itself,
 //   ranking score s + b, optional group limit (each expert's rank inside its group),
-//   top-k by wave-wide maxima of (score, index) keys, gates.
-// router_counts: load histogram from topk_idx (LDS histogram per workgroup, then one
-//   global atomic per expert and workgroup).
+//   top-k by wave-wide maxima of (score, index) keys, gates; for few tokens it also
+//   counts the selections with global atomics.
+// router_counts (many tokens): load histogram from topk_idx (LDS histogram per
+//   workgroup, then one global atomic per expert and workgroup).
 #include <algorithm>
 
 #include "common.h"
