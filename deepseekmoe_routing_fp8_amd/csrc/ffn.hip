@@ -213,7 +213,7 @@ constexpr int kScaleBytes = kScaleWaves * kWave * 4;
 constexpr int kAStage = kActBytes + kScaleBytes; // one ring slot, a multiple of 128 bytes
 constexpr int kJunk = 1024;                      // landing area of copies past the slot
 constexpr int kStepOps = 4 + kActDma + 1;        // vector-memory ops per wave per chunk
-constexpr int kMaxRing = 7;
+constexpr int kMaxRing = 5;   // ring slots (depth 4) + the epilogue staging slot
 constexpr int kMaxNbPerWg = 4;                   // n-blocks one workgroup runs back to back
 constexpr int kNbPerWg1 = 2, kNbPerWg2 = 4;      // gate/up (16 blocks at I = 2048), down
 constexpr int kXcds = 8;
@@ -592,8 +592,6 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   __shared__ __attribute__((aligned(128))) uint8_t ast2[kAStage];
   __shared__ __attribute__((aligned(128))) uint8_t ast3[kAStage];
   __shared__ __attribute__((aligned(128))) uint8_t ast4[kAStage];
-  __shared__ __attribute__((aligned(128))) uint8_t ast5[kAStage];
-  __shared__ __attribute__((aligned(128))) uint8_t ast6[kAStage];
   __shared__ __attribute__((aligned(16))) uint8_t junk[kJunk];
   __shared__ int tok_s[kMT];
   constexpr int kWscRow = kMaxChunks + kMaxRing;
@@ -648,16 +646,20 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   }
   __syncthreads();
 
-  const FfnLds sh{{ast0, ast1, ast2, ast3, ast4, ast5, ast6}, junk, tok_s, &wsc[0][0], red};
-  constexpr int R1 = PHASE == 1 ? 5 : 4;   // ring depth for tiles of up to 8 16-row tiles
-  constexpr int R2 = 4;                    // and for taller tiles
+  const FfnLds sh{{ast0, ast1, ast2, ast3, ast4}, junk, tok_s, &wsc[0][0], red};
+  // Ring depth 4: three chunks (96 KB of weights per CU) in flight cover the loaded HBM
+  // latency, the accumulators of 10 16-row tiles still fit beside the ring, and K
+  // chunk counts of the usual shapes (56, 16) divide by it, so no block ends in steps
+  // of zero weights. (A depth of 5 for the shorter tiles measured 1.5% slower on the
+  // V3 prefill gate/up: its 60 padded steps per block cost more than the depth gained.)
+  constexpr int R = 4;
   switch ((tl.mlen + 15) >> 4) {
-    case 1: case 2: ffn_main<PHASE, YT, 2, R1>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 3: case 4: ffn_main<PHASE, YT, 4, R1>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 5: case 6: ffn_main<PHASE, YT, 6, R1>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 7: case 8: ffn_main<PHASE, YT, 8, R1>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 9: ffn_main<PHASE, YT, 9, R2>(a, tl, nb0, nbn, wave, lane, sh); break;
-    default: ffn_main<PHASE, YT, 10, R2>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 1: case 2: ffn_main<PHASE, YT, 2, R>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 3: case 4: ffn_main<PHASE, YT, 4, R>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 5: case 6: ffn_main<PHASE, YT, 6, R>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 7: case 8: ffn_main<PHASE, YT, 8, R>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 9: ffn_main<PHASE, YT, 9, R>(a, tl, nb0, nbn, wave, lane, sh); break;
+    default: ffn_main<PHASE, YT, 10, R>(a, tl, nb0, nbn, wave, lane, sh); break;
   }
 }
 

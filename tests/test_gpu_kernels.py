@@ -392,6 +392,9 @@ def _relerr(a, b):
     (512, 256, 3, [193, 1, 400], False),          # several M tiles, tiny tail
     (384, 256, 2, [16, 33], True),                 # identity token map, H % 256 == 128
     (1024, 512, 5, [130, 0, 0, 7, 250], False),
+    # every tile height the kernel specialises (2, 4, 6, 8, 9, 10 16-row tiles) on both
+    # sides of its boundary, and the 160-row split into two tiles
+    (256, 256, 12, [160, 161, 16, 17, 48, 80, 112, 113, 128, 129, 144, 145], False),
 ])
 def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity):
     import dataclasses
