@@ -260,6 +260,8 @@ struct FfnLds {
   const int* tok_s;         // source row of every tile row (-1: none)
   const float* wsc;         // [n-block][2][kMaxChunks + kMaxRing] weight-block scales
   float* red;               // [kFWaves][kMT] phase-1 amax partials
+  uint8_t* ystage;          // phase 2, bf16 output: [kMT/2][512 bytes] block rows (the
+                            // last slot, enlarged)
 };
 
 // A wave-uniform pointer in scalar registers (buffer descriptors must be uniform; the
@@ -440,7 +442,9 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   // chunks are awaited (the first group of steps of a block) the wait allows for the
   // stores behind them.
   constexpr int kStageStores = (kMT * 8 + kFThreads - 1) / kFThreads;   // 16-byte units
-  constexpr int kEpiStores = PHASE == 1 ? kStageStores + 1 : (sizeof(YT) == 2 ? NT : 2 * NT);
+  constexpr int kYStores = kMT * 32 / kFThreads;   // 16-byte units of a staged output block
+  static_assert(kMT * 32 % (2 * kFThreads) == 0 && kNTS % 2 == 0, "whole store rounds per half");
+  constexpr int kEpiStores = PHASE == 1 ? kStageStores + 1 : (sizeof(YT) == 2 ? kYStores : 2 * NT);
   static_assert(RING < kMaxRing, "the last LDS slot stages the epilogue");
   constexpr int kWaitRing = (RING - 2) * kStepOps;
   static_assert(kWaitRing + kEpiStores <= 63, "vmcnt range");
@@ -556,15 +560,42 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
       // (acc0 the first four, acc1 the next four)
       const uint32_t cb =
           (uint32_t)((wrow < a.H ? (int)wrow : (1 << 28)) + 8 * (lane >> 4)) * (uint32_t)sizeof(YT);
+      if constexpr (sizeof(YT) == 2) {
+        // bf16: the block's rows are staged in LDS, half the tile at a time (row r: 512
+        // bytes, 16-byte segment s at s ^ (r & 15)), and written as whole 512-byte row
+        // pieces
+        (void)cb;
+        uint8_t* st = sh.ystage;
+        const int sg = 4 * wave + (lane >> 4);   // this lane's segment of the 256-feature block
+        const int fb = nb * 256;
+        constexpr int kHalfTiles = kNTS / 2;
 #pragma unroll
-      for (int ts = 0; ts < NT; ++ts) {
-        const int r = ts * 16 + (lane & 15);
-        const uint32_t off = (uint32_t)(r * a.H) * (uint32_t)sizeof(YT) + cb;
-        if constexpr (sizeof(YT) == 2) {
-          const v4u u = {pack_bf16x2(acc0[ts][0], acc0[ts][1]), pack_bf16x2(acc0[ts][2], acc0[ts][3]),
-                         pack_bf16x2(acc1[ts][0], acc1[ts][1]), pack_bf16x2(acc1[ts][2], acc1[ts][3])};
-          __builtin_amdgcn_raw_buffer_store_b128(u, ydesc, (int)off, 0, 0);
-        } else {
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+          for (int ts = hf * kHalfTiles; ts < (hf + 1) * kHalfTiles && ts < NT; ++ts) {
+            const int r = (ts - hf * kHalfTiles) * 16 + (lane & 15);
+            const v4u u = {pack_bf16x2(acc0[ts][0], acc0[ts][1]), pack_bf16x2(acc0[ts][2], acc0[ts][3]),
+                           pack_bf16x2(acc1[ts][0], acc1[ts][1]), pack_bf16x2(acc1[ts][2], acc1[ts][3])};
+            *reinterpret_cast<v4u*>(st + r * 512 + ((sg ^ (r & 15)) << 4)) = u;
+          }
+          lds_barrier();
+#pragma unroll
+          for (int q = 0; q < kYStores / 2; ++q) {
+            const int u = (q * kFWaves + wave) * kWave + lane;   // row u/32 of the half, segment u%32
+            const int rh = u >> 5, seg = u & 31;
+            const v4u v = *reinterpret_cast<const v4u*>(st + rh * 512 + ((seg ^ (rh & 15)) << 4));
+            const int row = hf * kHalfTiles * 16 + rh;
+            const int feat = fb + seg * 8;   // features past H (a half-used last block) are dropped
+            const int off = feat < a.H ? (row * a.H + feat) * (int)sizeof(YT) : (1 << 30);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ydesc, off, 0, 0);
+          }
+          if (hf == 0) lds_barrier();   // the first half is read before the second is written
+        }
+      } else {
+#pragma unroll
+        for (int ts = 0; ts < NT; ++ts) {
+          const int r = ts * 16 + (lane & 15);
+          const uint32_t off = (uint32_t)(r * a.H) * (uint32_t)sizeof(YT) + cb;
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc0[ts]), ydesc, (int)off, 0, 0);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc1[ts]), ydesc, (int)(off + 16), 0, 0);
         }
@@ -591,7 +622,9 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   __shared__ __attribute__((aligned(128))) uint8_t ast1[kAStage];
   __shared__ __attribute__((aligned(128))) uint8_t ast2[kAStage];
   __shared__ __attribute__((aligned(128))) uint8_t ast3[kAStage];
-  __shared__ __attribute__((aligned(128))) uint8_t ast4[kAStage];
+  // the last slot stages the epilogue: phase-1 h codes, or a phase-2 bf16 output block
+  __shared__ __attribute__((aligned(128)))
+  uint8_t ast4[PHASE == 2 && sizeof(YT) == 2 ? kMT / 2 * 512 : kAStage];
   __shared__ __attribute__((aligned(16))) uint8_t junk[kJunk];
   __shared__ int tok_s[kMT];
   constexpr int kWscRow = kMaxChunks + kMaxRing;
@@ -646,7 +679,7 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   }
   __syncthreads();
 
-  const FfnLds sh{{ast0, ast1, ast2, ast3, ast4}, junk, tok_s, &wsc[0][0], red};
+  const FfnLds sh{{ast0, ast1, ast2, ast3, ast4}, junk, tok_s, &wsc[0][0], red, ast4};
   // Ring depth 4: three chunks (96 KB of weights per CU) in flight cover the loaded HBM
   // latency, the accumulators of 10 16-row tiles still fit beside the ring, and K
   // chunk counts of the usual shapes (56, 16) divide by it, so no block ends in steps
