@@ -112,46 +112,85 @@ def cpu_baseline(cfg, n_tokens: int):
             "seconds": dt}
 
 
-def decode_step(layer, steps: int, warmup: int):
-    """The T=128 decode step of the same layer (same weights): weight-streaming bound, so
-    it is reported as the grouped FFN's algorithmic HBM bytes per second."""
+def measure(layer, cfg, xs, steps: int, warmup: int):
+    """Times ``steps`` forward steps of ``layer`` (bias update included) cycling over the
+    device batches ``xs``; stage spans from HIP events on the launch stream."""
     import numpy as np
     import torch
 
-    import synth
     from deepseekmoe_routing_fp8_amd import MoELayer
-    cfg = synth.PRESETS["v3_decode"]
-    x = torch.from_numpy(synth.hidden_states(cfg)).to(
-        torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32).cuda()
-    for _ in range(warmup):
-        layer.forward(x)
+    for i in range(warmup):
+        layer.forward(xs[i % len(xs)])
     torch.cuda.synchronize()
     nst = len(MoELayer.STAGES)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
-    log(f"[bench] decode: timing {steps} steps of T={cfg.tokens}")
+    loads = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        layer.forward(x, events=evs[i])
+        layer.forward(xs[i % len(xs)], events=evs[i])
+        if cfg.skewed:
+            loads.append(layer.counts.clone())
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nst)]
                          for i in range(steps)])
     st = {s: float(stage_ms[:, j].mean()) for j, s in enumerate(MoELayer.STAGES)}
     ab = ffn_algorithmic_bytes(cfg, layer.counts.cpu().numpy())
+    H, I, T = cfg.hidden_size, cfg.moe_intermediate_size, cfg.tokens
+    k, S = cfg.num_experts_per_tok, cfg.num_shared_experts
+    ms = wall * 1e3 / steps
     ffn_ms = st["ffn_gate_up"] + st["ffn_down"]
+    tflops = 6.0 * H * I * T * (k + S) / (ms * 1e-3) / 1e12
     gbs = (ab["gate_up"] + ab["down"]) / (ffn_ms * 1e-3) / 1e9
-    gu = ab["gate_up"] / (st["ffn_gate_up"] * 1e-3) / 1e9
-    dn = ab["down"] / (st["ffn_down"] * 1e-3) / 1e9
-    return {"workload": cfg.name, "tokens": cfg.tokens, "steps": steps,
-            "ms_per_step": round(wall * 1e3 / steps, 4),
-            "tokens_per_s": round(cfg.tokens * steps / wall, 1),
-            "experts_touched": ab["experts"],
-            "ffn_algorithmic_bytes": ab["gate_up"] + ab["down"],
-            "ffn_ms": round(ffn_ms, 4),
-            "ffn_gbs": round(gbs, 1), "ffn_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-            "gate_up_gbs": round(gu, 1), "down_gbs": round(dn, 1),
-            "stage_ms": {s: round(v, 4) for s, v in st.items()}}
+    out = {"workload": cfg.name, "tokens": T, "steps": steps,
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(T * steps / wall, 1),
+           "tflops_fp8": round(tflops, 1), "frac_fp8_mfma_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+           "experts_touched": ab["experts"], "ffn_algorithmic_bytes": ab["gate_up"] + ab["down"],
+           "ffn_ms": round(ffn_ms, 4), "ffn_gbs": round(gbs, 1),
+           "ffn_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+           "gate_up_gbs": round(ab["gate_up"] / (st["ffn_gate_up"] * 1e-3) / 1e9, 1),
+           "down_gbs": round(ab["down"] / (st["ffn_down"] * 1e-3) / 1e9, 1),
+           "stage_ms": {s: round(v, 4) for s, v in st.items()}}
+    if loads:
+        c = torch.stack(loads).float()
+        ratio = (c.max(dim=1).values / c.mean(dim=1)).cpu().numpy()
+        out["max_over_mean_load_per_step"] = [round(float(v), 3) for v in ratio]
+    return out
+
+
+def device_batches(cfg, n: int):
+    import torch
+
+    import synth
+    dt = torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32
+    if n == 1:
+        return [torch.from_numpy(synth.hidden_states(cfg)).to(dt).cuda()]
+    return [torch.from_numpy(synth.hidden_states(cfg, step=i)).to(dt).cuda() for i in range(n)]
+
+
+def other_configs(layer, warmup: int, decode_steps: int):
+    """The other workloads of the same method, outside the headline number: the T=128
+    decode step and the skewed T=16384 step on the same V3 layer, and the reduced layer
+    (its own weights)."""
+    import synth
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    res = {}
+    if decode_steps > 0:
+        cfg = synth.PRESETS["v3_decode"]
+        log(f"[bench] decode: T={cfg.tokens}, {decode_steps} steps")
+        res["decode"] = measure(layer, cfg, device_batches(cfg, 1), decode_steps, warmup)
+        cfg = synth.PRESETS["v3_skewed"]
+        log(f"[bench] skewed: T={cfg.tokens}, fresh clustered batches (seeds 0..2), bias from 0, "
+            "updated each step")
+        layer.bias.zero_()
+        res["skewed"] = measure(layer, cfg, device_batches(cfg, 3), 12, 3)
+        cfg = synth.PRESETS["reduced"]
+        log("[bench] reduced layer: weights on the device")
+        small = MoELayer(cfg)
+        small.load_from_synth()
+        res["reduced"] = measure(small, cfg, device_batches(cfg, 1), 30, warmup)
+    return res
 
 
 def main():
@@ -163,7 +202,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=50,
-                    help="steps of the T=128 decode workload timed after the main one (0: skip)")
+                    help="steps of the T=128 decode workload timed after the main one; the "
+                         "skewed and reduced workloads follow it (0: skip all three)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -255,8 +295,8 @@ def main():
         "event_ms_per_step": round(float(step_ms.mean()), 4),
         "max_over_mean_load": round(float(counts.max() / counts.mean()), 3),
     }
-    if args.decode_steps > 0 and args.workload != "v3_decode":
-        res["decode"] = decode_step(layer, args.decode_steps, args.warmup)
+    if args.workload == "v3_prefill":
+        res.update(other_configs(layer, args.warmup, args.decode_steps))
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
