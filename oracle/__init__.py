@@ -29,7 +29,9 @@ from .moe import (  # noqa: F401
     layer_forward,
     permute,
     quantize_1x128,
+    quantize_1x128_pow2,
     quantize_128x128,
+    quantize_128x128_pow2,
     route,
     silu,
 )

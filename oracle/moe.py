@@ -54,6 +54,51 @@ def quantize_128x128(w: np.ndarray):
     return encode(q).reshape(N, K), s
 
 
+# ----------------------------------------------------------------------------------------
+# Power-of-two scale variant (opt-in; the pages call the fine-grained scheme close to
+# micro-scaling, zhihu commentary training part and 2kiu.com digest section 4.3, without
+# fixing this variant). Reading: the same 1x128 / 128x128 groups, each with the smallest
+# power of two s such that amax / s <= 448 (s = 1 for an all-zero group; s >= 2^-126),
+# codes = E4M3_RNE_SAT(x / s), where the division by a power of two is exact.
+# ----------------------------------------------------------------------------------------
+def _pow2_scale_from_amax(amax: np.ndarray) -> np.ndarray:
+    amax = np.asarray(amax, dtype=np.float64)
+    out = np.ones(amax.shape, dtype=np.float32)
+    for i in np.ndindex(amax.shape):
+        a = float(amax[i])
+        if a == 0.0:
+            continue
+        k = int(np.ceil(np.log2(a / E4M3_MAX)))
+        while E4M3_MAX * 2.0 ** (k - 1) >= a:   # smallest k with 448 * 2^k >= amax
+            k -= 1
+        while E4M3_MAX * 2.0 ** k < a:
+            k += 1
+        out[i] = np.float32(2.0 ** max(k, -126))
+    return out
+
+
+def quantize_1x128_pow2(x: np.ndarray):
+    """x [R, C] float32 -> (codes [R, C] u8, power-of-two scales [R, C/128] f32)."""
+    x = np.asarray(x, dtype=np.float32)
+    R, C = x.shape
+    assert C % TILE == 0
+    xt = x.reshape(R, C // TILE, TILE)
+    s = _pow2_scale_from_amax(np.max(np.abs(xt), axis=2))
+    q = (xt.astype(np.float64) / s[:, :, None]).astype(np.float32)
+    return encode(q).reshape(R, C), s
+
+
+def quantize_128x128_pow2(w: np.ndarray):
+    """w [N, K] float32 -> (codes [N, K] u8, power-of-two scales [N/128, K/128] f32)."""
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert N % TILE == 0 and K % TILE == 0
+    wb = w.reshape(N // TILE, TILE, K // TILE, TILE)
+    s = _pow2_scale_from_amax(np.max(np.abs(wb), axis=(1, 3)))
+    q = (wb.astype(np.float64) / s[:, None, :, None]).astype(np.float32)
+    return encode(q).reshape(N, K), s
+
+
 def dequant_1x128(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """DQ of a 1x128-tiled operand: value(code) * scale, float64 (exact)."""
     v = decode(codes)
@@ -171,13 +216,14 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(aq, a_s, w1q, w1s, w3q, w3s, w2q, w2s):
-    """One SwiGLU expert on M rows. Returns (y [M,H] f64, hq, hs, h f32)."""
+def expert_ffn(aq, a_s, w1q, w1s, w3q, w3s, w2q, w2s, pow2: bool = False):
+    """One SwiGLU expert on M rows. Returns (y [M,H] f64, hq, hs, h f32).
+    ``pow2``: h is re-quantised with power-of-two scales (the opt-in variant)."""
     a = dequant_1x128(aq, a_s)
     g = a @ dequant_128x128(w1q, w1s).T
     u = a @ dequant_128x128(w3q, w3s).T
     h = (silu(g) * u).astype(np.float32)
-    hq, hs = quantize_1x128(h)
+    hq, hs = quantize_1x128_pow2(h) if pow2 else quantize_1x128(h)
     y = dequant_1x128(hq, hs) @ dequant_128x128(w2q, w2s).T
     return y, hq, hs, h
 
@@ -224,17 +270,18 @@ ExpertGetter = Callable[[int], tuple]  # e -> (w1q, w1s, w3q, w3s, w2q, w2s)
 
 def layer_forward(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray, cfg,
                   routed: ExpertGetter, shared: ExpertGetter,
-                  force_idx: Optional[np.ndarray] = None) -> dict:
+                  force_idx: Optional[np.ndarray] = None, pow2: bool = False) -> dict:
     """Full MoE-layer forward for the tokens of x (float32 values).
 
     ``cfg`` supplies num_experts, num_shared_experts, num_experts_per_tok, n_group,
     topk_group, group_score_topn and routed_scaling_factor. ``routed``/``shared`` return
     the E4M3 codes and scales of one expert. Returns every intermediate and ``out``
-    (float64) before the bf16 rounding of the output.
+    (float64) before the bf16 rounding of the output. ``pow2`` selects the power-of-two
+    scale variant for x and h (the experts' codes come quantised already).
     """
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
-    xq, xs = quantize_1x128(x)
+    xq, xs = quantize_1x128_pow2(x) if pow2 else quantize_1x128(x)
     r = route(x, w_router, bias, cfg.num_experts_per_tok, cfg.n_group, cfg.topk_group,
               cfg.group_score_topn, cfg.routed_scaling_factor, force_idx=force_idx)
     offsets, row_token, row_of = permute(r["idx"], cfg.num_experts)
@@ -245,11 +292,11 @@ def layer_forward(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray, cfg,
         if hi == lo:
             continue
         toks = row_token[lo:hi]
-        y, _, _, _ = expert_ffn(xq[toks], xs[toks], *routed(e))
+        y, _, _, _ = expert_ffn(xq[toks], xs[toks], *routed(e), pow2=pow2)
         y_rows[lo:hi] = y
     y_shared = []
     for s in range(cfg.num_shared_experts):
-        y, _, _, _ = expert_ffn(xq, xs, *shared(s))
+        y, _, _, _ = expert_ffn(xq, xs, *shared(s), pow2=pow2)
         y_shared.append(y)
     out = combine(y_rows, row_of, r["gate"], y_shared)
     return {"xq": xq, "xs": xs, "route": r, "offsets": offsets, "row_token": row_token,
