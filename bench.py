@@ -190,6 +190,15 @@ def other_configs(layer, warmup: int, decode_steps: int):
         small = MoELayer(cfg)
         small.load_from_synth()
         res["reduced"] = measure(small, cfg, device_batches(cfg, 1), 30, warmup)
+        del small
+        # the opt-in power-of-two scale variant on the headline workload (its own weights)
+        cfg = synth.PRESETS["v3_prefill"]
+        log("[bench] power-of-two scale variant: weights on the device")
+        p2 = MoELayer(cfg, scale_mode=1)
+        p2.load_from_synth()
+        res["pow2_scales"] = measure(p2, cfg, device_batches(cfg, 1), 30, warmup)
+        res["pow2_scales"]["note"] = ("opt-in variant (scale_mode 1): power-of-two 1x128 / 128x128 "
+                                      "scales applied by the MFMA, FP32 accumulation across K")
     return res
 
 

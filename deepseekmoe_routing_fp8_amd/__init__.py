@@ -25,7 +25,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 MOE_F32, MOE_BF16 = 0, 1
 
 ENTRY_POINTS = (
-    "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_pack_fp8_weights",
+    "moe_status_string", "moe_quantize_1x128", "moe_quantize_128x128", "moe_quantize_1x128_pow2",
+    "moe_quantize_128x128_pow2", "moe_pack_fp8_weights",
     "moe_pack_router_weights", "moe_router_weights_elems", "moe_route", "moe_route_workspace_bytes",
     "moe_permute", "moe_permute_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8",
     "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
@@ -40,15 +41,19 @@ class moe_config(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("n_group", ctypes.c_int32),
         ("topk_group", ctypes.c_int32), ("group_topn", ctypes.c_int32),
         ("routed_scaling", ctypes.c_float), ("bias_gamma", ctypes.c_float),
+        ("scale_mode", ctypes.c_int32),
     ]
 
+SCALE_FP32, SCALE_POW2 = 0, 1
 
-def make_config(cfg) -> moe_config:
-    """moe_config from any object with the synth.MoEConfig field names."""
+
+def make_config(cfg, scale_mode: int = SCALE_FP32) -> moe_config:
+    """moe_config from any object with the synth.MoEConfig field names. ``scale_mode``:
+    SCALE_FP32 (the pages' FP32 group scales) or SCALE_POW2 (the opt-in variant)."""
     return moe_config(cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts,
                       cfg.num_shared_experts, cfg.num_experts_per_tok, cfg.n_group,
                       cfg.topk_group, cfg.group_score_topn, cfg.routed_scaling_factor,
-                      cfg.expert_bias_update_rate)
+                      cfg.expert_bias_update_rate, scale_mode)
 
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -57,6 +62,8 @@ _sig = {
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_quantize_1x128": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "moe_quantize_128x128": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "moe_quantize_1x128_pow2": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "moe_quantize_128x128_pow2": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "moe_pack_fp8_weights": ([_P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
     "moe_pack_router_weights": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "moe_router_weights_elems": ([_I64, _I64], _SZ),
@@ -116,22 +123,24 @@ def _xdtype(x: torch.Tensor) -> int:
 
 
 def moe_quantize_1x128(x: torch.Tensor, q: torch.Tensor = None, scales: torch.Tensor = None,
-                       stream=None):
-    """1x128 E4M3 quantisation of x [rows, cols] -> (q uint8 [rows, cols], scales f32)."""
+                       stream=None, pow2: bool = False):
+    """1x128 E4M3 quantisation of x [rows, cols] -> (q uint8 [rows, cols], scales f32).
+    ``pow2``: power-of-two scales (moe_quantize_1x128_pow2)."""
     rows, cols = x.shape
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
     if scales is None:
         scales = torch.empty((rows, max(cols // 128, 0)), dtype=torch.float32, device=x.device)
-    _check(_lib.moe_quantize_1x128(_dev(x, x.dtype, "x"), _xdtype(x), rows, cols,
-                                   _dev(q, torch.uint8, "q", (rows, cols)),
-                                   _dev(scales, torch.float32, "scales"), _stream(stream)),
-           "moe_quantize_1x128")
+    name = "moe_quantize_1x128_pow2" if pow2 else "moe_quantize_1x128"
+    _check(getattr(_lib, name)(_dev(x, x.dtype, "x"), _xdtype(x), rows, cols,
+                               _dev(q, torch.uint8, "q", (rows, cols)),
+                               _dev(scales, torch.float32, "scales"), _stream(stream)), name)
     return q, scales
 
 
 def moe_quantize_128x128(w: torch.Tensor, q: torch.Tensor = None, scales: torch.Tensor = None,
-                         stream=None):
-    """128x128-block E4M3 quantisation of w [mats, rows, cols] (or [rows, cols]) float32."""
+                         stream=None, pow2: bool = False):
+    """128x128-block E4M3 quantisation of w [mats, rows, cols] (or [rows, cols]) float32.
+    ``pow2``: power-of-two scales (moe_quantize_128x128_pow2)."""
     squeeze = w.dim() == 2
     w3 = w.unsqueeze(0) if squeeze else w
     mats, rows, cols = w3.shape
@@ -140,10 +149,10 @@ def moe_quantize_128x128(w: torch.Tensor, q: torch.Tensor = None, scales: torch.
     if scales is None:
         sshape = (rows // 128, cols // 128) if squeeze else (mats, rows // 128, cols // 128)
         scales = torch.empty(sshape, dtype=torch.float32, device=w.device)
-    _check(_lib.moe_quantize_128x128(_dev(w, torch.float32, "w"), mats, rows, cols,
-                                     _dev(q, torch.uint8, "q", w.shape),
-                                     _dev(scales, torch.float32, "scales"), _stream(stream)),
-           "moe_quantize_128x128")
+    name = "moe_quantize_128x128_pow2" if pow2 else "moe_quantize_128x128"
+    _check(getattr(_lib, name)(_dev(w, torch.float32, "w"), mats, rows, cols,
+                               _dev(q, torch.uint8, "q", w.shape),
+                               _dev(scales, torch.float32, "scales"), _stream(stream)), name)
     return q, scales
 
 

@@ -35,6 +35,7 @@ inline moe_status check_config(const moe_config* c) {
   if (c->inter <= 0 || c->inter % kTile) return MOE_ERR_SHAPE;
   if (c->n_routed < 1 || c->n_routed > kMaxRouted) return MOE_ERR_SHAPE;
   if (c->n_shared < 0 || c->n_shared > kMaxShared) return MOE_ERR_SHAPE;
+  if (c->scale_mode != 0 && c->scale_mode != 1) return MOE_ERR_UNSUPPORTED;
   if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_routed) return MOE_ERR_SHAPE;
   if (c->n_group < 1 || c->n_group > kMaxGroups || c->n_routed % c->n_group) return MOE_ERR_SHAPE;
   if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_ERR_SHAPE;
@@ -95,6 +96,26 @@ __device__ __forceinline__ float group_scale(float amax) {
   const float s = __fdiv_rn(amax, kE4M3Max);
   return s == 0.0f ? 1.0f : s;
 }
+
+// Power-of-two scale of a group: the smallest 2^k with amax / 2^k <= 448, k >= -126; 1 for
+// amax == 0. With amax = m * 2^E (m in [1, 2)) and 448 = 1.75 * 2^8, k = E - 8, plus one
+// when m > 1.75 (fraction bits above 0x600000).
+__device__ __forceinline__ float group_scale_pow2(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xFFu) - 127;
+  int k = E - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  k = max(k, -126);
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+// 1 / s for a power-of-two s in [2^-126, 2^126] (exact).
+__device__ __forceinline__ float inv_pow2(float s) {
+  return __uint_as_float((254u - ((__float_as_uint(s) >> 23) & 0xFFu)) << 23);
+}
+
+// E8M0 exponent byte of a power-of-two float (the MFMA block-scale operand: 2^(e - 127)).
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
 
 template <int W>
 __device__ __forceinline__ float group_max(float v) {

@@ -52,6 +52,15 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
 }
 
+// Power-of-two scale variant: the MFMA applies the E8M0 block scales itself (A: the
+// weight block's, uniform over the fragment; B: lane l carries the scale of column
+// l % 16, the token, for its K block l / 16 - every block of the chunk has the same) and
+// accumulates into c in FP32 across K, so no partial sum needs promoting.
+__device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& a, const v8i& b, const v4f& c, int ea,
+                                               int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
 __device__ __forceinline__ v8i join(const uint4& lo, const uint4& hi) {
   v8i r;
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
@@ -289,7 +298,7 @@ __device__ __forceinline__ v8i buf_wfrag(__amdgpu_buffer_rsrc_t d, int voff) {
 // conditionally and every wait is the same immediate; chunks past the last one read
 // zero weights (and carry weight scales 0), adding exact zeros.
 // ------------------------------------------------------------------------------------
-template <int PHASE, typename YT, int NT, int RING>
+template <int PHASE, typename YT, int NT, int RING, bool MX>
 __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int nb0, int nbn,
                                          int wave, int lane, const FfnLds& sh) {
   static_assert(RING >= 3 && RING <= kMaxRing, "ring depth");
@@ -392,6 +401,20 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
       const v4i y = *reinterpret_cast<lds_v4i*>(bh + ts * 16 * kTile);
       return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
     };
+    if constexpr (MX) {
+      // each tile's operands are read and multiplied into its accumulators in turn (the
+      // other wave on the SIMD covers the LDS latency)
+      const int e0 = e8m0_of(s0), e1 = e8m0_of(s1);
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const v8i bq = frag(ts);
+        const int ea = e8m0_of(*reinterpret_cast<lds_f32*>(bs + ts * 64));
+        acc0[ts] = mfma_fp8_scaled(A0, bq, acc0[ts], e0, ea);
+        acc1[ts] = mfma_fp8_scaled(A1, bq, acc1[ts], e1, ea);
+        __builtin_amdgcn_sched_barrier(0);   // one tile's operands at a time
+      }
+      return;
+    }
     // operands of tile t+2 are read while tile t+1 multiplies and tile t is promoted
     v8i bq[3];
     float sa[3];
@@ -528,10 +551,10 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
           float m = red[0][r];
 #pragma unroll
           for (int w = 1; w < kFWaves; ++w) m = fmaxf(m, red[w][r]);
-          const float s = group_scale(m);
+          const float s = MX ? group_scale_pow2(m) : group_scale(m);
           // h / s as h * (1/s): within an ulp of the quotient, which the encoder rounds
-          // and clamps to +-448
-          const float inv = __builtin_amdgcn_rcpf(s);
+          // and clamps to +-448 (exact for a power-of-two s)
+          const float inv = MX ? inv_pow2(s) : __builtin_amdgcn_rcpf(s);
           const uint32_t packed = e4m3_pack4(acc0[ts][0] * inv, acc0[ts][1] * inv,
                                              acc0[ts][2] * inv, acc0[ts][3] * inv);
           *reinterpret_cast<uint32_t*>(stage + r * kTile + ((((col >> 4) ^ (r & 7))) << 4) + (col & 15)) =
@@ -616,7 +639,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
 // Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD,
 // so the tile's activation rows are fetched into that XCD's L2 once.
 // ------------------------------------------------------------------------------------
-template <int PHASE, typename YT>
+template <int PHASE, typename YT, bool MX>
 __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   __shared__ __attribute__((aligned(128))) uint8_t ast0[kAStage];
   __shared__ __attribute__((aligned(128))) uint8_t ast1[kAStage];
@@ -687,12 +710,12 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   // V3 prefill gate/up: its 60 padded steps per block cost more than the depth gained.)
   constexpr int R = 4;
   switch ((tl.mlen + 15) >> 4) {
-    case 1: case 2: ffn_main<PHASE, YT, 2, R>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 3: case 4: ffn_main<PHASE, YT, 4, R>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 5: case 6: ffn_main<PHASE, YT, 6, R>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 7: case 8: ffn_main<PHASE, YT, 8, R>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 9: ffn_main<PHASE, YT, 9, R>(a, tl, nb0, nbn, wave, lane, sh); break;
-    default: ffn_main<PHASE, YT, 10, R>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 1: case 2: ffn_main<PHASE, YT, 2, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 3: case 4: ffn_main<PHASE, YT, 4, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 5: case 6: ffn_main<PHASE, YT, 6, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 7: case 8: ffn_main<PHASE, YT, 8, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 9: ffn_main<PHASE, YT, 9, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
+    default: ffn_main<PHASE, YT, 10, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
   }
 }
 
@@ -799,8 +822,12 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
   FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, f.xsp, n_tokens,
              row_token, w1, w1s, w3, w3s, H, I, I / kTile, kNbPerWg1, f.hq, f.hs, nullptr};
   const unsigned nwg = (unsigned)((a1.n_nb + a1.nb_per - 1) / a1.nb_per);
-  hipLaunchKernelGGL((ffn_kernel<1, uint16_t>), dim3(f.grid_tiles * nwg), dim3(kFThreads), 0, s,
-                     a1);
+  if (cfg->scale_mode == 1)
+    hipLaunchKernelGGL((ffn_kernel<1, uint16_t, true>), dim3(f.grid_tiles * nwg), dim3(kFThreads), 0,
+                       s, a1);
+  else
+    hipLaunchKernelGGL((ffn_kernel<1, uint16_t, false>), dim3(f.grid_tiles * nwg), dim3(kFThreads), 0,
+                       s, a1);
   return launch_status();
 }
 
@@ -819,10 +846,15 @@ moe_status ffn_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows, co
              nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256, kNbPerWg2, nullptr,
              nullptr, y};
   const dim3 grid(f.grid_tiles * (unsigned)((a2.n_nb + a2.nb_per - 1) / a2.nb_per));
-  if (yt == MOE_BF16)
-    hipLaunchKernelGGL((ffn_kernel<2, uint16_t>), grid, dim3(kFThreads), 0, s, a2);
+  const bool mx = cfg->scale_mode == 1;
+  if (yt == MOE_BF16 && mx)
+    hipLaunchKernelGGL((ffn_kernel<2, uint16_t, true>), grid, dim3(kFThreads), 0, s, a2);
+  else if (yt == MOE_BF16)
+    hipLaunchKernelGGL((ffn_kernel<2, uint16_t, false>), grid, dim3(kFThreads), 0, s, a2);
+  else if (mx)
+    hipLaunchKernelGGL((ffn_kernel<2, float, true>), grid, dim3(kFThreads), 0, s, a2);
   else
-    hipLaunchKernelGGL((ffn_kernel<2, float>), grid, dim3(kFThreads), 0, s, a2);
+    hipLaunchKernelGGL((ffn_kernel<2, float, false>), grid, dim3(kFThreads), 0, s, a2);
   return launch_status();
 }
 

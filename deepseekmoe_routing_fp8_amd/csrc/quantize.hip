@@ -13,7 +13,8 @@ namespace {
 constexpr int kQPer = 4;
 constexpr int kQTiles = 16 * kQPer;
 
-template <typename T>
+// POW2: power-of-two group scales (scale_mode 1), for which x / s is an exact product.
+template <typename T, bool POW2>
 __global__ __launch_bounds__(256) void quantize_1x128_kernel(const T* __restrict__ x,
                                                              int64_t n_tiles,
                                                              uint8_t* __restrict__ q,
@@ -52,10 +53,16 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(const T* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
     amax = group_max<16>(amax);
-    const float s = group_scale(amax);
+    const float s = POW2 ? group_scale_pow2(amax) : group_scale(amax);
     float qv[8];
+    if constexpr (POW2) {
+      const float inv = inv_pow2(s);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] = __fdiv_rn(v[u][i], s);
+      for (int i = 0; i < 8; ++i) qv[i] = v[u][i] * inv;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[i] = __fdiv_rn(v[u][i], s);
+    }
     const uint32_t lo = e4m3_pack4(qv[0], qv[1], qv[2], qv[3]);
     const uint32_t hi = e4m3_pack4(qv[4], qv[5], qv[6], qv[7]);
     if (tile < n_tiles) {
@@ -67,6 +74,7 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(const T* __restrict
 
 // One 256-thread block per 128x128 block. Thread t covers rows (t/32) + 8*i, i < 16,
 // and the 4 columns 4*(t%32)..+3 of each: 64 values kept in registers.
+template <bool POW2>
 __global__ __launch_bounds__(256) void quantize_128x128_kernel(const float* __restrict__ w,
                                                                int64_t rows, int64_t cols,
                                                                uint8_t* __restrict__ q,
@@ -93,21 +101,25 @@ __global__ __launch_bounds__(256) void quantize_128x128_kernel(const float* __re
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = group_scale(amax);
+  const float s = POW2 ? group_scale_pow2(amax) : group_scale(amax);
+  const float inv = POW2 ? inv_pow2(s) : 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + rsub + 8 * i;
-    const uint32_t packed = e4m3_pack4(__fdiv_rn(v[i].x, s), __fdiv_rn(v[i].y, s),
-                                       __fdiv_rn(v[i].z, s), __fdiv_rn(v[i].w, s));
+    const uint32_t packed =
+        POW2 ? e4m3_pack4(v[i].x * inv, v[i].y * inv, v[i].z * inv, v[i].w * inv)
+             : e4m3_pack4(__fdiv_rn(v[i].x, s), __fdiv_rn(v[i].y, s), __fdiv_rn(v[i].z, s),
+                          __fdiv_rn(v[i].w, s));
     *reinterpret_cast<uint32_t*>(dst + r * cols + c0 + col) = packed;
   }
   if (t == 0) scales[blk] = s;
 }
 
 // Fragment-packed weight layout read by the grouped FFN: for a [rows, cols] matrix,
-// fragment (n16, kc) = rows 16*n16..+15 x cols 128*kc..+127 occupies 2 KB at
+// fragment (n16, kc) = 16 rows x cols 128*kc..+127 occupies 2 KB at
 // ((n16 * cols/128) + kc) * 2048, as two 1 KB halves; byte b of lane l in half h is
-// W[16*n16 + l % 16][128*kc + 64*h + 16*(l / 16) + b]. One thread moves 16 bytes.
+// W[rho(n16, l % 16)][128*kc + 64*h + 16*(l / 16) + b] with the rows of each pair of
+// fragments interleaved by 4 (rho below). One thread moves 16 bytes.
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint8_t* __restrict__ q, int64_t mats,
                                                        int64_t rows, int64_t cols,
                                                        uint8_t* __restrict__ out) {
@@ -147,8 +159,9 @@ extern "C" moe_status moe_pack_fp8_weights(const uint8_t* q, int64_t mats, int64
   return launch_status();
 }
 
-extern "C" moe_status moe_quantize_1x128(const void* x, moe_dtype xt, int64_t rows, int64_t cols,
-                                         uint8_t* q, float* scales, void* stream) {
+template <bool POW2>
+moe_status quantize_1x128_launch(const void* x, moe_dtype xt, int64_t rows, int64_t cols,
+                                 uint8_t* q, float* scales, void* stream) {
   if (rows < 0 || cols <= 0 || cols % kTile) return MOE_ERR_SHAPE;
   if (xt != MOE_F32 && xt != MOE_BF16) return MOE_ERR_DTYPE;
   const int64_t tiles = rows * (cols / kTile);
@@ -157,22 +170,45 @@ extern "C" moe_status moe_quantize_1x128(const void* x, moe_dtype xt, int64_t ro
   const int64_t blocks = (tiles + kQTiles - 1) / kQTiles;
   if (blocks > 0x7fffffff) return MOE_ERR_SHAPE;
   if (xt == MOE_BF16)
-    hipLaunchKernelGGL(quantize_1x128_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, POW2>), dim3((unsigned)blocks), dim3(256), 0,
                        as_stream(stream), static_cast<const uint16_t*>(x), tiles, q, scales);
   else
-    hipLaunchKernelGGL(quantize_1x128_kernel<float>, dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((quantize_1x128_kernel<float, POW2>), dim3((unsigned)blocks), dim3(256), 0,
                        as_stream(stream), static_cast<const float*>(x), tiles, q, scales);
   return launch_status();
 }
 
-extern "C" moe_status moe_quantize_128x128(const float* w, int64_t mats, int64_t rows, int64_t cols,
-                                           uint8_t* q, float* scales, void* stream) {
+template <bool POW2>
+moe_status quantize_128x128_launch(const float* w, int64_t mats, int64_t rows, int64_t cols,
+                                   uint8_t* q, float* scales, void* stream) {
   if (mats < 0 || rows <= 0 || cols <= 0 || rows % kTile || cols % kTile) return MOE_ERR_SHAPE;
   const int64_t blocks = mats * (rows / kTile) * (cols / kTile);
   if (blocks == 0) return MOE_OK;
   if (!w || !q || !scales) return MOE_ERR_NULL;
   if (blocks > 0x7fffffff) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(quantize_128x128_kernel, dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL(quantize_128x128_kernel<POW2>, dim3((unsigned)blocks), dim3(256), 0,
                      as_stream(stream), w, rows, cols, q, scales);
   return launch_status();
+}
+
+extern "C" moe_status moe_quantize_1x128(const void* x, moe_dtype xt, int64_t rows, int64_t cols,
+                                         uint8_t* q, float* scales, void* stream) {
+  return quantize_1x128_launch<false>(x, xt, rows, cols, q, scales, stream);
+}
+
+extern "C" moe_status moe_quantize_1x128_pow2(const void* x, moe_dtype xt, int64_t rows,
+                                              int64_t cols, uint8_t* q, float* scales,
+                                              void* stream) {
+  return quantize_1x128_launch<true>(x, xt, rows, cols, q, scales, stream);
+}
+
+extern "C" moe_status moe_quantize_128x128(const float* w, int64_t mats, int64_t rows, int64_t cols,
+                                           uint8_t* q, float* scales, void* stream) {
+  return quantize_128x128_launch<false>(w, mats, rows, cols, q, scales, stream);
+}
+
+extern "C" moe_status moe_quantize_128x128_pow2(const float* w, int64_t mats, int64_t rows,
+                                                int64_t cols, uint8_t* q, float* scales,
+                                                void* stream) {
+  return quantize_128x128_launch<true>(w, mats, rows, cols, q, scales, stream);
 }

@@ -30,9 +30,12 @@ class MoELayer:
     ``load_from_synth``) once, then ``forward(x)`` per step.
     """
 
-    def __init__(self, cfg, device="cuda", y_dtype=torch.bfloat16):
+    def __init__(self, cfg, device="cuda", y_dtype=torch.bfloat16, scale_mode: int = 0):
+        """``scale_mode`` 0: the pages' FP32 group scales; 1: the power-of-two variant
+        (weights and activations quantised with power-of-two scales, applied by the MFMA)."""
         self.cfg = cfg
-        self.c = make_config(cfg)
+        self.scale_mode = scale_mode
+        self.c = make_config(cfg, scale_mode)
         self.dev = torch.device(device)
         self.y_dtype = y_dtype
         H, I, E, S = cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts, cfg.num_shared_experts
@@ -52,7 +55,7 @@ class MoELayer:
     # -- weights -------------------------------------------------------------------
     def _quant_into(self, w: np.ndarray, q: torch.Tensor, s: torch.Tensor):
         t = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(self.dev)
-        rowmajor, _ = moe_quantize_128x128(t, scales=s)
+        rowmajor, _ = moe_quantize_128x128(t, scales=s, pow2=self.scale_mode == 1)
         moe_pack_fp8_weights(rowmajor, q)
 
     @staticmethod
@@ -136,7 +139,7 @@ class MoELayer:
         EA, rows = N + S, T * (k + S)
         mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
         mark(0)
-        moe_quantize_1x128(x, self.xq, self.xs)
+        moe_quantize_1x128(x, self.xq, self.xs, pow2=self.scale_mode == 1)
         mark(1)
         moe_route(c, x, self.w_router, self.bias, self.scores, self.topk_idx, self.topk_gate,
                   self.counts, ws=self.route_ws)

@@ -67,6 +67,11 @@ typedef struct moe_config {
   int32_t group_topn;      /* affinities summed into a group score, 1..N_r/G          */
   float routed_scaling;    /* rho: gates of a token sum to rho ([guide] routed_scaling_factor) */
   float bias_gamma;        /* gamma: bias step ([guide] expert_bias_update_rate)      */
+  int32_t scale_mode;      /* grouped FFN scales: 0 = FP32 group scales, partial sums
+                              promoted in FP32 per 128-wide K chunk (the pages' scheme);
+                              1 = power-of-two group scales (moe_quantize_*_pow2), applied
+                              exactly by the MFMA's block-scale operands with FP32
+                              accumulation across K (opt-in variant)                  */
 } moe_config;
 
 /* Human-readable text for a status (static storage). */
@@ -97,6 +102,19 @@ moe_status moe_quantize_1x128(const void* x, moe_dtype xt, int64_t rows, int64_t
  */
 moe_status moe_quantize_128x128(const float* w, int64_t mats, int64_t rows, int64_t cols,
                                 uint8_t* q, float* scales, void* stream);
+
+/*
+ * moe_quantize_1x128_pow2, moe_quantize_128x128_pow2 — the same groups with power-of-two
+ * scales, for scale_mode 1 (an opt-in variant; the pages call the fine-grained scheme
+ * close to micro-scaling, [zhihu] training part, [digest] section 4.3). A group's scale
+ * is the smallest power of two s with amax / s <= 448 (s = 1 for an all-zero group,
+ * s >= 2^-126); codes = E4M3 round-to-nearest-even of x / s (exact division).
+ * Arguments, layouts and errors as moe_quantize_1x128 / moe_quantize_128x128.
+ */
+moe_status moe_quantize_1x128_pow2(const void* x, moe_dtype xt, int64_t rows, int64_t cols,
+                                   uint8_t* q, float* scales, void* stream);
+moe_status moe_quantize_128x128_pow2(const float* w, int64_t mats, int64_t rows, int64_t cols,
+                                     uint8_t* q, float* scales, void* stream);
 
 /*
  * moe_pack_fp8_weights — re-lays E4M3 weight codes for the grouped FFN (a byte

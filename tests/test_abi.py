@@ -51,7 +51,7 @@ def test_status_strings():
 
 def _cfg(m, **kw):
     base = dict(hidden=256, inter=128, n_routed=16, n_shared=1, top_k=4, n_group=1, topk_group=1,
-                group_topn=2, routed_scaling=2.5, bias_gamma=0.001)
+                group_topn=2, routed_scaling=2.5, bias_gamma=0.001, scale_mode=0)
     base.update(kw)
     return m.moe_config(*[base[f] for f, _ in m.moe_config._fields_])
 
@@ -79,6 +79,14 @@ def test_host_validation_status_codes():
         assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, fake,
                            1 << 30, None) == 2, b
         assert L.moe_permute(ctypes.byref(c), 4, fake, fake, fake, fake, fake, 1 << 30, None) == 2, b
+    # an unknown scale mode is unsupported (4)
+    c = _cfg(m, scale_mode=2)
+    assert L.moe_route(ctypes.byref(c), fake, 1, 4, fake, fake, fake, fake, fake, fake, fake,
+                       1 << 30, None) == 4
+    # the power-of-two quantisers validate like the others
+    assert L.moe_quantize_1x128_pow2(None, 0, 4, 128, fake, fake, None) == 1
+    assert L.moe_quantize_1x128_pow2(fake, 0, 4, 100, fake, fake, None) == 2
+    assert L.moe_quantize_128x128_pow2(fake, 1, 128, 130, fake, fake, None) == 2
     c = _cfg(m)
     big = 1 << 30
     assert L.moe_route(None, fake, 1, 4, fake, fake, fake, fake, fake, fake, fake, big, None) == 1

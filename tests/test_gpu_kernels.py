@@ -517,3 +517,71 @@ def test_update_bias_matches_oracle_over_trajectory(lib):
         b = oracle.bias_update(b, counts, T, k, cfg.expert_bias_update_rate)
     torch.cuda.synchronize()
     assert np.array_equal(host(bd).view(np.uint32), b.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------------------
+# Power-of-two scale variant (scale_mode 1)
+# ---------------------------------------------------------------------------------------
+def test_quantize_pow2_matches_oracle(lib):
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((67, 384)) * np.exp(rng.uniform(-20, 20, (67, 1)))).astype(np.float32)
+    x[3, :128] = 0.0
+    x[5, 7] = np.float32(448.0 * 2.0 ** -3)            # amax exactly 448 * 2^k
+    x[6, 130] = np.nextafter(np.float32(448.0), np.float32(1e9))
+    x[8, 260] = np.float32(1e-42)                      # subnormal-only tile
+    x[8, 256:260] = 0.0
+    xb = synth.to_bf16_exact(x)
+    for arr, dt in ((x, torch.float32), (xb, torch.bfloat16)):
+        say(f"quantize_1x128_pow2 {dt}")
+        q, s = lib.moe_quantize_1x128(dev(arr, dt), pow2=True)
+        torch.cuda.synchronize()
+        rq, rs = oracle.quantize_1x128_pow2(arr)
+        assert np.array_equal(host(q), rq)
+        assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    w = (rng.standard_normal((2, 256, 384)) * 0.05).astype(np.float32)
+    w[1, :128, 128:256] *= 1e-30
+    say("quantize_128x128_pow2")
+    q, s = lib.moe_quantize_128x128(dev(w), pow2=True)
+    torch.cuda.synchronize()
+    for m in range(2):
+        rq, rs = oracle.quantize_128x128_pow2(w[m])
+        assert np.array_equal(host(q)[m], rq)
+        assert np.array_equal(host(s)[m].view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("H,I,E,loads", [(256, 128, 4, [0, 17, 64, 3]),
+                                         (384, 256, 3, [160, 161, 33]),
+                                         (1024, 512, 5, [130, 0, 7, 250, 16])])
+def test_grouped_ffn_pow2_matches_oracle(lib, H, I, E, loads):
+    import dataclasses
+    rng = np.random.default_rng(H * 7 + E)
+    rows, T = int(sum(loads)), 200
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], hidden_size=H, moe_intermediate_size=I,
+                              num_experts=max(E, 4), num_experts_per_tok=1, tokens=T)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    xq, xs = oracle.quantize_1x128_pow2(x)
+    offsets = np.concatenate([[0], np.cumsum(loads)]).astype(np.int32)
+    row_token = rng.integers(0, T, rows).astype(np.int32)
+    w = []
+    for n, k in ((I, H), (I, H), (H, I)):
+        q = np.empty((E, n, k), np.uint8)
+        sc = np.empty((E, n // 128, k // 128), np.float32)
+        for e in range(E):
+            q[e], sc[e] = oracle.quantize_128x128_pow2((rng.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32))
+        w += [q, sc]
+    say(f"grouped_ffn pow2 H={H} I={I} E={E} loads={loads}")
+    c = lib.make_config(cfg, lib.SCALE_POW2)
+    for yt in (torch.float32, torch.bfloat16):
+        y = lib.moe_grouped_ffn_fp8(c, E, rows, dev(xq), dev(xs), dev(row_token), dev(offsets),
+                                    *_device_weights(lib, w), y_dtype=yt)
+        torch.cuda.synchronize()
+        y = host(y.float()).astype(np.float64)
+        for e in range(E):
+            lo, hi = offsets[e], offsets[e + 1]
+            if hi == lo:
+                continue
+            toks = row_token[lo:hi]
+            ref = oracle.expert_ffn(xq[toks], xs[toks], w[0][e], w[1][e], w[2][e], w[3][e], w[4][e],
+                                    w[5][e], pow2=True)[0]
+            err = _relerr(y[lo:hi], ref)
+            assert err < 5e-3, (yt, e, err)

@@ -33,6 +33,12 @@ def q3(w):
     return (*oracle.quantize_128x128(w1), *oracle.quantize_128x128(w3), *oracle.quantize_128x128(w2))
 
 
+def q3_pow2(w):
+    w1, w3, w2 = w
+    return (*oracle.quantize_128x128_pow2(w1), *oracle.quantize_128x128_pow2(w3),
+            *oracle.quantize_128x128_pow2(w2))
+
+
 def x_device(cfg, x):
     dt = torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32
     return torch.from_numpy(x).to(dt).cuda()
@@ -40,6 +46,37 @@ def x_device(cfg, x):
 
 def routing_ties(r):
     return (r["kth_gap"] < NEAR_TIE) | (r["group_gap"] < NEAR_TIE)
+
+
+@pytest.mark.parametrize("name", ["tiny", "reduced"])
+def test_layer_pow2_matches_oracle(name):
+    """The power-of-two scale variant end to end (scale_mode 1)."""
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    cfg = synth.PRESETS[name]
+    say(f"layer pow2 {name}: loading weights")
+    layer = MoELayer(cfg, scale_mode=1)
+    layer.load_from_synth()
+    x = synth.hidden_states(cfg)
+    b0 = synth.expert_bias(cfg)
+    say(f"layer pow2 {name}: forward T={cfg.tokens}")
+    out = layer.forward(x_device(cfg, x)).float().cpu().numpy()
+    g_idx = layer.topk_idx.cpu().numpy()
+    wr = synth.router_weight(cfg)
+    routed = [q3_pow2(synth.routed_expert_weights(cfg, e)) for e in range(cfg.num_experts)]
+    shared = [q3_pow2(synth.shared_expert_weights(cfg, s)) for s in range(cfg.num_shared_experts)]
+    assert np.array_equal(layer.w2s[0].cpu().numpy(), routed[0][5])
+    assert np.array_equal(MoELayer.unpack(layer.w1[1].cpu().numpy()), routed[1][0])
+    ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s], pow2=True)
+    r = ref["route"]
+    tie = routing_ties(r)
+    diff = np.any(g_idx != r["idx"], axis=1)
+    assert not np.any(diff & ~tie)
+    if np.any(diff):
+        ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s],
+                                   force_idx=g_idx, pow2=True)
+    err = relerr(out, ref["out"])
+    say(f"layer pow2 {name}: normwise error {err:.3e}")
+    assert err < TOL
 
 
 @pytest.mark.parametrize("name", ["tiny", "reduced"])
