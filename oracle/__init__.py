@@ -11,8 +11,9 @@ Each function cites the passage it follows, by page title and section:
     block with e4m3, tile_wise_1x128 inputs and block_wise_128x128 weights);
   * the 2kiu.com DeepSeek-V3 report digest (section 3.2: sigmoid affinities, bias
     used only for ranking, normalised gates, bincount load and the +-gamma update;
-    section 3.4: node/group-limited routing, no token dropping; section 4.3: block
-    scales and higher-precision accumulation);
+    section 3.3: the sequence-level balance loss; section 3.4: node/group-limited
+    routing, no token dropping; section 4.3: block scales and higher-precision
+    accumulation; section 5.5: the per-sequence allocation entropy);
   * the zhihu infra commentary on the report (training part: E4M3 everywhere,
     1x128 / 128x128 groups, GEMM by partial-sum promotion; SwiGLU recomputed).
 
@@ -33,5 +34,7 @@ from .moe import (  # noqa: F401
     quantize_128x128,
     quantize_128x128_pow2,
     route,
+    seq_assignment_entropy,
+    seq_balance_loss,
     silu,
 )

@@ -263,6 +263,43 @@ def bias_update(bias: np.ndarray, counts: np.ndarray, tokens: int, top_k: int,
 
 
 # ----------------------------------------------------------------------------------------
+# Sequence-wise balance statistic (2kiu.com digest section 3.3: a complementary
+# sequence-level balance loss, the sum over experts of each expert's share of the
+# sequence's assignments times its mean affinity, times a small coefficient alpha;
+# lpnh.cn guide section 3: aux_loss_alpha 0.001 with seq_aux). Reading: for each sequence of
+# L consecutive tokens, f_i = (assignments of expert i) / (k L), P_i = mean over the L
+# tokens of the sigmoid affinity s_{t,i}, loss = alpha * sum_i f_i P_i.
+# ----------------------------------------------------------------------------------------
+def seq_balance_loss(scores: np.ndarray, idx: np.ndarray, seq_len: int, alpha: float) -> np.ndarray:
+    scores = np.asarray(scores, dtype=np.float64)
+    T, N = scores.shape
+    k = idx.shape[1]
+    assert T % seq_len == 0
+    out = np.zeros(T // seq_len, dtype=np.float64)
+    for q in range(T // seq_len):
+        rows = slice(q * seq_len, (q + 1) * seq_len)
+        f = np.bincount(np.asarray(idx[rows]).ravel(), minlength=N)[:N] / (k * seq_len)
+        p = scores[rows].mean(axis=0)
+        out[q] = alpha * float(np.sum(f * p))
+    return out
+
+
+def seq_assignment_entropy(idx: np.ndarray, n_experts: int, seq_len: int) -> np.ndarray:
+    """Entropy (natural log) of each sequence's expert allocation f_i = count_i / (k L)
+    (2kiu.com digest section 5.5: the per-sequence allocation entropy is the quantity to
+    watch before turning the sequence loss on). Terms with f_i = 0 contribute 0."""
+    T, k = idx.shape
+    assert T % seq_len == 0
+    out = np.zeros(T // seq_len, dtype=np.float64)
+    for q in range(T // seq_len):
+        f = np.bincount(np.asarray(idx[q * seq_len:(q + 1) * seq_len]).ravel(),
+                        minlength=n_experts)[:n_experts] / (k * seq_len)
+        nz = f[f > 0]
+        out[q] = float(-np.sum(nz * np.log(nz)))
+    return out
+
+
+# ----------------------------------------------------------------------------------------
 # Whole layer.
 # ----------------------------------------------------------------------------------------
 ExpertGetter = Callable[[int], tuple]  # e -> (w1q, w1s, w3q, w3s, w2q, w2s)
