@@ -270,6 +270,13 @@ def bias_update(bias: np.ndarray, counts: np.ndarray, tokens: int, top_k: int,
 # L consecutive tokens, f_i = (assignments of expert i) / (k L), P_i = mean over the L
 # tokens of the sigmoid affinity s_{t,i}, loss = alpha * sum_i f_i P_i.
 # ----------------------------------------------------------------------------------------
+def _seq_counts(idx_rows: np.ndarray, n: int) -> np.ndarray:
+    """Assignments per expert; entries outside [0, n) name no expert and count for none
+    (the same reading as the permutation's, where such entries route nowhere)."""
+    v = np.asarray(idx_rows).ravel()
+    return np.bincount(v[(v >= 0) & (v < n)], minlength=n)
+
+
 def seq_balance_loss(scores: np.ndarray, idx: np.ndarray, seq_len: int, alpha: float) -> np.ndarray:
     scores = np.asarray(scores, dtype=np.float64)
     T, N = scores.shape
@@ -278,7 +285,7 @@ def seq_balance_loss(scores: np.ndarray, idx: np.ndarray, seq_len: int, alpha: f
     out = np.zeros(T // seq_len, dtype=np.float64)
     for q in range(T // seq_len):
         rows = slice(q * seq_len, (q + 1) * seq_len)
-        f = np.bincount(np.asarray(idx[rows]).ravel(), minlength=N)[:N] / (k * seq_len)
+        f = _seq_counts(idx[rows], N) / (k * seq_len)
         p = scores[rows].mean(axis=0)
         out[q] = alpha * float(np.sum(f * p))
     return out
@@ -292,8 +299,7 @@ def seq_assignment_entropy(idx: np.ndarray, n_experts: int, seq_len: int) -> np.
     assert T % seq_len == 0
     out = np.zeros(T // seq_len, dtype=np.float64)
     for q in range(T // seq_len):
-        f = np.bincount(np.asarray(idx[q * seq_len:(q + 1) * seq_len]).ravel(),
-                        minlength=n_experts)[:n_experts] / (k * seq_len)
+        f = _seq_counts(idx[q * seq_len:(q + 1) * seq_len], n_experts) / (k * seq_len)
         nz = f[f > 0]
         out[q] = float(-np.sum(nz * np.log(nz)))
     return out

@@ -66,3 +66,12 @@ def test_entropy_matches_scipy_and_loss_bounds():
         # f sums to 1, so the loss is a convex combination of mean affinities
         p = s[q * L:(q + 1) * L].mean(axis=0)
         assert p.min() - 1e-15 <= loss[q] <= p.max() + 1e-15
+
+
+def test_entries_naming_no_expert_count_for_none():
+    # k = 2, L = 2: three valid entries on expert 1, one entry -1; f_1 = 3/4
+    idx = np.array([[1, -1], [1, 1]], np.int32)
+    s = np.zeros((2, 4))
+    s[:, 1] = [0.2, 0.6]
+    assert abs(oracle.seq_balance_loss(s, idx, 2, 1.0)[0] - 0.75 * 0.4) < 1e-15
+    assert abs(oracle.seq_assignment_entropy(idx, 4, 2)[0] - (-0.75 * np.log(0.75))) < 1e-15
