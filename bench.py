@@ -173,6 +173,9 @@ def other_configs(layer, warmup: int, decode_steps: int):
     """The other workloads of the same method, outside the headline number: the T=128
     decode step and the skewed T=16384 step on the same V3 layer, and the reduced layer
     (its own weights)."""
+    import numpy as np
+    import torch
+
     import synth
     from deepseekmoe_routing_fp8_amd import MoELayer
     res = {}
@@ -185,6 +188,21 @@ def other_configs(layer, warmup: int, decode_steps: int):
             "updated each step")
         layer.bias.zero_()
         res["skewed"] = measure(layer, cfg, device_batches(cfg, 3), 12, 3)
+        # per-sequence balance loss / allocation entropy of the last skewed step's routing
+        # (4 sequences of 4096 tokens); timed on its own, it is not part of the forward step
+        L = 4096
+        for _ in range(3):
+            layer.seq_balance(L)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            loss, ent = layer.seq_balance(L)
+        e1.record()
+        torch.cuda.synchronize()
+        res["seq_balance"] = {"tokens": cfg.tokens, "seq_len": L, "us_per_call": e0.elapsed_time(e1) * 50.0,
+                              "loss": [round(float(v), 8) for v in loss.cpu()],
+                              "entropy_nats": [round(float(v), 4) for v in ent.cpu()],
+                              "max_entropy_nats": round(float(np.log(cfg.num_experts)), 4)}
         cfg = synth.PRESETS["reduced"]
         log("[bench] reduced layer: weights on the device")
         small = MoELayer(cfg)

@@ -30,7 +30,7 @@ ENTRY_POINTS = (
     "moe_pack_router_weights", "moe_router_weights_elems", "moe_route", "moe_route_workspace_bytes",
     "moe_permute", "moe_permute_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8",
     "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
-    "moe_update_bias",
+    "moe_update_bias", "moe_seq_balance", "moe_seq_balance_workspace_bytes",
 )
 
 
@@ -80,6 +80,9 @@ _sig = {
                                  ctypes.c_int),
     "moe_combine": ([_CFG, _I64, _P, ctypes.c_int, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_update_bias": ([_CFG, _I64, _P, _P, _P], ctypes.c_int),
+    "moe_seq_balance": ([_CFG, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _SZ, _P],
+                        ctypes.c_int),
+    "moe_seq_balance_workspace_bytes": ([_CFG, _I64, _I64], _SZ),
 }
 for _name, (_args, _res) in _sig.items():
     _f = getattr(_lib, _name)
@@ -349,6 +352,34 @@ def moe_update_bias(cfg: moe_config, T: int, counts: torch.Tensor, bias: torch.T
                                 _dev(bias, torch.float32, "bias", (cfg.n_routed,)), _stream(stream)),
            "moe_update_bias")
     return bias
+
+
+def moe_seq_balance_workspace_bytes(cfg: moe_config, T: int, seq_len: int) -> int:
+    return int(_lib.moe_seq_balance_workspace_bytes(ctypes.byref(cfg), T, seq_len))
+
+
+def moe_seq_balance(cfg: moe_config, scores: torch.Tensor, topk_idx: torch.Tensor, seq_len: int,
+                    alpha: float = 0.001, loss: torch.Tensor = None, entropy: torch.Tensor = None,
+                    with_entropy: bool = True, ws: torch.Tensor = None, stream=None):
+    """Per-sequence balance loss and allocation entropy over sequences of seq_len
+    consecutive tokens -> (loss [T/seq_len], entropy [T/seq_len] or None), float32."""
+    T = scores.shape[0]
+    dev = scores.device
+    nseq = T // seq_len if seq_len > 0 else 0
+    if loss is None:
+        loss = torch.empty((nseq,), dtype=torch.float32, device=dev)
+    if entropy is None and with_entropy:
+        entropy = torch.empty((nseq,), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty((max(moe_seq_balance_workspace_bytes(cfg, T, seq_len), 1),),
+                         dtype=torch.uint8, device=dev)
+    _check(_lib.moe_seq_balance(
+        ctypes.byref(cfg), T, seq_len, _dev(scores, torch.float32, "scores", (T, cfg.n_routed)),
+        _dev(topk_idx, torch.int32, "topk_idx", (T, cfg.top_k)), alpha,
+        _dev(loss, torch.float32, "loss", (nseq,)),
+        _dev(entropy, torch.float32, "entropy", (nseq,)) if entropy is not None else None,
+        _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "moe_seq_balance")
+    return loss, entropy
 
 
 from .layer import MoELayer  # noqa: E402,F401

@@ -20,7 +20,7 @@ from . import (MOE_F32, make_config, moe_combine, moe_grouped_ffn_fp8_down,
                moe_grouped_ffn_fp8_gate_up, moe_grouped_ffn_workspace_bytes, moe_pack_fp8_weights,
                moe_pack_router_weights, moe_permute, moe_permute_workspace_bytes,
                moe_quantize_1x128, moe_quantize_128x128, moe_route, moe_route_workspace_bytes,
-               moe_update_bias)
+               moe_seq_balance, moe_seq_balance_workspace_bytes, moe_update_bias)
 
 
 class MoELayer:
@@ -157,3 +157,19 @@ class MoELayer:
             moe_update_bias(c, T, self.counts, self.bias)
         mark(7)
         return self.out
+
+    def seq_balance(self, seq_len: int, alpha: float = 0.001, with_entropy: bool = True):
+        """Per-sequence balance loss and allocation entropy of the last forward's routing
+        (sequences of seq_len consecutive tokens) -> (loss, entropy or None), float32."""
+        T = self._T
+        key = (T, seq_len)
+        if getattr(self, "_sb_key", None) != key:
+            nseq = T // seq_len
+            self.sb_loss = torch.empty((nseq,), dtype=torch.float32, device=self.dev)
+            self.sb_entropy = torch.empty((nseq,), dtype=torch.float32, device=self.dev)
+            self.sb_ws = torch.empty((max(moe_seq_balance_workspace_bytes(self.c, T, seq_len), 1),),
+                                     dtype=torch.uint8, device=self.dev)
+            self._sb_key = key
+        return moe_seq_balance(self.c, self.scores, self.topk_idx, seq_len, alpha, loss=self.sb_loss,
+                               entropy=self.sb_entropy if with_entropy else None,
+                               with_entropy=with_entropy, ws=self.sb_ws)

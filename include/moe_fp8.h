@@ -11,9 +11,11 @@
  *            block_wise_128x128 weights, moe_gating kept out of FP8).
  *   [digest] 2kiu.com DeepSeek-V3 technical-report digest: section 3.2 (sigmoid
  *            affinities, bias used only for ranking, normalised gates, load bincount,
- *            +-gamma update after each step), section 3.4 (group/node-limited routing,
+ *            +-gamma update after each step), section 3.3 (sequence-level balance
+ *            loss), section 3.4 (group/node-limited routing,
  *            no token dropping), section 4.3 (per-group scales, higher-precision
- *            accumulation), section 5.2 (batch-level load statistics).
+ *            accumulation), section 5.2 (batch-level load statistics), section 5.5 (per-sequence
+ *            allocation entropy).
  *   [zhihu]  zhihu infra commentary on the report, training part (E4M3 throughout,
  *            1x128 / 128x128 groups, GEMM by partial-sum promotion; SwiGLU recompute).
  *
@@ -305,6 +307,33 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, moe
  */
 moe_status moe_update_bias(const moe_config* cfg, int64_t T, const int32_t* counts,
                            float* bias, void* stream);
+
+/*
+ * moe_seq_balance — per-sequence balance statistics of one routing step ([digest]
+ * section 3.3: the complementary sequence-level balance loss, alpha times the sum over
+ * experts of the expert's share of the sequence's assignments times its mean affinity;
+ * section 5.5: the per-sequence allocation entropy as the signal for that loss). The T
+ * tokens form T / seq_len sequences of seq_len consecutive tokens. For sequence q:
+ *   f_i = (entries of topk_idx in q equal to i) / (top_k * seq_len)
+ *   P_i = mean over q's tokens of scores[t, i]
+ *   loss[q] = alpha * sum_i f_i * P_i,   entropy[q] = -sum_{f_i > 0} f_i * ln f_i
+ * Sums in FP64 in a fixed order (deterministic), each output rounded once to FP32.
+ * Entries of topk_idx outside [0, N_r) count for no expert (f no longer sums to 1).
+ *   scores    [T, N_r] float (the sigmoid affinities moe_route writes)
+ *   topk_idx  [T, top_k] int32
+ *   alpha     loss coefficient ([guide] aux_loss_alpha, 0.001)
+ *   loss      [T / seq_len] float, output
+ *   entropy   [T / seq_len] float, output; NULL skips it
+ *   ws        moe_seq_balance_workspace_bytes(cfg, T, seq_len) bytes, 8-byte aligned
+ * Errors: NULL pointers (T > 0); invalid config; T < 0, T >= 2^31, seq_len <= 0 or
+ * T % seq_len != 0, or more than 2^24 workgroups (SHAPE); workspace NULL or small
+ * (WORKSPACE); misaligned workspace (UNSUPPORTED). T == 0 launches nothing.
+ */
+size_t moe_seq_balance_workspace_bytes(const moe_config* cfg, int64_t T, int64_t seq_len);
+moe_status moe_seq_balance(const moe_config* cfg, int64_t T, int64_t seq_len,
+                           const float* scores, const int32_t* topk_idx, float alpha,
+                           float* loss, float* entropy, void* ws, size_t ws_bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ def test_header_declares_the_six_calls():
     names = _declared()
     for n in ("moe_quantize_1x128", "moe_route", "moe_permute", "moe_grouped_ffn_fp8",
               "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
-              "moe_update_bias"):
+              "moe_update_bias", "moe_seq_balance"):
         assert n in names
 
 
@@ -133,6 +133,21 @@ def test_host_validation_status_codes():
                                       None) == 3
     assert L.moe_grouped_ffn_fp8_down(ctypes.byref(c), 16, 256, fake, None, fake, 1, fake, need,
                                       None) == 1
+    # sequence balance statistics
+    need_s = L.moe_seq_balance_workspace_bytes(ctypes.byref(c), 1000, 100)
+    assert need_s == 10 * 4 * 16 * 12      # 10 sequences x 4 chunks x 16 experts x (f64 + i32)
+    assert L.moe_seq_balance_workspace_bytes(ctypes.byref(c), 1000, 300) == 0
+    sb = L.moe_seq_balance
+    assert sb(ctypes.byref(c), 1000, 0, fake, fake, 0.001, fake, None, fake, need_s, None) == 2
+    assert sb(ctypes.byref(c), 1000, 300, fake, fake, 0.001, fake, None, fake, need_s, None) == 2
+    assert sb(ctypes.byref(c), -4, 2, fake, fake, 0.001, fake, None, fake, need_s, None) == 2
+    assert sb(ctypes.byref(c), 1000, 100, None, fake, 0.001, fake, None, fake, need_s, None) == 1
+    assert sb(ctypes.byref(c), 1000, 100, fake, fake, 0.001, None, fake, fake, need_s, None) == 1
+    assert sb(ctypes.byref(c), 1000, 100, fake, fake, 0.001, fake, None, fake, need_s - 1, None) == 6
+    assert sb(ctypes.byref(c), 1000, 100, fake, fake, 0.001, fake, None, None, need_s, None) == 6
+    assert sb(ctypes.byref(c), 1000, 100, fake, fake, 0.001, fake, None, P(0x1004), need_s, None) == 4
+    assert sb(ctypes.byref(c), 0, 100, None, None, 0.001, None, None, None, 0, None) == 0
+    assert sb(ctypes.byref(c), 1 << 30, 1, fake, fake, 0.001, fake, None, fake, 1 << 62, None) == 2
     # too large for 32-bit operand offsets
     big = _cfg(m, hidden=16384, inter=16384)
     assert L.moe_grouped_ffn_fp8_gate_up(ctypes.byref(big), 16, 1 << 18, 64, fake, fake, None,

@@ -585,3 +585,53 @@ def test_grouped_ffn_pow2_matches_oracle(lib, H, I, E, loads):
                                     w[5][e], pow2=True)[0]
             err = _relerr(y[lo:hi], ref)
             assert err < 5e-3, (yt, e, err)
+
+
+# ---------------------------------------------------------------------------------------
+# Per-sequence balance loss and allocation entropy
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,N,k,L,skew", [(64, 16, 4, 64, None), (300, 64, 6, 100, None),
+                                          (4096, 256, 8, 4096, None), (4096, 256, 8, 1024, 1.1),
+                                          (17, 512, 16, 1, None), (16384, 256, 8, 4096, 1.1)])
+def test_seq_balance_matches_oracle(lib, T, N, k, L, skew):
+    import dataclasses
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], num_experts=N, num_experts_per_tok=k, tokens=T)
+    rng = np.random.default_rng(T + L)
+    idx = _idx(rng, T, N, k, skew)
+    s = rng.uniform(0.0, 1.0, (T, N)).astype(np.float32)
+    say(f"seq_balance T={T} N={N} k={k} L={L} skew={skew}")
+    loss, ent = lib.moe_seq_balance(lib.make_config(cfg), dev(s), dev(idx), L, alpha=0.001)
+    torch.cuda.synchronize()
+    rl = oracle.seq_balance_loss(s, idx, L, 0.001)
+    rh = oracle.seq_assignment_entropy(idx, N, L)
+    # FP64 sums on both sides, one FP32 rounding of the result: |err| <= 2^-24 |ref| (+ slack)
+    assert np.all(np.abs(host(loss) - rl) <= 1.2e-7 * np.abs(rl) + 1e-30)
+    assert np.all(np.abs(host(ent) - rh) <= 1.2e-7 * np.abs(rh) + 1e-12)
+
+
+def test_seq_balance_collapse_invalid_entries_and_empty(lib):
+    import dataclasses
+    N, k, L = 32, 4, 40
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], num_experts=N, num_experts_per_tok=k, tokens=2 * L)
+    c = lib.make_config(cfg)
+    rng = np.random.default_rng(4)
+    s = rng.uniform(0.0, 1.0, (2 * L, N)).astype(np.float32)
+    # sequence 0: every token on experts 0..3 (entropy ln 4); sequence 1: some entries -1 or N
+    idx = np.tile(np.arange(k, dtype=np.int32), (2 * L, 1))
+    idx[L:] = _idx(rng, L, N, k)
+    idx[L + 3, 1] = -1
+    idx[L + 7, 0] = N
+    say("seq_balance collapse / invalid entries")
+    loss, ent = lib.moe_seq_balance(c, dev(s), dev(idx), L, alpha=0.5)
+    torch.cuda.synchronize()
+    rl = oracle.seq_balance_loss(s, idx, L, 0.5)
+    rh = oracle.seq_assignment_entropy(idx, N, L)
+    assert np.all(np.abs(host(loss) - rl) <= 1.2e-7 * np.abs(rl))
+    assert np.all(np.abs(host(ent) - rh) <= 1.2e-7 * np.abs(rh) + 1e-12)
+    assert abs(host(ent)[0] - np.log(k)) < 1e-6
+    # entropy optional; T = 0 launches nothing
+    loss2, none = lib.moe_seq_balance(c, dev(s), dev(idx), L, alpha=0.5, with_entropy=False)
+    torch.cuda.synchronize()
+    assert none is None and np.array_equal(host(loss2), host(loss))
+    e_loss, _ = lib.moe_seq_balance(c, dev(s[:0]), dev(idx[:0]), L)
+    assert e_loss.numel() == 0
