@@ -169,6 +169,27 @@ def device_batches(cfg, n: int):
     return [torch.from_numpy(synth.hidden_states(cfg, step=i)).to(dt).cuda() for i in range(n)]
 
 
+def time_seq_balance(layer, cfg, seq_len: int, calls: int = 20):
+    """Time moe_seq_balance on the layer's last routing (sequences of seq_len tokens)."""
+    import numpy as np
+    import torch
+    for _ in range(3):
+        layer.seq_balance(seq_len)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        loss, ent = layer.seq_balance(seq_len)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    nbytes = cfg.tokens * (cfg.num_experts + cfg.num_experts_per_tok) * 4
+    return {"tokens": cfg.tokens, "seq_len": seq_len, "us_per_call": round(us, 2),
+            "algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "loss": [round(float(v), 8) for v in loss.cpu()],
+            "entropy_nats": [round(float(v), 4) for v in ent.cpu()],
+            "max_entropy_nats": round(float(np.log(cfg.num_experts)), 4)}
+
+
 def other_configs(layer, warmup: int, decode_steps: int):
     """The other workloads of the same method, outside the headline number: the T=128
     decode step and the skewed T=16384 step on the same V3 layer, and the reduced layer
@@ -190,19 +211,7 @@ def other_configs(layer, warmup: int, decode_steps: int):
         res["skewed"] = measure(layer, cfg, device_batches(cfg, 3), 12, 3)
         # per-sequence balance loss / allocation entropy of the last skewed step's routing
         # (4 sequences of 4096 tokens); timed on its own, it is not part of the forward step
-        L = 4096
-        for _ in range(3):
-            layer.seq_balance(L)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(20):
-            loss, ent = layer.seq_balance(L)
-        e1.record()
-        torch.cuda.synchronize()
-        res["seq_balance"] = {"tokens": cfg.tokens, "seq_len": L, "us_per_call": e0.elapsed_time(e1) * 50.0,
-                              "loss": [round(float(v), 8) for v in loss.cpu()],
-                              "entropy_nats": [round(float(v), 4) for v in ent.cpu()],
-                              "max_entropy_nats": round(float(np.log(cfg.num_experts)), 4)}
+        res["seq_balance"] = time_seq_balance(layer, cfg, 4096)
         cfg = synth.PRESETS["reduced"]
         log("[bench] reduced layer: weights on the device")
         small = MoELayer(cfg)
@@ -228,6 +237,9 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="also time the per-sequence balance statistic on the last step's "
+                         "routing, over sequences of this many tokens (0: only in the extras)")
     ap.add_argument("--decode-steps", type=int, default=50,
                     help="steps of the T=128 decode workload timed after the main one; the "
                          "skewed and reduced workloads follow it (0: skip all three)")
@@ -322,6 +334,8 @@ def main():
         "event_ms_per_step": round(float(step_ms.mean()), 4),
         "max_over_mean_load": round(float(counts.max() / counts.mean()), 3),
     }
+    if args.seq_len > 0:
+        res["seq_balance"] = time_seq_balance(layer, cfg, args.seq_len)
     if args.workload == "v3_prefill":
         res.update(other_configs(layer, args.warmup, args.decode_steps))
     if not args.no_cpu_baseline:
