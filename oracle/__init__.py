@@ -15,11 +15,24 @@ Each function cites the passage it follows, by page title and section:
     routing, no token dropping; section 4.3: block scales and higher-precision
     accumulation; section 5.5: the per-sequence allocation entropy);
   * the zhihu infra commentary on the report (training part: E4M3 everywhere,
-    1x128 / 128x128 groups, GEMM by partial-sum promotion; SwiGLU recomputed).
+    1x128 / 128x128 groups, GEMM by partial-sum promotion; SwiGLU recomputed);
+  * for the backward (``backward.py``): the guide's [fp8] block (gemm_dgrad and
+    gemm_wgrad in FP8, moe_gating kept in BF16/FP32) and the zhihu commentary (E4M3 in
+    both directions).
 
 Every function here is pinned by a CPU test against something other than itself
 (closed forms, brute force, library routines, invariants). None is "parity unpinned".
 """
+from .backward import (  # noqa: F401
+    combine_backward,
+    dequant_128x1,
+    expert_ffn_backward,
+    layer_backward,
+    quantize_128x1,
+    round_bf16,
+    route_backward,
+    silu_grad,
+)
 from .e4m3 import E4M3_MAX, decode, encode, finite_values  # noqa: F401
 from .moe import (  # noqa: F401
     bias_update,
