@@ -31,6 +31,9 @@ ENTRY_POINTS = (
     "moe_permute", "moe_permute_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn_fp8",
     "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
     "moe_update_bias", "moe_seq_balance", "moe_seq_balance_workspace_bytes",
+    "moe_combine_backward", "moe_route_backward", "moe_route_backward_workspace_bytes",
+    "moe_unpermute_sum", "moe_transpose_fp8_blocks", "moe_grouped_ffn_fp8_backward",
+    "moe_grouped_ffn_backward_workspace_bytes",
 )
 
 
@@ -83,6 +86,16 @@ _sig = {
     "moe_seq_balance": ([_CFG, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _SZ, _P],
                         ctypes.c_int),
     "moe_seq_balance_workspace_bytes": ([_CFG, _I64, _I64], _SZ),
+    "moe_combine_backward": ([_CFG, _I64, _P, _P, ctypes.c_int, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_route_backward_workspace_bytes": ([_CFG, _I64], _SZ),
+    "moe_route_backward": ([_CFG, _I64, _P, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                            _SZ, _P], ctypes.c_int),
+    "moe_unpermute_sum": ([_CFG, _I64, _P, ctypes.c_int, _P, _P, _P, _P], ctypes.c_int),
+    "moe_transpose_fp8_blocks": ([_I64, _I64, _I64, _P, _P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "moe_grouped_ffn_backward_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
+    "moe_grouped_ffn_fp8_backward": ([_CFG, _I32, _I64, _I64, _P, _P, _P, ctypes.c_int, _P, _P, _P,
+                                      _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P,
+                                      ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _sig.items():
     _f = getattr(_lib, _name)
@@ -380,6 +393,127 @@ def moe_seq_balance(cfg: moe_config, scores: torch.Tensor, topk_idx: torch.Tenso
         _dev(entropy, torch.float32, "entropy", (nseq,)) if entropy is not None else None,
         _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "moe_seq_balance")
     return loss, entropy
+
+
+# ---------------------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------------------
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise MoEError(f"unsupported dtype {t.dtype}")
+
+
+def moe_combine_backward(cfg: moe_config, dout: torch.Tensor, y_rows: torch.Tensor,
+                         row_of: torch.Tensor, topk_gate: torch.Tensor, dy: torch.Tensor = None,
+                         dgate: torch.Tensor = None, stream=None):
+    """-> (dy [T*(k+N_s), H] f32, dgate [T, k] f32) from dout [T, H] bf16."""
+    T, H = dout.shape
+    k, S = cfg.top_k, cfg.n_shared
+    dev = dout.device
+    dy = torch.empty((T * (k + S), H), dtype=torch.float32, device=dev) if dy is None else dy
+    dgate = torch.empty((T, k), dtype=torch.float32, device=dev) if dgate is None else dgate
+    _check(_lib.moe_combine_backward(
+        ctypes.byref(cfg), T, _dev(dout, torch.bfloat16, "dout", (T, cfg.hidden)),
+        _dev(y_rows, y_rows.dtype, "y_rows", (T * (k + S), H)), _dt(y_rows),
+        _dev(row_of, torch.int32, "row_of", (T, k)), _dev(topk_gate, torch.float32, "topk_gate", (T, k)),
+        _dev(dy, torch.float32, "dy", (T * (k + S), H)), _dev(dgate, torch.float32, "dgate", (T, k)),
+        _stream(stream)), "moe_combine_backward")
+    return dy, dgate
+
+
+def moe_route_backward_workspace_bytes(cfg: moe_config, T: int) -> int:
+    return int(_lib.moe_route_backward_workspace_bytes(ctypes.byref(cfg), T))
+
+
+def moe_route_backward(cfg: moe_config, x: torch.Tensor, w_router: torch.Tensor, scores: torch.Tensor,
+                       topk_idx: torch.Tensor, dgate: torch.Tensor, offsets: torch.Tensor,
+                       row_token: torch.Tensor, row_of: torch.Tensor, dx: torch.Tensor = None,
+                       dw_router: torch.Tensor = None, ws: torch.Tensor = None, stream=None):
+    """-> (dx [T, H] f32, dw_router [N_r, H] f32): the gates' gradient through the router."""
+    T, H = x.shape
+    N, k = cfg.n_routed, cfg.top_k
+    dev = x.device
+    dx = torch.empty((T, H), dtype=torch.float32, device=dev) if dx is None else dx
+    dw_router = torch.empty((N, H), dtype=torch.float32, device=dev) if dw_router is None else dw_router
+    if ws is None:
+        ws = torch.empty((max(moe_route_backward_workspace_bytes(cfg, T), 1),), dtype=torch.uint8, device=dev)
+    _check(_lib.moe_route_backward(
+        ctypes.byref(cfg), T, _dev(x, x.dtype, "x", (T, cfg.hidden)), _dt(x),
+        _dev(w_router, torch.float32, "w_router", (N, H)), _dev(scores, torch.float32, "scores", (T, N)),
+        _dev(topk_idx, torch.int32, "topk_idx", (T, k)), _dev(dgate, torch.float32, "dgate", (T, k)),
+        _dev(offsets, torch.int32, "offsets"), _dev(row_token, torch.int32, "row_token"),
+        _dev(row_of, torch.int32, "row_of", (T, k)), _dev(dx, torch.float32, "dx", (T, H)),
+        _dev(dw_router, torch.float32, "dw_router", (N, H)), _dev(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "moe_route_backward")
+    return dx, dw_router
+
+
+def moe_unpermute_sum(cfg: moe_config, rows: torch.Tensor, row_of: torch.Tensor,
+                      extra: torch.Tensor = None, out: torch.Tensor = None, stream=None):
+    """-> out [T, H] bf16 = sum of each token's rows (shared, then slots) + extra."""
+    T, k = row_of.shape
+    H = cfg.hidden
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=rows.device) if out is None else out
+    _check(_lib.moe_unpermute_sum(
+        ctypes.byref(cfg), T, _dev(rows, rows.dtype, "rows", (T * (k + cfg.n_shared), H)), _dt(rows),
+        _dev(row_of, torch.int32, "row_of", (T, k)),
+        _dev(extra, torch.float32, "extra", (T, H)) if extra is not None else None,
+        _dev(out, torch.bfloat16, "out", (T, H)), _stream(stream)), "moe_unpermute_sum")
+    return out
+
+
+def moe_transpose_fp8_blocks(q: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor,
+                             dst_scales: torch.Tensor, col0: int = 0, stream=None):
+    """dst[e][c][col0 + r] = q[e][r][c] (codes [E, R, C] -> [E, C, dst_cols]) with the block
+    scales moved along."""
+    E, R, C = q.shape
+    dst_cols = dst.shape[2]
+    _check(_lib.moe_transpose_fp8_blocks(
+        E, R, C, _dev(q, torch.uint8, "q"), _dev(scales, torch.float32, "scales", (E, R // 128, C // 128)),
+        _dev(dst, torch.uint8, "dst", (E, C, dst_cols)),
+        _dev(dst_scales, torch.float32, "dst_scales", (E, C // 128, dst_cols // 128)), dst_cols, col0,
+        _stream(stream)), "moe_transpose_fp8_blocks")
+    return dst, dst_scales
+
+
+def moe_grouped_ffn_backward_workspace_bytes(cfg: moe_config, n_experts: int, n_rows: int) -> int:
+    return int(_lib.moe_grouped_ffn_backward_workspace_bytes(ctypes.byref(cfg), n_experts, n_rows))
+
+
+def moe_grouped_ffn_fp8_backward(cfg: moe_config, n_experts: int, xq, xs, x, row_token, offsets,
+                                 w1, w1s, w3, w3s, w2t, w2ts, w13t, w13ts, dy,
+                                 dx_rows: torch.Tensor = None, dx_dtype=torch.float32,
+                                 dw1: torch.Tensor = None, dw3: torch.Tensor = None,
+                                 dw2: torch.Tensor = None, dw_dtype=torch.float32,
+                                 ws: torch.Tensor = None, stream=None):
+    """-> (dx_rows [n_rows, H], dw1 [E, I, H], dw3 [E, I, H], dw2 [E, H, I])."""
+    n_rows = dy.shape[0]
+    T = xq.shape[0]
+    H, I, E = cfg.hidden, cfg.inter, n_experts
+    dev = dy.device
+    if dx_rows is None:
+        dx_rows = torch.empty((n_rows, H), dtype=dx_dtype, device=dev)
+    dw1 = torch.empty((E, I, H), dtype=dw_dtype, device=dev) if dw1 is None else dw1
+    dw3 = torch.empty((E, I, H), dtype=dw_dtype, device=dev) if dw3 is None else dw3
+    dw2 = torch.empty((E, H, I), dtype=dw_dtype, device=dev) if dw2 is None else dw2
+    if ws is None:
+        ws = torch.empty((max(moe_grouped_ffn_backward_workspace_bytes(cfg, E, n_rows), 1),),
+                         dtype=torch.uint8, device=dev)
+    _check(_lib.moe_grouped_ffn_fp8_backward(
+        ctypes.byref(cfg), E, n_rows, T, _dev(xq, torch.uint8, "xq", (T, H)),
+        _dev(xs, torch.float32, "xs", (T, H // 128)), _dev(x, x.dtype, "x", (T, H)), _dt(x),
+        _dev(row_token, torch.int32, "row_token", (n_rows,)), _dev(offsets, torch.int32, "offsets", (E + 1,)),
+        _dev(w1, torch.uint8, "w1"), _dev(w1s, torch.float32, "w1s"), _dev(w3, torch.uint8, "w3"),
+        _dev(w3s, torch.float32, "w3s"), _dev(w2t, torch.uint8, "w2t"), _dev(w2ts, torch.float32, "w2ts"),
+        _dev(w13t, torch.uint8, "w13t"), _dev(w13ts, torch.float32, "w13ts"),
+        _dev(dy, torch.float32, "dy", (n_rows, H)), _dev(dx_rows, dx_rows.dtype, "dx_rows", (n_rows, H)),
+        _dt(dx_rows), _dev(dw1, dw1.dtype, "dw1", (E, I, H)), _dev(dw3, dw1.dtype, "dw3", (E, I, H)),
+        _dev(dw2, dw1.dtype, "dw2", (E, H, I)), _dt(dw1), _dev(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "moe_grouped_ffn_fp8_backward")
+    return dx_rows, dw1, dw3, dw2
 
 
 from .layer import MoELayer  # noqa: E402,F401

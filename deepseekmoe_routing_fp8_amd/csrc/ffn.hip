@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "ffn_internal.h"
 
 namespace moe {
 namespace {
@@ -859,6 +860,62 @@ moe_status ffn_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows, co
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------------------------
+// The phase-2 kernel as a plain grouped GEMM, for the backward pass:
+// y[rows, N] = A[rows, K] x W_e[N, K]^T per expert segment, on a tile plan of the same
+// segments. A: E4M3 codes with 1x128 scales chunk-major ([K/128][n_rows]); W_e packed by
+// moe_pack_fp8_weights with 128x128 block scales [E][N/128][K/128].
+// ------------------------------------------------------------------------------------
+namespace moe {
+
+size_t ffn_plan_bytes(int32_t n_experts, int64_t n_rows) {
+  const int64_t max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
+  return align256((size_t)max_tiles * sizeof(Tile)) + 256;
+}
+
+moe_status ffn_plan_launch(const int32_t* offsets, int32_t n_experts, int64_t n_rows, void* plan,
+                           hipStream_t s) {
+  if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 1 || n_rows >= ((int64_t)1 << 31))
+    return MOE_ERR_SHAPE;
+  const int64_t max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
+  Tile* tiles = static_cast<Tile*>(plan);
+  int32_t* nt = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(plan) +
+                                           align256((size_t)max_tiles * sizeof(Tile)));
+  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
+                     (int)n_rows, (int)max_tiles, tiles, nt);
+  return launch_status();
+}
+
+moe_status ffn_grouped_gemm_launch(const void* plan, int32_t n_experts, int64_t n_rows,
+                                   const uint8_t* aq, const float* as_cm, const uint8_t* w,
+                                   const float* wsc, int N, int K, void* y, moe_dtype yt,
+                                   hipStream_t s) {
+  if (N <= 0 || K <= 0 || N % kTile || K % kTile || K > kMaxChunks * kTile) return MOE_ERR_SHAPE;
+  if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 1 || n_rows >= ((int64_t)1 << 31))
+    return MOE_ERR_SHAPE;
+  // per-lane operand offsets into A and the scale array are 32-bit
+  if (n_rows * (int64_t)K >= ((int64_t)1 << 32) || n_rows * (int64_t)(K / kTile) * 4 >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
+  const int64_t grid_tiles = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  const int n_nb = (N + 255) / 256;
+  const int64_t nwg = (n_nb + kNbPerWg2 - 1) / kNbPerWg2;
+  if (grid_tiles * nwg * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  const Tile* tiles = static_cast<const Tile*>(plan);
+  const int32_t* nt = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(plan) +
+                                                       align256((size_t)max_tiles * sizeof(Tile)));
+  FfnArgs a{tiles, nt, (int)max_tiles, n_experts, (int)n_rows, aq, as_cm, n_rows, nullptr, w, wsc,
+            nullptr, nullptr, N, K, n_nb, kNbPerWg2, nullptr, nullptr, y};
+  const dim3 grid((unsigned)(grid_tiles * nwg));
+  if (yt == MOE_BF16)
+    hipLaunchKernelGGL((ffn_kernel<2, uint16_t, false>), grid, dim3(kFThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_kernel<2, float, false>), grid, dim3(kFThreads), 0, s, a);
+  return launch_status();
+}
+
+}  // namespace moe
 
 extern "C" moe_status moe_grouped_ffn_fp8_gate_up(const moe_config* cfg, int32_t n_experts,
                                                   int64_t n_rows, int64_t n_tokens,

@@ -16,11 +16,14 @@ from typing import Callable, Iterable, Optional
 import numpy as np
 import torch
 
-from . import (MOE_F32, make_config, moe_combine, moe_grouped_ffn_fp8_down,
-               moe_grouped_ffn_fp8_gate_up, moe_grouped_ffn_workspace_bytes, moe_pack_fp8_weights,
-               moe_pack_router_weights, moe_permute, moe_permute_workspace_bytes,
-               moe_quantize_1x128, moe_quantize_128x128, moe_route, moe_route_workspace_bytes,
-               moe_seq_balance, moe_seq_balance_workspace_bytes, moe_update_bias)
+from . import (MOE_F32, make_config, moe_combine, moe_combine_backward,
+               moe_grouped_ffn_backward_workspace_bytes, moe_grouped_ffn_fp8_backward,
+               moe_grouped_ffn_fp8_down, moe_grouped_ffn_fp8_gate_up,
+               moe_grouped_ffn_workspace_bytes, moe_pack_fp8_weights, moe_pack_router_weights,
+               moe_permute, moe_permute_workspace_bytes, moe_quantize_1x128, moe_quantize_128x128,
+               moe_route, moe_route_backward, moe_route_backward_workspace_bytes, moe_route_workspace_bytes,
+               moe_seq_balance, moe_seq_balance_workspace_bytes, moe_transpose_fp8_blocks,
+               moe_unpermute_sum, moe_update_bias)
 
 
 class MoELayer:
@@ -30,9 +33,12 @@ class MoELayer:
     ``load_from_synth``) once, then ``forward(x)`` per step.
     """
 
-    def __init__(self, cfg, device="cuda", y_dtype=torch.bfloat16, scale_mode: int = 0):
+    def __init__(self, cfg, device="cuda", y_dtype=torch.bfloat16, scale_mode: int = 0,
+                 backward: bool = False, dw_dtype=torch.float32):
         """``scale_mode`` 0: the pages' FP32 group scales; 1: the power-of-two variant
-        (weights and activations quantised with power-of-two scales, applied by the MFMA)."""
+        (weights and activations quantised with power-of-two scales, applied by the MFMA).
+        ``backward``: also keep what ``backward`` needs (the transposed packed weights for
+        the dgrad GEMMs and the FP32 router weight); weight gradients come in ``dw_dtype``."""
         self.cfg = cfg
         self.scale_mode = scale_mode
         self.c = make_config(cfg, scale_mode)
@@ -51,12 +57,36 @@ class MoELayer:
         self.w_router = None
         self.bias = None
         self._T = None
+        self.backward_enabled = backward
+        self.dw_dtype = dw_dtype
+        if backward:
+            # dgrad operands: W2^T [I, H] and [W1^T | W3^T] [H, 2I] per expert, packed
+            self.w2t = torch.empty((EA, I, H), dtype=u8, device=d)
+            self.w2ts = torch.empty((EA, I // 128, H // 128), dtype=f32, device=d)
+            self.w13t = torch.empty((EA, H, 2 * I), dtype=u8, device=d)
+            self.w13ts = torch.empty((EA, H // 128, 2 * I // 128), dtype=f32, device=d)
+            self.w_router_f32 = None
+            self._bT = None
 
     # -- weights -------------------------------------------------------------------
     def _quant_into(self, w: np.ndarray, q: torch.Tensor, s: torch.Tensor):
+        """Quantise and pack one matrix; returns its row-major codes."""
         t = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(self.dev)
         rowmajor, _ = moe_quantize_128x128(t, scales=s, pow2=self.scale_mode == 1)
         moe_pack_fp8_weights(rowmajor, q)
+        return rowmajor
+
+    def _transposed_into(self, e: int, q1, q3, q2):
+        """Pack expert e's dgrad operands from its row-major codes."""
+        H, I = self.cfg.hidden_size, self.cfg.moe_intermediate_size
+        u8, f32, d = torch.uint8, torch.float32, self.dev
+        t2 = torch.empty((1, I, H), dtype=u8, device=d)
+        moe_transpose_fp8_blocks(q2.unsqueeze(0), self.w2s[e:e + 1], t2, self.w2ts[e:e + 1])
+        moe_pack_fp8_weights(t2[0], self.w2t[e])
+        t13 = torch.empty((1, H, 2 * I), dtype=u8, device=d)
+        moe_transpose_fp8_blocks(q1.unsqueeze(0), self.w1s[e:e + 1], t13, self.w13ts[e:e + 1], col0=0)
+        moe_transpose_fp8_blocks(q3.unsqueeze(0), self.w3s[e:e + 1], t13, self.w13ts[e:e + 1], col0=I)
+        moe_pack_fp8_weights(t13[0], self.w13t[e])
 
     @staticmethod
     def unpack(packed: np.ndarray) -> np.ndarray:
@@ -73,11 +103,15 @@ class MoELayer:
         self.w_router = moe_pack_router_weights(
             torch.from_numpy(np.ascontiguousarray(w_router, np.float32)).to(self.dev))
         self.bias = torch.from_numpy(np.ascontiguousarray(bias, np.float32)).to(self.dev)
+        if self.backward_enabled:
+            self.w_router_f32 = torch.from_numpy(np.ascontiguousarray(w_router, np.float32)).to(self.dev)
 
         def put_routed(e, w):
-            self._quant_into(w[0], self.w1[e], self.w1s[e])
-            self._quant_into(w[1], self.w3[e], self.w3s[e])
-            self._quant_into(w[2], self.w2[e], self.w2s[e])
+            q1 = self._quant_into(w[0], self.w1[e], self.w1s[e])
+            q3 = self._quant_into(w[1], self.w3[e], self.w3s[e])
+            q2 = self._quant_into(w[2], self.w2[e], self.w2s[e])
+            if self.backward_enabled:
+                self._transposed_into(e, q1, q3, q2)
 
         def put_shared(s, w):
             put_routed(self.cfg.num_experts + s, w)
@@ -139,6 +173,7 @@ class MoELayer:
         EA, rows = N + S, T * (k + S)
         mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
         mark(0)
+        self.x = x
         moe_quantize_1x128(x, self.xq, self.xs, pow2=self.scale_mode == 1)
         mark(1)
         moe_route(c, x, self.w_router, self.bias, self.scores, self.topk_idx, self.topk_gate,
@@ -157,6 +192,60 @@ class MoELayer:
             moe_update_bias(c, T, self.counts, self.bias)
         mark(7)
         return self.out
+
+    # -- backward ------------------------------------------------------------------
+    BWD_STAGES = ("combine_bwd", "ffn_bwd", "route_bwd", "unpermute")
+
+    def _bwd_buffers(self, T: int):
+        if self._bT == T:
+            return
+        cfg, d = self.cfg, self.dev
+        H, I, N, k, S = (cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts,
+                         cfg.num_experts_per_tok, cfg.num_shared_experts)
+        EA, rows, f32 = N + S, T * (k + S), torch.float32
+        self.dy = torch.empty((rows, H), dtype=f32, device=d)
+        self.dgate = torch.empty((T, k), dtype=f32, device=d)
+        self.dx_rows = torch.empty((rows, H), dtype=f32, device=d)
+        self.dx_route = torch.empty((T, H), dtype=f32, device=d)
+        self.dx = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+        self.dw1 = torch.empty((EA, I, H), dtype=self.dw_dtype, device=d)
+        self.dw3 = torch.empty((EA, I, H), dtype=self.dw_dtype, device=d)
+        self.dw2 = torch.empty((EA, H, I), dtype=self.dw_dtype, device=d)
+        self.dw_router = torch.empty((N, H), dtype=f32, device=d)
+        self.bwd_ws = torch.empty((max(moe_grouped_ffn_backward_workspace_bytes(self.c, EA, rows), 1),),
+                                  dtype=torch.uint8, device=d)
+        self.route_bwd_ws = torch.empty((max(moe_route_backward_workspace_bytes(self.c, T), 1),),
+                                        dtype=torch.uint8, device=d)
+        self._bT = T
+
+    def backward(self, dout: torch.Tensor, events=None) -> torch.Tensor:
+        """Gradients of the last forward for upstream gradient dout [T, H] (bf16): returns
+        dx [T, H] bf16 (a reused buffer); weight gradients land in dw1, dw3 [E, I, H],
+        dw2 [E, H, I] (routed experts, then shared) and dw_router [N_r, H]."""
+        if not self.backward_enabled:
+            raise RuntimeError("MoELayer was built without backward=True")
+        cfg, c = self.cfg, self.c
+        T = dout.shape[0]
+        assert T == self._T, "backward needs the forward of the same batch"
+        self._bwd_buffers(T)
+        EA = cfg.num_experts + cfg.num_shared_experts
+        mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        mark(0)
+        moe_combine_backward(c, dout, self.y_rows, self.row_of, self.topk_gate, dy=self.dy,
+                             dgate=self.dgate)
+        mark(1)
+        moe_grouped_ffn_fp8_backward(c, EA, self.xq, self.xs, self.x, self.row_token, self.offsets,
+                                     self.w1, self.w1s, self.w3, self.w3s, self.w2t, self.w2ts,
+                                     self.w13t, self.w13ts, self.dy, dx_rows=self.dx_rows,
+                                     dw1=self.dw1, dw3=self.dw3, dw2=self.dw2, ws=self.bwd_ws)
+        mark(2)
+        moe_route_backward(c, self.x, self.w_router_f32, self.scores, self.topk_idx, self.dgate,
+                           self.offsets, self.row_token, self.row_of, dx=self.dx_route,
+                           dw_router=self.dw_router, ws=self.route_bwd_ws)
+        mark(3)
+        moe_unpermute_sum(c, self.dx_rows, self.row_of, extra=self.dx_route, out=self.dx)
+        mark(4)
+        return self.dx
 
     def seq_balance(self, seq_len: int, alpha: float = 0.001, with_entropy: bool = True):
         """Per-sequence balance loss and allocation entropy of the last forward's routing

@@ -335,6 +335,119 @@ moe_status moe_seq_balance(const moe_config* cfg, int64_t T, int64_t seq_len,
                            float* loss, float* entropy, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* ===================================================================================
+ * Backward pass ([guide] section 3: gemm_dgrad and gemm_wgrad run in FP8 e4m3 like
+ * gemm_fprop, moe_gating stays in BF16/FP32; [zhihu] training part: E4M3 in both
+ * directions, 1x128 / 128x128 groups, partial-sum promotion, SwiGLU recomputed).
+ * Quantisers are straight-through. Each FP8 GEMM quantises its operands along its own
+ * contraction axis: 1x128 tiles along H or I for dgrad, and 1x128 tiles along the token
+ * axis for wgrad (128 consecutive rows of one expert's segment per tile, from the
+ * segment's first row; the last tile may be shorter). Weights keep their 128x128 blocks.
+ * Scale rule everywhere: s = fl32(amax / 448) (1 for a zero group), codes =
+ * E4M3(fl32(v / s)). Call order for one layer: moe_combine_backward,
+ * moe_grouped_ffn_fp8_backward, moe_route_backward, moe_unpermute_sum.
+ * =================================================================================== */
+
+/*
+ * moe_combine_backward — gradient of the combine ([digest] section 3.2: out_t = shared
+ * rows + sum_j gate_tj y_{row_of[t,j]}).
+ *   dout      [T, H] bf16 bits: gradient of the layer output
+ *   y_rows    [T*(k+N_s), H] (yt = MOE_BF16 or MOE_F32): the forward's expert output rows
+ *   row_of, topk_gate: from the forward ([T, k] int32 / float)
+ *   dy        [T*(k+N_s), H] float, output: gate_tj * dout_t (one FP32 rounding) on routed
+ *             rows, dout_t on shared rows T*k + s*T + t; rows that no (token, slot) names
+ *             are not written
+ *   dgate     [T, k] float, output: sum_h dout_t[h] * y_row[h] (FP32, fixed order); 0 for a
+ *             slot with row -1
+ * Errors: NULL pointers (T > 0); invalid config; T < 0 or T >= 2^31; yt not BF16/F32.
+ */
+moe_status moe_combine_backward(const moe_config* cfg, int64_t T, const uint16_t* dout,
+                                const void* y_rows, moe_dtype yt, const int32_t* row_of,
+                                const float* topk_gate, float* dy, float* dgate, void* stream);
+
+/*
+ * moe_route_backward — gradient of the gates through the router, in FP32 ([digest]
+ * section 3.2: gate_j = rho * s_j / sum of the selected s, s = sigmoid(x . W_r^T); the
+ * bias and the group limit only select, so the selection carries no gradient).
+ *   ds_m = (rho / Z) (dgate_m - sum_j dgate_j gate_j / rho) for the selected m, Z = sum of
+ *   the selected s; dlogit = ds * s * (1 - s); dx = dlogit . W_r; dW_r[e] = sum over the
+ *   rows of e's segment (row order) of dlogit * x_token.
+ *   x [T, H] (xt), w_router [N_r, H] float (plain row-major), scores [T, N_r] (moe_route's
+ *   s), topk_idx [T, k], dgate [T, k], offsets / row_token / row_of from moe_permute.
+ *   dx        [T, H] float, output (the router's share of the input gradient)
+ *   dw_router [N_r, H] float, output
+ *   ws        moe_route_backward_workspace_bytes(cfg, T) bytes
+ * Errors: NULL pointers (T > 0; offsets and dw_router always); invalid config; T out of
+ * range (SHAPE); xt not BF16/F32 (DTYPE); workspace missing or small (WORKSPACE).
+ */
+size_t moe_route_backward_workspace_bytes(const moe_config* cfg, int64_t T);
+moe_status moe_route_backward(const moe_config* cfg, int64_t T, const void* x, moe_dtype xt,
+                              const float* w_router, const float* scores,
+                              const int32_t* topk_idx, const float* dgate,
+                              const int32_t* offsets, const int32_t* row_token,
+                              const int32_t* row_of, float* dx, float* dw_router, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * moe_unpermute_sum — input gradient per token from its permuted rows ([digest] section
+ * 3.2: each token's output sums its experts, so its input gradient sums theirs):
+ * out_t = bf16( sum_s rows[T*k + s*T + t] + sum_j rows[row_of[t, j]] + extra_t ), FP32 in
+ * that order. rows [T*(k+N_s), H] (rt = BF16/F32); extra [T, H] float or NULL; out [T, H]
+ * bf16 bits. Errors: NULL pointers (T > 0); invalid config; T out of range; bad rt.
+ */
+moe_status moe_unpermute_sum(const moe_config* cfg, int64_t T, const void* rows, moe_dtype rt,
+                             const int32_t* row_of, const float* extra, uint16_t* out,
+                             void* stream);
+
+/*
+ * moe_transpose_fp8_blocks — set-up for the dgrad GEMMs, which contract the weights over
+ * their other axis: dst[e][c][col0 + r] = src[e][r][c] for E4M3 codes ([E, R, C] ->
+ * rows of dst_cols), and each 128x128 block scale moves with its block:
+ * dst_scales[e][c/128][(col0 + r)/128] = src_scales[e][r/128][c/128]. The result is
+ * row-major codes for moe_pack_fp8_weights (W2^T: [E, I, H]; [W1^T | W3^T]: [E, H, 2I]
+ * from two calls with col0 = 0 and I).
+ * Errors: R, C, dst_cols, col0 not multiples of 128, col0 + R > dst_cols, E > 65535
+ * (SHAPE); NULL pointers.
+ */
+moe_status moe_transpose_fp8_blocks(int64_t E, int64_t R, int64_t C, const uint8_t* src,
+                                    const float* src_scales, uint8_t* dst, float* dst_scales,
+                                    int64_t dst_cols, int64_t col0, void* stream);
+
+/*
+ * moe_grouped_ffn_fp8_backward — backward of the grouped SwiGLU experts with FP8 GEMMs, on
+ * the same permuted rows and segments as moe_grouped_ffn_fp8 (routed then shared).
+ *   Recompute: a = xq W1^T, b = xq W3^T (FP8 fprop GEMMs on the forward's codes).
+ *   dgrad:     dh = dy W2 (dy in 1x128 tiles along H); dg = dh b silu'(a), du = dh silu(a)
+ *              (FP32); dx_rows = dg W1 + du W3 ([dg | du] in 1x128 tiles along I, one
+ *              GEMM over K = 2I with the packed [W1^T | W3^T]).
+ *   wgrad:     dW2 = dy^T h, dW1 = dg^T x, dW3 = du^T x with h = silu(a) b (FP32) and x
+ *              the layer input rows; every operand in 128-row tiles along the token axis.
+ *   Rows with row_token < 0 count as zero rows (their dy is ignored).
+ *   xq, xs       [T, H] u8 / [T, H/128] float: the forward's activation codes and scales
+ *   x            [T, H] (xt = BF16/F32): the layer input
+ *   w1, w3 (+s)  the forward's packed weights; w2t (+s): packed W2^T [E, I, H] with
+ *                scales [E, I/128, H/128]; w13t (+s): packed [W1^T | W3^T] [E, H, 2I]
+ *                with scales [E, H/128, 2I/128] (moe_transpose_fp8_blocks, then
+ *                moe_pack_fp8_weights)
+ *   dy           [n_rows, H] float (moe_combine_backward)
+ *   dx_rows      [n_rows, H] output (dxt = BF16/F32)
+ *   dw1, dw3     [E, I, H] and dw2 [E, H, I] outputs (dwt = BF16/F32): FP32-promoted
+ *                sums, written for every expert (zero for an expert without rows)
+ *   ws           moe_grouped_ffn_backward_workspace_bytes(cfg, E, n_rows) bytes
+ * Errors: NULL pointers; invalid config; scale_mode != 0 (UNSUPPORTED); E outside
+ * 1..1024, n_rows or T out of range (SHAPE); bad dtypes (DTYPE); workspace (WORKSPACE);
+ * n_rows * H or n_rows * 2I >= 2^32, H or 2I > 16384 (UNSUPPORTED).
+ */
+size_t moe_grouped_ffn_backward_workspace_bytes(const moe_config* cfg, int32_t n_experts,
+                                                int64_t n_rows);
+moe_status moe_grouped_ffn_fp8_backward(
+    const moe_config* cfg, int32_t n_experts, int64_t n_rows, int64_t n_tokens, const uint8_t* xq,
+    const float* xs, const void* x, moe_dtype xt, const int32_t* row_token, const int32_t* offsets,
+    const uint8_t* w1, const float* w1s, const uint8_t* w3, const float* w3s, const uint8_t* w2t,
+    const float* w2ts, const uint8_t* w13t, const float* w13ts, const float* dy, void* dx_rows,
+    moe_dtype dxt, void* dw1, void* dw3, void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes,
+    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

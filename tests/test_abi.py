@@ -30,7 +30,8 @@ def test_header_declares_the_six_calls():
     names = _declared()
     for n in ("moe_quantize_1x128", "moe_route", "moe_permute", "moe_grouped_ffn_fp8",
               "moe_grouped_ffn_fp8_gate_up", "moe_grouped_ffn_fp8_down", "moe_combine",
-              "moe_update_bias", "moe_seq_balance"):
+              "moe_update_bias", "moe_seq_balance", "moe_combine_backward", "moe_route_backward",
+              "moe_unpermute_sum", "moe_grouped_ffn_fp8_backward"):
         assert n in names
 
 
@@ -148,6 +149,42 @@ def test_host_validation_status_codes():
     assert sb(ctypes.byref(c), 1000, 100, fake, fake, 0.001, fake, None, P(0x1004), need_s, None) == 4
     assert sb(ctypes.byref(c), 0, 100, None, None, 0.001, None, None, None, 0, None) == 0
     assert sb(ctypes.byref(c), 1 << 30, 1, fake, fake, 0.001, fake, None, fake, 1 << 62, None) == 2
+    # backward entry points
+    assert L.moe_combine_backward(ctypes.byref(c), 4, None, fake, 1, fake, fake, fake, fake, None) == 1
+    assert L.moe_combine_backward(ctypes.byref(c), 4, fake, fake, 7, fake, fake, fake, fake, None) == 3
+    assert L.moe_combine_backward(ctypes.byref(c), -1, fake, fake, 1, fake, fake, fake, fake, None) == 2
+    assert L.moe_combine_backward(ctypes.byref(c), 0, None, None, 1, None, None, None, None, None) == 0
+    need_rb = L.moe_route_backward_workspace_bytes(ctypes.byref(c), 10)
+    assert need_rb >= 2 * 10 * 4 * 4
+    rb = L.moe_route_backward
+    assert rb(ctypes.byref(c), 10, fake, 1, fake, fake, fake, fake, fake, fake, fake, fake, None, None, 0,
+              None) == 1
+    assert rb(ctypes.byref(c), 10, fake, 1, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+              need_rb - 1, None) == 6
+    assert rb(ctypes.byref(c), 10, fake, 5, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+              need_rb, None) == 3
+    assert L.moe_unpermute_sum(ctypes.byref(c), 4, fake, 1, None, None, fake, None) == 1
+    assert L.moe_unpermute_sum(ctypes.byref(c), 4, fake, 9, fake, None, fake, None) == 3
+    tr = L.moe_transpose_fp8_blocks
+    assert tr(2, 128, 100, fake, fake, fake, fake, 128, 0, None) == 2
+    assert tr(2, 128, 128, fake, fake, fake, fake, 128, 128, None) == 2      # col0 + R > dst_cols
+    assert tr(2, 128, 128, None, fake, fake, fake, 256, 128, None) == 1
+    assert tr(0, 128, 128, None, None, None, None, 256, 0, None) == 0
+    need_fb = L.moe_grouped_ffn_backward_workspace_bytes(ctypes.byref(c), 4, 100)
+    assert need_fb > 100 * 256
+    fb = L.moe_grouped_ffn_fp8_backward
+    args15 = [fake] * 15
+    assert fb(ctypes.byref(c), 4, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 0, fake, fake, fake, 0,
+              fake, need_fb - 1, None) == 6
+    assert fb(ctypes.byref(c), 0, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 0, fake, fake, fake, 0,
+              fake, need_fb, None) == 2
+    assert fb(ctypes.byref(c), 4, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 5, fake, fake, fake, 0,
+              fake, need_fb, None) == 3
+    assert fb(ctypes.byref(c), 4, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 0, None, fake, fake, 0,
+              fake, need_fb, None) == 1
+    p2 = _cfg(m, scale_mode=1)
+    assert fb(ctypes.byref(p2), 4, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 0, fake, fake, fake, 0,
+              fake, need_fb, None) == 4
     # too large for 32-bit operand offsets
     big = _cfg(m, hidden=16384, inter=16384)
     assert L.moe_grouped_ffn_fp8_gate_up(ctypes.byref(big), 16, 1 << 18, 64, fake, fake, None,

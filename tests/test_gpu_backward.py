@@ -1,0 +1,311 @@
+"""Parity of the backward pass (HIP, through the C ABI) against the CPU oracle.
+
+Bit-exact: the weight transposition, dy (one FP32 product per element). Within stated
+tolerances: the gates' gradient and the router's gradients (FP32 sums against FP64), the
+FFN backward and the whole-layer gradients (FP8 GEMMs, normwise; see TOL).
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+# Both sides quantise the same operands at the same points, so they differ by
+#  - the FP8 MFMA's own 128-deep dot product, which is not exact: a probe of
+#    v_mfma_scale_f32_16x16x128_f8f6f4 measured |err| up to 2.9e-4 of sum |a_k b_k| (about
+#    2^-12; exact when all products share one binade), the limited accumulation precision
+#    that the per-128 FP32 promotion exists for;
+#  - and the E4M3 codes that this flips downstream, each worth up to one E4M3 step (2^-3
+#    relative) of its element: dh -> [dg | du] codes -> dx and the wgrad operands, and the
+#    forward's rows -> dgate.
+# Measured normwise: FFN backward <= 3.4e-3 per expert, whole layer 5-6e-3 (two chained
+# requantisations of GEMM outputs, against one in the forward's 5e-3 budget).
+TOL = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import deepseekmoe_routing_fp8_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def relerr(a, b):
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+
+
+def _cfg(**kw):
+    return dataclasses.replace(synth.PRESETS["tiny"], **kw)
+
+
+# ---------------------------------------------------------------------------------------
+# Weight transposition: bit-exact
+# ---------------------------------------------------------------------------------------
+def test_transpose_fp8_blocks_exact(lib):
+    rng = np.random.default_rng(1)
+    E, R, C = 3, 256, 384
+    q = rng.integers(0, 256, (E, R, C)).astype(np.uint8)
+    s = rng.uniform(0.1, 2, (E, R // 128, C // 128)).astype(np.float32)
+    dst = torch.zeros((E, C, 2 * R), dtype=torch.uint8, device=DEV)
+    dsts = torch.zeros((E, C // 128, 2 * R // 128), dtype=torch.float32, device=DEV)
+    say("transpose_fp8_blocks")
+    lib.moe_transpose_fp8_blocks(dev(q), dev(s), dst, dsts, col0=R)
+    torch.cuda.synchronize()
+    d, ds = host(dst), host(dsts)
+    assert np.array_equal(d[:, :, R:], q.transpose(0, 2, 1))
+    assert np.all(d[:, :, :R] == 0)
+    assert np.array_equal(ds[:, :, R // 128:], s.transpose(0, 2, 1))
+
+
+# ---------------------------------------------------------------------------------------
+# Combine backward
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,N,k,S,ydt", [(64, 256, 16, 4, 1, torch.bfloat16),
+                                            (300, 2048, 64, 6, 2, torch.float32),
+                                            (17, 7168, 256, 8, 1, torch.bfloat16)])
+def test_combine_backward_matches_oracle(lib, T, H, N, k, S, ydt):
+    rng = np.random.default_rng(T + H)
+    cfg = _cfg(tokens=T, hidden_size=H, num_experts=N, num_experts_per_tok=k, num_shared_experts=S)
+    c = lib.make_config(cfg)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(T)]).astype(np.int32)
+    _, _, row_of = oracle.permute(idx, N)
+    rows = T * (k + S)
+    y = rng.standard_normal((rows, H)).astype(np.float32)
+    if ydt == torch.bfloat16:
+        y = oracle.round_bf16(y)
+    gate = rng.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    dout = oracle.round_bf16(rng.standard_normal((T, H)).astype(np.float32))
+    say(f"combine_backward T={T} H={H} k={k} S={S} {ydt}")
+    dy, dgate = lib.moe_combine_backward(c, dev(dout, torch.bfloat16), dev(y, ydt), dev(row_of), dev(gate))
+    torch.cuda.synchronize()
+    rdy, rdg = oracle.combine_backward(dout, y, row_of, gate, S)
+    assert np.array_equal(host(dy).view(np.uint32), rdy.view(np.uint32))
+    # FP32 sum of H products against FP64: |err| <= ~H 2^-24 sum |terms|
+    bound = H * 2.0 ** -24 * (np.abs(dout).astype(np.float64) @ np.abs(y).T.astype(np.float64)).max()
+    assert np.max(np.abs(host(dgate) - rdg)) <= bound
+
+
+# ---------------------------------------------------------------------------------------
+# Router backward
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,N,k", [(64, 256, 16, 4), (1000, 2048, 64, 6), (256, 7168, 256, 8)])
+def test_route_backward_matches_oracle(lib, T, H, N, k):
+    rng = np.random.default_rng(T + N)
+    cfg = _cfg(tokens=T, hidden_size=H, num_experts=N, num_experts_per_tok=k, num_shared_experts=1)
+    c = lib.make_config(cfg)
+    x = oracle.round_bf16(rng.standard_normal((T, H)).astype(np.float32))
+    wr = (rng.standard_normal((N, H)) / np.sqrt(H)).astype(np.float32)
+    s = rng.uniform(0.01, 0.99, (T, N)).astype(np.float32)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(T)]).astype(np.int32)
+    offsets, row_token, row_of = oracle.permute(idx, N)
+    dgate = rng.standard_normal((T, k)).astype(np.float32)
+    rho = cfg.routed_scaling_factor
+    say(f"route_backward T={T} H={H} N={N} k={k}")
+    dx, dw = lib.moe_route_backward(c, dev(x, torch.bfloat16), dev(wr), dev(s), dev(idx), dev(dgate),
+                                    dev(offsets), dev(row_token), dev(row_of))
+    torch.cuda.synchronize()
+    r = oracle.route_backward(x, wr, s, idx, dgate, rho)
+    e1, e2 = relerr(host(dx), r["dx"]), relerr(host(dw), r["dw"])
+    say(f"  dx {e1:.2e}  dW_r {e2:.2e}")
+    assert e1 < 1e-5 and e2 < 1e-5
+
+
+# ---------------------------------------------------------------------------------------
+# Unpermute-sum
+# ---------------------------------------------------------------------------------------
+def test_unpermute_sum(lib):
+    rng = np.random.default_rng(3)
+    T, H, N, k, S = 100, 512, 32, 4, 2
+    cfg = _cfg(tokens=T, hidden_size=H, num_experts=N, num_experts_per_tok=k, num_shared_experts=S)
+    c = lib.make_config(cfg)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(T)]).astype(np.int32)
+    _, _, row_of = oracle.permute(idx, N)
+    rows = rng.standard_normal((T * (k + S), H)).astype(np.float32)
+    extra = rng.standard_normal((T, H)).astype(np.float32)
+    say("unpermute_sum")
+    out = lib.moe_unpermute_sum(c, dev(rows), dev(row_of), extra=dev(extra))
+    torch.cuda.synchronize()
+    ref = extra.astype(np.float64) + sum(rows[T * k + s * T:T * k + (s + 1) * T].astype(np.float64)
+                                         for s in range(S))
+    for j in range(k):
+        ref = ref + rows[row_of[:, j]]
+    # one bf16 rounding of an FP32 sum of k + S + 1 terms
+    bound = np.abs(ref) * 2.0 ** -8 + 1e-6 * (k + S + 1) * 4
+    assert np.all(np.abs(host(out) - ref) <= bound)
+
+
+# ---------------------------------------------------------------------------------------
+# Grouped FFN backward against the oracle, per expert
+# ---------------------------------------------------------------------------------------
+def _rand_codes(rng, shape):
+    q = rng.integers(0, 256, shape).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x3C        # no NaN codes
+    return q
+
+
+def _expert_set(rng, E, H, I):
+    out = []
+    for _ in range(E):
+        w1 = _rand_codes(rng, (I, H))
+        w3 = _rand_codes(rng, (I, H))
+        w2 = _rand_codes(rng, (H, I))
+        sc = lambda r, c: rng.uniform(0.5, 2.0, (r // 128, c // 128)).astype(np.float32) * 2.0 ** -9
+        out.append((w1, sc(I, H), w3, sc(I, H), w2, sc(H, I)))
+    return out
+
+
+def _device_weights(lib, ws, H, I):
+    """Packed forward weights and the packed dgrad operands, built on the device."""
+    E = len(ws)
+    st = lambda i: dev(np.stack([w[i] for w in ws]))
+    q1, s1, q3, s3, q2, s2 = (st(i) for i in range(6))
+    w1, w3, w2 = lib.moe_pack_fp8_weights(q1), lib.moe_pack_fp8_weights(q3), lib.moe_pack_fp8_weights(q2)
+    t2 = torch.empty((E, I, H), dtype=torch.uint8, device=DEV)
+    t2s = torch.empty((E, I // 128, H // 128), dtype=torch.float32, device=DEV)
+    lib.moe_transpose_fp8_blocks(q2, s2, t2, t2s)
+    t13 = torch.empty((E, H, 2 * I), dtype=torch.uint8, device=DEV)
+    t13s = torch.empty((E, H // 128, 2 * I // 128), dtype=torch.float32, device=DEV)
+    lib.moe_transpose_fp8_blocks(q1, s1, t13, t13s, col0=0)
+    lib.moe_transpose_fp8_blocks(q3, s3, t13, t13s, col0=I)
+    return (w1, s1, w3, s3, lib.moe_pack_fp8_weights(t2), t2s, lib.moe_pack_fp8_weights(t13), t13s)
+
+
+@pytest.mark.parametrize("H,I,loads,gaps", [
+    (256, 128, [0, 17, 200, 3], 0),
+    (512, 256, [300, 1, 129, 128], 5),
+    (7168, 2048, [256, 37, 140], 0),
+])
+def test_grouped_ffn_backward_matches_oracle(lib, H, I, loads, gaps):
+    rng = np.random.default_rng(H + sum(loads))
+    E = len(loads)
+    T = 96
+    cfg = _cfg(tokens=T, hidden_size=H, moe_intermediate_size=I, num_experts=max(E, 4),
+               num_experts_per_tok=4, num_shared_experts=0)
+    c = lib.make_config(cfg)
+    n_rows = sum(loads)
+    offsets = np.concatenate([[0], np.cumsum(loads)]).astype(np.int32)
+    row_token = rng.integers(0, T, n_rows).astype(np.int32)
+    if gaps:
+        row_token[rng.choice(n_rows, gaps, replace=False)] = -1
+    xq = _rand_codes(rng, (T, H))
+    xs = (rng.uniform(0.5, 2.0, (T, H // 128)) * 2.0 ** -6).astype(np.float32)
+    x = oracle.round_bf16(oracle.dequant_1x128(xq, xs).astype(np.float32)
+                          * rng.uniform(0.9, 1.1, (T, H)).astype(np.float32))
+    dy = (rng.standard_normal((n_rows, H)) * 0.01).astype(np.float32)
+    ws = _expert_set(rng, E, H, I)
+    say(f"ffn_backward H={H} I={I} loads={loads} gaps={gaps}")
+    w = _device_weights(lib, ws, H, I)
+    dxr, dw1, dw3, dw2 = lib.moe_grouped_ffn_fp8_backward(
+        c, E, dev(xq), dev(xs), dev(x, torch.bfloat16), dev(row_token), dev(offsets), *w, dev(dy))
+    torch.cuda.synchronize()
+    dxr, dw1, dw3, dw2 = host(dxr), host(dw1), host(dw3), host(dw2)
+    live = row_token >= 0
+    worst = 0.0
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            assert not np.any(dw1[e]) and not np.any(dw3[e]) and not np.any(dw2[e])
+            continue
+        tok = np.where(live[lo:hi], row_token[lo:hi], 0)
+        m = live[lo:hi][:, None]
+        aq = np.where(m, xq[tok], 0).astype(np.uint8)
+        a_s = np.where(m, xs[tok], 0).astype(np.float32)
+        xr = np.where(m, x[tok], 0).astype(np.float32)
+        dyr = np.where(m, dy[lo:hi], 0).astype(np.float32)
+        b = oracle.expert_ffn_backward(aq, a_s, xr, *ws[e], dyr)
+        errs = [relerr(dxr[lo:hi], b["dx"]), relerr(dw1[e], b["dw1"]), relerr(dw3[e], b["dw3"]),
+                relerr(dw2[e], b["dw2"])]
+        say(f"  expert {e} rows {hi - lo}: dx {errs[0]:.2e} dW1 {errs[1]:.2e} dW3 {errs[2]:.2e} "
+            f"dW2 {errs[3]:.2e}")
+        worst = max(worst, *errs)
+        assert np.all(dxr[lo:hi][~live[lo:hi]] == 0)
+    assert worst < TOL
+
+
+# ---------------------------------------------------------------------------------------
+# Whole layer backward
+# ---------------------------------------------------------------------------------------
+def _q3(w):
+    return (*oracle.quantize_128x128(w[0]), *oracle.quantize_128x128(w[1]), *oracle.quantize_128x128(w[2]))
+
+
+@pytest.mark.parametrize("name,tokens", [("tiny", None), ("reduced", 512)])
+def test_layer_backward_matches_oracle(lib, name, tokens):
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    cfg = synth.PRESETS[name]
+    if tokens:
+        cfg = cfg.with_tokens(tokens)
+    T, H = cfg.tokens, cfg.hidden_size
+    N, k, S = cfg.num_experts, cfg.num_experts_per_tok, cfg.num_shared_experts
+    say(f"layer backward {name} T={T}: loading weights")
+    layer = MoELayer(cfg, backward=True)
+    layer.load_from_synth()
+    x = synth.hidden_states(cfg)
+    xd = torch.from_numpy(x).to(torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32).cuda()
+    x_used = xd.float().cpu().numpy()
+    b0 = synth.expert_bias(cfg)
+    dout = oracle.round_bf16(np.random.default_rng(5).standard_normal((T, H)).astype(np.float32))
+    layer.forward(xd, update_bias=False)
+    dx = layer.backward(dev(dout, torch.bfloat16))
+    torch.cuda.synchronize()
+    g_idx = layer.topk_idx.cpu().numpy()
+    wr = synth.router_weight(cfg)
+    routed = [_q3(synth.routed_expert_weights(cfg, e)) for e in range(N)]
+    shared = [_q3(synth.shared_expert_weights(cfg, s)) for s in range(S)]
+    fwd = oracle.layer_forward(x_used, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s])
+    r = fwd["route"]
+    tie = (r["kth_gap"] < 1e-6) | (r["group_gap"] < 1e-6)
+    diff = np.any(g_idx != r["idx"], axis=1)
+    assert not np.any(diff & ~tie)
+    if np.any(diff):   # an equally valid near-tie choice: evaluate the oracle on it
+        fwd = oracle.layer_forward(x_used, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s],
+                                   force_idx=g_idx)
+    say(f"layer backward {name}: oracle")
+    bw = oracle.layer_backward(x_used, wr, cfg, fwd, lambda e: routed[e], lambda s: shared[s], dout)
+    e_dx = relerr(host(dx), bw["dx"])
+    # the parts: expert rows summed per token (FP32, before the bf16 rounding), router
+    dxr = host(layer.dx_rows)
+    row_of = fwd["row_of"]
+    part = sum(dxr[T * k + s_ * T:T * k + (s_ + 1) * T] for s_ in range(S)) + sum(
+        dxr[row_of[:, j]] for j in range(k))
+    e_part = relerr(part, bw["dx_experts"])
+    e_route = relerr(host(layer.dx_route), bw["route"]["dx"])
+    e_dg = relerr(host(layer.dgate), bw["dgate"])
+    say(f"  parts: expert dx {e_part:.2e}, router dx {e_route:.2e}, dgate {e_dg:.2e}, "
+        f"|router dx|/|dx| {np.linalg.norm(bw['route']['dx']) / np.linalg.norm(bw['dx']):.3f}")
+    e_r = relerr(host(layer.dw_router), bw["dw_router"])
+    g1, g3, g2 = host(layer.dw1), host(layer.dw3), host(layer.dw2)
+    num = den = 0.0
+    for e in range(N + S):
+        if bw["dw"][e] is None:
+            assert not np.any(g1[e]) and not np.any(g2[e])
+            continue
+        for got, ref in zip((g1[e], g3[e], g2[e]), bw["dw"][e]):
+            num += float(np.sum((got - ref) ** 2))
+            den += float(np.sum(ref ** 2))
+    e_w = float(np.sqrt(num / den))
+    say(f"layer backward {name}: dx {e_dx:.2e}, expert dW {e_w:.2e}, dW_r {e_r:.2e}")
+    assert e_dx < TOL and e_w < TOL and e_r < TOL
