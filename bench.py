@@ -169,6 +169,52 @@ def device_batches(cfg, n: int):
     return [torch.from_numpy(synth.hidden_states(cfg, step=i)).to(dt).cuda() for i in range(n)]
 
 
+def measure_backward(layer, cfg, x, steps: int, warmup: int):
+    """Times ``steps`` training steps (forward, then the FP8 backward of a seeded bf16
+    upstream gradient; weight gradients in FP32) on one device batch; per-stage spans of
+    the backward from HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    T, H, I = cfg.tokens, cfg.hidden_size, cfg.moe_intermediate_size
+    k, S, N = cfg.num_experts_per_tok, cfg.num_shared_experts, cfg.num_experts
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    dout = torch.randn((T, H), generator=g).to(torch.bfloat16).cuda()
+    for _ in range(warmup):
+        layer.forward(x, update_bias=False)
+        layer.backward(dout)
+    torch.cuda.synchronize()
+    nb = len(MoELayer.BWD_STAGES)
+    fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    be = [[torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fe[i][0].record()
+        layer.forward(x, update_bias=False)
+        fe[i][1].record()
+        layer.backward(dout, events=be[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = float(np.mean([a.elapsed_time(b) for a, b in fe]))
+    bwd = float(np.mean([e[0].elapsed_time(e[-1]) for e in be]))
+    st = {s_: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in be]))
+          for j, s_ in enumerate(MoELayer.BWD_STAGES)}
+    rows = T * (k + S)
+    # FP8 GEMM work of the backward: recomputed a and b, dh, dx over K = 2I, three wgrads
+    flops = 16.0 * rows * H * I
+    dw_bytes = 3 * (N + S) * H * I * 4
+    return {"tokens": T, "steps": steps, "train_step_ms": round(wall * 1e3 / steps, 4),
+            "train_tokens_per_s": round(T * steps / wall, 1), "forward_ms": round(fwd, 4),
+            "backward_ms": round(bwd, 4), "backward_stage_ms": {k_: round(v, 4) for k_, v in st.items()},
+            "backward_fp8_tflops": round(flops / (bwd * 1e-3) / 1e12, 1),
+            "ffn_backward_fp8_tflops": round(flops / (st["ffn_bwd"] * 1e-3) / 1e12, 1),
+            "weight_grad_bytes_f32": dw_bytes,
+            "note": ("forward + FP8 backward (dgrad and wgrad in E4M3, weight gradients FP32); "
+                     "no optimizer")}
+
+
 def time_seq_balance(layer, cfg, seq_len: int, calls: int = 20):
     """Time moe_seq_balance on the layer's last routing (sequences of seq_len tokens)."""
     import numpy as np
@@ -226,6 +272,14 @@ def other_configs(layer, warmup: int, decode_steps: int):
         res["pow2_scales"] = measure(p2, cfg, device_batches(cfg, 1), 30, warmup)
         res["pow2_scales"]["note"] = ("opt-in variant (scale_mode 1): power-of-two 1x128 / 128x128 "
                                       "scales applied by the MFMA, FP32 accumulation across K")
+        del p2
+        # forward + FP8 backward on the headline workload (its own layer with the dgrad
+        # operands and FP32 weight-gradient buffers)
+        log("[bench] backward: weights and transposed dgrad operands on the device")
+        bl = MoELayer(cfg, backward=True)
+        bl.load_from_synth()
+        res["backward"] = measure_backward(bl, cfg, device_batches(cfg, 1)[0], 10, 2)
+        del bl
     return res
 
 
@@ -237,6 +291,9 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time forward + backward of the workload instead of the forward line "
+                         "(for profiling the backward kernels)")
     ap.add_argument("--seq-len", type=int, default=0,
                     help="also time the per-sequence balance statistic on the last step's "
                          "routing, over sequences of this many tokens (0: only in the extras)")
@@ -265,11 +322,16 @@ def main():
                      cfg.num_experts_per_tok, cfg.num_shared_experts)
     log(f"[bench] {cfg.name}: generating and quantising weights on the device")
     t0 = time.time()
-    layer = MoELayer(cfg)
+    layer = MoELayer(cfg, backward=args.backward_only)
     layer.load_from_synth()
     x = torch.from_numpy(synth.hidden_states(cfg)).to(
         torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32).cuda()
     log(f"[bench] weights ready in {time.time() - t0:.1f} s; warmup {args.warmup}")
+    if args.backward_only:
+        r = measure_backward(layer, cfg, x, args.steps, args.warmup)
+        r.update({"workload": cfg.name, "dtype": "fp8-e4m3 GEMMs, fp32 accumulation"})
+        print(json.dumps(r), flush=True)
+        return
     for _ in range(args.warmup):
         layer.forward(x)
     torch.cuda.synchronize()
