@@ -439,76 +439,96 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__
 // wgrad: out_e[n][m] = sum over expert e's padded rows p of A_T[n][p] B_T[m][p], FP8 E4M3
 // operands in 128-row tiles along p with scales chunk-major (sa[g][n], sb[g][m]); each
 // 128-row chunk is one MFMA per 16x16 block, promoted in FP32 by sa[n] sb[m]. A 256-thread
-// workgroup computes a 128x128 output tile, each wave a 64x64 quarter (4x4 blocks).
-// Workgroups are spread so that each XCD runs one contiguous range of (expert, tile)
-// pairs, keeping an expert's operands in one L2.
+// workgroup computes a 128 x kWgM output tile, each wave 64 x kWgM/2 (4 x kWJ blocks; at
+// 128 x 64 with four waves per SIMD it measured 7% slower: twice the A loads). The
+// MFMA takes B_T as its first operand, so a lane's four results are four consecutive m of
+// one n: one 16-byte store each (plain stores: measured non-temporal ones of this pattern,
+// half cache lines per row, at 60% of the plain rate).
 // ------------------------------------------------------------------------------------
+constexpr int kWJ = 4;              // 16-column blocks per wave
+constexpr int kWgM = 32 * kWJ;      // output columns per workgroup
+
 template <typename OT>
-__global__ __launch_bounds__(256) void wgrad_kernel(const uint8_t* __restrict__ at, const float* __restrict__ sa,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wgrad_kernel(const uint8_t* __restrict__ at, const float* __restrict__ sa,
                                                     const uint8_t* __restrict__ bt, const float* __restrict__ sb,
                                                     const int32_t* __restrict__ poff, int n_experts,
                                                     int NA, int NB, int64_t pstride,
                                                     OT* __restrict__ out) {
-  const int64_t tiles_e = (int64_t)(NA / kTile) * (NB / kTile);
-  const int64_t total = tiles_e * n_experts;
-  const int64_t per_xcd = (total + 7) / 8;
+  // A group is the NB/128 tiles that share one 128-row block of A_T. Group q runs on XCD
+  // q % 8, its tiles on consecutive slots there (the A rows stay in that L2), and each
+  // expert's groups spread over all XCDs, so a long segment (a shared expert) is split
+  // evenly instead of loading one XCD.
+  const int ga = NA / kTile, tg = NB / kWgM;
+  const int64_t groups = (int64_t)ga * n_experts;
   const int64_t L = blockIdx.x;
-  const int64_t id = (L % 8) * per_xcd + L / 8;
-  if (id >= total) return;
-  const int e = (int)(id / tiles_e);
-  const int64_t tt = id % tiles_e;
-  const int n0 = (int)(tt / (NB / kTile)) * kTile, m0 = (int)(tt % (NB / kTile)) * kTile;
+  const int64_t slot = L / 8;
+  const int64_t q = (L % 8) + 8 * (slot / tg);
+  if (q >= groups) return;
+  const int e = (int)(q / ga);
+  const int n0 = (int)(q % ga) * kTile, m0 = (int)(slot % tg) * kWgM;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * 64;
+  const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * (kWgM / 2);
   const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
-  const int lr = lane & 15, lk = (lane >> 4) * 32;
+  const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
 
-  v4f acc[4][4];
+  // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v
+  v4f acc[4][kWJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kWJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int ch = 0; ch < nch; ++ch) {
     const int64_t p = p0 + (int64_t)ch * kTile;
-    v8i A[4], B[4];
+    v8i A[4], B[kWJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4* pa = reinterpret_cast<const uint4*>(at + (int64_t)(wn + 16 * i + lr) * pstride + p + lk);
-      const uint4* pb = reinterpret_cast<const uint4*>(bt + (int64_t)(wm + 16 * i + lr) * pstride + p + lk);
-      const uint4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+      const uint4 a0 = pa[0], a1 = pa[1];
       A[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      B[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    }
+#pragma unroll
+    for (int j = 0; j < kWJ; ++j) {
+      const uint4* pb = reinterpret_cast<const uint4*>(bt + (int64_t)(wm + 16 * j + lr) * pstride + p + lk);
+      const uint4 b0 = pb[0], b1 = pb[1];
+      B[j] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
     }
     const int64_t g = p / kTile;
-    float4 sav[4];
-    float sbv[4];
+    float san[4];
+    float4 sbm[kWJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sav[i] = *reinterpret_cast<const float4*>(sa + g * NA + wn + 16 * i + 4 * (lane >> 4));
-      sbv[i] = sb[g * NB + wm + 16 * i + lr];
-    }
+    for (int i = 0; i < 4; ++i) san[i] = sa[g * NA + wn + 16 * i + lr];
+#pragma unroll
+    for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + wm + 16 * j + 4 * lg);
     const v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[i], B[j], z, 0, 0, 0, 127, 0, 127);
-        acc[i][j][0] = fmaf(d[0], sav[i].x * sbv[j], acc[i][j][0]);
-        acc[i][j][1] = fmaf(d[1], sav[i].y * sbv[j], acc[i][j][1]);
-        acc[i][j][2] = fmaf(d[2], sav[i].z * sbv[j], acc[i][j][2]);
-        acc[i][j][3] = fmaf(d[3], sav[i].w * sbv[j], acc[i][j][3]);
+      for (int j = 0; j < kWJ; ++j) {
+        // rows of the result: m (from B_T), columns: n (from A_T)
+        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[j], A[i], z, 0, 0, 0, 127, 0, 127);
+        acc[i][j][0] = fmaf(d[0], san[i] * sbm[j].x, acc[i][j][0]);
+        acc[i][j][1] = fmaf(d[1], san[i] * sbm[j].y, acc[i][j][1]);
+        acc[i][j][2] = fmaf(d[2], san[i] * sbm[j].z, acc[i][j][2]);
+        acc[i][j][3] = fmaf(d[3], san[i] * sbm[j].w, acc[i][j][3]);
       }
     }
   }
   OT* o = out + (int64_t)e * NA * NB;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        st_val(o, (int64_t)(wn + 16 * i + 4 * (lane >> 4) + v) * NB + wm + 16 * j + lr, acc[i][j][v]);
+    for (int j = 0; j < kWJ; ++j) {
+      const int64_t off = (int64_t)(wn + 16 * i + lr) * NB + wm + 16 * j + 4 * lg;
+      if constexpr (sizeof(OT) == 4) {
+        *reinterpret_cast<v4f*>(o + off) = acc[i][j];
+      } else {
+        typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+        const v2u pk = {pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+        *reinterpret_cast<v2u*>(o + off) = pk;
+      }
+    }
+  }
 }
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -780,21 +800,24 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
                        offsets, poff, chunk_e, (int)I, P, utt, uts);
   }
   // wgrad GEMMs (every expert's gradient written; zero for an expert without rows)
-  const int64_t tiles = (int64_t)n_experts * (H / kTile) * (I / kTile);
-  const unsigned gw = (unsigned)((tiles + 7) / 8 * 8);
+  // grid: 8 XCDs x ceil(groups / 8) groups x tiles per group
+  auto wgrid = [&](int64_t NA, int64_t NB) {
+    const int64_t groups = (NA / kTile) * n_experts;
+    return dim3((unsigned)(8 * ((groups + 7) / 8) * (NB / kWgM)));
+  };
   if (dwt == MOE_F32) {
-    hipLaunchKernelGGL(wgrad_kernel<float>, dim3(gw), dim3(256), 0, s, dyt, dyts, htt, hts, poff,
+    hipLaunchKernelGGL(wgrad_kernel<float>, wgrid(H, I), dim3(256), 0, s, dyt, dyts, htt, hts, poff,
                        n_experts, (int)H, (int)I, P, static_cast<float*>(dw2));
-    hipLaunchKernelGGL(wgrad_kernel<float>, dim3(gw), dim3(256), 0, s, gtt, gts, xtt, xts, poff,
+    hipLaunchKernelGGL(wgrad_kernel<float>, wgrid(I, H), dim3(256), 0, s, gtt, gts, xtt, xts, poff,
                        n_experts, (int)I, (int)H, P, static_cast<float*>(dw1));
-    hipLaunchKernelGGL(wgrad_kernel<float>, dim3(gw), dim3(256), 0, s, utt, uts, xtt, xts, poff,
+    hipLaunchKernelGGL(wgrad_kernel<float>, wgrid(I, H), dim3(256), 0, s, utt, uts, xtt, xts, poff,
                        n_experts, (int)I, (int)H, P, static_cast<float*>(dw3));
   } else {
-    hipLaunchKernelGGL(wgrad_kernel<uint16_t>, dim3(gw), dim3(256), 0, s, dyt, dyts, htt, hts, poff,
+    hipLaunchKernelGGL(wgrad_kernel<uint16_t>, wgrid(H, I), dim3(256), 0, s, dyt, dyts, htt, hts, poff,
                        n_experts, (int)H, (int)I, P, static_cast<uint16_t*>(dw2));
-    hipLaunchKernelGGL(wgrad_kernel<uint16_t>, dim3(gw), dim3(256), 0, s, gtt, gts, xtt, xts, poff,
+    hipLaunchKernelGGL(wgrad_kernel<uint16_t>, wgrid(I, H), dim3(256), 0, s, gtt, gts, xtt, xts, poff,
                        n_experts, (int)I, (int)H, P, static_cast<uint16_t*>(dw1));
-    hipLaunchKernelGGL(wgrad_kernel<uint16_t>, dim3(gw), dim3(256), 0, s, utt, uts, xtt, xts, poff,
+    hipLaunchKernelGGL(wgrad_kernel<uint16_t>, wgrid(I, H), dim3(256), 0, s, utt, uts, xtt, xts, poff,
                        n_experts, (int)I, (int)H, P, static_cast<uint16_t*>(dw3));
   }
   return launch_status();
