@@ -309,3 +309,105 @@ def test_layer_backward_matches_oracle(lib, name, tokens):
     e_w = float(np.sqrt(num / den))
     say(f"layer backward {name}: dx {e_dx:.2e}, expert dW {e_w:.2e}, dW_r {e_r:.2e}")
     assert e_dx < TOL and e_w < TOL and e_r < TOL
+
+
+@pytest.mark.timeout(900)
+def test_layer_backward_v3_prefill_sampled(lib):
+    """The V3 prefill layer in the benchmark's configuration (T = 4096, 256 routed + 1
+    shared expert, FP32 weight gradients). The oracle checks what it can compute one by
+    one: every token's routing, the gates' gradient and dx of sampled tokens (their
+    experts' rows only), and the weight gradients of the shared expert (all 4096 rows, 32
+    token tiles) and of one routed expert (all its rows)."""
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    cfg = synth.PRESETS["v3_prefill"]
+    T, H, k, S, N = cfg.tokens, cfg.hidden_size, cfg.num_experts_per_tok, cfg.num_shared_experts, cfg.num_experts
+    rho = cfg.routed_scaling_factor
+    say("V3 backward: generating, quantising and transposing 257 experts on the device")
+    layer = MoELayer(cfg, backward=True)
+    layer.load_from_synth()
+    x = synth.hidden_states(cfg)
+    xd = dev(x, torch.bfloat16)
+    xb = xd.float().cpu().numpy()
+    b0 = synth.expert_bias(cfg)
+    dout = oracle.round_bf16(np.random.default_rng(21).standard_normal((T, H)).astype(np.float32))
+    say("V3 backward: forward + backward")
+    layer.forward(xd, update_bias=False)
+    layer.backward(dev(dout, torch.bfloat16))
+    torch.cuda.synchronize()
+    g_idx = layer.topk_idx.cpu().numpy()
+    wr = synth.router_weight(cfg)
+    r = oracle.route(xb, wr, b0, k, cfg.n_group, cfg.topk_group, cfg.group_score_topn, rho)
+    tie = (r["kth_gap"] < 1e-6) | (r["group_gap"] < 1e-6)
+    diff = np.any(g_idx != r["idx"], axis=1)
+    assert not np.any(diff & ~tie)
+    offsets, row_token, row_of = oracle.permute(g_idx, N)
+    toks = np.array([0, 1234, T - 1])
+    toks = toks[~tie[toks]]
+    experts = sorted(set(g_idx[toks].ravel().tolist()))
+    heavy = int(np.argmax(np.diff(offsets)))
+    cache = {}
+    synth.map_experts(cfg, lambda e, w: cache.__setitem__(e, _q3(w)), sorted(set(experts + [heavy])))
+    sh = _q3(synth.shared_expert_weights(cfg, 0))
+    xq, xs = oracle.quantize_1x128(xb)
+    gate = np.asarray(oracle.route(xb, wr, b0, k, cfg.n_group, cfg.topk_group, cfg.group_score_topn, rho,
+                                   force_idx=g_idx)["gate"], dtype=np.float32)
+    slot_of_row = np.zeros(T * k, np.int64)
+    for j in range(k):
+        slot_of_row[row_of[:, j]] = j
+
+    def dy_rows(lo, hi):
+        """dy of permuted rows [lo, hi): gate * dout on routed rows, dout on shared rows."""
+        if lo >= T * k:
+            return dout[(lo - T * k) % T:(lo - T * k) % T + (hi - lo)]
+        tk = row_token[lo:hi]
+        return (gate[tk, slot_of_row[lo:hi]][:, None] * dout[tk]).astype(np.float32)
+
+    # sampled tokens: the gates' gradient (Cauchy-Schwarz bound on the forward rows'
+    # difference) and dx (their rows' dgrad plus the router's share)
+    g_dgate = host(layer.dgate)
+    g_dx = host(layer.dx)
+    ref_dx, got_dx = [], []
+    for t in toks:
+        ys, dxs, dg = [], np.zeros(H), np.zeros(k)
+        for j in range(k):
+            e = int(g_idx[t, j])
+            w = cache[e]
+            y = oracle.expert_ffn(xq[t:t + 1], xs[t:t + 1], *w)[0][0]
+            dg[j] = float(np.dot(dout[t].astype(np.float64), oracle.round_bf16(y.astype(np.float32))))
+            bw = oracle.expert_ffn_backward(xq[t:t + 1], xs[t:t + 1], xb[t:t + 1], *w,
+                                            (gate[t, j] * dout[t:t + 1]).astype(np.float32))
+            dxs += bw["dx"][0]
+            ys.append(y)
+        bsh = oracle.expert_ffn_backward(xq[t:t + 1], xs[t:t + 1], xb[t:t + 1], *sh, dout[t:t + 1])
+        dxs += bsh["dx"][0]
+        bound = 1e-2 * np.linalg.norm(dout[t]) * np.array([np.linalg.norm(v) for v in ys])
+        assert np.all(np.abs(g_dgate[t] - dg) <= bound), (t, g_dgate[t], dg)
+        rb = oracle.route_backward(xb[t:t + 1], wr, r["s"][t:t + 1], g_idx[t:t + 1], dg[None, :], rho)
+        ref_dx.append(dxs + rb["dx"][0])
+        got_dx.append(g_dx[t])
+    e_dx = relerr(np.array(got_dx), np.array(ref_dx))
+    say(f"  sampled tokens {toks.tolist()}: dx {e_dx:.2e}")
+    assert e_dx < TOL
+
+    # weight gradients of the shared expert and of the most loaded routed expert. The FP8
+    # wgrad of a routed expert is chaotic at the 1e-2 level: moving every gate by one
+    # float32 ulp (dy by ~1e-7) flips a few dy codes and moves the oracle's own dW1 by
+    # ~9e-3. The bound adds twice that measured sensitivity to TOL, so the GPU must be as
+    # close to the oracle as the oracle is to itself under a last-bit change of its input.
+    for e, w, lo, hi in ((N, sh, T * k, T * k + T), (heavy, cache[heavy], int(offsets[heavy]), int(offsets[heavy + 1]))):
+        tk = row_token[lo:hi] if e < N else np.arange(T)
+        dyr = dy_rows(lo, hi)
+        bw = oracle.expert_ffn_backward(xq[tk], xs[tk], xb[tk], *w, dyr)
+        if e < N:
+            g_up = np.nextafter(gate, np.float32(np.inf))
+            dyp = (g_up[tk, slot_of_row[lo:hi]][:, None] * dout[tk]).astype(np.float32)
+        else:   # shared rows carry dout itself: perturb dout by one bf16-free float32 ulp
+            dyp = np.nextafter(dyr, np.float32(np.inf))
+        bp = oracle.expert_ffn_backward(xq[tk], xs[tk], xb[tk], *w, dyp)
+        for name in ("dw1", "dw3", "dw2"):
+            floor = relerr(bp[name], bw[name])
+            err = relerr(host(getattr(layer, name)[e]), bw[name])
+            say(f"  expert {e} ({hi - lo} rows) {name}: {err:.2e} (oracle sensitivity {floor:.2e})")
+            assert err < TOL + 2 * floor
+    del layer
+    torch.cuda.empty_cache()
