@@ -47,6 +47,30 @@ __device__ __forceinline__ void st_val(T* p, int64_t i, float v) {
     reinterpret_cast<float*>(p)[i] = v;
 }
 
+// 8 consecutive values at p[i..i+8) (i a multiple of 8) as floats / stored from floats.
+template <typename T>
+__device__ __forceinline__ void ld8(const T* p, int64_t i, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ void st8(float* p, int64_t i, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 // Sum over the 256 threads of a block, one value per slot (k <= kMaxTopK slots), in a fixed
 // order: lanes by butterfly, then the four waves in order.
 __device__ __forceinline__ void block_sum_slots(float (&v)[kMaxTopK], int k, float* red,
@@ -92,17 +116,26 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
   float part[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) part[j] = 0.0f;
-  for (int c = threadIdx.x; c < H; c += 256) {
-    const float d = __uint_as_float((uint32_t)dout[t * H + c] << 16);
+  // 8 consecutive features per thread and step; every slot's row is read before any is
+  // used, so a step's loads are in flight together
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float d[8];
+    ld8(dout, t * H + c, d);
+    for (int s = 0; s < S; ++s) st8(dy, (T * k + s * T + t) * H + c, d);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k && rows[j] >= 0) {
         const int64_t o = (int64_t)rows[j] * H + c;
-        dy[o] = g[j] * d;
-        part[j] = fmaf(d, ld_val(y_rows, o), part[j]);
+        float y[8], v[8];
+        ld8(y_rows, o, y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[i] = g[j] * d[i];
+          part[j] = fmaf(d[i], y[i], part[j]);
+        }
+        st8(dy, o, v);
       }
     }
-    for (int s = 0; s < S; ++s) dy[(T * k + s * T + t) * H + c] = d;
   }
   block_sum_slots(part, k, red, res);
   if (threadIdx.x < k) dgate[t * k + threadIdx.x] = rows[threadIdx.x] >= 0 ? res[threadIdx.x] : 0.0f;
@@ -216,13 +249,32 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(const YT* __restrict
     rs[threadIdx.x] = (r >= 0 && r < n_rows) ? r : -1;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < H; c += 256) {
-    float acc = 0.0f;
-    for (int s = 0; s < S; ++s) acc += ld_val(rows, (T * k + s * T + t) * H + c);
-    for (int j = 0; j < k; ++j)
-      if (rs[j] >= 0) acc += ld_val(rows, (int64_t)rs[j] * H + c);
-    if (extra) acc += extra[t * H + c];
-    out[t * H + c] = f32_to_bf16(acc);
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float v[8];
+    for (int s = 0; s < S; ++s) {
+      ld8(rows, (T * k + s * T + t) * H + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    for (int j = 0; j < k; ++j) {
+      if (rs[j] >= 0) {
+        ld8(rows, (int64_t)rs[j] * H + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      }
+    }
+    if (extra) {
+      ld8(extra, t * H + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(out + t * H + c) = o;
   }
 }
 
@@ -269,26 +321,38 @@ __device__ __forceinline__ void quant_tile_wave(float v0, float v1, float& s, ui
 }
 
 // dy [rows, H] FP32 -> codes [rows, H] and scales chunk-major [H/128][rows]; rows without
-// a token (row_token < 0) quantise as zeros. One wave per 128-wide tile.
+// a token (row_token < 0) quantise as zeros. One workgroup per row; each wave takes every
+// fourth 128-wide tile, kQB tiles' loads in flight before any is quantised.
+constexpr int kQB = 8;
+
 __global__ __launch_bounds__(256) void quant_rows_kernel(const float* __restrict__ v,
                                                          const int32_t* __restrict__ row_token,
                                                          int64_t n_rows, int C,
                                                          uint8_t* __restrict__ q,
                                                          float* __restrict__ s_cm) {
-  const int lane = threadIdx.x & 63;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = blockIdx.x;
   const int nct = C / kTile;
-  if (tile >= n_rows * nct) return;
-  const int64_t r = tile / nct;
-  const int ct = (int)(tile % nct);
   const bool live = row_token == nullptr || row_token[r] >= 0;
-  const float* p = v + r * C + ct * kTile + 2 * lane;
-  const float2 x = live ? *reinterpret_cast<const float2*>(p) : make_float2(0.0f, 0.0f);
-  float s;
-  uint32_t c0, c1;
-  quant_tile_wave(x.x, x.y, s, c0, c1);
-  reinterpret_cast<uint16_t*>(q + r * C + ct * kTile)[lane] = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) s_cm[(int64_t)ct * n_rows + r] = s;
+  for (int t0 = wave; t0 < nct; t0 += 4 * kQB) {
+    float2 x[kQB];
+#pragma unroll
+    for (int u = 0; u < kQB; ++u) {
+      const int ct = min(t0 + 4 * u, nct - 1);
+      x[u] = *reinterpret_cast<const float2*>(v + r * C + ct * kTile + 2 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < kQB; ++u) {
+      const int ct = t0 + 4 * u;
+      if (ct < nct) {
+        float s;
+        uint32_t c0, c1;
+        quant_tile_wave(live ? x[u].x : 0.0f, live ? x[u].y : 0.0f, s, c0, c1);
+        reinterpret_cast<uint16_t*>(q + r * C + ct * kTile)[lane] = (uint16_t)(c0 | (c1 << 8));
+        if (lane == 0) s_cm[(int64_t)ct * n_rows + r] = s;
+      }
+    }
+  }
 }
 
 // Gather the forward's activation codes per permuted row: xg[r] = xq[row_token[r]] (zeros
@@ -392,6 +456,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__
                                                            uint8_t* __restrict__ qt,
                                                            float* __restrict__ s_cm) {
   __shared__ float amx[4][64];
+  __shared__ int64_t srow[kTile];   // source row of each of the chunk's rows, -1: zero
   const int64_t g = blockIdx.x;
   const int e = chunk_e[g];
   if (e < 0) return;
@@ -399,25 +464,36 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__
   const int c = blockIdx.y * 64 + cg;
   const int64_t first = offsets[e] + (g * kTile - poff[e]);   // permuted row of padded row 128 g
   const int64_t end = min((int64_t)offsets[e + 1], n_rows);
+  if (threadIdx.x < kTile) {
+    const int64_t r = first + threadIdx.x;
+    int64_t sr = -1;
+    if (r < end) {
+      if (MODE == 1) {
+        const int64_t t = row_token[r];
+        sr = (t >= 0 && t < src_rows) ? t : -1;
+      } else if (MODE == 2) {
+        sr = row_token[r] >= 0 ? r : -1;
+      } else {
+        sr = r;
+      }
+    }
+    srow[threadIdx.x] = sr;
+  }
+  __syncthreads();
+  // all 32 loads of a thread are issued before any is used (rows without a source read
+  // row 0 and are dropped)
+  const int cc = min(c, C - 1);
   float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int64_t sr = srow[rg * 32 + i];
+    v[i] = ld_val(src, (sr >= 0 ? sr : 0) * C + cc);
+  }
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const int64_t r = first + rg * 32 + i;
-    float x = 0.0f;
-    if (r < end && c < C) {
-      int64_t sr = r;
-      bool ok = true;
-      if (MODE == 1) {
-        sr = row_token[r];
-        ok = sr >= 0 && sr < src_rows;
-      } else if (MODE == 2) {
-        ok = row_token[r] >= 0;
-      }
-      if (ok) x = ld_val(src, sr * C + c);
-    }
-    v[i] = x;
-    m = fmaxf(m, fabsf(x));
+    v[i] = srow[rg * 32 + i] >= 0 ? v[i] : 0.0f;
+    m = fmaxf(m, fabsf(v[i]));
   }
   amx[rg][cg] = m;
   __syncthreads();
@@ -748,8 +824,8 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     r = ffn_plan_launch(offsets, n_experts, n_rows, plan, s);
     if (r != MOE_OK) return r;
     // dgrad of the down projection and the recomputed gate/up inputs (K = H)
-    const int64_t ht = n_rows * (H / kTile), it = n_rows * (I / kTile);
-    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((ht + 3) / 4)), dim3(256), 0, s, dy, row_token,
+    const int64_t it = n_rows * (I / kTile);
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, dy, row_token,
                        n_rows, (int)H, dyq, dys);
     hipLaunchKernelGGL(gather_codes_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, xq, xs, row_token,
                        n_tokens, n_rows, (int)H, xg, xgs);
