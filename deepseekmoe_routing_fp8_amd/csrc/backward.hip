@@ -15,8 +15,8 @@
 //                      router GEMM and dW_r summed per expert in segment order;
 //   FFN backward       per expert segment, on the forward's tile plan:
 //     dy  -> 1x128 along H                  (dgrad operand)
-//     xq  -> gathered rows                  (recompute operand)
-//     a = xq W1^T, b = xq W3^T, dh = dy W2  (three FP8 grouped GEMMs, K = H, FP32 out)
+//     a = xq W1^T, b = xq W3^T              (the forward's gate/up launch, FP32 out)
+//     dh = dy W2                            (FP8 grouped GEMM, K = H, FP32 out)
 //     dg, du, h (FP32) -> [dg | du] 1x128 along I   (dgrad operand, K = 2I)
 //     dx_rows = [dg | du] [W1 ; W3]         (one FP8 grouped GEMM on [W1^T | W3^T])
 //     dy, h, dg, du, x  -> 128-row tiles along the token axis, stored transposed
@@ -355,24 +355,6 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const float* __restrict
   }
 }
 
-// Gather the forward's activation codes per permuted row: xg[r] = xq[row_token[r]] (zeros
-// for rows without a token) and their scales chunk-major [H/128][rows].
-__global__ __launch_bounds__(256) void gather_codes_kernel(const uint8_t* __restrict__ xq,
-                                                           const float* __restrict__ xs,
-                                                           const int32_t* __restrict__ row_token,
-                                                           int64_t T, int64_t n_rows, int H,
-                                                           uint8_t* __restrict__ xg,
-                                                           float* __restrict__ xs_cm) {
-  const int64_t r = blockIdx.x;
-  const int32_t t = row_token[r];
-  const bool ok = t >= 0 && t < T;
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  for (int u = threadIdx.x; u < H / 16; u += 256)
-    reinterpret_cast<uint4*>(xg + r * H)[u] = ok ? reinterpret_cast<const uint4*>(xq + (int64_t)t * H)[u] : z;
-  for (int c = threadIdx.x; c < H / kTile; c += 256)
-    xs_cm[(int64_t)c * n_rows + r] = ok ? xs[(int64_t)t * (H / kTile) + c] : 0.0f;
-}
-
 // SwiGLU backward on FP32 a, b, dh [rows, I], in place: a <- dg = dh b silu'(a),
 // b <- du = dh silu(a), dh <- h = silu(a) b; and [dg | du] quantised 1x128 along I into
 // codes [rows, 2I] with scales chunk-major [2I/128][rows]. One wave per 128-wide tile.
@@ -611,7 +593,7 @@ inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace of the FFN backward.
 struct BwdLayout {
-  size_t plan, dyq, dys, xg, xgs, fa, fb, fdh, q3, s3, poff, chunk_e, dyt, dyts, xt, xts, ht, hts,
+  size_t plan, dyq, dys, xgs, fa, fb, fdh, q3, s3, poff, chunk_e, dyt, dyts, xt, xts, ht, hts,
       gt, gts, ut, uts, total;
   int64_t max_chunks, pstride;
 };
@@ -631,7 +613,6 @@ inline BwdLayout bwd_layout(const moe_config* c, int32_t E, int64_t n_rows) {
   L.plan = take(ffn_plan_bytes(E, n_rows));
   L.dyq = take((size_t)n_rows * H);
   L.dys = take((size_t)n_rows * (H / kTile) * 4);
-  L.xg = take((size_t)n_rows * H);
   L.xgs = take((size_t)n_rows * (H / kTile) * 4);
   L.fa = take((size_t)n_rows * I * 4);
   L.fb = take((size_t)n_rows * I * 4);
@@ -807,7 +788,6 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   void* plan = base + L.plan;
   uint8_t* dyq = base + L.dyq;
   float* dys = reinterpret_cast<float*>(base + L.dys);
-  uint8_t* xg = base + L.xg;
   float* xgs = reinterpret_cast<float*>(base + L.xgs);
   float* fa = reinterpret_cast<float*>(base + L.fa);
   float* fb = reinterpret_cast<float*>(base + L.fb);
@@ -827,13 +807,8 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     const int64_t it = n_rows * (I / kTile);
     hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, dy, row_token,
                        n_rows, (int)H, dyq, dys);
-    hipLaunchKernelGGL(gather_codes_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, xq, xs, row_token,
-                       n_tokens, n_rows, (int)H, xg, xgs);
-    if ((r = ffn_grouped_gemm_launch(plan, n_experts, n_rows, xg, xgs, w1, w1s, (int)I, (int)H, fa,
-                                     MOE_F32, s)) != MOE_OK)
-      return r;
-    if ((r = ffn_grouped_gemm_launch(plan, n_experts, n_rows, xg, xgs, w3, w3s, (int)I, (int)H, fb,
-                                     MOE_F32, s)) != MOE_OK)
+    if ((r = ffn_recompute_launch(plan, n_experts, n_rows, n_tokens, xq, xs, row_token, w1, w1s, w3,
+                                  w3s, (int)H, (int)I, xgs, fa, fb, s)) != MOE_OK)
       return r;
     if ((r = ffn_grouped_gemm_launch(plan, n_experts, n_rows, dyq, dys, w2t, w2ts, (int)I, (int)H, fdh,
                                      MOE_F32, s)) != MOE_OK)

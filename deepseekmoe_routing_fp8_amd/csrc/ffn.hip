@@ -247,7 +247,8 @@ struct FfnArgs {
   int nb_per;            // n-blocks per workgroup (1..kMaxNbPerWg)
   uint8_t* hq;           // phase 1 outputs
   float* hs;
-  void* y;               // phase 2 output
+  void* y;               // phase 2 output; phase 3: a = x W1^T (FP32)
+  float* y2;             // phase 3: b = x W3^T (FP32)
 };
 
 // Activation rows in a slot: row r keeps its 16-byte segment seg at position seg ^ (r&7).
@@ -304,8 +305,9 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
                                          int wave, int lane, const FfnLds& sh) {
   static_assert(RING >= 3 && RING <= kMaxRing, "ring depth");
   static_assert(NT * 16 <= kMT, "tile rows");
+  constexpr bool GU = PHASE != 2;   // phases 1 and 3: the gate/up GEMMs (W1 and W3)
   const int tid = wave * kWave + lane;
-  const int K = PHASE == 1 ? a.H : a.I;
+  const int K = GU ? a.H : a.I;
   const int nkc = K / kTile;
   const int last = nkc - 1;
   const int nsteps = (nkc + RING - 1) / RING * RING;   // steps per n-block
@@ -333,12 +335,12 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   const int64_t per_expert = (int64_t)a.H * a.I;
   const int64_t frow = (int64_t)nkc * kFragBytes;   // bytes of one 16-row fragment row
   auto wrow_of = [&](int nb) -> int64_t {
-    return PHASE == 1 ? (int64_t)nb * kTile + wave * 16 : (int64_t)nb * 256 + wave * 32;
+    return GU ? (int64_t)nb * kTile + wave * 16 : (int64_t)nb * 256 + wave * 32;
   };
   auto wdesc = [&](int nb, int f) __attribute__((always_inline)) {
     const int64_t wrow = wrow_of(nb);
     const uint8_t* fb;
-    if (PHASE == 1) {
+    if (GU) {
       fb = (f == 0 ? a.wa : a.wb) + (int64_t)tl.e * per_expert + (wrow / 16) * frow;
     } else {
       // H % 256 == 128: the last block is half used; its idle waves read block 0
@@ -348,8 +350,8 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
     return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(fb), 0, (int)frow, 0x00020000);
   };
   constexpr int kWscRow = kMaxChunks + kMaxRing;
-  const int wsel0 = PHASE == 1 ? 0 : (wave >= 4 ? 1 : 0);   // scale row block of fragment 0
-  const int wsel1 = PHASE == 1 ? 1 : wsel0;
+  const int wsel0 = GU ? 0 : (wave >= 4 ? 1 : 0);   // scale row block of fragment 0
+  const int wsel1 = GU ? 1 : wsel0;
 
   // one chunk's loads, in a fixed order: 4 weight loads, kActDma activation copies, 1 scale.
   // Step g of n-block it loads chunk g of that block; chunks past the block's last one
@@ -468,7 +470,8 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   constexpr int kStageStores = (kMT * 8 + kFThreads - 1) / kFThreads;   // 16-byte units
   constexpr int kYStores = kMT * 32 / kFThreads;   // 16-byte units of a staged output block
   static_assert(kMT * 32 % (2 * kFThreads) == 0 && kNTS % 2 == 0, "whole store rounds per half");
-  constexpr int kEpiStores = PHASE == 1 ? kStageStores + 1 : (sizeof(YT) == 2 ? kYStores : 2 * NT);
+  constexpr int kEpiStores =
+      PHASE == 1 ? kStageStores + 1 : (PHASE == 3 || sizeof(YT) == 4 ? 2 * NT : kYStores);
   static_assert(RING < kMaxRing, "the last LDS slot stages the epilogue");
   constexpr int kWaitRing = (RING - 2) * kStepOps;
   static_assert(kWaitRing + kEpiStores <= 63, "vmcnt range");
@@ -574,6 +577,23 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
         const v4u v = *reinterpret_cast<const v4u*>(stage + rr * kTile + ((seg ^ (rr & 7)) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(v, qdesc, row * a.I + seg * 16, 0, 0);
       }
+    } else if (PHASE == 3) {
+      // a and b as FP32 rows (the recompute of the backward pass): this lane's four
+      // values are columns col .. col+3 of the block's 128 (the packed W1/W3 row order);
+      // rows past the tile fall outside the descriptors' ranges
+      const int col = 32 * (wave >> 1) + 8 * (lane >> 4) + 4 * (wave & 1);
+      const __amdgpu_buffer_rsrc_t adesc2 = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(static_cast<float*>(a.y) + (int64_t)tl.m0 * a.I + (int64_t)nb * kTile), 0,
+          tl.mlen * a.I * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t bdesc2 = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(a.y2 + (int64_t)tl.m0 * a.I + (int64_t)nb * kTile), 0, tl.mlen * a.I * 4,
+          0x00020000);
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int off = ((ts * 16 + (lane & 15)) * a.I + col) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc0[ts]), adesc2, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc1[ts]), bdesc2, off, 0, 0);
+      }
     } else {
       // rows past the tile fall outside the descriptor's range; the idle waves of a
       // half-used last block (H % 256 == 128) store past it as well
@@ -637,6 +657,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
 //            re-quantised 1x128 (amax over the 128 columns reduced across the 8
 //            waves through LDS).
 //   PHASE 2: 256 output features per workgroup.
+//   PHASE 3: phase 1's GEMMs with G and U written as FP32 rows (the backward's recompute).
 // Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD,
 // so the tile's activation rows are fetched into that XCD's L2 once.
 // ------------------------------------------------------------------------------------
@@ -655,6 +676,7 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   __shared__ float wsc[kMaxNbPerWg * 2][kWscRow];   // weight-block scales per n-block, row
                                                      // block and K chunk; 0 past the last chunk
   __shared__ float red[PHASE == 1 ? kFWaves * kMT : 1];
+  constexpr bool GU = PHASE != 2;
   const int L = blockIdx.x;
   const int xcd = L % kXcds, slot = L / kXcds;
   const int nwg = (a.n_nb + a.nb_per - 1) / a.nb_per;   // workgroups per tile
@@ -669,14 +691,14 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
     return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int K = PHASE == 1 ? a.H : a.I;
+  const int K = GU ? a.H : a.I;
   const int nkc = K / kTile;
 
   // source row of every tile row: a token (phase 1) or a permuted row (phase 2)
   for (int r = tid; r < kMT; r += kFThreads) {
     int t = -1;
     if (r < tl.mlen) {
-      if (PHASE == 1) {
+      if (GU) {
         const int64_t v = a.row_token ? (int64_t)a.row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
         t = (v >= 0 && v < a.n_tokens) ? (int)v : -1;
       } else {
@@ -687,13 +709,13 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   }
   // weight-block scales for every K chunk (0 past the last one) of each n-block: phase 1
   // (W1, W3) of row block nb; phase 2 the two W2 row blocks of the block's 256 rows
-  const int64_t nrb = (PHASE == 1 ? a.I : a.H) / kTile;
+  const int64_t nrb = (GU ? a.I : a.H) / kTile;
   for (int c = tid; c < nbn * 2 * kWscRow; c += kFThreads) {
     const int it = c / (2 * kWscRow), which = (c / kWscRow) & 1, kc = c % kWscRow;
     const int nb = nb0 + it;
     float v = 0.0f;
     if (kc >= nkc) {
-    } else if (PHASE == 1) {
+    } else if (GU) {
       v = (which == 0 ? a.wsa : a.wsb)[((int64_t)tl.e * nrb + nb) * nkc + kc];
     } else {
       const int64_t rb = min((int64_t)nb * 2 + which, nrb - 1);
@@ -912,6 +934,38 @@ moe_status ffn_grouped_gemm_launch(const void* plan, int32_t n_experts, int64_t 
     hipLaunchKernelGGL((ffn_kernel<2, uint16_t, false>), grid, dim3(kFThreads), 0, s, a);
   else
     hipLaunchKernelGGL((ffn_kernel<2, float, false>), grid, dim3(kFThreads), 0, s, a);
+  return launch_status();
+}
+
+moe_status ffn_recompute_launch(const void* plan, int32_t n_experts, int64_t n_rows,
+                                int64_t n_tokens, const uint8_t* xq, const float* xs,
+                                const int32_t* row_token, const uint8_t* w1, const float* w1s,
+                                const uint8_t* w3, const float* w3s, int H, int I, float* xsp,
+                                float* a_out, float* b_out, hipStream_t s) {
+  if (H <= 0 || I <= 0 || H % kTile || I % kTile || H > kMaxChunks * kTile) return MOE_ERR_SHAPE;
+  if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 1 || n_rows >= ((int64_t)1 << 31) ||
+      n_tokens < 0)
+    return MOE_ERR_SHAPE;
+  // per-lane operand offsets into xq and the chunk-major scales are 32-bit
+  if (n_tokens * (int64_t)H >= ((int64_t)1 << 32) || n_rows * (int64_t)(H / kTile) * 4 >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
+  const int64_t grid_tiles = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  const int n_nb = I / kTile;
+  const int64_t nwg = (n_nb + kNbPerWg1 - 1) / kNbPerWg1;
+  if (grid_tiles * nwg * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  const Tile* tiles = static_cast<const Tile*>(plan);
+  const int32_t* nt = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(plan) +
+                                                       align256((size_t)max_tiles * sizeof(Tile)));
+  if (n_tokens > 0)
+    hipLaunchKernelGGL(ffn_gather_scales_kernel,
+                       dim3((unsigned)max_tiles, (unsigned)((H / kTile + kGatherChunks - 1) / kGatherChunks)),
+                       dim3(kMT), 0, s, tiles, nt, (int)max_tiles, n_experts, (int)n_rows, xs, n_tokens,
+                       row_token, H / kTile, xsp);
+  FfnArgs a{tiles, nt, (int)max_tiles, n_experts, (int)n_rows, xq, xsp, n_tokens, row_token, w1, w1s,
+            w3, w3s, H, I, n_nb, kNbPerWg1, nullptr, nullptr, a_out, b_out};
+  hipLaunchKernelGGL((ffn_kernel<3, float, false>), dim3((unsigned)(grid_tiles * nwg)), dim3(kFThreads), 0,
+                     s, a);
   return launch_status();
 }
 

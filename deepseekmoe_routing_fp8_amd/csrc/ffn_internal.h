@@ -22,4 +22,14 @@ moe_status ffn_grouped_gemm_launch(const void* plan, int32_t n_experts, int64_t 
                                    const float* wsc, int N, int K, void* y, moe_dtype yt,
                                    hipStream_t s);
 
+// The gate/up GEMMs of the forward with their FP32 results kept: a = x W1^T and
+// b = x W3^T ([n_rows, I] each) for every planned tile, x gathered from xq by row_token
+// (rows without a token give zeros). xsp: scratch for the gathered scales, chunk-major
+// [H/128][n_rows].
+moe_status ffn_recompute_launch(const void* plan, int32_t n_experts, int64_t n_rows,
+                                int64_t n_tokens, const uint8_t* xq, const float* xs,
+                                const int32_t* row_token, const uint8_t* w1, const float* w1s,
+                                const uint8_t* w3, const float* w3s, int H, int I, float* xsp,
+                                float* a_out, float* b_out, hipStream_t s);
+
 }  // namespace moe
