@@ -193,12 +193,13 @@ def _device_weights(lib, ws, H, I):
     return (w1, s1, w3, s3, lib.moe_pack_fp8_weights(t2), t2s, lib.moe_pack_fp8_weights(t13), t13s)
 
 
-@pytest.mark.parametrize("H,I,loads,gaps", [
-    (256, 128, [0, 17, 200, 3], 0),
-    (512, 256, [300, 1, 129, 128], 5),
-    (7168, 2048, [256, 37, 140], 0),
+@pytest.mark.parametrize("H,I,loads,gaps,bf16", [
+    (256, 128, [0, 17, 200, 3], 0, False),
+    (512, 256, [300, 1, 129, 128], 5, False),
+    (7168, 2048, [256, 37, 140], 0, False),
+    (384, 256, [130, 0, 61], 3, True),      # bf16 dx rows and weight gradients
 ])
-def test_grouped_ffn_backward_matches_oracle(lib, H, I, loads, gaps):
+def test_grouped_ffn_backward_matches_oracle(lib, H, I, loads, gaps, bf16):
     rng = np.random.default_rng(H + sum(loads))
     E = len(loads)
     T = 96
@@ -218,8 +219,11 @@ def test_grouped_ffn_backward_matches_oracle(lib, H, I, loads, gaps):
     ws = _expert_set(rng, E, H, I)
     say(f"ffn_backward H={H} I={I} loads={loads} gaps={gaps}")
     w = _device_weights(lib, ws, H, I)
+    odt = torch.bfloat16 if bf16 else torch.float32
     dxr, dw1, dw3, dw2 = lib.moe_grouped_ffn_fp8_backward(
-        c, E, dev(xq), dev(xs), dev(x, torch.bfloat16), dev(row_token), dev(offsets), *w, dev(dy))
+        c, E, dev(xq), dev(xs), dev(x, torch.bfloat16), dev(row_token), dev(offsets), *w, dev(dy),
+        dx_dtype=odt, dw_dtype=odt)
+    assert dxr.dtype == odt and dw1.dtype == odt and dw2.dtype == odt
     torch.cuda.synchronize()
     dxr, dw1, dw3, dw2 = host(dxr), host(dw1), host(dw3), host(dw2)
     live = row_token >= 0
