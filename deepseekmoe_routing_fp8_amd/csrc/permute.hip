@@ -6,7 +6,8 @@
 // Three launches over blocks of kPB tokens:
 //   count   - per block, the expert histogram of its pairs (LDS atomics) -> ws[b][e];
 //   scan    - one workgroup: per expert, the exclusive prefix over blocks, then the
-//             exclusive prefix over experts (offsets); ws[b][e] becomes the first row
+//             exclusive prefix over experts (offsets, a wave-parallel scan); ws[b][e]
+//             becomes the first row
 //             of expert e's pairs from block b;
 //   scatter - per block, each pair's rank among the block's earlier pairs of the same
 //             expert: each wave ORs its lane bit into a per-(wave, expert) 64-bit mask,
@@ -69,13 +70,23 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(int32_t* __rest
     cnt[e] = run;
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < N; ++e) {
-      base[e] = run;
-      run += cnt[e];
+  // exclusive prefix over experts: per wave by lane shifts, then the wave totals in order
+  {
+    __shared__ int wtot[kScanThreads / kWave];
+    const int lane = tid & (kWave - 1), w = tid / kWave;
+    const int v = tid < N ? cnt[tid] : 0;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int u = __shfl_up(inc, d, kWave);
+      if (lane >= d) inc += u;
     }
-    base[N] = run;
+    if (lane == kWave - 1) wtot[w] = inc;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < w; ++i) before += wtot[i];
+    if (tid < N) base[tid] = before + inc - v;
+    if (tid == N - 1) base[N] = before + inc;
   }
   __syncthreads();
   for (int i = tid; i <= N; i += kScanThreads) offsets[i] = base[i];
