@@ -204,15 +204,14 @@ def measure_backward(layer, cfg, x, steps: int, warmup: int):
     rows = T * (k + S)
     # FP8 GEMM work of the backward: recomputed a and b, dh, dx over K = 2I, three wgrads
     flops = 16.0 * rows * H * I
-    dw_bytes = 3 * (N + S) * H * I * 4
+    dw_bytes = 3 * (N + S) * H * I * layer.dw_dtype.itemsize
     return {"tokens": T, "steps": steps, "train_step_ms": round(wall * 1e3 / steps, 4),
             "train_tokens_per_s": round(T * steps / wall, 1), "forward_ms": round(fwd, 4),
             "backward_ms": round(bwd, 4), "backward_stage_ms": {k_: round(v, 4) for k_, v in st.items()},
             "backward_fp8_tflops": round(flops / (bwd * 1e-3) / 1e12, 1),
             "ffn_backward_fp8_tflops": round(flops / (st["ffn_bwd"] * 1e-3) / 1e12, 1),
-            "weight_grad_bytes_f32": dw_bytes,
-            "note": ("forward + FP8 backward (dgrad and wgrad in E4M3, weight gradients FP32); "
-                     "no optimizer")}
+            "weight_grad_bytes": dw_bytes, "weight_grad_dtype": str(layer.dw_dtype).replace("torch.", ""),
+            "note": ("forward + FP8 backward (dgrad and wgrad in E4M3); no optimizer")}
 
 
 def time_seq_balance(layer, cfg, seq_len: int, calls: int = 20):
@@ -294,6 +293,8 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="time forward + backward of the workload instead of the forward line "
                          "(for profiling the backward kernels)")
+    ap.add_argument("--dw-dtype", default="f32", choices=("f32", "bf16"),
+                    help="weight-gradient dtype of the backward measurement")
     ap.add_argument("--seq-len", type=int, default=0,
                     help="also time the per-sequence balance statistic on the last step's "
                          "routing, over sequences of this many tokens (0: only in the extras)")
@@ -322,7 +323,8 @@ def main():
                      cfg.num_experts_per_tok, cfg.num_shared_experts)
     log(f"[bench] {cfg.name}: generating and quantising weights on the device")
     t0 = time.time()
-    layer = MoELayer(cfg, backward=args.backward_only)
+    layer = MoELayer(cfg, backward=args.backward_only,
+                     dw_dtype=torch.bfloat16 if args.dw_dtype == "bf16" else torch.float32)
     layer.load_from_synth()
     x = torch.from_numpy(synth.hidden_states(cfg)).to(
         torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32).cuda()
