@@ -1,7 +1,7 @@
 """Build libmoe_fp8.so (gfx950 only) from csrc/*.hip with hipcc.
 
 Usage: python deepseekmoe_routing_fp8_amd/build.py  (run as a file: importing the
-package would first load the library this builds).
+package would first load the library being built).
 Objects go to <repo>/_build/, the library next to this file. Also builds
 bench/ffn_counters, a native driver of the grouped FFN for profiler counter runs.
 """

@@ -836,8 +836,8 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
   const int H = cfg->hidden, I = cfg->inter;
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
                      (int)n_rows, (int)f.L.max_tiles, f.tiles, f.ntiles);
-  if (n_tokens > 0)
-    hipLaunchKernelGGL(ffn_gather_scales_kernel,
+  // also without tokens: every row's scale is then written as 0, never left undefined
+  hipLaunchKernelGGL(ffn_gather_scales_kernel,
                        dim3((unsigned)f.L.max_tiles, (unsigned)((H / kTile + kGatherChunks - 1) / kGatherChunks)),
                        dim3(kMT), 0, s,
                        f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xs, n_tokens,
@@ -957,8 +957,8 @@ moe_status ffn_recompute_launch(const void* plan, int32_t n_experts, int64_t n_r
   const Tile* tiles = static_cast<const Tile*>(plan);
   const int32_t* nt = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(plan) +
                                                        align256((size_t)max_tiles * sizeof(Tile)));
-  if (n_tokens > 0)
-    hipLaunchKernelGGL(ffn_gather_scales_kernel,
+  // also without tokens: every row's scale is then written as 0, never left undefined
+  hipLaunchKernelGGL(ffn_gather_scales_kernel,
                        dim3((unsigned)max_tiles, (unsigned)((H / kTile + kGatherChunks - 1) / kGatherChunks)),
                        dim3(kMT), 0, s, tiles, nt, (int)max_tiles, n_experts, (int)n_rows, xs, n_tokens,
                        row_token, H / kTile, xsp);

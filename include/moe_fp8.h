@@ -49,7 +49,7 @@ typedef enum moe_status {
   MOE_ERR_NULL = 1,        /* a required pointer is NULL                        */
   MOE_ERR_SHAPE = 2,       /* a size or config field is out of range            */
   MOE_ERR_DTYPE = 3,       /* unsupported dtype for this argument               */
-  MOE_ERR_UNSUPPORTED = 4, /* valid request this build does not implement       */
+  MOE_ERR_UNSUPPORTED = 4, /* valid request the library does not implement       */
   MOE_ERR_HIP = 5,         /* a HIP launch or runtime call failed               */
   MOE_ERR_WORKSPACE = 6    /* workspace NULL or smaller than the queried size   */
 } moe_status;
