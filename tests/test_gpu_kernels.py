@@ -211,7 +211,11 @@ def test_route_general_shapes(lib):
                dict(tokens=1), dict(tokens=130, num_experts=32, num_experts_per_tok=3),
                dict(tokens=300, num_experts=20, num_experts_per_tok=3, n_group=4, topk_group=2),
                dict(tokens=700, hidden_size=1024, num_experts=200, num_experts_per_tok=6, n_group=8,
-                    topk_group=3, group_score_topn=2)]:
+                    topk_group=3, group_score_topn=2),
+               # the largest configuration the library accepts: N_r = 512, k = 16, G = 64
+               dict(tokens=257, num_experts=512, num_experts_per_tok=16, n_group=64, topk_group=4,
+                    group_score_topn=2),
+               dict(tokens=100, hidden_size=512, num_experts=512, num_experts_per_tok=16)]:
         cfg = dataclasses.replace(base, **kw)
         say(f"route general {kw}")
         x = synth.hidden_states(cfg)
@@ -395,6 +399,9 @@ def _relerr(a, b):
     # every tile height the kernel specialises (2, 4, 6, 8, 9, 10 16-row tiles) on both
     # sides of its boundary, and the 160-row split into two tiles
     (256, 256, 12, [160, 161, 16, 17, 48, 80, 112, 113, 128, 129, 144, 145], False),
+    # the largest contraction the kernel takes: K = 16384 in each phase
+    (16384, 256, 2, [40, 7], False),
+    (256, 16384, 2, [33, 0], False),
 ])
 def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity):
     import dataclasses
@@ -481,7 +488,8 @@ def test_grouped_ffn_bf16_output_and_bad_tokens(lib):
 # ---------------------------------------------------------------------------------------
 # Combine and bias update
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("T,H,k,S", [(64, 256, 4, 1), (300, 2048, 6, 2), (17, 7168, 8, 1), (5, 128, 2, 0)])
+@pytest.mark.parametrize("T,H,k,S", [(64, 256, 4, 1), (300, 2048, 6, 2), (17, 7168, 8, 1), (5, 128, 2, 0),
+                                     (40, 512, 16, 16)])   # k and N_s at their maxima
 def test_combine_matches_oracle(lib, T, H, k, S):
     import dataclasses
     rng = np.random.default_rng(T * H)
