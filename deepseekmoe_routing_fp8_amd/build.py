@@ -3,7 +3,8 @@
 Usage: python deepseekmoe_routing_fp8_amd/build.py  (run as a file: importing the
 package would first load the library being built).
 Objects go to <repo>/_build/, the library next to this file. Also builds
-bench/ffn_counters, a native driver of the grouped FFN for profiler counter runs.
+bench/ffn_counters, a native driver of the grouped FFN for profiler counter runs, and
+bench/hbm_read, the plain streaming read that the HBM rooflines are compared with.
 """
 from __future__ import annotations
 
@@ -17,6 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoe_fp8.so")
 COUNTERS = os.path.join(PKG, "bench", "ffn_counters")
+HBM_READ = os.path.join(PKG, "bench", "hbm_read")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -53,6 +55,9 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, *FLAGS, COUNTERS + ".hip", "-L" + PKG, "-lmoe_fp8", "-Wl,-rpath,$ORIGIN/..",
           "-o", tmp])
     os.replace(tmp, COUNTERS)
+    tmp = HBM_READ + ".tmp"
+    _run([HIPCC, *FLAGS, HBM_READ + ".hip", "-o", tmp])
+    os.replace(tmp, HBM_READ)
     return LIB
 
 
