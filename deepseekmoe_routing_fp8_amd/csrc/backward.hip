@@ -526,10 +526,12 @@ __device__ __forceinline__ void wgrad_store(OT* o, int NB, int wn, int wm, int l
   }
 }
 
-// DUAL: two gradients that share B_T (dW1 = dg^T x and dW3 = du^T x) in one launch: each
+// SHARE 1: two gradients that share B_T (dW1 = dg^T x and dW3 = du^T x) in one launch: each
 // workgroup loads the B fragments once and runs both A operands against them (measured
 // 7.8 ms for the pair at the V3 shape against 2 x 5.0 ms for two launches).
-template <typename OT, bool DUAL>
+// SHARE 2: one gradient, two adjacent 128-column tiles per workgroup sharing the A
+// fragments (out2 unused; the second tile's columns start 128 after the first's).
+template <typename OT, int SHARE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wgrad_kernel(
     const uint8_t* __restrict__ at, const float* __restrict__ sa, const uint8_t* __restrict__ at2,
     const float* __restrict__ sa2, const uint8_t* __restrict__ bt, const float* __restrict__ sb,
@@ -539,70 +541,96 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   // q % 8, its tiles on consecutive slots there (the A rows stay in that L2), and each
   // expert's groups spread over all XCDs, so a long segment (a shared expert) is split
   // evenly instead of loading one XCD.
-  const int ga = NA / kTile, tg = NB / kWgM;
+  constexpr int kSpan = SHARE == 2 ? 2 * kWgM : kWgM;   // output columns per workgroup
+  const int ga = NA / kTile, tg = NB / kSpan;
   const int64_t groups = (int64_t)ga * n_experts;
   const int64_t L = blockIdx.x;
   const int64_t slot = L / 8;
   const int64_t q = (L % 8) + 8 * (slot / tg);
   if (q >= groups) return;
   const int e = (int)(q / ga);
-  const int n0 = (int)(q % ga) * kTile, m0 = (int)(slot % tg) * kWgM;
+  const int n0 = (int)(q % ga) * kTile, m0 = (int)(slot % tg) * kSpan;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * (kWgM / 2);
   const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
   const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
 
-  // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v (acc2: the second gradient)
+  // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v; acc2: the second gradient
+  // (SHARE 1) or the columns 128 further on (SHARE 2)
   v4f acc[4][kWJ], acc2[4][kWJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < kWJ; ++j) acc[i][j] = acc2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int ch = 0; ch < nch; ++ch) {
-    const int64_t p = p0 + (int64_t)ch * kTile;
-    const int64_t g = p / kTile;
-    v8i B[kWJ];
-    float4 sbm[kWJ];
+  auto load_a = [&](const uint8_t* aa, const float* ss, int64_t p, int64_t g, v8i (&A)[4],
+                    float (&san)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4* pa = reinterpret_cast<const uint4*>(aa + (int64_t)(wn + 16 * i + lr) * pstride + p + lk);
+      const uint4 a0 = pa[0], a1 = pa[1];
+      A[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      san[i] = ss[g * NA + wn + 16 * i + lr];
+    }
+  };
+  auto load_b = [&](int mb, int64_t p, int64_t g, v8i (&B)[kWJ], float4 (&sbm)[kWJ])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kWJ; ++j) {
-      const uint4* pb = reinterpret_cast<const uint4*>(bt + (int64_t)(wm + 16 * j + lr) * pstride + p + lk);
+      const uint4* pb = reinterpret_cast<const uint4*>(bt + (int64_t)(mb + 16 * j + lr) * pstride + p + lk);
       const uint4 b0 = pb[0], b1 = pb[1];
       B[j] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
     }
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + wm + 16 * j + 4 * lg);
+    for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + mb + 16 * j + 4 * lg);
+  };
+  auto mma = [&](const v8i (&A)[4], const float (&san)[4], const v8i (&B)[kWJ],
+                 const float4 (&sbm)[kWJ], v4f (&ac)[4][kWJ]) __attribute__((always_inline)) {
     const v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int pass = 0; pass < (DUAL ? 2 : 1); ++pass) {
-      const uint8_t* aa = pass ? at2 : at;
-      const float* ss = pass ? sa2 : sa;
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < kWJ; ++j) {
+        // rows of the result: m (from B_T), columns: n (from A_T)
+        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[j], A[i], z, 0, 0, 0, 127, 0, 127);
+        ac[i][j][0] = fmaf(d[0], san[i] * sbm[j].x, ac[i][j][0]);
+        ac[i][j][1] = fmaf(d[1], san[i] * sbm[j].y, ac[i][j][1]);
+        ac[i][j][2] = fmaf(d[2], san[i] * sbm[j].z, ac[i][j][2]);
+        ac[i][j][3] = fmaf(d[3], san[i] * sbm[j].w, ac[i][j][3]);
+      }
+    }
+  };
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int64_t p = p0 + (int64_t)ch * kTile;
+    const int64_t g = p / kTile;
+    if constexpr (SHARE == 2) {
       v8i A[4];
       float san[4];
+      load_a(at, sa, p, g, A, san);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4* pa = reinterpret_cast<const uint4*>(aa + (int64_t)(wn + 16 * i + lr) * pstride + p + lk);
-        const uint4 a0 = pa[0], a1 = pa[1];
-        A[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        san[i] = ss[g * NA + wn + 16 * i + lr];
+      for (int pass = 0; pass < 2; ++pass) {
+        v8i B[kWJ];
+        float4 sbm[kWJ];
+        load_b(wm + pass * kWgM, p, g, B, sbm);
+        mma(A, san, B, sbm, pass ? acc2 : acc);
       }
+    } else {
+      v8i B[kWJ];
+      float4 sbm[kWJ];
+      load_b(wm, p, g, B, sbm);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < kWJ; ++j) {
-          // rows of the result: m (from B_T), columns: n (from A_T)
-          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[j], A[i], z, 0, 0, 0, 127, 0, 127);
-          v4f& ac = pass ? acc2[i][j] : acc[i][j];
-          ac[0] = fmaf(d[0], san[i] * sbm[j].x, ac[0]);
-          ac[1] = fmaf(d[1], san[i] * sbm[j].y, ac[1]);
-          ac[2] = fmaf(d[2], san[i] * sbm[j].z, ac[2]);
-          ac[3] = fmaf(d[3], san[i] * sbm[j].w, ac[3]);
-        }
+      for (int pass = 0; pass < (SHARE == 1 ? 2 : 1); ++pass) {
+        v8i A[4];
+        float san[4];
+        load_a(pass ? at2 : at, pass ? sa2 : sa, p, g, A, san);
+        mma(A, san, B, sbm, pass ? acc2 : acc);
       }
     }
   }
   wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc);
-  if constexpr (DUAL) wgrad_store(out2 + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc2);
+  if constexpr (SHARE == 1) wgrad_store(out2 + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc2);
+  if constexpr (SHARE == 2) wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm + kWgM, lr, lg, acc2);
 }
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -868,22 +896,34 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   }
   // wgrad GEMMs (every expert's gradient written; zero for an expert without rows)
   // grid: 8 XCDs x ceil(groups / 8) groups x tiles per group
-  auto wgrid = [&](int64_t NA, int64_t NB) {
+  auto wgrid = [&](int64_t NA, int64_t NB, int64_t span) {
     const int64_t groups = (NA / kTile) * n_experts;
-    return dim3((unsigned)(8 * ((groups + 7) / 8) * (NB / kWgM)));
+    return dim3((unsigned)(8 * ((groups + 7) / 8) * (NB / span)));
   };
+  // dW2 pairs adjacent column tiles when I allows (I % 256 == 0)
+  const bool pair = I % (2 * kWgM) == 0;
   if (dwt == MOE_F32) {
-    hipLaunchKernelGGL((wgrad_kernel<float, false>), wgrid(H, I), dim3(256), 0, s, dyt, dyts, nullptr,
-                       nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P, static_cast<float*>(dw2),
-                       nullptr);
-    hipLaunchKernelGGL((wgrad_kernel<float, true>), wgrid(I, H), dim3(256), 0, s, gtt, gts, utt, uts,
+    if (pair)
+      hipLaunchKernelGGL((wgrad_kernel<float, 2>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts,
+                         nullptr, nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P,
+                         static_cast<float*>(dw2), nullptr);
+    else
+      hipLaunchKernelGGL((wgrad_kernel<float, 0>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
+                         nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P, static_cast<float*>(dw2),
+                         nullptr);
+    hipLaunchKernelGGL((wgrad_kernel<float, 1>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts,
                        xtt, xts, poff, n_experts, (int)I, (int)H, P, static_cast<float*>(dw1),
                        static_cast<float*>(dw3));
   } else {
-    hipLaunchKernelGGL((wgrad_kernel<uint16_t, false>), wgrid(H, I), dim3(256), 0, s, dyt, dyts, nullptr,
-                       nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P, static_cast<uint16_t*>(dw2),
-                       nullptr);
-    hipLaunchKernelGGL((wgrad_kernel<uint16_t, true>), wgrid(I, H), dim3(256), 0, s, gtt, gts, utt, uts,
+    if (pair)
+      hipLaunchKernelGGL((wgrad_kernel<uint16_t, 2>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts,
+                         nullptr, nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P,
+                         static_cast<uint16_t*>(dw2), nullptr);
+    else
+      hipLaunchKernelGGL((wgrad_kernel<uint16_t, 0>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts,
+                         nullptr, nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P,
+                         static_cast<uint16_t*>(dw2), nullptr);
+    hipLaunchKernelGGL((wgrad_kernel<uint16_t, 1>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts,
                        xtt, xts, poff, n_experts, (int)I, (int)H, P, static_cast<uint16_t*>(dw1),
                        static_cast<uint16_t*>(dw3));
   }
