@@ -204,13 +204,15 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave) {
 //     stream from HBM straight into a VGPR ring; no other wave needs them, so they never
 //     touch LDS.
 //   the tile's activation rows and scales (gathered rows, L2-resident) are copied by all
-//     8 waves into an LDS ring by direct buffer->LDS loads. One workgroup barrier per K
-//     chunk publishes chunk c and frees chunk c-1.
-// Both rings have RING slots and run RING-1 chunks ahead: a wave's loads complete in
-// issue order, so the activation copies, which every chunk waits for, must be as deep
-// as the weight stream or they would drain it. All global reads are buffer loads: an
-// SGPR descriptor plus a 32-bit lane offset, and reads past a descriptor's range return
-// zeros without touching memory.
+//     8 waves into an LDS ring by direct buffer->LDS loads. One workgroup barrier per
+//     pair of K chunks publishes chunks c and c+1 and frees c-2 and c-1 (a barrier per
+//     chunk measured 5% slower on the V3 prefill gate/up: the waves wait for the slowest
+//     one twice as often).
+// Both rings have RING slots. The weights run RING-1 chunks ahead, the activation copies
+// a pair ahead; a wave's loads complete in issue order, so the copies are issued before
+// the weights of the chunks after them and never wait behind those. All global reads are
+// buffer loads: an SGPR descriptor plus a 32-bit lane offset, and reads past a
+// descriptor's range return zeros without touching memory.
 constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;       // 512
 constexpr int kNTS = kMT / 16;                   // 16-row tiles per M tile
@@ -360,17 +362,20 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   const int wsel0 = GU ? 0 : (wave >= 4 ? 1 : 0);   // scale row block of fragment 0
   const int wsel1 = GU ? 1 : wsel0;
 
-  // one chunk's loads, in a fixed order: 4 weight loads, kActDma activation copies, 1 scale.
-  // Step g of n-block it loads chunk g of that block; chunks past the block's last one
-  // (and blocks past the workgroup's range) read zero weights.
+  // A chunk's loads come in two groups: its weights (4 loads) and its activation copies
+  // (kActDma copies and 1 scale). Step g of n-block it loads the weights of chunk g of
+  // that block; chunks past the block's last one (and blocks past the workgroup's range)
+  // read zero weights. Activation copies depend on the chunk only.
   v8i W0[RING], W1[RING];
   const int wlane = lane * 16;
-  auto issue = [&](int it, int c, int ws, uint8_t* st) __attribute__((always_inline)) {
+  auto issue_w = [&](int it, int c, int ws) __attribute__((always_inline)) {
     const bool real = it < nbn && c < nkc;
     const int nb = nb0 + min(it, nbn - 1);
     const int off = wlane + (real ? c : nkc) * kFragBytes;
     W0[ws] = buf_wfrag(wdesc(nb, 0), off);
     W1[ws] = buf_wfrag(wdesc(nb, 1), off);
+  };
+  auto issue_a = [&](int c, uint8_t* st) __attribute__((always_inline)) {
     const int cc = min(c, last);
 #pragma unroll
     for (int j = 0; j < kActDma; ++j) {
@@ -457,22 +462,33 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
     }
   };
 
-  // Chunks 0 .. RING-2 go out first; step c waits for chunk c, meets the barrier (every
-  // wave's copies of c are in LDS, every wave is done with c-1), issues chunk c+RING-1
-  // into the slots of c-1 and computes c.
-  // Every chunk's loads stay one group in the order of issue(): the compiler's own
-  // waits for the weight registers then see the same history on loop entry as on the
-  // back edge and never ask for more than the ring's own wait.
-#pragma unroll
-  for (int r = 0; r < RING - 1; ++r) {
-    issue(0, r, r, sh.ast[r]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  // Steps go in pairs (2p, 2p+1) with one workgroup barrier per pair. Weights run
+  // RING-1 = 3 chunks ahead: step c issues the weights of chunk c+3 into the registers of
+  // chunk c-1. Activations go a pair at a time: step 2p waits for the copies of chunks 2p
+  // and 2p+1 (and the weights of 2p), meets the barrier (every wave's copies are in LDS,
+  // every wave is done with 2p-2 and 2p-1), and issues the copies of 2p+2 and 2p+3 into
+  // the slots of 2p-2 and 2p-1; step 2p+1 only waits for its weights. A wave's
+  // vector-memory operations complete in issue order, so the issue order (weights of
+  // 2p, copies of 2p and 2p+1, weights of 2p+1, weights of 2p+2, ...) makes every wait a
+  // fixed count: at an even step the weights of the next two chunks stay in flight, at an
+  // odd step also the copies of the next pair and the weights issued with them.
+  // Every chunk's loads stay in the same order on loop entry as on the back edge, so the
+  // compiler's own waits for the weight registers never ask for more than these.
+  static_assert(RING == 4, "pairs of steps over a 4-slot ring");
+  issue_w(0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a(0, sh.ast[0]);
+  issue_a(1, sh.ast[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_w(0, 1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_w(0, 2, 2);
+  __builtin_amdgcn_sched_barrier(0);
   // Every n-block ends with an epilogue that issues exactly kEpiStores stores per wave
   // (lanes with nothing to store are dropped by the buffer range check, never skipped),
-  // behind the next block's first RING-1 chunks; the first block gets as many dummy
-  // stores behind the prologue. Loads and stores complete in issue order, so while those
-  // chunks are awaited (the first group of steps of a block) the wait allows for the
+  // behind the loads of the next block's first chunks; the first block gets as many dummy
+  // stores behind the prologue. Loads and stores complete in issue order, so the waits of
+  // a block's first two steps (before the next pair of copies is awaited) allow for the
   // stores behind them.
   constexpr int kStageStores = (kMT * 8 + kFThreads - 1) / kFThreads;   // 16-byte units
   constexpr int kYStores = kMT * 32 / kFThreads;   // 16-byte units of a staged output block
@@ -480,8 +496,11 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   constexpr int kEpiStores =
       PHASE == 1 ? kStageStores + 1 : (PHASE == 3 || sizeof(YT) == 4 ? 2 * NT : kYStores);
   static_assert(RING < kMaxRing, "the last LDS slot stages the epilogue");
-  constexpr int kWaitRing = (RING - 2) * kStepOps;
-  static_assert(kWaitRing + kEpiStores <= 63, "vmcnt range");
+  constexpr int kWOps = 4, kAOps = kActDma + 1;        // loads per chunk: weights, copies
+  static_assert(kWOps + kAOps == kStepOps, "loads per chunk");
+  constexpr int kWaitEven = 2 * kWOps;                  // weights of the next two chunks
+  constexpr int kWaitOdd = 2 * kWOps + 2 * kAOps;       // + the next pair's copies
+  static_assert(kWaitOdd + kEpiStores <= 63, "vmcnt range");
   {
     const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.as), 0, 0, 0x00020000);
 #pragma unroll
@@ -491,16 +510,29 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   auto group = [&](int it, int s0, auto first) __attribute__((always_inline)) {
 #pragma unroll
     for (int S = 0; S < RING; ++S) {
-      asm volatile("" ::: "memory");
-      if (decltype(first)::value && S <= RING - 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWaitRing + kEpiStores));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWaitRing));
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      const int g = s0 + S + RING - 1;     // step whose chunk is issued now
+      const int g = s0 + S + RING - 1;     // step whose weights are issued now
       const int nx = g >= nsteps ? 1 : 0;  // it belongs to the next n-block
-      issue(it + nx, g - nx * nsteps, (S + RING - 1) % RING, sh.ast[(S + RING - 1) % RING]);
+      asm volatile("" ::: "memory");
+      if (S % 2 == 0) {
+        if (decltype(first)::value && S == 0)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWaitEven + kEpiStores));
+        else
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWaitEven));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // copies of chunks s0+S+2 and s0+S+3 (the next block's chunks 0 and 1 in the
+        // last group) into the slots of s0+S-2 and s0+S-1
+        const int c2 = s0 + S + 2 - (s0 + S + 2 >= nsteps ? nsteps : 0);
+        issue_a(c2, sh.ast[(S + 2) % RING]);
+        issue_a(c2 + 1, sh.ast[(S + 3) % RING]);
+      } else {
+        if (decltype(first)::value && S == 1)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWaitOdd + kEpiStores));
+        else
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWaitOdd));
+        asm volatile("" ::: "memory");
+      }
+      issue_w(it + nx, g - nx * nsteps, (S + RING - 1) % RING);
       __builtin_amdgcn_sched_barrier(0);
       compute(s0 + S, S);
     }
