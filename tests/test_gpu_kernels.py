@@ -97,6 +97,43 @@ def test_quantize_1x128_edge_cases(lib):
     assert np.array_equal(host(q), rq)
 
 
+def _midpoint_tiles():
+    """Tiles whose quotients v / s sit on, and one float32 ulp either side of, every E4M3
+    rounding midpoint, under scales away from 1 (codes are decided on fl32(v / s), so an
+    error of one ulp in the division shows as a different code). Scales cover both sides
+    of 2^-80 and 2^80, and values below 2^-100 of both signs."""
+    rng = np.random.default_rng(11)
+    pos = e4m3.finite_values().astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2
+    targets = list(rng.uniform(0.5, 2.0, 12)) + list(np.exp2(rng.uniform(-60, 60, 12))) + \
+        [2.0 ** -79, 2.0 ** -81, 7e23, 2e24, 1e-30, 1e30]
+    tiles = []
+    for st in targets:
+        amax = np.float32(448.0 * st)
+        s = np.float32(amax / np.float32(448.0))
+        base = (mids * np.float64(s)).astype(np.float32)
+        cand = np.concatenate([base, np.nextafter(base, np.float32(0)), np.nextafter(base, np.float32(3e38))])
+        cand = np.concatenate([cand, -cand, np.float32([2.0 ** -101, -2.0 ** -101, 1e-35, -1e-35, 0.0, -0.0])])
+        cand = cand[np.abs(cand) <= amax]
+        for i in range(0, len(cand), 127):
+            t = np.zeros(128, np.float32)
+            chunk = cand[i:i + 127]
+            t[:len(chunk)] = chunk
+            t[127] = amax
+            tiles.append(t)
+    return np.stack(tiles)
+
+
+def test_quantize_1x128_midpoints_non_unit_scales(lib):
+    x = _midpoint_tiles()
+    say(f"quantize_1x128 midpoint tiles {x.shape}")
+    q, s = lib.moe_quantize_1x128(dev(x))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_1x128(x)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(q), rq)
+
+
 def test_quantize_1x128_bf16_sweep(lib):
     """Every finite bf16 bit pattern, 127 per tile next to a fixed amax of 448."""
     b = np.arange(0, 1 << 16, dtype=np.uint32)
