@@ -439,6 +439,8 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__
                                                            float* __restrict__ s_cm) {
   __shared__ float amx[4][64];
   __shared__ int64_t srow[kTile];   // source row of each of the chunk's rows, -1: zero
+  __shared__ uint4 stg[64][8];      // codes of the 64 columns (128 bytes each), 16-byte
+                                    // segment q of column c at q ^ (c & 7)
   const int64_t g = blockIdx.x;
   const int e = chunk_e[g];
   if (e < 0) return;
@@ -481,16 +483,23 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__
   __syncthreads();
   const float amax = fmaxf(fmaxf(amx[0][cg], amx[1][cg]), fmaxf(amx[2][cg], amx[3][cg]));
   const float s = group_scale(amax);
-  if (c >= C) return;
   uint32_t w[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     w[i] = e4m3_encode(__fdiv_rn(v[4 * i], s)) | (e4m3_encode(__fdiv_rn(v[4 * i + 1], s)) << 8) |
            (e4m3_encode(__fdiv_rn(v[4 * i + 2], s)) << 16) | (e4m3_encode(__fdiv_rn(v[4 * i + 3], s)) << 24);
-  uint4* d = reinterpret_cast<uint4*>(qt + (int64_t)c * pstride + g * kTile + rg * 32);
-  d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  if (rg == 0) s_cm[g * C + c] = s;
+  // through LDS, so that every store writes whole 128-byte rows of qt (8 lanes per row)
+  stg[cg][(2 * rg) ^ (cg & 7)] = make_uint4(w[0], w[1], w[2], w[3]);
+  stg[cg][(2 * rg + 1) ^ (cg & 7)] = make_uint4(w[4], w[5], w[6], w[7]);
+  if (rg == 0 && c < C) s_cm[g * C + c] = s;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = threadIdx.x + 256 * i, cc = u >> 3, q = u & 7;
+    const int col = blockIdx.y * 64 + cc;
+    if (col < C)
+      *reinterpret_cast<uint4*>(qt + (int64_t)col * pstride + g * kTile + q * 16) = stg[cc][q ^ (cc & 7)];
+  }
 }
 
 // ------------------------------------------------------------------------------------
