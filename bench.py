@@ -159,6 +159,25 @@ def measure(layer, cfg, xs, steps: int, warmup: int):
     return out
 
 
+def measure_graph(layer, x, steps: int, warmup: int):
+    """The same step (bias update included) captured once into a HIP graph and replayed
+    ``steps`` times: the launches' host overhead leaves the timed region."""
+    import torch
+    layer.capture(x, update_bias=True)
+    for _ in range(warmup):
+        layer.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    layer._graph = None
+    T = x.shape[0]
+    return {"ms_per_step": round(wall * 1e3 / steps, 4), "tokens_per_s": round(T * steps / wall, 1),
+            "steps": steps, "note": "MoELayer.capture / replay: one HIP graph per step"}
+
+
 def device_batches(cfg, n: int):
     import torch
 
@@ -248,7 +267,9 @@ def other_configs(layer, warmup: int, decode_steps: int):
     if decode_steps > 0:
         cfg = synth.PRESETS["v3_decode"]
         log(f"[bench] decode: T={cfg.tokens}, {decode_steps} steps")
-        res["decode"] = measure(layer, cfg, device_batches(cfg, 1), decode_steps, warmup)
+        xd = device_batches(cfg, 1)
+        res["decode"] = measure(layer, cfg, xd, decode_steps, warmup)
+        res["decode"]["graph"] = measure_graph(layer, xd[0], decode_steps, warmup)
         cfg = synth.PRESETS["v3_skewed"]
         log(f"[bench] skewed: T={cfg.tokens}, fresh clustered batches (seeds 0..2), bias from 0, "
             "updated each step")
@@ -398,6 +419,8 @@ def main():
         "event_ms_per_step": round(float(step_ms.mean()), 4),
         "max_over_mean_load": round(float(counts.max() / counts.mean()), 3),
     }
+    log(f"[bench] graph replay: {args.steps} steps")
+    res["graph"] = measure_graph(layer, x, args.steps, args.warmup)
     if args.seq_len > 0:
         res["seq_balance"] = time_seq_balance(layer, cfg, args.seq_len)
     if args.workload == "v3_prefill":

@@ -57,6 +57,7 @@ class MoELayer:
         self.w_router = None
         self.bias = None
         self._T = None
+        self._graph = None
         self.backward_enabled = backward
         self.dw_dtype = dw_dtype
         if backward:
@@ -136,6 +137,7 @@ class MoELayer:
         H, I, N, k, S = (cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts,
                          cfg.num_experts_per_tok, cfg.num_shared_experts)
         i32, f32 = torch.int32, torch.float32
+        self._graph = None   # a captured step holds the old buffers' addresses
         self.xq = torch.empty((T, H), dtype=torch.uint8, device=d)
         self.xs = torch.empty((T, H // 128), dtype=f32, device=d)
         self.scores = torch.empty((T, N), dtype=f32, device=d)
@@ -191,6 +193,36 @@ class MoELayer:
         if update_bias:
             moe_update_bias(c, T, self.counts, self.bias)
         mark(7)
+        return self.out
+
+    # -- graph capture ---------------------------------------------------------------
+    def capture(self, x: torch.Tensor, update_bias: bool = True) -> "torch.cuda.CUDAGraph":
+        """Captures one forward step on x into a HIP graph and keeps it for replay().
+
+        The graph holds the addresses of x and of the layer's buffers: write the next input
+        into x in place, then replay(); the outputs land in self.out and the routing
+        attributes as with forward(). A step is library kernel launches only (no host
+        synchronisation, no allocation, no memset nodes), so a replay runs the eager step's
+        kernels on the same buffers and gives bit-identical results, without the per-launch
+        host overhead that dominates the small kernels of a decode step."""
+        self._buffers(x.shape[0])
+        side = torch.cuda.Stream(device=self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):   # settle lazy state before capturing
+            self.forward(x, update_bias=False)
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        torch.cuda.synchronize(self.dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x, update_bias=update_bias)
+        self._graph = g
+        return g
+
+    def replay(self) -> torch.Tensor:
+        """Runs the captured step on torch's current stream; returns self.out."""
+        if getattr(self, "_graph", None) is None:
+            raise RuntimeError("replay(): no captured step (call capture() first)")
+        self._graph.replay()
         return self.out
 
     # -- backward ------------------------------------------------------------------

@@ -120,6 +120,45 @@ def test_layer_matches_oracle(name):
     assert np.array_equal(g_bias.view(np.uint32), nb.view(np.uint32))
 
 
+@pytest.mark.parametrize("name", ["tiny", "reduced"])
+def test_graph_replay_matches_eager(name):
+    """A captured step replays the eager step bit for bit: outputs and routing, with the
+    program's own eager work and synchronisations between replays; with the bias update
+    inside the graph, several replays give the same biases and outputs as as many eager
+    steps of a second layer."""
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    cfg = synth.PRESETS[name]
+    say(f"graph {name}: loading two layers")
+    a, b = MoELayer(cfg), MoELayer(cfg)
+    a.load_from_synth()
+    b.load_from_synth()
+    x = x_device(cfg, synth.hidden_states(cfg))
+    out0 = a.forward(x, update_bias=False).clone()
+    idx0, gate0 = a.topk_idx.clone(), a.topk_gate.clone()
+    say(f"graph {name}: capture without the bias update, 3 replays")
+    a.capture(x, update_bias=False)
+    for rep in range(3):
+        a.out.zero_()
+        a.topk_idx.fill_(-1)
+        a.y_rows.zero_()
+        torch.cuda.synchronize()
+        a.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, out0), rep
+        assert torch.equal(a.topk_idx, idx0) and torch.equal(a.topk_gate, gate0), rep
+    say(f"graph {name}: capture with the bias update, 3 replays against 3 eager steps")
+    b.capture(x, update_bias=True)
+    bias_ref = b.bias.clone()
+    for rep in range(3):
+        ref = a.forward(x, update_bias=True).clone()
+        torch.cuda.synchronize()
+        b.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(b.out, ref), rep
+        assert torch.equal(b.bias.view(torch.int32), a.bias.view(torch.int32)), rep
+    assert not torch.equal(b.bias, bias_ref)   # the replays did update the bias
+
+
 @pytest.fixture(scope="module")
 def v3_layer():
     from deepseekmoe_routing_fp8_amd import MoELayer
