@@ -436,6 +436,10 @@ def _relerr(a, b):
     # every tile height the kernel specialises (2, 4, 6, 8, 9, 10 16-row tiles) on both
     # sides of its boundary, and the 160-row split into two tiles
     (256, 256, 12, [160, 161, 16, 17, 48, 80, 112, 113, 128, 129, 144, 145], False),
+    # K chunk counts of 5, 7 (gate/up) and 3, 5 (down): blocks end in padding steps
+    # inside a pair of steps, with several n-blocks per workgroup
+    (640, 384, 3, [150, 9, 200], False),
+    (896, 640, 2, [77, 161], True),
     # the largest contraction the kernel takes: K = 16384 in each phase
     (16384, 256, 2, [40, 7], False),
     (256, 16384, 2, [33, 0], False),
