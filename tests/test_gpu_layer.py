@@ -228,6 +228,26 @@ def test_v3_decode_sampled(v3_layer):
 
 
 @pytest.mark.timeout(900)
+def test_v3_decode_graph_replay(v3_layer):
+    """The V3 decode step (T=128) captured into a HIP graph, as the benchmark times it,
+    replays the eager step bit for bit, twice, with eager work between the replays."""
+    cfg = synth.PRESETS["v3_decode"]
+    x = x_device(cfg, synth.hidden_states(cfg))
+    ref = v3_layer.forward(x, update_bias=False).clone()
+    idx = v3_layer.topk_idx.clone()
+    v3_layer.capture(x, update_bias=False)
+    for rep in range(2):
+        v3_layer.out.zero_()
+        v3_layer.y_rows.zero_()
+        torch.cuda.synchronize()
+        v3_layer.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(v3_layer.out, ref), rep
+        assert torch.equal(v3_layer.topk_idx, idx), rep
+    v3_layer._graph = None
+
+
+@pytest.mark.timeout(900)
 def test_v3_skewed_steps(v3_layer):
     """Forward + bias update on the skewed workload: every step's bias follows the
     oracle's update of the GPU's own counts, and its routing matches the oracle."""
