@@ -33,7 +33,7 @@ ENTRY_POINTS = (
     "moe_update_bias", "moe_seq_balance", "moe_seq_balance_workspace_bytes",
     "moe_combine_backward", "moe_route_backward", "moe_route_backward_workspace_bytes",
     "moe_unpermute_sum", "moe_transpose_fp8_blocks", "moe_grouped_ffn_fp8_backward",
-    "moe_grouped_ffn_backward_workspace_bytes",
+    "moe_grouped_ffn_backward_workspace_bytes", "moe_grouped_ffn_intermediate_offsets",
 )
 
 
@@ -77,6 +77,8 @@ _sig = {
     "moe_grouped_ffn_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
     "moe_grouped_ffn_fp8": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _P, ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
+    "moe_grouped_ffn_intermediate_offsets": ([_CFG, _I32, _I64, ctypes.POINTER(_SZ),
+                                              ctypes.POINTER(_SZ)], ctypes.c_int),
     "moe_grouped_ffn_fp8_gate_up": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _SZ, _P], ctypes.c_int),
     "moe_grouped_ffn_fp8_down": ([_CFG, _I32, _I64, _P, _P, _P, ctypes.c_int, _P, _SZ, _P],
@@ -309,6 +311,25 @@ def moe_grouped_ffn_fp8(cfg: moe_config, n_experts: int, n_rows: int, xq: torch.
         *_down_args(cfg, n_experts, n_rows, w2, w2s, y), _dev(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)), "moe_grouped_ffn_fp8")
     return y
+
+
+def moe_grouped_ffn_intermediate_offsets(cfg: moe_config, n_experts: int, n_rows: int):
+    """Byte offsets (hq, hs) of the quantised intermediate inside a grouped-FFN workspace."""
+    hq, hs = _SZ(0), _SZ(0)
+    _check(_lib.moe_grouped_ffn_intermediate_offsets(ctypes.byref(cfg), n_experts, n_rows,
+                                                     ctypes.byref(hq), ctypes.byref(hs)),
+           "moe_grouped_ffn_intermediate_offsets")
+    return int(hq.value), int(hs.value)
+
+
+def grouped_ffn_intermediate(cfg: moe_config, n_experts: int, n_rows: int, ws: torch.Tensor):
+    """Views of the quantised intermediate in a grouped-FFN workspace: hq [n_rows, I] uint8
+    codes and hs [I/128, n_rows] float32 scales (chunk-major)."""
+    hq_off, hs_off = moe_grouped_ffn_intermediate_offsets(cfg, n_experts, n_rows)
+    I = cfg.inter
+    hq = ws[hq_off:hq_off + n_rows * I].view(n_rows, I)
+    hs = ws[hs_off:hs_off + n_rows * (I // 128) * 4].view(torch.float32).view(I // 128, n_rows)
+    return hq, hs
 
 
 def moe_grouped_ffn_fp8_gate_up(cfg: moe_config, n_experts: int, n_rows: int, xq: torch.Tensor,

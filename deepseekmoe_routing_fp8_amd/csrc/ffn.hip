@@ -1048,3 +1048,17 @@ extern "C" moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_exper
   if (st != MOE_OK) return st;
   return ffn_down(cfg, n_experts, n_rows, w2, w2s, y, yt, ws, ws_bytes, stream);
 }
+
+extern "C" moe_status moe_grouped_ffn_intermediate_offsets(const moe_config* cfg,
+                                                           int32_t n_experts, int64_t n_rows,
+                                                           size_t* hq_offset, size_t* hs_offset) {
+  const moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!hq_offset || !hs_offset) return MOE_ERR_NULL;
+  if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 0 || n_rows >= ((int64_t)1 << 31))
+    return MOE_ERR_SHAPE;
+  const WsLayout L = ws_layout(cfg, n_experts, n_rows);
+  *hq_offset = L.hq;
+  *hs_offset = L.hs;
+  return MOE_OK;
+}

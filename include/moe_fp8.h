@@ -231,7 +231,13 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_config* cfg, int32_t n_experts,
  * t = row_token[r] (or t = r - offsets[e] when row_token is NULL):
  *   G = DQ(xq_t) . DQ(W1_e)^T, U = DQ(xq_t) . DQ(W3_e)^T — every 128-wide K chunk is one
  *   FP8 MFMA partial sum, promoted into an FP32 accumulator times a_scale * w_scale;
- *   h = fl32(silu(G) * U), re-quantised 1x128 (rule of moe_quantize_1x128);
+ *   h = silu(G) * U in FP32, with silu(g) = g * rcp(1 + exp2(-g * log2(e))) on the
+ *   hardware exp2 and reciprocal (relative error a few 1e-7); then 1x128 groups of h
+ *   along I: s = fl32(amax / 448) (1 when 0) as in moe_quantize_1x128, but codes =
+ *   E4M3 of h * rcp(s) (within an ulp of the correctly rounded quotient that
+ *   moe_quantize_1x128 uses). G and U carry FP32 accumulation differences anyway, so hq
+ *   is not a bit-exact quantity: a code can differ by one E4M3 step from a reference
+ *   quantisation of an exact h where h / s sits next to a rounding boundary;
  *   y_r = DQ(hq) . DQ(W2_e)^T with the same promotion, stored as yt.
  *   n_tokens  rows of xq / xs
  *   xq, xs    [n_tokens, H] uint8, [n_tokens, H/128] float
@@ -257,6 +263,20 @@ moe_status moe_grouped_ffn_fp8(const moe_config* cfg, int32_t n_experts, int64_t
                                const float* w3s, const uint8_t* w2, const float* w2s,
                                void* y, moe_dtype yt, void* ws, size_t ws_bytes,
                                void* stream);
+
+/*
+ * moe_grouped_ffn_intermediate_offsets — where moe_grouped_ffn_fp8_gate_up (and
+ * moe_grouped_ffn_fp8) leave the quantised intermediate inside the workspace, for
+ * callers that read it: hq at byte *hq_offset, [n_rows, I] uint8 E4M3 codes, row-major;
+ * hs at byte *hs_offset, [I/128][n_rows] float, chunk-major (the scale of row r's
+ * group c is hs[c * n_rows + r]). Only rows inside the expert segments are written.
+ * Host-only, launches nothing.
+ * Errors: NULL outputs; invalid config; n_experts outside 1..1024 or n_rows outside
+ * 0..2^31-1 (SHAPE).
+ */
+moe_status moe_grouped_ffn_intermediate_offsets(const moe_config* cfg, int32_t n_experts,
+                                                int64_t n_rows, size_t* hq_offset,
+                                                size_t* hs_offset);
 
 /*
  * moe_grouped_ffn_fp8_gate_up — first half of moe_grouped_ffn_fp8 (same passages):

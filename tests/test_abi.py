@@ -227,3 +227,23 @@ def test_unpack_inverts_documented_pack_map():
     for m in range(rows // 32):
         got = sorted([32 * m + 8 * (j // 4) + 4 * p + j % 4 for p in range(2) for j in js])
         assert got == list(range(32 * m, 32 * m + 32))
+
+
+def test_intermediate_offsets():
+    """The intermediate's offsets follow the workspace's documented contents (hq after the
+    tile plan, hs after hq) and are validated on the host."""
+    m = _lib()
+    L = m._lib
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    c = _cfg(m, hidden=7168, inter=2048, n_routed=256, n_shared=1, top_k=8)
+    hq, hs = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rows = 1152
+    assert L.moe_grouped_ffn_intermediate_offsets(ctypes.byref(c), 257, rows, ctypes.byref(hq),
+                                                  ctypes.byref(hs)) == 0
+    assert hq.value % 256 == 0 and hs.value >= hq.value + rows * 2048 and hs.value % 256 == 0
+    need = L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 257, rows)
+    assert hs.value + rows * 16 * 4 <= need
+    assert L.moe_grouped_ffn_intermediate_offsets(ctypes.byref(c), 0, rows, ctypes.byref(hq),
+                                                  ctypes.byref(hs)) == 2
+    assert L.moe_grouped_ffn_intermediate_offsets(ctypes.byref(c), 257, rows, None, ctypes.byref(hs)) == 1

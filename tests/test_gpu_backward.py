@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import synth
+from routing_check import assert_routing_valid
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -282,9 +283,8 @@ def test_layer_backward_matches_oracle(lib, name, tokens):
     fwd = oracle.layer_forward(x_used, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s])
     r = fwd["route"]
     tie = (r["kth_gap"] < 1e-6) | (r["group_gap"] < 1e-6)
-    diff = np.any(g_idx != r["idx"], axis=1)
-    assert not np.any(diff & ~tie)
-    if np.any(diff):   # an equally valid near-tie choice: evaluate the oracle on it
+    assert_routing_valid(r, g_idx, cfg)
+    if np.any(g_idx != r["idx"]):   # an equally valid choice: evaluate the oracle on it
         fwd = oracle.layer_forward(x_used, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s],
                                    force_idx=g_idx)
     say(f"layer backward {name}: oracle")
@@ -342,8 +342,7 @@ def test_layer_backward_v3_prefill_sampled(lib):
     wr = synth.router_weight(cfg)
     r = oracle.route(xb, wr, b0, k, cfg.n_group, cfg.topk_group, cfg.group_score_topn, rho)
     tie = (r["kth_gap"] < 1e-6) | (r["group_gap"] < 1e-6)
-    diff = np.any(g_idx != r["idx"], axis=1)
-    assert not np.any(diff & ~tie)
+    assert_routing_valid(r, g_idx, cfg)
     offsets, row_token, row_of = oracle.permute(g_idx, N)
     toks = np.array([0, 1234, T - 1])
     toks = toks[~tie[toks]]
@@ -393,11 +392,12 @@ def test_layer_backward_v3_prefill_sampled(lib):
     say(f"  sampled tokens {toks.tolist()}: dx {e_dx:.2e}")
     assert e_dx < TOL
 
-    # weight gradients of the shared expert and of the most loaded routed expert. The FP8
-    # wgrad of a routed expert is chaotic at the 1e-2 level: moving every gate by one
-    # float32 ulp (dy by ~1e-7) flips a few dy codes and moves the oracle's own dW1 by
-    # ~9e-3. The bound adds twice that measured sensitivity to TOL, so the GPU must be as
-    # close to the oracle as the oracle is to itself under a last-bit change of its input.
+    # weight gradients of the shared expert and of the most loaded routed expert. The
+    # shared expert's dy is dout itself, bit-identical on both sides, so its dW must meet
+    # TOL outright. The FP8 wgrad of a routed expert is chaotic at the 1e-2 level: its dy
+    # carries the gates, which differ from the oracle's by ~2e-7, and moving every gate by
+    # one float32 ulp flips a few dy codes and moves the oracle's own dW1 by ~9e-3. Its
+    # bound adds twice that measured sensitivity to TOL, capped at 2e-2.
     for e, w, lo, hi in ((N, sh, T * k, T * k + T), (heavy, cache[heavy], int(offsets[heavy]), int(offsets[heavy + 1]))):
         tk = row_token[lo:hi] if e < N else np.arange(T)
         dyr = dy_rows(lo, hi)
@@ -412,6 +412,6 @@ def test_layer_backward_v3_prefill_sampled(lib):
             floor = relerr(bp[name], bw[name])
             err = relerr(host(getattr(layer, name)[e]), bw[name])
             say(f"  expert {e} ({hi - lo} rows) {name}: {err:.2e} (oracle sensitivity {floor:.2e})")
-            assert err < TOL + 2 * floor
+            assert err < (TOL if e == N else min(TOL + 2 * floor, 2e-2))
     del layer
     torch.cuda.empty_cache()

@@ -12,6 +12,7 @@ import torch
 import oracle
 import synth
 from oracle import e4m3
+from routing_check import NEAR_TIE, assert_routing_valid
 
 pytestmark = pytest.mark.gpu
 
@@ -183,20 +184,16 @@ def test_quantize_128x128_matches_oracle(lib):
 # ---------------------------------------------------------------------------------------
 # Router
 # ---------------------------------------------------------------------------------------
-NEAR_TIE = 1e-6
-
-
 def check_routing(cfg, x, wr, b, g_scores, g_idx, g_gate, g_counts):
     """Indices exact outside declared near-ties; gates and scores within tolerance."""
     r = oracle.route(x, wr, b, cfg.num_experts_per_tok, cfg.n_group, cfg.topk_group,
                      cfg.group_score_topn, cfg.routed_scaling_factor)
     assert np.max(np.abs(g_scores - r["s"])) < 5e-7
+    # the same set as the oracle's outside declared near-ties; inside them, every substituted
+    # expert or group within the band; slots in descending score outside the band
+    assert_routing_valid(r, g_idx, cfg)
     tie = (r["kth_gap"] < NEAR_TIE) | (r["group_gap"] < NEAR_TIE)
-    diff = np.any(g_idx != r["idx"], axis=1)
-    assert not np.any(diff & ~tie), f"routing differs outside near-ties at tokens {np.where(diff & ~tie)[0][:10]}"
-    # the GPU's own selections: distinct experts, counts consistent
     k = cfg.num_experts_per_tok
-    assert np.all(np.sort(g_idx, 1)[:, 1:] != np.sort(g_idx, 1)[:, :-1]) if k > 1 else True
     assert np.array_equal(g_counts, np.bincount(g_idx.ravel(), minlength=cfg.num_experts))
     if not np.any(tie):
         assert np.array_equal(g_counts, r["counts"])
@@ -440,6 +437,8 @@ def _relerr(a, b):
     # inside a pair of steps, with several n-blocks per workgroup
     (640, 384, 3, [150, 9, 200], False),
     (896, 640, 2, [77, 161], True),
+    # the V3 expert shape (H = 7168, I = 2048): a full 160-row tile, a ragged one, one row
+    (7168, 2048, 3, [160, 137, 1], False),
     # the largest contraction the kernel takes: K = 16384 in each phase
     (16384, 256, 2, [40, 7], False),
     (256, 16384, 2, [33, 0], False),

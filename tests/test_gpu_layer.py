@@ -13,9 +13,9 @@ import torch
 
 import oracle
 import synth
+from routing_check import NEAR_TIE, assert_routing_valid
 
 pytestmark = pytest.mark.gpu
-NEAR_TIE = 1e-6
 TOL = 5e-3
 
 
@@ -68,10 +68,8 @@ def test_layer_pow2_matches_oracle(name):
     assert np.array_equal(MoELayer.unpack(layer.w1[1].cpu().numpy()), routed[1][0])
     ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s], pow2=True)
     r = ref["route"]
-    tie = routing_ties(r)
-    diff = np.any(g_idx != r["idx"], axis=1)
-    assert not np.any(diff & ~tie)
-    if np.any(diff):
+    assert_routing_valid(r, g_idx, cfg)
+    if np.any(g_idx != r["idx"]):
         ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s],
                                    force_idx=g_idx, pow2=True)
     err = relerr(out, ref["out"])
@@ -107,9 +105,8 @@ def test_layer_matches_oracle(name):
     ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s])
     r = ref["route"]
     tie = routing_ties(r)
-    diff = np.any(g_idx != r["idx"], axis=1)
-    assert not np.any(diff & ~tie)
-    if np.any(diff):   # re-evaluate the oracle on the GPU's (equally valid) near-tie choice
+    assert_routing_valid(r, g_idx, cfg)
+    if np.any(g_idx != r["idx"]):   # re-evaluate the oracle on the GPU's (equally valid) choice
         ref = oracle.layer_forward(x, wr, b0, cfg, lambda e: routed[e], lambda s: shared[s],
                                    force_idx=g_idx)
     err = relerr(out, ref["out"])
@@ -175,10 +172,8 @@ def _sampled_parity(layer, cfg, x, bias, n_sample, seed):
     # routing of every token
     r = oracle.route(x, wr, bias, cfg.num_experts_per_tok, cfg.n_group, cfg.topk_group,
                      cfg.group_score_topn, cfg.routed_scaling_factor)
-    tie = routing_ties(r)
-    diff = np.any(g_idx != r["idx"], axis=1)
-    assert not np.any(diff & ~tie), np.where(diff & ~tie)[0][:10]
-    say(f"  routing ok, near-tie tokens {int(tie.sum())}")
+    nt = assert_routing_valid(r, g_idx, cfg)
+    say(f"  routing ok, near-tie tokens {nt}")
     # outputs of sampled tokens
     rng = np.random.default_rng(seed)
     toks = np.sort(rng.choice(cfg.tokens, n_sample, replace=False))
@@ -204,8 +199,68 @@ def _sampled_parity(layer, cfg, x, bias, n_sample, seed):
     return g_idx
 
 
+def _full_checks(layer, cfg, x, bias, g_idx, inter_rows=640):
+    """Checks at full size wherever the oracle can follow: every token's gates, the
+    permutation, the combine of every token from the GPU's own expert rows and gates, the
+    whole output segments of the shared expert and of the most loaded routed expert, and
+    their quantised intermediate (hq, hs; the first ``inter_rows`` rows of a segment)."""
+    import deepseekmoe_routing_fp8_amd as lib
+    from intermediate_check import check_intermediate, h_band
+    T, H, k, N, S = cfg.tokens, cfg.hidden_size, cfg.num_experts_per_tok, cfg.num_experts, cfg.num_shared_experts
+    assert np.array_equal(layer.counts.cpu().numpy(), np.bincount(g_idx.ravel(), minlength=N))
+    # gates of every token at the GPU's selection; they sum to rho
+    wr = synth.router_weight(cfg)
+    rf = oracle.route(x, wr, bias, k, cfg.n_group, cfg.topk_group, cfg.group_score_topn,
+                      cfg.routed_scaling_factor, force_idx=g_idx)
+    g_gate = layer.topk_gate.cpu().numpy()
+    assert np.allclose(g_gate, rf["gate"], rtol=2e-6, atol=0)
+    assert np.allclose(g_gate.sum(1), cfg.routed_scaling_factor, rtol=1e-5)
+    # permutation bit-exact, shared segment in token order
+    off, rt, ro = oracle.permute(g_idx, N)
+    g_off = layer.offsets.cpu().numpy()
+    g_rt = layer.row_token.cpu().numpy()
+    assert np.array_equal(g_off[:N + 1], off) and g_off[N + 1] == T * (k + 1)
+    assert np.array_equal(g_rt[:T * k], rt) and np.array_equal(g_rt[T * k:], np.arange(T))
+    assert np.array_equal(layer.row_of.cpu().numpy(), ro)
+    # combine of all tokens from the GPU's own rows and gates (one bf16 rounding of an FP32 sum)
+    y_rows = layer.y_rows.float().cpu().numpy()
+    ref = oracle.combine(y_rows[:T * k], ro, g_gate, [y_rows[T * k:]])
+    got = layer.out.float().cpu().numpy().astype(np.float64)
+    mag = np.abs(y_rows[T * k:]).astype(np.float64)
+    for j in range(k):
+        mag += np.abs(g_gate[:, j:j + 1]) * np.abs(y_rows[ro[:, j]])
+    bound = np.abs(ref) * 2.0 ** -8 + 1e-5 * mag
+    assert np.all(np.abs(got - ref) <= bound)
+    del ref, got, mag
+    say(f"  combine of all {T} tokens ok")
+    # whole segments: the shared expert and the most loaded routed expert
+    xq, xs = oracle.quantize_1x128(x)
+    assert np.array_equal(layer.xq.cpu().numpy(), xq)
+    heavy = int(np.argmax(np.diff(off)))
+    cache = {}
+    synth.map_experts(cfg, lambda e, w: cache.__setitem__(e, q3(w)), [heavy])
+    sh = q3(synth.shared_expert_weights(cfg, 0))
+    c = lib.make_config(cfg)
+    hq_all, hs_all = lib.grouped_ffn_intermediate(c, N + S, T * (k + S), layer.ws)
+    hq_all, hs_all = hq_all.cpu().numpy(), hs_all.cpu().numpy()
+    for name, w, lo, hi, toks in (("shared", sh, T * k, T * k + T, np.arange(T)),
+                                  (f"routed {heavy}", cache[heavy], int(off[heavy]), int(off[heavy + 1]),
+                                   rt[off[heavy]:off[heavy + 1]])):
+        y_ref = oracle.expert_ffn(xq[toks], xs[toks], *w)[0]
+        err = relerr(y_rows[lo:hi], y_ref)
+        say(f"  {name} expert, {hi - lo} rows: normwise error {err:.3e}")
+        assert err < TOL
+        m = min(hi - lo, inter_rows)
+        h, dh = h_band(xq[toks[:m]], xs[toks[:m]], *w[:4])
+        st = check_intermediate(hq_all[lo:lo + m], hs_all[:, lo:lo + m].T, h, dh)
+        say(f"  {name} expert intermediate ({m} rows): {st}")
+
+
 @pytest.mark.timeout(900)
-def test_v3_prefill_sampled(v3_layer):
+def test_v3_prefill_full(v3_layer):
+    """The V3 prefill step (T = 4096) in the benchmark's launch configuration, at full
+    size wherever the oracle can follow (see _full_checks), and three sampled tokens end
+    to end (all their experts re-evaluated by the oracle)."""
     cfg = synth.PRESETS["v3_prefill"]
     x = synth.hidden_states(cfg)
     bias = v3_layer.bias.cpu().numpy()
@@ -213,7 +268,7 @@ def test_v3_prefill_sampled(v3_layer):
     v3_layer.forward(x_device(cfg, x), update_bias=False)
     torch.cuda.synchronize()
     g_idx = _sampled_parity(v3_layer, cfg, x, bias, 3, 0)
-    assert np.array_equal(v3_layer.counts.cpu().numpy(), np.bincount(g_idx.ravel(), minlength=256))
+    _full_checks(v3_layer, cfg, x, bias, g_idx)
 
 
 @pytest.mark.timeout(900)
@@ -224,7 +279,8 @@ def test_v3_decode_sampled(v3_layer):
     say("V3 decode forward T=128")
     v3_layer.forward(x_device(cfg, x), update_bias=False)
     torch.cuda.synchronize()
-    _sampled_parity(v3_layer, cfg, x, bias, 3, 1)
+    g_idx = _sampled_parity(v3_layer, cfg, x, bias, 3, 1)
+    _full_checks(v3_layer, cfg, x, bias, g_idx)
 
 
 @pytest.mark.timeout(900)
@@ -264,6 +320,13 @@ def test_v3_skewed_steps(v3_layer):
         loads.append(counts.max() / counts.mean())
         if step == 0:
             _sampled_parity(v3_layer, cfg, x, b, 2, 2)
+        else:   # every step's routing; at the last, the heaviest segment (many M tiles) in full
+            r = oracle.route(x, synth.router_weight(cfg), b, cfg.num_experts_per_tok, cfg.n_group,
+                             cfg.topk_group, cfg.group_score_topn, cfg.routed_scaling_factor)
+            g_idx = v3_layer.topk_idx.cpu().numpy()
+            assert_routing_valid(r, g_idx, cfg)
+            if step == 2:
+                _full_checks(v3_layer, cfg, x, b, g_idx, inter_rows=320)
         b = oracle.bias_update(b, counts, cfg.tokens, cfg.num_experts_per_tok, cfg.expert_bias_update_rate)
         assert np.array_equal(v3_layer.bias.cpu().numpy().view(np.uint32), b.view(np.uint32))
     say(f"  max/mean load per step: {[round(float(v), 2) for v in loads]}")
