@@ -34,7 +34,10 @@ ENTRY_POINTS = (
     "moe_combine_backward", "moe_route_backward", "moe_route_backward_workspace_bytes",
     "moe_unpermute_sum", "moe_transpose_fp8_blocks", "moe_grouped_ffn_fp8_backward",
     "moe_grouped_ffn_backward_workspace_bytes", "moe_grouped_ffn_intermediate_offsets",
+    "moe_grouped_ffn_fp8_noalloc",
 )
+MOE_ERR_SCRATCH = 7
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class moe_config(ctypes.Structure):
@@ -79,6 +82,8 @@ _sig = {
                              _P, ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
     "moe_grouped_ffn_intermediate_offsets": ([_CFG, _I32, _I64, ctypes.POINTER(_SZ),
                                               ctypes.POINTER(_SZ)], ctypes.c_int),
+    "moe_grouped_ffn_fp8_noalloc": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, ctypes.c_int, _P], ctypes.c_int),
     "moe_grouped_ffn_fp8_gate_up": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _SZ, _P], ctypes.c_int),
     "moe_grouped_ffn_fp8_down": ([_CFG, _I32, _I64, _P, _P, _P, ctypes.c_int, _P, _SZ, _P],
@@ -310,6 +315,21 @@ def moe_grouped_ffn_fp8(cfg: moe_config, n_experts: int, n_rows: int, xq: torch.
                                           w1, w1s, w3, w3s),
         *_down_args(cfg, n_experts, n_rows, w2, w2s, y), _dev(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)), "moe_grouped_ffn_fp8")
+    return y
+
+
+def moe_grouped_ffn_fp8_noalloc(cfg: moe_config, n_experts: int, n_rows: int, xq: torch.Tensor,
+                                xs: torch.Tensor, row_token: Optional[torch.Tensor],
+                                offsets: torch.Tensor, w1, w1s, w3, w3s, w2, w2s,
+                                y: torch.Tensor = None, y_dtype=torch.bfloat16, stream=None):
+    """moe_grouped_ffn_fp8 on the library's static scratch array (no workspace, no
+    allocation inside the call when ``y`` is given) -> y [n_rows, H]."""
+    if y is None:
+        y = torch.empty((n_rows, cfg.hidden), dtype=y_dtype, device=xq.device)
+    _check(_lib.moe_grouped_ffn_fp8_noalloc(
+        ctypes.byref(cfg), *_gate_up_args(cfg, n_experts, n_rows, xq, xs, row_token, offsets,
+                                          w1, w1s, w3, w3s),
+        *_down_args(cfg, n_experts, n_rows, w2, w2s, y), _stream(stream)), "moe_grouped_ffn_fp8_noalloc")
     return y
 
 

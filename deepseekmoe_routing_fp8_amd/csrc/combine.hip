@@ -165,6 +165,8 @@ extern "C" const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported request";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_SCRATCH:
+      return "the request needs more workspace than the library's static scratch buffer holds";
   }
   return "unknown status";
 }

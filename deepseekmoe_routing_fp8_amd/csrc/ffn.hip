@@ -22,6 +22,7 @@
 // output is re-quantised in the epilogue (amax reduced across waves through LDS).
 // Phase 2 (down): wave w owns 32 rows of W2; the workgroup covers 256 output features.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1061,4 +1062,63 @@ extern "C" moe_status moe_grouped_ffn_intermediate_offsets(const moe_config* cfg
   *hq_offset = L.hq;
   *hs_offset = L.hs;
   return MOE_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// The grouped FFN without a caller-provided workspace, for callers that cannot allocate
+// device memory (code under graph capture, serving loops, harnesses without hipMalloc).
+// The workspace is a static device array of MOE_NOALLOC_SCRATCH_BYTES per GPU. In host
+// code the array's name stands for a host-side shadow, so its device address is looked
+// up once per device with that device current (hipGetSymbolAddress) and only that
+// address is ever handed to a kernel. Nothing in the workspace needs clearing: the plan
+// kernel writes the tile list and its count, and every row a later launch reads is
+// written by an earlier one of the same call.
+// ------------------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kScratchDevices] = {};
+
+// Device address of this device's copy of `scratch` (looked up on the device's first call).
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_grouped_ffn_fp8_noalloc(const moe_config* cfg, int32_t n_experts,
+                                                  int64_t n_rows, int64_t n_tokens,
+                                                  const uint8_t* xq, const float* xs,
+                                                  const int32_t* row_token, const int32_t* offsets,
+                                                  const uint8_t* w1, const float* w1s,
+                                                  const uint8_t* w3, const float* w3s,
+                                                  const uint8_t* w2, const float* w2s, void* y,
+                                                  moe_dtype yt, void* stream) {
+  const moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 0 || n_rows >= ((int64_t)1 << 31))
+    return MOE_ERR_SHAPE;
+  if (ws_layout(cfg, n_experts, n_rows).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_SCRATCH;
+  if (n_rows == 0)   // validates the rest, launches nothing
+    return moe_grouped_ffn_fp8(cfg, n_experts, 0, n_tokens, xq, xs, row_token, offsets, w1, w1s,
+                               w3, w3s, w2, w2s, y, yt, nullptr, 0, stream);
+  void* ws = nullptr;
+  const moe_status sa = scratch_address(&ws);
+  if (sa != MOE_OK) return sa;
+  return moe_grouped_ffn_fp8(cfg, n_experts, n_rows, n_tokens, xq, xs, row_token, offsets, w1, w1s,
+                             w3, w3s, w2, w2s, y, yt, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }

@@ -23,7 +23,8 @@
  *   - Pointers are DEVICE pointers owned by the caller unless stated otherwise; a
  *     pointer to an array with zero elements may be NULL. The
  *     library never allocates, frees or keeps a pointer; scratch memory comes in
- *     through an explicit workspace whose size is queried first.
+ *     through an explicit workspace whose size is queried first. The one exception is
+ *     moe_grouped_ffn_fp8_noalloc, whose workspace is a static device array.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is
  *     enqueued asynchronously; results are valid after the caller synchronises.
  *   - Arguments are validated on the host before any launch. A failed check returns
@@ -32,7 +33,10 @@
  *   - All matrices are row-major and densely packed. E4M3 codes are OCP E4M3FN bytes
  *     (the bit patterns of torch.float8_e4m3fn). bf16 is passed as uint16 bits.
  *   - NaN/Inf in inputs give unspecified values but never out-of-bounds accesses.
- *   - No global mutable state: calls are thread-safe; results are deterministic.
+ *   - Calls are thread-safe and results deterministic. The only global state is the
+ *     per-device address of moe_grouped_ffn_fp8_noalloc's static array (looked up once
+ *     per device under a lock); concurrent calls of that entry point on one GPU race on
+ *     the array itself.
  */
 #ifndef MOE_FP8_H
 #define MOE_FP8_H
@@ -51,7 +55,9 @@ typedef enum moe_status {
   MOE_ERR_DTYPE = 3,       /* unsupported dtype for this argument               */
   MOE_ERR_UNSUPPORTED = 4, /* valid request the library does not implement       */
   MOE_ERR_HIP = 5,         /* a HIP launch or runtime call failed               */
-  MOE_ERR_WORKSPACE = 6    /* workspace NULL or smaller than the queried size   */
+  MOE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the queried size   */
+  MOE_ERR_SCRATCH = 7      /* request larger than the static scratch buffer of
+                              moe_grouped_ffn_fp8_noalloc                          */
 } moe_status;
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -299,6 +305,29 @@ moe_status moe_grouped_ffn_fp8_gate_up(const moe_config* cfg, int32_t n_experts,
 moe_status moe_grouped_ffn_fp8_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
                                     const uint8_t* w2, const float* w2s, void* y, moe_dtype yt,
                                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn_fp8_noalloc — moe_grouped_ffn_fp8 with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, kernels
+ * and results as moe_grouped_ffn_fp8 (bit for bit), with the workspace taken from a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on until the process ends (its address is looked up on a device's first call).
+ * Calls on one GPU share that array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give unspecified results; calls in one stream's order
+ * are safe. Nothing in the array needs to start cleared.
+ * Errors: as moe_grouped_ffn_fp8, and MOE_ERR_SCRATCH when
+ * moe_grouped_ffn_workspace_bytes(cfg, n_experts, n_rows) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (at the V3 shape, H = 7168 and I = 2048 with 257 experts,
+ * up to about 14,000 rows fit; a decode step of 128 tokens has 1,152).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_grouped_ffn_fp8_noalloc(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
+                                       int64_t n_tokens, const uint8_t* xq, const float* xs,
+                                       const int32_t* row_token, const int32_t* offsets,
+                                       const uint8_t* w1, const float* w1s, const uint8_t* w3,
+                                       const float* w3s, const uint8_t* w2, const float* w2s,
+                                       void* y, moe_dtype yt, void* stream);
 
 /*
  * moe_combine — weighted combine ([digest] section 3.2: y = sum_j gate[j] *

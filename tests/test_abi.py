@@ -45,8 +45,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     m = _lib()
-    for s in range(7):
+    for s in range(8):
         assert m._lib.moe_status_string(s).decode()
+    assert "scratch" in m._lib.moe_status_string(7).decode()
     assert m._lib.moe_status_string(0).decode() == "ok"
 
 
@@ -229,9 +230,10 @@ def test_unpack_inverts_documented_pack_map():
         assert got == list(range(32 * m, 32 * m + 32))
 
 
-def test_intermediate_offsets():
+def test_intermediate_offsets_and_noalloc_limit():
     """The intermediate's offsets follow the workspace's documented contents (hq after the
-    tile plan, hs after hq) and are validated on the host."""
+    tile plan, hs after hq), and the no-allocation grouped FFN rejects, on the host, a
+    request larger than its static scratch array with MOE_ERR_SCRATCH, before any HIP call."""
     m = _lib()
     L = m._lib
     P = ctypes.c_void_p
@@ -247,3 +249,13 @@ def test_intermediate_offsets():
     assert L.moe_grouped_ffn_intermediate_offsets(ctypes.byref(c), 0, rows, ctypes.byref(hq),
                                                   ctypes.byref(hs)) == 2
     assert L.moe_grouped_ffn_intermediate_offsets(ctypes.byref(c), 257, rows, None, ctypes.byref(hs)) == 1
+    # the limit: the largest row count that fits, and one 16-row unit more
+    assert need <= m.NOALLOC_SCRATCH_BYTES
+    big = 4096 * 9
+    assert L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 257, big) > m.NOALLOC_SCRATCH_BYTES
+    args = [fake] * 10
+    assert L.moe_grouped_ffn_fp8_noalloc(ctypes.byref(c), 257, big, 4096, *args, fake, 1, None) == 7
+    # ordinary validation still comes first
+    bad = _cfg(m, hidden=200)
+    assert L.moe_grouped_ffn_fp8_noalloc(ctypes.byref(bad), 257, 16, 16, *args, fake, 1, None) == 2
+    assert L.moe_grouped_ffn_fp8_noalloc(ctypes.byref(c), 0, 16, 16, *args, fake, 1, None) == 2
