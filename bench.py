@@ -75,62 +75,138 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(cfg, n_tokens: int):
-    """Times the CPU oracle on a bounded sample of the same workload."""
+def _blas_threads() -> int:
+    try:
+        import numpy as np
+        from threadpoolctl import threadpool_info
+        np.ones((64, 64)) @ np.ones((64, 64))   # loads the BLAS library
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def oracle_step_timed(x, wr, b, cfg, routed, shared):
+    """The oracle's layer forward (the calls of oracle.layer_forward, in its order) with a
+    wall-clock time per stage; returns (out, {stage: seconds})."""
     import numpy as np
 
     import oracle
-    import synth
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
-    x = synth.hidden_states(cfg)[:n_tokens]
-    wr = synth.router_weight(cfg)
-    b = synth.expert_bias(cfg)
+    t, c = {}, time.perf_counter()
+
+    def lap(name):
+        nonlocal c
+        now = time.perf_counter()
+        t[name] = t.get(name, 0.0) + now - c
+        c = now
+    xq, xs = oracle.quantize_1x128(x)
+    lap("quantize")
     r = oracle.route(x, wr, b, cfg.num_experts_per_tok, cfg.n_group, cfg.topk_group,
                      cfg.group_score_topn, cfg.routed_scaling_factor)
-    experts = sorted(set(r["idx"].ravel().tolist()))
-    cache, sh = {}, {}
+    lap("route")
+    offsets, row_token, row_of = oracle.permute(r["idx"], cfg.num_experts)
+    lap("permute")
+    y_rows = np.zeros((row_token.shape[0], x.shape[1]), dtype=np.float64)
+    for e in range(cfg.num_experts):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            y_rows[lo:hi] = oracle.expert_ffn(xq[row_token[lo:hi]], xs[row_token[lo:hi]], *routed(e))[0]
+    lap("ffn_routed")
+    y_shared = [oracle.expert_ffn(xq, xs, *shared(s))[0] for s in range(cfg.num_shared_experts)]
+    lap("ffn_shared")
+    out = oracle.combine(y_rows, row_of, r["gate"], y_shared)
+    lap("combine")
+    oracle.bias_update(b, r["counts"], x.shape[0], cfg.num_experts_per_tok, cfg.expert_bias_update_rate)
+    lap("bias_update")
+    return out, t
+
+
+def cpu_baseline(cfg, n_tokens: int, full=("tiny", "reduced")):
+    """Times the CPU oracle: a bounded sample of the headline workload (its first n_tokens
+    tokens, all BLAS threads), then the small workloads in full at 1 BLAS thread and at
+    all of them. Weight quantisation is input preparation and is not timed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
 
     def q3(w):
         return (*oracle.quantize_128x128(w[0]), *oracle.quantize_128x128(w[1]),
                 *oracle.quantize_128x128(w[2]))
-    synth.map_experts(cfg, lambda e, w: cache.__setitem__(e, q3(w)), experts)
-    synth.map_experts(cfg, lambda s, w: sh.__setitem__(s, q3(w)), range(cfg.num_shared_experts),
-                      shared=True)
+
+    def prepare(c, x):
+        r = oracle.route(x, synth.router_weight(c), synth.expert_bias(c), c.num_experts_per_tok,
+                         c.n_group, c.topk_group, c.group_score_topn, c.routed_scaling_factor)
+        cache, sh = {}, {}
+        synth.map_experts(c, lambda e, w: cache.__setitem__(e, q3(w)), sorted(set(r["idx"].ravel().tolist())))
+        synth.map_experts(c, lambda s, w: sh.__setitem__(s, q3(w)), range(c.num_shared_experts), shared=True)
+        return cache, sh
+
+    affinity = len(os.sched_getaffinity(0))
+    blas = _blas_threads()
+    x = synth.hidden_states(cfg)[:n_tokens]
+    log(f"[bench] cpu baseline: quantising the experts of {n_tokens} {cfg.name} tokens on the host")
+    cache, sh = prepare(cfg, x)
+    log(f"[bench] cpu baseline: oracle on {n_tokens} tokens, {blas} BLAS threads")
     t0 = time.perf_counter()
-    oracle.layer_forward(x, wr, b, cfg, lambda e: cache[e], lambda s: sh[s])
+    _, st = oracle_step_timed(x, synth.router_weight(cfg), synth.expert_bias(cfg), cfg,
+                              lambda e: cache[e], lambda s: sh[s])
     dt = time.perf_counter() - t0
-    cores = max(blas, min(16, os.cpu_count() or 1))
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{n_tokens} tokens of {cfg.name} through the FP64 oracle layer forward "
-                       f"(1x128 quantisation, routing against all {cfg.num_experts} experts, "
-                       f"{len(experts)} routed + {cfg.num_shared_experts} shared expert FFNs, "
-                       f"combine); weight quantisation of those experts excluded; {dt:.1f} s"),
-            "seconds": dt}
+    res = {"value": n_tokens / dt, "unit": "tokens/s", "cores": min(blas, affinity), "kind": "oracle",
+           "sample": (f"the first {n_tokens} tokens of {cfg.name} through the FP64 oracle layer forward "
+                      f"(1x128 quantisation, routing against all {cfg.num_experts} experts, "
+                      f"{len(cache)} routed + {cfg.num_shared_experts} shared expert FFNs, combine, "
+                      f"bias update), {blas} BLAS threads; weight quantisation excluded; {dt:.1f} s"),
+           "seconds": round(dt, 3), "affinity_cores": affinity, "blas_threads": blas,
+           "stages_s": {k: round(v, 4) for k, v in st.items()}, "full_workloads": {}}
+    for name in full:
+        c = synth.PRESETS[name]
+        xf = synth.hidden_states(c)
+        log(f"[bench] cpu baseline: {name} in full at 1 and {blas} BLAS threads")
+        cache_f, sh_f = prepare(c, xf)
+        runs = {}
+        for label, n in (("1_thread", 1), ("all_threads", blas)):
+            with threadpool_limits(limits=n, user_api="blas"):
+                t0 = time.perf_counter()
+                out, st = oracle_step_timed(xf, synth.router_weight(c), synth.expert_bias(c), c,
+                                            lambda e: cache_f[e], lambda s: sh_f[s])
+                dt = time.perf_counter() - t0
+            runs[label] = {"threads": n, "seconds": round(dt, 3), "tokens_per_s": round(c.tokens / dt, 1),
+                           "stages_s": {k: round(v, 4) for k, v in st.items()}}
+        res["full_workloads"][name] = runs
+    return res
 
 
-def measure(layer, cfg, xs, steps: int, warmup: int):
-    """Times ``steps`` forward steps of ``layer`` (bias update included) cycling over the
-    device batches ``xs``; stage spans from HIP events on the launch stream."""
+def measure(layer, cfg, xs, steps: int, warmup: int, reset_bias: bool = True):
+    """Times ``steps`` forward steps of ``layer`` (bias update included) over the device
+    batches ``xs`` (step i uses xs[i % len(xs)]); stage spans from HIP events on the
+    launch stream. ``reset_bias``: every step starts from the layer's current bias (a
+    1 KB device copy before each step), so that repeating one batch times the configured
+    workload rather than a bias drifted by earlier repetitions; otherwise the bias
+    follows its trajectory, and the per-step loads and bias range are recorded."""
     import numpy as np
     import torch
 
     from deepseekmoe_routing_fp8_amd import MoELayer
+    b0 = layer.bias.clone()
     for i in range(warmup):
         layer.forward(xs[i % len(xs)])
+        layer.bias.copy_(b0)
     torch.cuda.synchronize()
     nst = len(MoELayer.STAGES)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
-    loads = []
+    N = cfg.num_experts
+    loads = torch.empty((steps, N), dtype=torch.int32, device=layer.bias.device)
+    biases = torch.empty((steps, N), dtype=torch.float32, device=layer.bias.device)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        if reset_bias:
+            layer.bias.copy_(b0)
         layer.forward(xs[i % len(xs)], events=evs[i])
-        if cfg.skewed:
-            loads.append(layer.counts.clone())
+        if not reset_bias:
+            loads[i].copy_(layer.counts)
+            biases[i].copy_(layer.bias)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nst)]
@@ -151,11 +227,17 @@ def measure(layer, cfg, xs, steps: int, warmup: int):
            "ffn_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
            "gate_up_gbs": round(ab["gate_up"] / (st["ffn_gate_up"] * 1e-3) / 1e9, 1),
            "down_gbs": round(ab["down"] / (st["ffn_down"] * 1e-3) / 1e9, 1),
-           "stage_ms": {s: round(v, 4) for s, v in st.items()}}
-    if loads:
-        c = torch.stack(loads).float()
+           "ffn_tflops_fp8": round(6.0 * H * I * T * (k + S) / (ffn_ms * 1e-3) / 1e12, 1),
+           "stage_ms": {s: round(v, 4) for s, v in st.items()},
+           "bias": "reset to the configured value before every step" if reset_bias else
+                   "updated every step from the step's own loads (trajectory from the configured value)"}
+    if not reset_bias:
+        c = loads.float()
         ratio = (c.max(dim=1).values / c.mean(dim=1)).cpu().numpy()
         out["max_over_mean_load_per_step"] = [round(float(v), 3) for v in ratio]
+        b = biases.cpu().numpy()
+        out["bias_min_per_step"] = [round(float(v), 4) for v in b.min(axis=1)]
+        out["bias_max_per_step"] = [round(float(v), 4) for v in b.max(axis=1)]
     return out
 
 
@@ -175,17 +257,25 @@ def measure_graph(layer, x, steps: int, warmup: int):
     layer._graph = None
     T = x.shape[0]
     return {"ms_per_step": round(wall * 1e3 / steps, 4), "tokens_per_s": round(T * steps / wall, 1),
-            "steps": steps, "note": "MoELayer.capture / replay: one HIP graph per step"}
+            "steps": steps, "note": "MoELayer.capture / replay: one HIP graph per step (bias update "
+                                    "inside the graph, so the bias moves across replays)"}
 
 
 def device_batches(cfg, n: int):
+    """n seeded batches on the device (n = 1: the preset's own batch; otherwise the fresh
+    batches of steps 0..n-1), generated on a host thread pool outside any timed region."""
     import torch
+    from concurrent.futures import ThreadPoolExecutor
 
     import synth
     dt = torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32
     if n == 1:
         return [torch.from_numpy(synth.hidden_states(cfg)).to(dt).cuda()]
-    return [torch.from_numpy(synth.hidden_states(cfg, step=i)).to(dt).cuda() for i in range(n)]
+    out = []
+    with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+        for x in ex.map(lambda i: synth.hidden_states(cfg, step=i), range(n)):
+            out.append(torch.from_numpy(x).to(dt).cuda())
+    return out
 
 
 def measure_backward(layer, cfg, x, steps: int, warmup: int):
@@ -254,7 +344,7 @@ def time_seq_balance(layer, cfg, seq_len: int, calls: int = 20):
             "max_entropy_nats": round(float(np.log(cfg.num_experts)), 4)}
 
 
-def other_configs(layer, warmup: int, decode_steps: int):
+def other_configs(layer, warmup: int, decode_steps: int, args_skewed_steps: int = 100):
     """The other workloads of the same method, outside the headline number: the T=128
     decode step and the skewed T=16384 step on the same V3 layer, and the reduced layer
     (its own weights)."""
@@ -271,10 +361,12 @@ def other_configs(layer, warmup: int, decode_steps: int):
         res["decode"] = measure(layer, cfg, xd, decode_steps, warmup)
         res["decode"]["graph"] = measure_graph(layer, xd[0], decode_steps, warmup)
         cfg = synth.PRESETS["v3_skewed"]
-        log(f"[bench] skewed: T={cfg.tokens}, fresh clustered batches (seeds 0..2), bias from 0, "
-            "updated each step")
+        log(f"[bench] skewed: T={cfg.tokens}, generating {args_skewed_steps} fresh clustered batches")
+        xs = device_batches(cfg, args_skewed_steps)
+        log(f"[bench] skewed: {args_skewed_steps} steps, bias from 0, updated every step")
         layer.bias.zero_()
-        res["skewed"] = measure(layer, cfg, device_batches(cfg, 3), 12, 3)
+        res["skewed"] = measure(layer, cfg, xs, args_skewed_steps, 0, reset_bias=False)
+        del xs
         # per-sequence balance loss / allocation entropy of the last skewed step's routing
         # (4 sequences of 4096 tokens); timed on its own, it is not part of the forward step
         res["seq_balance"] = time_seq_balance(layer, cfg, 4096)
@@ -322,6 +414,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50,
                     help="steps of the T=128 decode workload timed after the main one; the "
                          "skewed and reduced workloads follow it (0: skip all three)")
+    ap.add_argument("--skewed-steps", type=int, default=100,
+                    help="forward + bias-update steps of the skewed T=16384 workload, each on a "
+                         "fresh clustered batch generated before the timed region")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -355,8 +450,12 @@ def main():
         r.update({"workload": cfg.name, "dtype": "fp8-e4m3 GEMMs, fp32 accumulation"})
         print(json.dumps(r), flush=True)
         return
+    # every step runs the configured workload: the bias update of a step is part of the
+    # timed work, and a 1 KB device copy restores the configured bias before the next one
+    b0 = layer.bias.clone()
     for _ in range(args.warmup):
         layer.forward(x)
+        layer.bias.copy_(b0)
     torch.cuda.synchronize()
 
     nst = len(MoELayer.STAGES)
@@ -365,6 +464,7 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
+        layer.bias.copy_(b0)
         layer.forward(x, events=evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -424,7 +524,8 @@ def main():
     if args.seq_len > 0:
         res["seq_balance"] = time_seq_balance(layer, cfg, args.seq_len)
     if args.workload == "v3_prefill":
-        res.update(other_configs(layer, args.warmup, args.decode_steps))
+        layer.bias.copy_(b0)
+        res.update(other_configs(layer, args.warmup, args.decode_steps, args.skewed_steps))
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)

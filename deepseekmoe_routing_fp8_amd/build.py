@@ -1,10 +1,11 @@
 """Build libmoe_fp8.so (gfx950 only) from csrc/*.hip with hipcc.
 
-Usage: python deepseekmoe_routing_fp8_amd/build.py  (run as a file: importing the
-package would first load the library being built).
-Objects go to <repo>/_build/, the library next to this file. Also builds
-bench/ffn_counters, a native driver of the grouped FFN for profiler counter runs, and
-bench/hbm_read, the plain streaming read that the HBM rooflines are compared with.
+Usage: python deepseekmoe_routing_fp8_amd/build.py [--tools]  (run as a file: importing
+the package would first load the library being built).
+Objects go to <repo>/_build/, the library next to this file. ``--tools`` (build_tools())
+also builds the measurement drivers: bench/moe_counters, a native driver of one layer
+step for profiler counter runs, and bench/hbm_read, the plain streaming read that the
+HBM rooflines are compared with.
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoe_fp8.so")
-COUNTERS = os.path.join(PKG, "bench", "ffn_counters")
+COUNTERS = os.path.join(PKG, "bench", "moe_counters")
 HBM_READ = os.path.join(PKG, "bench", "hbm_read")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,7 +26,6 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # no packed-FP32 (v_pk_*_f32) instructions anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics",
 ]
 
 
@@ -51,6 +51,13 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    return LIB
+
+
+def build_tools() -> None:
+    """The measurement drivers (not part of the library): moe_counters links the library."""
+    if not os.path.exists(LIB):
+        build()
     tmp = COUNTERS + ".tmp"
     _run([HIPCC, *FLAGS, COUNTERS + ".hip", "-L" + PKG, "-lmoe_fp8", "-Wl,-rpath,$ORIGIN/..",
           "-o", tmp])
@@ -58,8 +65,9 @@ def build(verbose: bool = False) -> str:
     tmp = HBM_READ + ".tmp"
     _run([HIPCC, *FLAGS, HBM_READ + ".hip", "-o", tmp])
     os.replace(tmp, HBM_READ)
-    return LIB
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if "--tools" in sys.argv:
+        build_tools()
