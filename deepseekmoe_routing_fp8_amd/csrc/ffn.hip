@@ -37,7 +37,19 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
-constexpr int kMT = 160;              // max rows of one expert per tile (multiple of 16)
+constexpr int kMT = 192;              // max rows of one expert per tile (multiple of 16)
+constexpr int kMTShort = 160;         // tile height when segments are short (and the bound
+                                      // on the tile count: every plan uses >= 160-row tiles)
+constexpr int kMTMx = 160;            // power-of-two variant: 12 tiles of it would spill
+
+// Tile height of a call: 192 rows when the segments average 256 rows or more (a tile's
+// weights are streamed once per M tile, so taller tiles cut the weight traffic of long
+// segments; measured 6% faster on the V3 gate/up at 16384 tokens), else 160 (at about
+// 140 rows per expert the shared expert's taller tiles only add compute where the
+// launch is balanced).
+inline int tile_rows(int64_t n_rows, int32_t n_experts, bool mx) {
+  return !mx && n_rows >= 256 * (int64_t)n_experts ? kMT : kMTShort;
+}
 constexpr int kThreads = 512;         // 8 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxExperts = 1024;
@@ -45,7 +57,7 @@ constexpr int kMaxExperts = 1024;
 struct Tile {
   int32_t e;     // expert
   int32_t m0;    // first permuted row of the tile
-  int32_t mlen;  // rows in the tile (1..kMT)
+  int32_t mlen;  // rows in the tile (1..the call's tile height <= kMT)
   int32_t lo;    // first permuted row of the expert (identity token map)
 };
 
@@ -72,9 +84,11 @@ __device__ __forceinline__ v8i join(const uint4& lo, const uint4& hi) {
 
 // Tile plan: split every expert's rows into near-equal M tiles of at most kMT rows and
 // order the experts by descending row count (ties: lower index first), so the longest
-// tiles start first and the short ones fill the end of the launch.
+// tiles start first and the short ones fill the end of the launch. n_tiles[0] is the tile
+// count; n_tiles[1] the tiles of experts with two or more (they come first), which the
+// GEMM kernels schedule so that an expert's tiles share its weight stream (wg_work).
 __global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
-                                                               int n_experts, int n_rows,
+                                                               int n_experts, int n_rows, int mt,
                                                                int max_tiles,
                                                                Tile* __restrict__ tiles,
                                                                int32_t* __restrict__ n_tiles) {
@@ -82,16 +96,19 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __
   __shared__ int nt_r[kMaxExperts];
   __shared__ int start_r[kMaxExperts];
   __shared__ int wsum[kMaxExperts / kWave];
+  __shared__ int multi_s;
   const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
+  if (e == 0) multi_s = 0;
   int lo = 0, hi = 0, nt = 0;
   if (e < n_experts) {
     lo = min(max(offsets[e], 0), n_rows);
     hi = min(max(offsets[e + 1], lo), n_rows);
-    nt = (hi - lo + kMT - 1) / kMT;
+    nt = (hi - lo + mt - 1) / mt;
   }
   const int m = hi - lo;
   len_s[e] = m;
   __syncthreads();
+  if (nt >= 2) atomicAdd(&multi_s, nt);
   int rank = 0;
   if (e < n_experts) {
     for (int j = 0; j < n_experts; ++j) {
@@ -116,7 +133,9 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __
   start_r[e] = before + inc - v;
   if (e == kMaxExperts - 1) {
     // offsets that are not monotone cannot overflow the grid
-    *n_tiles = min(before + inc, max_tiles);
+    const int total = min(before + inc, max_tiles);
+    n_tiles[0] = total;
+    n_tiles[1] = min(multi_s, total);
   }
   __syncthreads();
   if (e < n_experts && nt > 0) {
@@ -453,6 +472,9 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
         p0[(ts + 1) & 1] = mfma_fp8(A0, bq[(ts + 1) % 3]);
         p1[(ts + 1) & 1] = mfma_fp8(A1, bq[(ts + 1) % 3]);
       }
+      // the MFMAs of tile t+1 are issued before tile t is promoted (left to itself the
+      // compiler promotes each tile right behind its own MFMAs and waits out their latency)
+      __builtin_amdgcn_sched_barrier(0);
       const float c0 = sa[ts % 3] * s0, c1 = sa[ts % 3] * s1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -701,6 +723,44 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
 // Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD,
 // so the tile's activation rows are fetched into that XCD's L2 once.
 // ------------------------------------------------------------------------------------
+// Work of workgroup L: M tile `tile` and its workgroup `wg` of nwg (n-blocks wg*nb_per ..).
+// Workgroup L runs on XCD L % 8. When nwg is a multiple of 8, tiles of experts with
+// several M tiles (the first n_tiles[1] of the plan) are laid out so that workgroup wg of
+// every such tile runs on XCD wg % 8 at consecutive dispatch slots: the tiles of one
+// expert then stream the same weight chunks at the same time through one L2 (the V3
+// gate/up launch at 16384 tokens measured 6% faster). Other tiles, and every tile when
+// nwg is not a multiple of 8 (the layout would leave XCDs idle), keep all their
+// workgroups on one XCD, consecutively, so that XCD's L2 fetches the tile's activation
+// rows once. Returns false for a workgroup without work.
+__device__ __forceinline__ bool wg_work(const FfnArgs& a, int L, int* tile, int* wg) {
+  const int nwg = (a.n_nb + a.nb_per - 1) / a.nb_per;
+  const int total = min(a.n_tiles[0], a.max_tiles);
+  const int multi = nwg % kXcds == 0 ? min(max(a.n_tiles[1], 0), total) : 0;
+  const int G = (nwg + kXcds - 1) / kXcds;          // rows of 8 workgroups per shared tile
+  const int la = kXcds * G * multi;
+  if (L < la) {
+    const int r = L / kXcds;
+    *tile = r / G;
+    *wg = (r % G) * kXcds + L % kXcds;
+    return *wg < nwg;
+  }
+  const int lb = L - la, xcd = lb % kXcds, slot = lb / kXcds;
+  *tile = multi + (slot / nwg) * kXcds + xcd;
+  *wg = slot % nwg;
+  return *tile < total;
+}
+
+// Grid of a GEMM launch over at most max_tiles tiles of n_rows rows with nwg workgroups
+// each, enough for any split of the plan between the two layouts of wg_work: with NA
+// shared-layout tiles it needs 8*G*NA + nwg*(tiles - NA + 7) workgroups, and NA < n_rows/80
+// (an expert with nt >= 2 tiles holds more than 160 * (nt - 1) >= 80 * nt rows).
+inline int64_t ffn_grid(int64_t max_tiles, int64_t nwg, int64_t n_rows) {
+  if (nwg % kXcds != 0) return nwg * (max_tiles + kXcds);
+  const int64_t G = nwg / kXcds;
+  const int64_t na = std::min<int64_t>(max_tiles, n_rows / (kMTShort / 2) + 1);
+  return nwg * (max_tiles + kXcds) + (kXcds * G - nwg) * na;
+}
+
 template <int PHASE, typename YT, bool MX>
 __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   __shared__ __attribute__((aligned(128))) uint8_t ast0[kAStage];
@@ -717,16 +777,13 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
                                                      // block and K chunk; 0 past the last chunk
   __shared__ float red[PHASE == 1 ? kFWaves * kMT : 1];
   constexpr bool GU = PHASE != 2;
-  const int L = blockIdx.x;
-  const int xcd = L % kXcds, slot = L / kXcds;
-  const int nwg = (a.n_nb + a.nb_per - 1) / a.nb_per;   // workgroups per tile
-  const int tile = (slot / nwg) * kXcds + xcd;
-  const int nb0 = (slot % nwg) * a.nb_per;
+  int tile, wg;
+  if (!wg_work(a, blockIdx.x, &tile, &wg)) return;
+  const int nb0 = wg * a.nb_per;
   const int nbn = min(a.nb_per, a.n_nb - nb0);
-  if (tile >= min(*a.n_tiles, a.max_tiles)) return;
   const Tile tl = a.tiles[tile];
   // a workspace that does not hold this call's plan must not lead out of bounds
-  if (tl.e < 0 || tl.e >= a.n_experts || tl.mlen < 1 || tl.mlen > kMT || tl.m0 < 0 ||
+  if (tl.e < 0 || tl.e >= a.n_experts || tl.mlen < 1 || tl.mlen > (MX ? kMTMx : kMT) || tl.m0 < 0 ||
       tl.m0 > a.n_rows - tl.mlen)
     return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -778,7 +835,10 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
     case 5: case 6: ffn_main<PHASE, YT, 6, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
     case 7: case 8: ffn_main<PHASE, YT, 8, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
     case 9: ffn_main<PHASE, YT, 9, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
-    default: ffn_main<PHASE, YT, 10, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 10: ffn_main<PHASE, YT, 10, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
+    default:
+      if constexpr (!MX) ffn_main<PHASE, YT, 12, R, MX>(a, tl, nb0, nbn, wave, lane, sh);
+      break;
   }
 }
 
@@ -791,7 +851,7 @@ struct WsLayout {
 
 inline WsLayout ws_layout(const moe_config* c, int32_t n_experts, int64_t n_rows) {
   WsLayout L;
-  L.max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
+  L.max_tiles = (n_rows + kMTShort - 1) / kMTShort + n_experts;
   size_t off = 0;
   L.tiles = off;
   off = align256(off + (size_t)L.max_tiles * sizeof(Tile));
@@ -828,7 +888,6 @@ struct FfnCall {
   uint8_t* hq;
   float* hs;
   float* xsp;
-  unsigned grid_tiles;   // M-tile slots, padded to a multiple of the XCD count
 };
 
 moe_status ffn_check(const moe_config* cfg, int32_t n_experts, int64_t n_rows, void* ws,
@@ -846,16 +905,15 @@ moe_status ffn_check(const moe_config* cfg, int32_t n_experts, int64_t n_rows, v
   if (n_rows == 0) return MOE_OK;
   if (!ws || ws_bytes < f->L.total) return MOE_ERR_WORKSPACE;
   // total work-items of the larger launch must fit the 32-bit grid size
-  const int64_t grid_tiles = (f->L.max_tiles + kXcds - 1) / kXcds * kXcds;
   const int64_t nb_max = std::max<int64_t>(cfg->inter / kTile, (cfg->hidden + 255) / 256);
-  if (grid_tiles * nb_max * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (ffn_grid(f->L.max_tiles, nb_max, n_rows) * kFThreads >= ((int64_t)1 << 32))
+    return MOE_ERR_UNSUPPORTED;
   uint8_t* base = static_cast<uint8_t*>(ws);
   f->tiles = reinterpret_cast<Tile*>(base + f->L.tiles);
   f->ntiles = reinterpret_cast<int32_t*>(base + f->L.ntiles);
   f->hq = base + f->L.hq;
   f->hs = reinterpret_cast<float*>(base + f->L.hs);
   f->xsp = reinterpret_cast<float*>(base + f->L.xsp);
-  f->grid_tiles = (unsigned)grid_tiles;
   return MOE_OK;
 }
 
@@ -875,7 +933,8 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
   hipStream_t s = as_stream(stream);
   const int H = cfg->hidden, I = cfg->inter;
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
-                     (int)n_rows, (int)f.L.max_tiles, f.tiles, f.ntiles);
+                     (int)n_rows, tile_rows(n_rows, n_experts, cfg->scale_mode == 1),
+                     (int)f.L.max_tiles, f.tiles, f.ntiles);
   // also without tokens: every row's scale is then written as 0, never left undefined
   hipLaunchKernelGGL(ffn_gather_scales_kernel,
                        dim3((unsigned)f.L.max_tiles, (unsigned)((H / kTile + kGatherChunks - 1) / kGatherChunks)),
@@ -884,13 +943,11 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
                        row_token, H / kTile, f.xsp);
   FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, f.xsp, n_tokens,
              row_token, w1, w1s, w3, w3s, H, I, I / kTile, kNbPerWg1, f.hq, f.hs, nullptr};
-  const unsigned nwg = (unsigned)((a1.n_nb + a1.nb_per - 1) / a1.nb_per);
+  const dim3 grid((unsigned)ffn_grid(f.L.max_tiles, (a1.n_nb + a1.nb_per - 1) / a1.nb_per, n_rows));
   if (cfg->scale_mode == 1)
-    hipLaunchKernelGGL((ffn_kernel<1, uint16_t, true>), dim3(f.grid_tiles * nwg), dim3(kFThreads), 0,
-                       s, a1);
+    hipLaunchKernelGGL((ffn_kernel<1, uint16_t, true>), grid, dim3(kFThreads), 0, s, a1);
   else
-    hipLaunchKernelGGL((ffn_kernel<1, uint16_t, false>), dim3(f.grid_tiles * nwg), dim3(kFThreads), 0,
-                       s, a1);
+    hipLaunchKernelGGL((ffn_kernel<1, uint16_t, false>), grid, dim3(kFThreads), 0, s, a1);
   return launch_status();
 }
 
@@ -908,7 +965,7 @@ moe_status ffn_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows, co
   FfnArgs a2{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, f.hq, f.hs, n_rows,
              nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256, down_nb_per(n_rows, n_experts),
              nullptr, nullptr, y};
-  const dim3 grid(f.grid_tiles * (unsigned)((a2.n_nb + a2.nb_per - 1) / a2.nb_per));
+  const dim3 grid((unsigned)ffn_grid(f.L.max_tiles, (a2.n_nb + a2.nb_per - 1) / a2.nb_per, n_rows));
   const bool mx = cfg->scale_mode == 1;
   if (yt == MOE_BF16 && mx)
     hipLaunchKernelGGL((ffn_kernel<2, uint16_t, true>), grid, dim3(kFThreads), 0, s, a2);
@@ -932,7 +989,7 @@ moe_status ffn_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows, co
 namespace moe {
 
 size_t ffn_plan_bytes(int32_t n_experts, int64_t n_rows) {
-  const int64_t max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
+  const int64_t max_tiles = (n_rows + kMTShort - 1) / kMTShort + n_experts;
   return align256((size_t)max_tiles * sizeof(Tile)) + 256;
 }
 
@@ -940,12 +997,12 @@ moe_status ffn_plan_launch(const int32_t* offsets, int32_t n_experts, int64_t n_
                            hipStream_t s) {
   if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 1 || n_rows >= ((int64_t)1 << 31))
     return MOE_ERR_SHAPE;
-  const int64_t max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
+  const int64_t max_tiles = (n_rows + kMTShort - 1) / kMTShort + n_experts;
   Tile* tiles = static_cast<Tile*>(plan);
   int32_t* nt = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(plan) +
                                            align256((size_t)max_tiles * sizeof(Tile)));
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
-                     (int)n_rows, (int)max_tiles, tiles, nt);
+                     (int)n_rows, tile_rows(n_rows, n_experts, false), (int)max_tiles, tiles, nt);
   return launch_status();
 }
 
@@ -959,18 +1016,17 @@ moe_status ffn_grouped_gemm_launch(const void* plan, int32_t n_experts, int64_t 
   // per-lane operand offsets into A and the scale array are 32-bit
   if (n_rows * (int64_t)K >= ((int64_t)1 << 32) || n_rows * (int64_t)(K / kTile) * 4 >= ((int64_t)1 << 31))
     return MOE_ERR_UNSUPPORTED;
-  const int64_t max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
-  const int64_t grid_tiles = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  const int64_t max_tiles = (n_rows + kMTShort - 1) / kMTShort + n_experts;
   const int n_nb = (N + 255) / 256;
   const int nbp = down_nb_per(n_rows, n_experts);
   const int64_t nwg = (n_nb + nbp - 1) / nbp;
-  if (grid_tiles * nwg * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (ffn_grid(max_tiles, nwg, n_rows) * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   const Tile* tiles = static_cast<const Tile*>(plan);
   const int32_t* nt = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(plan) +
                                                        align256((size_t)max_tiles * sizeof(Tile)));
   FfnArgs a{tiles, nt, (int)max_tiles, n_experts, (int)n_rows, aq, as_cm, n_rows, nullptr, w, wsc,
             nullptr, nullptr, N, K, n_nb, nbp, nullptr, nullptr, y};
-  const dim3 grid((unsigned)(grid_tiles * nwg));
+  const dim3 grid((unsigned)ffn_grid(max_tiles, nwg, n_rows));
   if (yt == MOE_BF16)
     hipLaunchKernelGGL((ffn_kernel<2, uint16_t, false>), grid, dim3(kFThreads), 0, s, a);
   else
@@ -990,11 +1046,10 @@ moe_status ffn_recompute_launch(const void* plan, int32_t n_experts, int64_t n_r
   // per-lane operand offsets into xq and the chunk-major scales are 32-bit
   if (n_tokens * (int64_t)H >= ((int64_t)1 << 32) || n_rows * (int64_t)(H / kTile) * 4 >= ((int64_t)1 << 31))
     return MOE_ERR_UNSUPPORTED;
-  const int64_t max_tiles = (n_rows + kMT - 1) / kMT + n_experts;
-  const int64_t grid_tiles = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  const int64_t max_tiles = (n_rows + kMTShort - 1) / kMTShort + n_experts;
   const int n_nb = I / kTile;
   const int64_t nwg = (n_nb + kNbPerWg1 - 1) / kNbPerWg1;
-  if (grid_tiles * nwg * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (ffn_grid(max_tiles, nwg, n_rows) * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   const Tile* tiles = static_cast<const Tile*>(plan);
   const int32_t* nt = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(plan) +
                                                        align256((size_t)max_tiles * sizeof(Tile)));
@@ -1005,7 +1060,7 @@ moe_status ffn_recompute_launch(const void* plan, int32_t n_experts, int64_t n_r
                        row_token, H / kTile, xsp);
   FfnArgs a{tiles, nt, (int)max_tiles, n_experts, (int)n_rows, xq, xsp, n_tokens, row_token, w1, w1s,
             w3, w3s, H, I, n_nb, kNbPerWg1, nullptr, nullptr, a_out, b_out};
-  hipLaunchKernelGGL((ffn_kernel<3, float, false>), dim3((unsigned)(grid_tiles * nwg)), dim3(kFThreads), 0,
+  hipLaunchKernelGGL((ffn_kernel<3, float, false>), dim3((unsigned)ffn_grid(max_tiles, nwg, n_rows)), dim3(kFThreads), 0,
                      s, a);
   return launch_status();
 }

@@ -439,6 +439,10 @@ def _relerr(a, b):
     (896, 640, 2, [77, 161], True),
     # the V3 expert shape (H = 7168, I = 2048): a full 160-row tile, a ragged one, one row
     (7168, 2048, 3, [160, 137, 1], False),
+    # segments averaging >= 256 rows get 192-row tiles (12 16-row tiles: 380 -> 192 + 188,
+    # 370 -> 192 + 178) beside shorter ones (200 -> 112 + 96)
+    (1024, 512, 3, [380, 370, 200], False),
+    (768, 384, 2, [384, 191], True),
     # the largest contraction the kernel takes: K = 16384 in each phase
     (16384, 256, 2, [40, 7], False),
     (256, 16384, 2, [33, 0], False),
