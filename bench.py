@@ -48,7 +48,7 @@ def ffn_algorithmic_bytes(cfg, counts):
             "experts": experts}
 
 
-COUNTER_FILE = os.path.join(ROOT, "profiles", "ffn_gate_up_v3_prefill_counters.txt")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "moe_step_v3_prefill_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "deepseekmoe_routing_fp8_amd", "csrc", f)
                   for f in ("ffn.hip", "common.h")]
 
@@ -366,7 +366,10 @@ def other_configs(layer, warmup: int, decode_steps: int, args_skewed_steps: int 
         log(f"[bench] skewed: {args_skewed_steps} steps, bias from 0, updated every step")
         layer.bias.zero_()
         res["skewed"] = measure(layer, cfg, xs, args_skewed_steps, 0, reset_bias=False)
+        xs_p2 = xs[:20]   # the power-of-two variant is compared on the first 20 batches
         del xs
+        layer.bias.zero_()
+        skewed_default_20 = measure(layer, cfg, xs_p2, len(xs_p2), 0, reset_bias=False)
         # per-sequence balance loss / allocation entropy of the last skewed step's routing
         # (4 sequences of 4096 tokens); timed on its own, it is not part of the forward step
         res["seq_balance"] = time_seq_balance(layer, cfg, 4096)
@@ -384,7 +387,18 @@ def other_configs(layer, warmup: int, decode_steps: int, args_skewed_steps: int 
         res["pow2_scales"] = measure(p2, cfg, device_batches(cfg, 1), 30, warmup)
         res["pow2_scales"]["note"] = ("opt-in variant (scale_mode 1): power-of-two 1x128 / 128x128 "
                                       "scales applied by the MFMA, FP32 accumulation across K")
-        del p2
+        # the same variant where compute matters: the skewed T=16384 step, 20 fresh batches
+        # from bias 0, beside the default path on the same batches
+        cs = synth.PRESETS["v3_skewed"]
+        p2.bias.zero_()
+        r2 = measure(p2, cs, xs_p2, len(xs_p2), 0, reset_bias=False)
+        res["pow2_scales_skewed"] = {
+            "steps": len(xs_p2), "pow2_ms_per_step": r2["ms_per_step"],
+            "default_ms_per_step": skewed_default_20["ms_per_step"],
+            "pow2_ffn_ms": r2["ffn_ms"], "default_ffn_ms": skewed_default_20["ffn_ms"],
+            "pow2_tflops_fp8": r2["tflops_fp8"], "default_tflops_fp8": skewed_default_20["tflops_fp8"],
+            "note": "first 20 fresh skewed batches, bias from 0 updated every step, both paths"}
+        del p2, xs_p2
         # forward + FP8 backward on the headline workload (its own layer with the dgrad
         # operands and FP32 weight-gradient buffers)
         log("[bench] backward: weights and transposed dgrad operands on the device")

@@ -11,6 +11,7 @@ kernel-trace average duration, and from these GB/s and the MFMA figures.
 
 Usage: python summarize_counters.py --workload v3_prefill --log driver.log --fetch D
          --write D --util D --trace D --cmd "<commands>" [--sources f1 f2 ...]
+       python summarize_counters.py --trace-only --trace D --title T --cmd "<command>"
 """
 from __future__ import annotations
 
@@ -54,13 +55,48 @@ def mean(v):
     return sum(v) / len(v) if v else float("nan")
 
 
+def trace_table(trace: str, title: str, cmd: str, note: str):
+    """Markdown table of a --kernel-trace --stats run (kernel, calls, average/min/max us,
+    share of GPU time)."""
+    st = rows(trace, "kernel_stats.csv")
+    print(f"# Kernel trace: {title}\n")
+    if note:
+        print(note + "\n")
+    print("Command (repository root `$R`; library built with "
+          "`python deepseekmoe_routing_fp8_amd/build.py --tools`):\n")
+    print("```\ncd /tmp && export TMPDIR=/tmp")
+    for c in cmd.split(" ;; "):
+        print(c)
+    print("```\n")
+    # steady state: every dispatch of a kernel but its first (the first call of a kernel
+    # in a process also loads its code object)
+    per = defaultdict(list)
+    for r in rows(trace, "kernel_trace.csv"):
+        per[short(r["Kernel_Name"])].append(
+            (int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    print("| kernel | calls | average us | average us without the first call | min us | max us | "
+          "share of GPU time |")
+    print("|---|---|---|---|---|---|---|")
+    for r in sorted(st, key=lambda r: -float(r["TotalDurationNs"])):
+        k = short(r["Name"])
+        d = [v for _, v in sorted(per.get(k, []))][1:]
+        steady = f"{sum(d) / len(d):.1f}" if d else "-"
+        print(f"| `{k}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {steady} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+              f"{float(r['Percentage']):.2f}% |")
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--workload", required=True)
-    ap.add_argument("--log", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--util", required=True)
+    ap.add_argument("--trace-only", action="store_true",
+                    help="print only the kernel-trace table of --trace (with --title, --note)")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--note", default="")
+    ap.add_argument("--workload")
+    ap.add_argument("--log")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--util")
     ap.add_argument("--trace", required=True)
     ap.add_argument("--cmd", required=True)
     ap.add_argument("--flops", nargs="*", default=[],
@@ -69,6 +105,9 @@ def main():
                     help="kernel=bytes per dispatch (algorithmic), for the traffic ratio")
     ap.add_argument("--sources", nargs="*", default=[])
     a = ap.parse_args()
+    if a.trace_only:
+        trace_table(a.trace, a.title, a.cmd, a.note)
+        return
 
     log = open(a.log).read()
     m = re.search(r"copy_kernel: (\d+) bytes read \+ (\d+) bytes written", log)
