@@ -50,8 +50,6 @@ constexpr int kMTMx = 160;            // power-of-two variant: 12 tiles of it wo
 inline int tile_rows(int64_t n_rows, int32_t n_experts, bool mx) {
   return !mx && n_rows >= 256 * (int64_t)n_experts ? kMT : kMTShort;
 }
-constexpr int kThreads = 512;         // 8 waves
-constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxExperts = 1024;
 
 struct Tile {
@@ -75,12 +73,6 @@ __device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& a, const v8i& b, const
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 
-__device__ __forceinline__ v8i join(const uint4& lo, const uint4& hi) {
-  v8i r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-  return r;
-}
 
 // Tile plan: split every expert's rows into near-equal M tiles of at most mt rows and
 // order the experts by descending row count (ties: lower index first), so the longest
@@ -189,16 +181,6 @@ __global__ __launch_bounds__(kMT) void ffn_gather_scales_kernel(const Tile* __re
 // lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0070; }
 
-// Wait for this wave's operations of one pipeline stage, then a workgroup barrier. The
-// empty asm statements keep the compiler from moving LDS accesses across it.
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations but not for
 // its global loads in flight (__syncthreads() would add s_waitcnt vmcnt(0) and drain the
 // weight ring).
@@ -208,16 +190,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct global -> LDS copy: lane i of the wave writes its 16 bytes at lds + i * 16.
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds_wave) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave, 4, 0, 0);
 }
 
 // Tile geometry. A workgroup of 8 waves computes 256 weight rows (16 fragments of 16
@@ -251,6 +223,13 @@ constexpr int kStepOps = 4 + kActDma + 1;        // vector-memory ops per wave p
 constexpr int kMaxRing = 5;   // ring slots (depth 4) + the epilogue staging slot
 constexpr int kMaxNbPerWg = 4;                   // n-blocks one workgroup runs back to back
 constexpr int kNbPerWg1 = 2, kNbPerWg2 = 4;      // gate/up (16 blocks at I = 2048), down
+
+// n-blocks per gate/up workgroup: one with tall tiles (measured 1.7% faster on the V3
+// gate/up at 16384 skewed tokens: twice the workgroups balance the long launch better),
+// else two (the same at 4096 tokens; four measured 2-4% slower everywhere).
+inline int gate_up_nb_per(int64_t n_rows, int32_t n_experts, bool mx) {
+  return tile_rows(n_rows, n_experts, mx) == kMT ? 1 : kNbPerWg1;
+}
 
 // n-blocks per down-projection workgroup: with a few rows per expert (decode) each
 // workgroup streams weights for little compute, and one block per workgroup balances the
@@ -363,21 +342,23 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   }
   const int soff = (tl.m0 + min(tid, tl.mlen - 1)) * 4;   // permuted row of this lane's scale
 
-  // this wave's two fragments of n-block nb: the first fragment row and the row offset
-  const int64_t per_expert = (int64_t)a.H * a.I;
-  const int64_t frow = (int64_t)nkc * kFragBytes;   // bytes of one 16-row fragment row
-  auto wrow_of = [&](int nb) -> int64_t {
-    return GU ? (int64_t)nb * kTile + wave * 16 : (int64_t)nb * 256 + wave * 32;
+  // This wave's two fragments of n-block nb: one descriptor per fragment row, formed per
+  // step from the expert's base (32-bit offsets: H * I < 2^31, checked by every launch)
+  const uint32_t frow = (uint32_t)nkc * kFragBytes;   // bytes of one 16-row fragment row
+  const uint8_t* const wbaseA = a.wa + (int64_t)tl.e * a.H * a.I;
+  const uint8_t* const wbaseB = GU ? a.wb + (int64_t)tl.e * a.H * a.I : wbaseA;
+  auto wrow_of = [&](int nb) -> int {
+    return GU ? nb * kTile + wave * 16 : nb * 256 + wave * 32;
   };
   auto wdesc = [&](int nb, int f) __attribute__((always_inline)) {
-    const int64_t wrow = wrow_of(nb);
+    const int wrow = wrow_of(nb);
     const uint8_t* fb;
     if (GU) {
-      fb = (f == 0 ? a.wa : a.wb) + (int64_t)tl.e * per_expert + (wrow / 16) * frow;
+      fb = (f == 0 ? wbaseA : wbaseB) + (uint32_t)(wrow / 16) * frow;
     } else {
       // H % 256 == 128: the last block is half used; its idle waves read block 0
-      const int64_t n16 = (wrow < a.H ? wrow : 0) / 16;
-      fb = a.wa + (int64_t)tl.e * per_expert + (n16 + f) * frow;
+      const uint32_t n16 = (uint32_t)(wrow < a.H ? wrow : 0) / 16;
+      fb = wbaseA + (n16 + f) * frow;
     }
     return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(fb), 0, (int)frow, 0x00020000);
   };
@@ -573,7 +554,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
     for (int s0 = RING; s0 < nsteps; s0 += RING) group(it, s0, std::false_type{});
 
     // epilogue of n-block nb; the next block's first chunks are already in flight
-    const int64_t wrow = wrow_of(nb);
+    const int wrow = wrow_of(nb);
     if (PHASE == 1) {
       // SwiGLU, amax over the 128 columns of the group (4 per lane, 4 lane groups, 8 waves)
       // h = silu(G) * U replaces G in acc0. silu(g) = g / (1 + 2^(-g log2 e)) with the
@@ -945,7 +926,8 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
                        f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xs, n_tokens,
                        row_token, H / kTile, f.xsp);
   FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, f.xsp, n_tokens,
-             row_token, w1, w1s, w3, w3s, H, I, I / kTile, kNbPerWg1, f.hq, f.hs, nullptr};
+             row_token, w1, w1s, w3, w3s, H, I, I / kTile,
+             gate_up_nb_per(n_rows, n_experts, cfg->scale_mode == 1), f.hq, f.hs, nullptr};
   const dim3 grid((unsigned)ffn_grid(f.L.max_tiles, (a1.n_nb + a1.nb_per - 1) / a1.nb_per, n_rows));
   if (cfg->scale_mode == 1)
     hipLaunchKernelGGL((ffn_kernel<1, uint16_t, true>), grid, dim3(kFThreads), 0, s, a1);
@@ -1016,6 +998,7 @@ moe_status ffn_grouped_gemm_launch(const void* plan, int32_t n_experts, int64_t 
   if (N <= 0 || K <= 0 || N % kTile || K % kTile || K > kMaxChunks * kTile) return MOE_ERR_SHAPE;
   if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 1 || n_rows >= ((int64_t)1 << 31))
     return MOE_ERR_SHAPE;
+  if ((int64_t)N * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;   // 32-bit weight offsets
   // per-lane operand offsets into A and the scale array are 32-bit
   if (n_rows * (int64_t)K >= ((int64_t)1 << 32) || n_rows * (int64_t)(K / kTile) * 4 >= ((int64_t)1 << 31))
     return MOE_ERR_UNSUPPORTED;
@@ -1046,6 +1029,7 @@ moe_status ffn_recompute_launch(const void* plan, int32_t n_experts, int64_t n_r
   if (n_experts < 1 || n_experts > kMaxExperts || n_rows < 1 || n_rows >= ((int64_t)1 << 31) ||
       n_tokens < 0)
     return MOE_ERR_SHAPE;
+  if ((int64_t)H * I >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;   // 32-bit weight offsets
   // per-lane operand offsets into xq and the chunk-major scales are 32-bit
   if (n_tokens * (int64_t)H >= ((int64_t)1 << 32) || n_rows * (int64_t)(H / kTile) * 4 >= ((int64_t)1 << 31))
     return MOE_ERR_UNSUPPORTED;

@@ -443,11 +443,16 @@ def _relerr(a, b):
     # 370 -> 192 + 178) beside shorter ones (200 -> 112 + 96)
     (1024, 512, 3, [380, 370, 200], False),
     (768, 384, 2, [384, 191], True),
+    # tall tiles with one n-block per gate/up workgroup: 8 and 16 workgroups per tile, the
+    # shared-weight XCD layout for the multi-tile experts (600 -> 4 tiles, 520 -> 3)
+    (512, 1024, 2, [600, 300], False),
+    (256, 2048, 2, [520, 100], False),
     # the largest contraction the kernel takes: K = 16384 in each phase
     (16384, 256, 2, [40, 7], False),
     (256, 16384, 2, [33, 0], False),
 ])
-def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity):
+@pytest.mark.parametrize("ydt", ["float32", "bfloat16"])   # the two down-projection layouts
+def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity, ydt):
     import dataclasses
     rng = np.random.default_rng(H + I + E)
     rows = int(sum(loads))
@@ -460,12 +465,12 @@ def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity):
     row_token = (np.arange(rows) - np.repeat(offsets[:-1], loads)).astype(np.int32) if identity \
         else rng.integers(0, T, rows).astype(np.int32)
     w = _expert_set(rng, E, H, I)
-    say(f"grouped_ffn H={H} I={I} E={E} loads={loads} identity={identity}")
+    say(f"grouped_ffn H={H} I={I} E={E} loads={loads} identity={identity} y={ydt}")
     y = lib.moe_grouped_ffn_fp8(lib.make_config(cfg), E, rows, dev(xq), dev(xs),
                                 None if identity else dev(row_token), dev(offsets),
-                                *_device_weights(lib, w), y_dtype=torch.float32)
+                                *_device_weights(lib, w), y_dtype=getattr(torch, ydt))
     torch.cuda.synchronize()
-    y = host(y)
+    y = y.float().cpu().numpy()
     for e in range(E):
         lo, hi = offsets[e], offsets[e + 1]
         if hi == lo:
@@ -476,7 +481,8 @@ def test_grouped_ffn_matches_oracle(lib, H, I, E, loads, identity):
         assert err < 5e-3, (e, err)
 
 
-def test_grouped_ffn_halves_equal_fused_call(lib):
+@pytest.mark.parametrize("ydt", ["float32", "bfloat16"])
+def test_grouped_ffn_halves_equal_fused_call(lib, ydt):
     """gate_up + down on one workspace gives the fused call's output bit for bit (a load
     mix with several M tiles per expert, so the tile order differs from expert order)."""
     import dataclasses
@@ -493,12 +499,12 @@ def test_grouped_ffn_halves_equal_fused_call(lib):
     row_token = rng.integers(0, T, rows).astype(np.int32)
     w = _device_weights(lib, _expert_set(rng, E, H, I))
     args = (dev(xq), dev(xs), dev(row_token), dev(offsets))
-    say("grouped_ffn halves vs fused")
-    y_fused = lib.moe_grouped_ffn_fp8(c, E, rows, *args, *w, y_dtype=torch.float32)
+    say(f"grouped_ffn halves vs fused, y={ydt}")
+    y_fused = lib.moe_grouped_ffn_fp8(c, E, rows, *args, *w, y_dtype=getattr(torch, ydt))
     ws = lib.moe_grouped_ffn_fp8_gate_up(c, E, rows, *args, *w[:4])
-    y_split = lib.moe_grouped_ffn_fp8_down(c, E, rows, w[4], w[5], ws, y_dtype=torch.float32)
+    y_split = lib.moe_grouped_ffn_fp8_down(c, E, rows, w[4], w[5], ws, y_dtype=getattr(torch, ydt))
     torch.cuda.synchronize()
-    assert np.array_equal(host(y_fused).view(np.uint32), host(y_split).view(np.uint32))
+    assert torch.equal(y_fused.view(torch.uint8), y_split.view(torch.uint8))
 
 
 def test_grouped_ffn_bf16_output_and_bad_tokens(lib):
