@@ -5,12 +5,16 @@ Each run directory holds rocprofv3's CSV output of one pass over the same driver
   --util   MfmaUtil, VALUBusy, LdsUtil, LDSBankConflict, SQ_INSTS_VALU_MFMA_MOPS_F8,
            SQ_INSTS_VALU_MFMA_MOPS_F6F4, GRBM_GUI_ACTIVE
   --trace  --kernel-trace --stats
+  --sq     optional: two passes of SQ wave-state counters (SQ_WAVE_CYCLES, SQ_WAIT_ANY,
+           SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_{ANY,VALU,LDS,VMEM,SCA}; SQ_INSTS_{VALU,MFMA,
+           LDS,SALU}, SQ_WAIT_INST_LDS, SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_IDX_ACTIVE,
+           SQ_WAVES, GRBM_GUI_ACTIVE)
 The copy kernel's readings calibrate the byte counters (its bytes are known from the
 driver's log). Per kernel: the mean per dispatch of every counter, HBM bytes, the
 kernel-trace average duration, and from these GB/s and the MFMA figures.
 
 Usage: python summarize_counters.py --workload v3_prefill --log driver.log --fetch D
-         --write D --util D --trace D --cmd "<commands>" [--sources f1 f2 ...]
+         --write D --util D --trace D [--sq D1 D2] --cmd "<commands>" [--sources f1 f2 ...]
        python summarize_counters.py --trace-only --trace D --title T --cmd "<command>"
 """
 from __future__ import annotations
@@ -104,6 +108,8 @@ def main():
     ap.add_argument("--bytes", nargs="*", default=[],
                     help="kernel=bytes per dispatch (algorithmic), for the traffic ratio")
     ap.add_argument("--sources", nargs="*", default=[])
+    ap.add_argument("--sq", nargs="*", default=[],
+                    help="run directories of the SQ wave-state passes (printed for the FFN kernels)")
     a = ap.parse_args()
     if a.trace_only:
         trace_table(a.trace, a.title, a.cmd, a.note)
@@ -176,6 +182,35 @@ def main():
             print(f"      algorithmic {alg_f[k] / 1e12:.4f} TFLOP per dispatch; counted "
                   f"{512 * mops / 1e12:.4f} TFLOP (x{512 * mops / alg_f[k]:.3f}); "
                   f"{alg_f[k] / (us * 1e-6) / 1e12:.1f} TFLOP/s algorithmic")
+    if a.sq:
+        sq = {}
+        for d in a.sq:
+            for k, cs in counters(d).items():
+                sq.setdefault(k, {}).update(cs)
+        print("#\n# Wave states of the FFN kernels (SQ counters, mean per dispatch). Wave time is "
+              "SQ_WAVE_CYCLES (quad-cycles summed over waves) = 100%: SQ_ACTIVE_INST_ANY (issuing or "
+              "executing an instruction), SQ_WAIT_INST_ANY (waiting for an instruction to issue: "
+              "dependencies, issue arbitration), SQ_WAIT_ANY (waiting at s_waitcnt or s_barrier); "
+              "the active time by instruction type (VALU includes the MFMA issue). MFMA busy = "
+              "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs): GRBM_GUI_ACTIVE as "
+              "collected sums the 8 XCDs' counts, so this matches the Mfma% column. Instructions "
+              "per MFMA from SQ_INSTS_*.")
+        for k in sorted(sq):
+            if not k.startswith("ffn_kernel"):
+                continue
+            c = {n: mean(v) for n, v in sq[k].items()}
+            wc = c.get("SQ_WAVE_CYCLES", float("nan"))
+            pct = lambda n: 100.0 * c.get(n, float("nan")) / wc
+            mf = c.get("SQ_INSTS_MFMA", float("nan"))
+            busy = 100.0 * c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (
+                c.get("GRBM_GUI_ACTIVE", float("nan")) / 8 * 1024)
+            print(f"  {k}: active {pct('SQ_ACTIVE_INST_ANY'):.1f}%, waiting to issue "
+                  f"{pct('SQ_WAIT_INST_ANY'):.1f}%, waiting at waitcnt/barrier {pct('SQ_WAIT_ANY'):.1f}%; "
+                  f"active on VALU {pct('SQ_ACTIVE_INST_VALU'):.1f}%, LDS {pct('SQ_ACTIVE_INST_LDS'):.1f}%, "
+                  f"VMEM {pct('SQ_ACTIVE_INST_VMEM'):.1f}%, scalar {pct('SQ_ACTIVE_INST_SCA'):.1f}%; "
+                  f"waiting for LDS issue {pct('SQ_WAIT_INST_LDS'):.1f}%; MFMA busy {busy:.1f}%; per MFMA "
+                  f"{(c.get('SQ_INSTS_VALU', 0) - mf) / mf:.2f} other VALU, {c.get('SQ_INSTS_LDS', 0) / mf:.2f} LDS, "
+                  f"{c.get('SQ_INSTS_SALU', 0) / mf:.2f} SALU instructions; {c.get('SQ_WAVES', 0):.0f} waves")
     if a.sources:
         h = hashlib.sha256()
         for f in a.sources:
