@@ -323,14 +323,17 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   const int last = nkc - 1;
   const int nsteps = (nkc + RING - 1) / RING * RING;   // steps per n-block
 
-  // activation copies of this lane: kActDma 16-byte units and one scale
+  // activation copies of this lane: kDma 16-byte units (rounds of 64 rows, as many as the
+  // NT 16-row tiles need) and one scale
+  constexpr int kDma = (NT * 16 * kTile + kActRound - 1) / kActRound;
+  static_assert(kDma <= kActDma, "copy rounds");
   const __amdgpu_buffer_rsrc_t adesc =
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.aq), 0, (int)(uint32_t)(a.n_tokens * K), 0x00020000);
   const __amdgpu_buffer_rsrc_t sdesc =
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.as), 0, (int)(uint32_t)((int64_t)a.n_rows * nkc * 4), 0x00020000);
-  int aoff[kActDma];
+  int aoff[kDma];
 #pragma unroll
-  for (int j = 0; j < kActDma; ++j) {
+  for (int j = 0; j < kDma; ++j) {
     const int unit = min((j * kActRound + wave * 1024 + lane * 16) / 16, kActBytes / 16 - 1);
     const int r = unit >> 3, seg = (unit & 7) ^ (r & 7);
     // rows past the tile and rows without a token read zeros (an offset at the end of
@@ -367,7 +370,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   const int wsel1 = GU ? 1 : wsel0;
 
   // A chunk's loads come in two groups: its weights (4 loads) and its activation copies
-  // (kActDma copies and 1 scale). Step g of n-block it loads the weights of chunk g of
+  // (kDma copies and 1 scale). Step g of n-block it loads the weights of chunk g of
   // that block; chunks past the block's last one (and blocks past the workgroup's range)
   // read zero weights. Activation copies depend on the chunk only.
   v8i W0[RING], W1[RING];
@@ -382,7 +385,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   auto issue_a = [&](int c, uint8_t* st) __attribute__((always_inline)) {
     const int cc = min(c, last);
 #pragma unroll
-    for (int j = 0; j < kActDma; ++j) {
+    for (int j = 0; j < kDma; ++j) {
       const int at = j * kActRound + wave * 1024;
       uint8_t* dst = at < kActBytes ? st + at : sh.junk;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(adesc, (lds_u8*)dst, 16, aoff[j], cc * kTile, 0, 0);
@@ -503,8 +506,8 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   constexpr int kEpiStores =
       PHASE == 1 ? kStageStores + 1 : (PHASE == 3 || sizeof(YT) == 4 ? 2 * NT : kYStores);
   static_assert(RING < kMaxRing, "the last LDS slot stages the epilogue");
-  constexpr int kWOps = 4, kAOps = kActDma + 1;        // loads per chunk: weights, copies
-  static_assert(kWOps + kAOps == kStepOps, "loads per chunk");
+  constexpr int kWOps = 4, kAOps = kDma + 1;           // loads per chunk: weights, copies
+  static_assert(kWOps + kAOps <= kStepOps, "loads per chunk");
   constexpr int kWaitEven = 2 * kWOps;                  // weights of the next two chunks
   constexpr int kWaitOdd = 2 * kWOps + 2 * kAOps;       // + the next pair's copies
   static_assert(kWaitOdd + kEpiStores <= 63, "vmcnt range");
