@@ -212,7 +212,7 @@ constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;       // 512
 constexpr int kNTS = kMT / 16;                   // 16-row tiles per M tile
 constexpr int kFragBytes = 16 * kTile;           // one 16 x 128 fragment: 2 KB
-constexpr int kActBytes = kMT * kTile;           // activation codes per chunk (20 KB)
+constexpr int kActBytes = kMT * kTile;           // activation codes per chunk (24 KB)
 constexpr int kActRound = kFThreads * 16;        // bytes one copy instruction per wave moves
 constexpr int kActDma = (kActBytes + kActRound - 1) / kActRound;   // copies per lane (3)
 constexpr int kScaleWaves = (kMT + kWave - 1) / kWave;             // waves copying scales
@@ -811,7 +811,8 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
 
   const FfnLds sh{{ast0, ast1, ast2, ast3, ast4}, junk, tok_s, &wsc[0][0], red, ast4};
   // Ring depth 4: three chunks (96 KB of weights per CU) in flight cover the loaded HBM
-  // latency, the accumulators of 10 16-row tiles still fit beside the ring, and K
+  // latency, the accumulators of 12 16-row tiles still fit beside the ring (three
+  // registers spilled, reloaded only in the epilogue), and K
   // chunk counts of the usual shapes (56, 16) divide by it, so no block ends in steps
   // of zero weights. (A depth of 5 for the shorter tiles measured 1.5% slower on the
   // V3 prefill gate/up: its 60 padded steps per block cost more than the depth gained.)
