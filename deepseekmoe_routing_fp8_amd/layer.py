@@ -11,7 +11,7 @@ shared segments) evaluates both; ``unpack`` recovers the row-major codes of one 
 """
 from __future__ import annotations
 
-from typing import Callable, Iterable, Optional
+from typing import Callable, Optional
 
 import numpy as np
 import torch
