@@ -79,8 +79,19 @@ def test_layer_pow2_matches_oracle(name):
 
 @pytest.mark.parametrize("name", ["tiny", "reduced"])
 def test_layer_matches_oracle(name):
+    _check_layer(synth.PRESETS[name], name)
+
+
+@pytest.mark.parametrize("T", [1, 17, 129])
+def test_layer_ragged_token_counts(T):
+    """One token (a decode step of one sequence), a count below one 16-row tile per
+    expert, and one past a multiple of 128 (a ragged last block in every token-axis pass)."""
+    import dataclasses
+    _check_layer(dataclasses.replace(synth.PRESETS["tiny"], tokens=T), f"tiny T={T}")
+
+
+def _check_layer(cfg, name):
     from deepseekmoe_routing_fp8_amd import MoELayer
-    cfg = synth.PRESETS[name]
     say(f"layer {name}: loading weights")
     layer = MoELayer(cfg)
     layer.load_from_synth()
@@ -280,6 +291,21 @@ def test_v3_decode_sampled(v3_layer):
     v3_layer.forward(x_device(cfg, x), update_bias=False)
     torch.cuda.synchronize()
     g_idx = _sampled_parity(v3_layer, cfg, x, bias, 3, 1)
+    _full_checks(v3_layer, cfg, x, bias, g_idx)
+
+
+@pytest.mark.timeout(900)
+def test_v3_single_token(v3_layer):
+    """One token through the V3 layer: 8 routed rows in 8 one-row segments + the shared
+    row; every check of the decode case at its smallest size."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.PRESETS["v3_decode"], tokens=1)
+    x = synth.hidden_states(cfg)
+    bias = v3_layer.bias.cpu().numpy()
+    say("V3 forward T=1")
+    v3_layer.forward(x_device(cfg, x), update_bias=False)
+    torch.cuda.synchronize()
+    g_idx = _sampled_parity(v3_layer, cfg, x, bias, 1, 2)
     _full_checks(v3_layer, cfg, x, bias, g_idx)
 
 
