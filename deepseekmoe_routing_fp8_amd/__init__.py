@@ -34,7 +34,7 @@ ENTRY_POINTS = (
     "moe_combine_backward", "moe_route_backward", "moe_route_backward_workspace_bytes",
     "moe_unpermute_sum", "moe_transpose_fp8_blocks", "moe_grouped_ffn_fp8_backward",
     "moe_grouped_ffn_backward_workspace_bytes", "moe_grouped_ffn_intermediate_offsets",
-    "moe_grouped_ffn_fp8_noalloc",
+    "moe_grouped_ffn_fp8_noalloc", "moe_grouped_ffn_fp8_gate_up_train",
 )
 MOE_ERR_SCRATCH = 7
 NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES
@@ -86,6 +86,8 @@ _sig = {
                                      _P, _P, ctypes.c_int, _P], ctypes.c_int),
     "moe_grouped_ffn_fp8_gate_up": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _SZ, _P], ctypes.c_int),
+    "moe_grouped_ffn_fp8_gate_up_train": ([_CFG, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "moe_grouped_ffn_fp8_down": ([_CFG, _I32, _I64, _P, _P, _P, ctypes.c_int, _P, _SZ, _P],
                                  ctypes.c_int),
     "moe_combine": ([_CFG, _I64, _P, ctypes.c_int, _P, _P, _P, _P, _P], ctypes.c_int),
@@ -101,8 +103,8 @@ _sig = {
     "moe_transpose_fp8_blocks": ([_I64, _I64, _I64, _P, _P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "moe_grouped_ffn_backward_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
     "moe_grouped_ffn_fp8_backward": ([_CFG, _I32, _I64, _I64, _P, _P, _P, ctypes.c_int, _P, _P, _P,
-                                      _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P,
-                                      ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
+                                      _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
+                                      _P, _P, ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _sig.items():
     _f = getattr(_lib, _name)
@@ -135,6 +137,11 @@ def _dev(t: torch.Tensor, dtype, name: str, shape=None):
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise MoEError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t: Optional[torch.Tensor], dtype, name: str, shape=None):
+    """_dev, or a NULL pointer for None."""
+    return ctypes.c_void_p(0) if t is None else _dev(t, dtype, name, shape)
 
 
 def _xdtype(x: torch.Tensor) -> int:
@@ -366,6 +373,25 @@ def moe_grouped_ffn_fp8_gate_up(cfg: moe_config, n_experts: int, n_rows: int, xq
     return ws
 
 
+def moe_grouped_ffn_fp8_gate_up_train(cfg: moe_config, n_experts: int, n_rows: int,
+                                      xq: torch.Tensor, xs: torch.Tensor,
+                                      row_token: Optional[torch.Tensor], offsets: torch.Tensor,
+                                      w1, w1s, w3, w3s, a: torch.Tensor = None,
+                                      b: torch.Tensor = None, ws: torch.Tensor = None, stream=None):
+    """moe_grouped_ffn_fp8_gate_up that also keeps the SwiGLU inputs -> (ws, a, b), with
+    a, b [n_rows, I] float32 for moe_grouped_ffn_fp8_backward."""
+    dev = xq.device
+    ws = _ffn_ws(cfg, n_experts, n_rows, ws, dev)
+    a = torch.empty((n_rows, cfg.inter), dtype=torch.float32, device=dev) if a is None else a
+    b = torch.empty((n_rows, cfg.inter), dtype=torch.float32, device=dev) if b is None else b
+    _check(_lib.moe_grouped_ffn_fp8_gate_up_train(
+        ctypes.byref(cfg), *_gate_up_args(cfg, n_experts, n_rows, xq, xs, row_token, offsets,
+                                          w1, w1s, w3, w3s),
+        _dev(a, torch.float32, "a", (n_rows, cfg.inter)), _dev(b, torch.float32, "b", (n_rows, cfg.inter)),
+        _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "moe_grouped_ffn_fp8_gate_up_train")
+    return ws, a, b
+
+
 def moe_grouped_ffn_fp8_down(cfg: moe_config, n_experts: int, n_rows: int, w2, w2s,
                              ws: torch.Tensor, y: torch.Tensor = None, y_dtype=torch.bfloat16,
                              stream=None):
@@ -529,8 +555,11 @@ def moe_grouped_ffn_fp8_backward(cfg: moe_config, n_experts: int, xq, xs, x, row
                                  dx_rows: torch.Tensor = None, dx_dtype=torch.float32,
                                  dw1: torch.Tensor = None, dw3: torch.Tensor = None,
                                  dw2: torch.Tensor = None, dw_dtype=torch.float32,
-                                 ws: torch.Tensor = None, stream=None):
-    """-> (dx_rows [n_rows, H], dw1 [E, I, H], dw3 [E, I, H], dw2 [E, H, I])."""
+                                 ws: torch.Tensor = None, a_saved: torch.Tensor = None,
+                                 b_saved: torch.Tensor = None, stream=None):
+    """-> (dx_rows [n_rows, H], dw1 [E, I, H], dw3 [E, I, H], dw2 [E, H, I]). ``a_saved``,
+    ``b_saved``: the SwiGLU inputs kept by moe_grouped_ffn_fp8_gate_up_train (both or
+    neither; without them they are recomputed from xq, xs)."""
     n_rows = dy.shape[0]
     T = xq.shape[0]
     H, I, E = cfg.hidden, cfg.inter, n_experts
@@ -550,6 +579,7 @@ def moe_grouped_ffn_fp8_backward(cfg: moe_config, n_experts: int, xq, xs, x, row
         _dev(w1, torch.uint8, "w1"), _dev(w1s, torch.float32, "w1s"), _dev(w3, torch.uint8, "w3"),
         _dev(w3s, torch.float32, "w3s"), _dev(w2t, torch.uint8, "w2t"), _dev(w2ts, torch.float32, "w2ts"),
         _dev(w13t, torch.uint8, "w13t"), _dev(w13ts, torch.float32, "w13ts"),
+        _opt(a_saved, torch.float32, "a_saved", (n_rows, I)), _opt(b_saved, torch.float32, "b_saved", (n_rows, I)),
         _dev(dy, torch.float32, "dy", (n_rows, H)), _dev(dx_rows, dx_rows.dtype, "dx_rows", (n_rows, H)),
         _dt(dx_rows), _dev(dw1, dw1.dtype, "dw1", (E, I, H)), _dev(dw3, dw1.dtype, "dw3", (E, I, H)),
         _dev(dw2, dw1.dtype, "dw2", (E, H, I)), _dt(dw1), _dev(ws, torch.uint8, "ws"), ws.numel(),

@@ -15,7 +15,8 @@
 //                      router GEMM and dW_r summed per expert in segment order;
 //   FFN backward       per expert segment, on the forward's tile plan:
 //     dy  -> 1x128 along H                  (dgrad operand)
-//     a = xq W1^T, b = xq W3^T              (the forward's gate/up launch, FP32 out)
+//     a = xq W1^T, b = xq W3^T              (the SwiGLU inputs: kept by a training forward,
+//                                            else recomputed by the gate/up launch, FP32)
 //     dh = dy W2                            (FP8 grouped GEMM, K = H, FP32 out)
 //     dg, du, h (FP32) -> [dg | du] 1x128 along I   (dgrad operand, K = 2I)
 //     dx_rows = [dg | du] [W1 ; W3]         (one FP8 grouped GEMM on [W1^T | W3^T])
@@ -189,7 +190,8 @@ __global__ __launch_bounds__(256) void route_bwd_gates_kernel(const float* __res
   }
 }
 
-template <typename XT>
+// dx: one block per token, four consecutive features per thread and step; every slot's
+// row of W_r is loaded before any is added, and the slots are added in order.
 __global__ __launch_bounds__(256) void route_bwd_dx_kernel(const float* __restrict__ dl,
                                                            const int32_t* __restrict__ idx,
                                                            const float* __restrict__ w_router,
@@ -198,19 +200,55 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(const float* __restri
   __shared__ int32_t es[kMaxTopK];
   __shared__ float ds[kMaxTopK];
   const int64_t t = blockIdx.x;
-  if (threadIdx.x < k) {
-    const int e = idx[t * k + threadIdx.x];
+  if (threadIdx.x < kMaxTopK) {
+    int32_t e = -1;
+    float d = 0.0f;
+    if (threadIdx.x < k) {
+      e = idx[t * k + threadIdx.x];
+      d = dl[t * k + threadIdx.x];
+    }
     es[threadIdx.x] = (e >= 0 && e < N) ? e : -1;
-    ds[threadIdx.x] = dl[t * k + threadIdx.x];
+    ds[threadIdx.x] = d;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < H; c += 256) {
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j)
-      if (es[j] >= 0) acc = fmaf(ds[j], w_router[(int64_t)es[j] * H + c], acc);
-    dx[t * H + c] = acc;
+  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
+    float4 w[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k && es[j] >= 0) w[j] = *reinterpret_cast<const float4*>(w_router + (int64_t)es[j] * H + c);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k && es[j] >= 0) {
+        acc.x = fmaf(ds[j], w[j].x, acc.x);
+        acc.y = fmaf(ds[j], w[j].y, acc.y);
+        acc.z = fmaf(ds[j], w[j].z, acc.z);
+        acc.w = fmaf(ds[j], w[j].w, acc.w);
+      }
+    }
+    *reinterpret_cast<float4*>(dx + t * H + c) = acc;
   }
 }
+
+// 4 consecutive values at p[i..i+4) (i a multiple of 4) as floats.
+template <typename T>
+__device__ __forceinline__ void ld4(const T* p, int64_t i, float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 raw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    v[0] = __uint_as_float(raw.x << 16);
+    v[1] = __uint_as_float(raw.x & 0xffff0000u);
+    v[2] = __uint_as_float(raw.y << 16);
+    v[3] = __uint_as_float(raw.y & 0xffff0000u);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+}
+
+// dW_r: one block per (expert, 1024 features), four consecutive features per thread; the
+// expert's rows go in ascending order, in batches of kDwRows whose loads are all issued
+// before any is added.
+constexpr int kDwRows = 8;
 
 template <typename XT>
 __global__ __launch_bounds__(256) void route_bwd_dw_kernel(const float* __restrict__ dl_row,
@@ -219,15 +257,32 @@ __global__ __launch_bounds__(256) void route_bwd_dw_kernel(const float* __restri
                                                            const XT* __restrict__ x, int64_t T,
                                                            int H, float* __restrict__ dw) {
   const int e = blockIdx.y;
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
   const int lo = offsets[e], hi = offsets[e + 1];
-  float acc = 0.0f;
-  for (int r = lo; r < hi; ++r) {
-    const int32_t t = row_token[r];
-    if (t >= 0 && t < T) acc = fmaf(dl_row[r], ld_val(x, (int64_t)t * H + c), acc);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int r0 = lo; r0 < hi; r0 += kDwRows) {
+    float v[kDwRows][4], g[kDwRows];
+    bool ok[kDwRows];
+#pragma unroll
+    for (int u = 0; u < kDwRows; ++u) {
+      const int r = r0 + u;
+      int64_t t = -1;
+      g[u] = 0.0f;
+      if (r < hi) {
+        t = row_token[r];
+        g[u] = dl_row[r];
+      }
+      ok[u] = t >= 0 && t < T;
+      ld4(x, (ok[u] ? t : 0) * H + c, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kDwRows; ++u)
+      if (ok[u])
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(g[u], v[u][i], acc[i]);
   }
-  dw[(int64_t)e * H + c] = acc;
+  *reinterpret_cast<float4*>(dw + (int64_t)e * H + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -355,12 +410,14 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const float* __restrict
   }
 }
 
-// SwiGLU backward on FP32 a, b, dh [rows, I], in place: a <- dg = dh b silu'(a),
-// b <- du = dh silu(a), dh <- h = silu(a) b; and [dg | du] quantised 1x128 along I into
-// codes [rows, 2I] with scales chunk-major [2I/128][rows]. One wave per 128-wide tile.
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(float* __restrict__ a, float* __restrict__ b,
+// SwiGLU backward on FP32 a, b, dh [rows, I]: dg = dh b silu'(a) -> dg_out, du = dh silu(a)
+// -> du_out, h = silu(a) b -> dh (in place; dg_out and du_out may be a and b); and
+// [dg | du] quantised 1x128 along I into codes [rows, 2I] with scales chunk-major
+// [2I/128][rows]. One wave per 128-wide tile.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* a, const float* b,
                                                          float* __restrict__ dh, int64_t n_rows,
-                                                         int I, uint8_t* __restrict__ q,
+                                                         int I, float* dg_out, float* du_out,
+                                                         uint8_t* __restrict__ q,
                                                          float* __restrict__ s_cm) {
   const int lane = threadIdx.x & 63;
   const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -383,8 +440,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(float* __restrict__ a, 
     du[i] = dvs[i] * si;
     h[i] = si * bvs[i];
   }
-  *reinterpret_cast<float2*>(a + o) = make_float2(dg[0], dg[1]);
-  *reinterpret_cast<float2*>(b + o) = make_float2(du[0], du[1]);
+  *reinterpret_cast<float2*>(dg_out + o) = make_float2(dg[0], dg[1]);
+  *reinterpret_cast<float2*>(du_out + o) = make_float2(du[0], du[1]);
   *reinterpret_cast<float2*>(dh + o) = make_float2(h[0], h[1]);
   float s;
   uint32_t c0, c1;
@@ -748,10 +805,10 @@ extern "C" moe_status moe_route_backward(const moe_config* cfg, int64_t T, const
     hipLaunchKernelGGL(route_bwd_gates_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s,
                        scores, topk_idx, dgate, row_of, T, N, k, cfg->routed_scaling, pairs, dl,
                        dl_row);
-    hipLaunchKernelGGL(route_bwd_dx_kernel<float>, dim3((unsigned)T), dim3(256), 0, s, dl, topk_idx,
+    hipLaunchKernelGGL(route_bwd_dx_kernel, dim3((unsigned)T), dim3(256), 0, s, dl, topk_idx,
                        w_router, N, k, H, dx);
   }
-  const dim3 g((unsigned)((H + 255) / 256), (unsigned)N);
+  const dim3 g((unsigned)((H / 4 + 255) / 256), (unsigned)N);
   if (xt == MOE_BF16)
     hipLaunchKernelGGL(route_bwd_dw_kernel<uint16_t>, g, dim3(256), 0, s, dl_row, offsets, row_token,
                        static_cast<const uint16_t*>(x), T, H, dw_router);
@@ -811,9 +868,9 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     const moe_config* cfg, int32_t n_experts, int64_t n_rows, int64_t n_tokens, const uint8_t* xq,
     const float* xs, const void* x, moe_dtype xt, const int32_t* row_token, const int32_t* offsets,
     const uint8_t* w1, const float* w1s, const uint8_t* w3, const float* w3s, const uint8_t* w2t,
-    const float* w2ts, const uint8_t* w13t, const float* w13ts, const float* dy, void* dx_rows,
-    moe_dtype dxt, void* dw1, void* dw3, void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes,
-    void* stream) {
+    const float* w2ts, const uint8_t* w13t, const float* w13ts, const float* a_saved,
+    const float* b_saved, const float* dy, void* dx_rows, moe_dtype dxt, void* dw1, void* dw3,
+    void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes, void* stream) {
   const moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->scale_mode != 0) return MOE_ERR_UNSUPPORTED;
@@ -834,7 +891,10 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   if (n_rows > 0 && (!row_token || !w1 || !w1s || !w3 || !w3s || !w2t || !w2ts || !w13t || !w13ts ||
                      !dy || !dx_rows))
     return MOE_ERR_NULL;
-  if (n_tokens > 0 && (!xq || !xs || !x)) return MOE_ERR_NULL;
+  // with the forward's SwiGLU inputs at hand, only h is recomputed (from them)
+  const bool saved = a_saved != nullptr || b_saved != nullptr;
+  if (saved && (!a_saved || !b_saved)) return MOE_ERR_NULL;
+  if (n_tokens > 0 && (!x || (!saved && (!xq || !xs)))) return MOE_ERR_NULL;
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -860,14 +920,14 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     const int64_t it = n_rows * (I / kTile);
     hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, dy, row_token,
                        n_rows, (int)H, dyq, dys);
-    if ((r = ffn_recompute_launch(plan, n_experts, n_rows, n_tokens, xq, xs, row_token, w1, w1s, w3,
-                                  w3s, (int)H, (int)I, xgs, fa, fb, s)) != MOE_OK)
+    if (!saved && (r = ffn_recompute_launch(plan, n_experts, n_rows, n_tokens, xq, xs, row_token, w1,
+                                            w1s, w3, w3s, (int)H, (int)I, xgs, fa, fb, s)) != MOE_OK)
       return r;
     if ((r = ffn_grouped_gemm_launch(plan, n_experts, n_rows, dyq, dys, w2t, w2ts, (int)I, (int)H, fdh,
                                      MOE_F32, s)) != MOE_OK)
       return r;
-    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((it + 3) / 4)), dim3(256), 0, s, fa, fb, fdh,
-                       n_rows, (int)I, q3, s3);
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((it + 3) / 4)), dim3(256), 0, s,
+                       saved ? a_saved : fa, saved ? b_saved : fb, fdh, n_rows, (int)I, fa, fb, q3, s3);
     // dgrad of gate/up (K = 2I)
     if ((r = ffn_grouped_gemm_launch(plan, n_experts, n_rows, q3, s3, w13t, w13ts, (int)H, (int)(2 * I),
                                      dx_rows, dxt, s)) != MOE_OK)

@@ -316,7 +316,8 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
                                          int wave, int lane, const FfnLds& sh) {
   static_assert(RING >= 3 && RING <= kMaxRing, "ring depth");
   static_assert(NT * 16 <= kMT, "tile rows");
-  constexpr bool GU = PHASE != 2;   // phases 1 and 3: the gate/up GEMMs (W1 and W3)
+  constexpr bool GU = PHASE != 2;   // phases 1, 3 and 4: the gate/up GEMMs (W1 and W3)
+  constexpr bool SWIGLU = PHASE == 1 || PHASE == 4;   // epilogue: h, re-quantised
   const int tid = wave * kWave + lane;
   const int K = GU ? a.H : a.I;
   const int nkc = K / kTile;
@@ -504,7 +505,8 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   constexpr int kYStores = kMT * 32 / kFThreads;   // 16-byte units of a staged output block
   static_assert(kMT * 32 % (2 * kFThreads) == 0 && kNTS % 2 == 0, "whole store rounds per half");
   constexpr int kEpiStores =
-      PHASE == 1 ? kStageStores + 1 : (PHASE == 3 || sizeof(YT) == 4 ? 2 * NT : kYStores);
+      SWIGLU ? kStageStores + 1 + (PHASE == 4 ? 2 * NT : 0)
+             : (PHASE == 3 || sizeof(YT) == 4 ? 2 * NT : kYStores);
   static_assert(RING < kMaxRing, "the last LDS slot stages the epilogue");
   constexpr int kWOps = 4, kAOps = kDma + 1;           // loads per chunk: weights, copies
   static_assert(kWOps + kAOps <= kStepOps, "loads per chunk");
@@ -558,7 +560,26 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
 
     // epilogue of n-block nb; the next block's first chunks are already in flight
     const int wrow = wrow_of(nb);
-    if (PHASE == 1) {
+    if constexpr (PHASE == 3 || PHASE == 4) {
+      // a = G and b = U as FP32 rows (phase 3: the backward's recompute; phase 4: the
+      // SwiGLU inputs a training forward keeps, stored before h replaces G): this lane's
+      // four values are columns col .. col+3 of the block's 128 (the packed W1/W3 row
+      // order); rows past the tile fall outside the descriptors' ranges
+      const int col = 32 * (wave >> 1) + 8 * (lane >> 4) + 4 * (wave & 1);
+      const __amdgpu_buffer_rsrc_t adesc2 = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(static_cast<float*>(a.y) + (int64_t)tl.m0 * a.I + (int64_t)nb * kTile), 0,
+          tl.mlen * a.I * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t bdesc2 = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(a.y2 + (int64_t)tl.m0 * a.I + (int64_t)nb * kTile), 0, tl.mlen * a.I * 4,
+          0x00020000);
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int off = ((ts * 16 + (lane & 15)) * a.I + col) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc0[ts]), adesc2, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc1[ts]), bdesc2, off, 0, 0);
+      }
+    }
+    if constexpr (SWIGLU) {
       // SwiGLU, amax over the 128 columns of the group (4 per lane, 4 lane groups, 8 waves)
       // h = silu(G) * U replaces G in acc0. silu(g) = g / (1 + 2^(-g log2 e)) with the
       // hardware exp2 and reciprocal: a relative error of a few 1e-7, far below the E4M3
@@ -626,24 +647,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
         const v4u v = *reinterpret_cast<const v4u*>(stage + rr * kTile + ((seg ^ (rr & 7)) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(v, qdesc, row * a.I + seg * 16, 0, 0);
       }
-    } else if (PHASE == 3) {
-      // a and b as FP32 rows (the recompute of the backward pass): this lane's four
-      // values are columns col .. col+3 of the block's 128 (the packed W1/W3 row order);
-      // rows past the tile fall outside the descriptors' ranges
-      const int col = 32 * (wave >> 1) + 8 * (lane >> 4) + 4 * (wave & 1);
-      const __amdgpu_buffer_rsrc_t adesc2 = __builtin_amdgcn_make_buffer_rsrc(
-          uniform_ptr(static_cast<float*>(a.y) + (int64_t)tl.m0 * a.I + (int64_t)nb * kTile), 0,
-          tl.mlen * a.I * 4, 0x00020000);
-      const __amdgpu_buffer_rsrc_t bdesc2 = __builtin_amdgcn_make_buffer_rsrc(
-          uniform_ptr(a.y2 + (int64_t)tl.m0 * a.I + (int64_t)nb * kTile), 0, tl.mlen * a.I * 4,
-          0x00020000);
-#pragma unroll
-      for (int ts = 0; ts < NT; ++ts) {
-        const int off = ((ts * 16 + (lane & 15)) * a.I + col) * 4;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc0[ts]), adesc2, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc1[ts]), bdesc2, off, 0, 0);
-      }
-    } else {
+    } else if constexpr (PHASE == 2) {
       // rows past the tile fall outside the descriptor's range; the idle waves of a
       // half-used last block (H % 256 == 128) store past it as well
       const __amdgpu_buffer_rsrc_t ydesc = __builtin_amdgcn_make_buffer_rsrc(
@@ -707,6 +711,8 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
 //            waves through LDS).
 //   PHASE 2: 256 output features per workgroup.
 //   PHASE 3: phase 1's GEMMs with G and U written as FP32 rows (the backward's recompute).
+//   PHASE 4: phase 1, and G and U also written as FP32 rows (a training forward keeps the
+//            SwiGLU inputs, so the backward recomputes only h from them).
 // Workgroup L runs on XCD L % 8; the n-blocks of one M tile are consecutive on one XCD,
 // so the tile's activation rows are fetched into that XCD's L2 once.
 // ------------------------------------------------------------------------------------
@@ -762,7 +768,7 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   constexpr int kWscRow = kMaxChunks + kMaxRing;
   __shared__ float wsc[kMaxNbPerWg * 2][kWscRow];   // weight-block scales per n-block, row
                                                      // block and K chunk; 0 past the last chunk
-  __shared__ float red[PHASE == 1 ? kFWaves * kMT : 1];
+  __shared__ float red[PHASE == 1 || PHASE == 4 ? kFWaves * kMT : 1];
   constexpr bool GU = PHASE != 2;
   int tile, wg;
   if (!wg_work(a, blockIdx.x, &tile, &wg)) return;
@@ -905,19 +911,24 @@ moe_status ffn_check(const moe_config* cfg, int32_t n_experts, int64_t n_rows, v
   return MOE_OK;
 }
 
+// save: a training forward, which also writes the SwiGLU inputs a = G and b = U to
+// a_out and b_out ([n_rows, I] FP32 each).
 moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows, int64_t n_tokens,
                        const uint8_t* xq, const float* xs, const int32_t* row_token,
                        const int32_t* offsets, const uint8_t* w1, const float* w1s,
                        const uint8_t* w3, const float* w3s, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       void* stream, bool save = false, float* a_out = nullptr,
+                       float* b_out = nullptr) {
   FfnCall f;
   const moe_status st = ffn_check(cfg, n_experts, n_rows, ws, ws_bytes, &f);
   if (st != MOE_OK) return st;
   if (n_tokens < 0 || n_tokens * (int64_t)cfg->hidden >= ((int64_t)1 << 32))
     return n_tokens < 0 ? MOE_ERR_SHAPE : MOE_ERR_UNSUPPORTED;
+  if (save && cfg->scale_mode != 0) return MOE_ERR_UNSUPPORTED;
   if (n_rows == 0) return MOE_OK;
   if (!offsets || !w1 || !w1s || !w3 || !w3s) return MOE_ERR_NULL;
   if (n_tokens > 0 && (!xq || !xs)) return MOE_ERR_NULL;
+  if (save && (!a_out || !b_out)) return MOE_ERR_NULL;
   hipStream_t s = as_stream(stream);
   const int H = cfg->hidden, I = cfg->inter;
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
@@ -931,9 +942,11 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
                        row_token, H / kTile, f.xsp);
   FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, f.xsp, n_tokens,
              row_token, w1, w1s, w3, w3s, H, I, I / kTile,
-             gate_up_nb_per(n_rows, n_experts, cfg->scale_mode == 1), f.hq, f.hs, nullptr};
+             gate_up_nb_per(n_rows, n_experts, cfg->scale_mode == 1), f.hq, f.hs, a_out, b_out};
   const dim3 grid((unsigned)ffn_grid(f.L.max_tiles, (a1.n_nb + a1.nb_per - 1) / a1.nb_per, n_rows));
-  if (cfg->scale_mode == 1)
+  if (save)
+    hipLaunchKernelGGL((ffn_kernel<4, uint16_t, false>), grid, dim3(kFThreads), 0, s, a1);
+  else if (cfg->scale_mode == 1)
     hipLaunchKernelGGL((ffn_kernel<1, uint16_t, true>), grid, dim3(kFThreads), 0, s, a1);
   else
     hipLaunchKernelGGL((ffn_kernel<1, uint16_t, false>), grid, dim3(kFThreads), 0, s, a1);
@@ -1068,6 +1081,15 @@ extern "C" moe_status moe_grouped_ffn_fp8_gate_up(const moe_config* cfg, int32_t
                                                   void* stream) {
   return ffn_gate_up(cfg, n_experts, n_rows, n_tokens, xq, xs, row_token, offsets, w1, w1s, w3,
                      w3s, ws, ws_bytes, stream);
+}
+
+extern "C" moe_status moe_grouped_ffn_fp8_gate_up_train(
+    const moe_config* cfg, int32_t n_experts, int64_t n_rows, int64_t n_tokens, const uint8_t* xq,
+    const float* xs, const int32_t* row_token, const int32_t* offsets, const uint8_t* w1,
+    const float* w1s, const uint8_t* w3, const float* w3s, float* a_out, float* b_out, void* ws,
+    size_t ws_bytes, void* stream) {
+  return ffn_gate_up(cfg, n_experts, n_rows, n_tokens, xq, xs, row_token, offsets, w1, w1s, w3,
+                     w3s, ws, ws_bytes, stream, true, a_out, b_out);
 }
 
 extern "C" moe_status moe_grouped_ffn_fp8_down(const moe_config* cfg, int32_t n_experts,

@@ -19,6 +19,7 @@ import torch
 from . import (MOE_F32, make_config, moe_combine, moe_combine_backward,
                moe_grouped_ffn_backward_workspace_bytes, moe_grouped_ffn_fp8_backward,
                moe_grouped_ffn_fp8_down, moe_grouped_ffn_fp8_gate_up,
+               moe_grouped_ffn_fp8_gate_up_train,
                moe_grouped_ffn_workspace_bytes, moe_pack_fp8_weights, moe_pack_router_weights,
                moe_permute, moe_permute_workspace_bytes, moe_quantize_1x128, moe_quantize_128x128,
                moe_route, moe_route_backward, moe_route_backward_workspace_bytes, moe_route_workspace_bytes,
@@ -34,11 +35,14 @@ class MoELayer:
     """
 
     def __init__(self, cfg, device="cuda", y_dtype=torch.bfloat16, scale_mode: int = 0,
-                 backward: bool = False, dw_dtype=torch.float32):
+                 backward: bool = False, dw_dtype=torch.float32, keep_swiglu_inputs: bool = True):
         """``scale_mode`` 0: the pages' FP32 group scales; 1: the power-of-two variant
         (weights and activations quantised with power-of-two scales, applied by the MFMA).
         ``backward``: also keep what ``backward`` needs (the transposed packed weights for
-        the dgrad GEMMs and the FP32 router weight); weight gradients come in ``dw_dtype``."""
+        the dgrad GEMMs and the FP32 router weight); weight gradients come in ``dw_dtype``.
+        ``keep_swiglu_inputs`` (with ``backward``): the forward keeps the SwiGLU inputs a, b
+        (FP32, [rows, I] each) so that the backward recomputes only h from them; False
+        recomputes a and b by the gate/up GEMMs in the backward instead (same values)."""
         self.cfg = cfg
         self.scale_mode = scale_mode
         self.c = make_config(cfg, scale_mode)
@@ -59,6 +63,7 @@ class MoELayer:
         self._T = None
         self._graph = None
         self.backward_enabled = backward
+        self.keep_ab = backward and keep_swiglu_inputs
         self.dw_dtype = dw_dtype
         if backward:
             # dgrad operands: W2^T [I, H] and [W1^T | W3^T] [H, 2I] per expert, packed
@@ -148,6 +153,9 @@ class MoELayer:
         self.row_token = torch.empty((T * (k + S),), dtype=i32, device=d)
         self.row_of = torch.empty((T, k), dtype=i32, device=d)
         self.y_rows = torch.empty((T * (k + S), H), dtype=self.y_dtype, device=d)
+        if self.keep_ab:   # the SwiGLU inputs of the last forward, for the backward
+            self.a_saved = torch.empty((T * (k + S), I), dtype=f32, device=d)
+            self.b_saved = torch.empty((T * (k + S), I), dtype=f32, device=d)
         self.ws = torch.empty((max(moe_grouped_ffn_workspace_bytes(self.c, N + S, T * (k + S)), 1),),
                               dtype=torch.uint8, device=d)
         self.y_shared = self.y_rows[T * k:] if S > 0 else None
@@ -183,8 +191,13 @@ class MoELayer:
         mark(2)
         moe_permute(c, self.topk_idx, self.offsets, self.row_token, self.row_of, ws=self.perm_ws)
         mark(3)
-        moe_grouped_ffn_fp8_gate_up(c, EA, rows, self.xq, self.xs, self.row_token, self.offsets,
-                                    self.w1, self.w1s, self.w3, self.w3s, ws=self.ws)
+        if self.keep_ab:
+            moe_grouped_ffn_fp8_gate_up_train(c, EA, rows, self.xq, self.xs, self.row_token,
+                                              self.offsets, self.w1, self.w1s, self.w3, self.w3s,
+                                              a=self.a_saved, b=self.b_saved, ws=self.ws)
+        else:
+            moe_grouped_ffn_fp8_gate_up(c, EA, rows, self.xq, self.xs, self.row_token, self.offsets,
+                                        self.w1, self.w1s, self.w3, self.w3s, ws=self.ws)
         mark(4)
         moe_grouped_ffn_fp8_down(c, EA, rows, self.w2, self.w2s, self.ws, y=self.y_rows)
         mark(5)
@@ -269,7 +282,9 @@ class MoELayer:
         moe_grouped_ffn_fp8_backward(c, EA, self.xq, self.xs, self.x, self.row_token, self.offsets,
                                      self.w1, self.w1s, self.w3, self.w3s, self.w2t, self.w2ts,
                                      self.w13t, self.w13ts, self.dy, dx_rows=self.dx_rows,
-                                     dw1=self.dw1, dw3=self.dw3, dw2=self.dw2, ws=self.bwd_ws)
+                                     dw1=self.dw1, dw3=self.dw3, dw2=self.dw2, ws=self.bwd_ws,
+                                     a_saved=self.a_saved if self.keep_ab else None,
+                                     b_saved=self.b_saved if self.keep_ab else None)
         mark(2)
         moe_route_backward(c, self.x, self.w_router_f32, self.scores, self.topk_idx, self.dgate,
                            self.offsets, self.row_token, self.row_of, dx=self.dx_route,

@@ -297,6 +297,27 @@ moe_status moe_grouped_ffn_fp8_gate_up(const moe_config* cfg, int32_t n_experts,
                                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_grouped_ffn_fp8_gate_up_train — moe_grouped_ffn_fp8_gate_up for a training step: the
+ * same launch and the same (hq, hs), and the SwiGLU inputs are kept for the backward
+ * ([zhihu] training part: SwiGLU is among the operators recomputed in the backward, so
+ * what is kept is its input, not its output h):
+ *   a_out, b_out  [n_rows, I] float each, output: a = G, b = U of every row of every expert
+ *                 segment (the FP32 accumulators h is formed from); rows outside every
+ *                 segment are not written. moe_grouped_ffn_fp8_backward takes them as
+ *                 a_saved, b_saved and then recomputes only h.
+ * Errors: as moe_grouped_ffn_fp8_gate_up; NULL a_out or b_out (n_rows > 0);
+ * scale_mode != 0 (UNSUPPORTED: the backward runs on the FP32 group scales only).
+ */
+moe_status moe_grouped_ffn_fp8_gate_up_train(const moe_config* cfg, int32_t n_experts,
+                                             int64_t n_rows, int64_t n_tokens,
+                                             const uint8_t* xq, const float* xs,
+                                             const int32_t* row_token, const int32_t* offsets,
+                                             const uint8_t* w1, const float* w1s,
+                                             const uint8_t* w3, const float* w3s, float* a_out,
+                                             float* b_out, void* ws, size_t ws_bytes,
+                                             void* stream);
+
+/*
  * moe_grouped_ffn_fp8_down — second half: y = DQ(hq) . DQ(W2_e)^T for every row, from
  * the plan and intermediate that the preceding moe_grouped_ffn_fp8_gate_up call with the
  * same cfg, n_experts and n_rows left in ws (stream-ordered after it). If ws holds no
@@ -465,7 +486,10 @@ moe_status moe_transpose_fp8_blocks(int64_t E, int64_t R, int64_t C, const uint8
 /*
  * moe_grouped_ffn_fp8_backward — backward of the grouped SwiGLU experts with FP8 GEMMs, on
  * the same permuted rows and segments as moe_grouped_ffn_fp8 (routed then shared).
- *   Recompute: a = xq W1^T, b = xq W3^T (FP8 fprop GEMMs on the forward's codes).
+ *   SwiGLU inputs: a = xq W1^T, b = xq W3^T as the training forward kept them
+ *              (a_saved, b_saved from moe_grouped_ffn_fp8_gate_up_train), or, when both
+ *              are NULL, recomputed by the FP8 fprop GEMMs on the forward's codes (the
+ *              same launch, so the same values bit for bit).
  *   dgrad:     dh = dy W2 (dy in 1x128 tiles along H); dg = dh b silu'(a), du = dh silu(a)
  *              (FP32); dx_rows = dg W1 + du W3 ([dg | du] in 1x128 tiles along I, one
  *              GEMM over K = 2I with the packed [W1^T | W3^T]).
@@ -473,18 +497,21 @@ moe_status moe_transpose_fp8_blocks(int64_t E, int64_t R, int64_t C, const uint8
  *              the layer input rows; every operand in 128-row tiles along the token axis.
  *   Rows with row_token < 0 count as zero rows (their dy is ignored).
  *   xq, xs       [T, H] u8 / [T, H/128] float: the forward's activation codes and scales
+ *                (read only to recompute a and b; may be NULL with a_saved, b_saved)
  *   x            [T, H] (xt = BF16/F32): the layer input
  *   w1, w3 (+s)  the forward's packed weights; w2t (+s): packed W2^T [E, I, H] with
  *                scales [E, I/128, H/128]; w13t (+s): packed [W1^T | W3^T] [E, H, 2I]
  *                with scales [E, H/128, 2I/128] (moe_transpose_fp8_blocks, then
  *                moe_pack_fp8_weights)
+ *   a_saved, b_saved  [n_rows, I] float each or both NULL: the forward's SwiGLU inputs
  *   dy           [n_rows, H] float (moe_combine_backward)
  *   dx_rows      [n_rows, H] output (dxt = BF16/F32)
  *   dw1, dw3     [E, I, H] and dw2 [E, H, I] outputs (dwt = BF16/F32): FP32-promoted
  *                sums, written for every expert (zero for an expert without rows)
  *   ws           moe_grouped_ffn_backward_workspace_bytes(cfg, E, n_rows) bytes
- * Errors: NULL pointers; invalid config; scale_mode != 0 (UNSUPPORTED); E outside
- * 1..1024, n_rows or T out of range (SHAPE); bad dtypes (DTYPE); workspace (WORKSPACE);
+ * Errors: NULL pointers (one of a_saved, b_saved NULL and the other not is NULL too);
+ * invalid config; scale_mode != 0 (UNSUPPORTED); E outside 1..1024, n_rows or T out of
+ * range (SHAPE); bad dtypes (DTYPE); workspace (WORKSPACE);
  * n_rows * H or n_rows * 2I >= 2^32, H or 2I > 16384 (UNSUPPORTED).
  */
 size_t moe_grouped_ffn_backward_workspace_bytes(const moe_config* cfg, int32_t n_experts,
@@ -493,9 +520,9 @@ moe_status moe_grouped_ffn_fp8_backward(
     const moe_config* cfg, int32_t n_experts, int64_t n_rows, int64_t n_tokens, const uint8_t* xq,
     const float* xs, const void* x, moe_dtype xt, const int32_t* row_token, const int32_t* offsets,
     const uint8_t* w1, const float* w1s, const uint8_t* w3, const float* w3s, const uint8_t* w2t,
-    const float* w2ts, const uint8_t* w13t, const float* w13ts, const float* dy, void* dx_rows,
-    moe_dtype dxt, void* dw1, void* dw3, void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes,
-    void* stream);
+    const float* w2ts, const uint8_t* w13t, const float* w13ts, const float* a_saved,
+    const float* b_saved, const float* dy, void* dx_rows, moe_dtype dxt, void* dw1, void* dw3,
+    void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -172,18 +172,29 @@ def test_host_validation_status_codes():
     need_fb = L.moe_grouped_ffn_backward_workspace_bytes(ctypes.byref(c), 4, 100)
     assert need_fb > 100 * 256
     fb = L.moe_grouped_ffn_fp8_backward
-    args15 = [fake] * 15
-    assert fb(ctypes.byref(c), 4, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 0, fake, fake, fake, 0,
-              fake, need_fb - 1, None) == 6
-    assert fb(ctypes.byref(c), 0, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 0, fake, fake, fake, 0,
-              fake, need_fb, None) == 2
-    assert fb(ctypes.byref(c), 4, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 5, fake, fake, fake, 0,
-              fake, need_fb, None) == 3
-    assert fb(ctypes.byref(c), 4, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 0, None, fake, fake, 0,
-              fake, need_fb, None) == 1
+    w10 = [fake] * 10   # row_token, offsets, w1, w1s, w3, w3s, w2t, w2ts, w13t, w13ts
+
+    def fbc(cfg, E, dxt, dx_rows, ws_bytes, ab=(None, None), xq=fake):
+        return fb(ctypes.byref(cfg), E, 100, 10, xq, fake, fake, 1, *w10, *ab, fake, dx_rows, dxt,
+                  fake, fake, fake, 0, fake, ws_bytes, None)
+    assert fbc(c, 4, 0, fake, need_fb - 1) == 6
+    assert fbc(c, 0, 0, fake, need_fb) == 2
+    assert fbc(c, 4, 5, fake, need_fb) == 3
+    assert fbc(c, 4, 0, None, need_fb) == 1
+    # the SwiGLU inputs come in pairs; without them the forward's codes are needed
+    assert fbc(c, 4, 0, fake, need_fb, ab=(fake, None)) == 1
+    assert fbc(c, 4, 0, fake, need_fb, ab=(None, fake)) == 1
+    assert fbc(c, 4, 0, fake, need_fb, xq=None) == 1
     p2 = _cfg(m, scale_mode=1)
-    assert fb(ctypes.byref(p2), 4, 100, 10, fake, fake, fake, 1, *args15[:11], fake, 0, fake, fake, fake, 0,
-              fake, need_fb, None) == 4
+    assert fbc(p2, 4, 0, fake, need_fb) == 4
+    # the training gate/up: both outputs, FP32 group scales only
+    tu = L.moe_grouped_ffn_fp8_gate_up_train
+    assert tu(ctypes.byref(c), 16, 256, 64, fake, fake, None, *args[:5], None, fake, fake, need,
+              None) == 1
+    assert tu(ctypes.byref(c), 16, 256, 64, fake, fake, None, *args[:5], fake, fake, fake, need - 1,
+              None) == 6
+    assert tu(ctypes.byref(p2), 16, 256, 64, fake, fake, None, *args[:5], fake, fake, fake, need,
+              None) == 4
     # too large for 32-bit operand offsets
     big = _cfg(m, hidden=16384, inter=16384)
     assert L.moe_grouped_ffn_fp8_gate_up(ctypes.byref(big), 16, 1 << 18, 64, fake, fake, None,

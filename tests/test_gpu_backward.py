@@ -315,6 +315,54 @@ def test_layer_backward_matches_oracle(lib, name, tokens):
     assert e_dx < TOL and e_w < TOL and e_r < TOL
 
 
+def test_kept_swiglu_inputs_match_recompute(lib):
+    """A training forward keeps the SwiGLU inputs a = G and b = U (FP32) and the backward
+    recomputes only h from them; without them the backward recomputes a and b by the
+    gate/up GEMMs. Both paths run the same launch, so every gradient must agree bit for
+    bit; a and b themselves are checked against the oracle's FP64 products."""
+    from deepseekmoe_routing_fp8_amd import MoELayer
+    cfg = synth.PRESETS["reduced"].with_tokens(512)
+    T, H, I = cfg.tokens, cfg.hidden_size, cfg.moe_intermediate_size
+    N, k, S = cfg.num_experts, cfg.num_experts_per_tok, cfg.num_shared_experts
+    say(f"kept SwiGLU inputs, reduced T={T}: loading two layers")
+    keep = MoELayer(cfg, backward=True)
+    rec = MoELayer(cfg, backward=True, keep_swiglu_inputs=False)
+    keep.load_from_synth()
+    rec.load_from_synth()
+    x = dev(synth.hidden_states(cfg), torch.bfloat16)
+    dout = dev(oracle.round_bf16(np.random.default_rng(9).standard_normal((T, H)).astype(np.float32)),
+               torch.bfloat16)
+    outs = []
+    for layer in (keep, rec):
+        o = layer.forward(x, update_bias=False).clone()
+        d = layer.backward(dout).clone()
+        torch.cuda.synchronize()
+        outs.append((o, d))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    for name in ("dx_rows", "dw1", "dw3", "dw2", "dw_router", "dgate"):
+        assert torch.equal(getattr(keep, name), getattr(rec, name)), name
+    # a and b of the shared expert (every token) and of the most loaded routed expert
+    offsets = keep.offsets.cpu().numpy()
+    row_token = keep.row_token.cpu().numpy()
+    xq, xs = host(keep.xq), host(keep.xs)
+    heavy = int(np.argmax(np.diff(offsets[:N + 1])))
+    for e, w in ((N, synth.shared_expert_weights(cfg, 0)), (heavy, synth.routed_expert_weights(cfg, heavy))):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        tk = row_token[lo:hi]
+        a_in = oracle.dequant_1x128(xq[tk], xs[tk])
+        g = a_in @ oracle.dequant_128x128(*oracle.quantize_128x128(w[0])).T
+        u = a_in @ oracle.dequant_128x128(*oracle.quantize_128x128(w[1])).T
+        e_a = relerr(host(keep.a_saved[lo:hi]), g)
+        e_b = relerr(host(keep.b_saved[lo:hi]), u)
+        say(f"  expert {e} ({hi - lo} rows): a {e_a:.2e}, b {e_b:.2e}")
+        # FP32 promotion of per-chunk MFMA partial sums (each within ~2^-12 of its chunk's
+        # sum of |products|) against the FP64 products
+        assert e_a < 1e-3 and e_b < 1e-3
+    del keep, rec
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.timeout(900)
 def test_layer_backward_v3_prefill_sampled(lib):
     """The V3 prefill layer in the benchmark's configuration (T = 4096, 256 routed + 1
