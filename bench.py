@@ -311,8 +311,9 @@ def measure_backward(layer, cfg, x, steps: int, warmup: int):
     st = {s_: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in be]))
           for j, s_ in enumerate(MoELayer.BWD_STAGES)}
     rows = T * (k + S)
-    # FP8 GEMM work of the backward: recomputed a and b, dh, dx over K = 2I, three wgrads
-    flops = 16.0 * rows * H * I
+    # FP8 GEMM work of the backward: dh, dx over K = 2I, three wgrads, and the recompute of a
+    # and b unless the forward kept them
+    flops = (12.0 if layer.keep_ab else 16.0) * rows * H * I
     dw_bytes = 3 * (N + S) * H * I * layer.dw_dtype.itemsize
     return {"tokens": T, "steps": steps, "train_step_ms": round(wall * 1e3 / steps, 4),
             "train_tokens_per_s": round(T * steps / wall, 1), "forward_ms": round(fwd, 4),
@@ -320,6 +321,8 @@ def measure_backward(layer, cfg, x, steps: int, warmup: int):
             "backward_fp8_tflops": round(flops / (bwd * 1e-3) / 1e12, 1),
             "ffn_backward_fp8_tflops": round(flops / (st["ffn_bwd"] * 1e-3) / 1e12, 1),
             "weight_grad_bytes": dw_bytes, "weight_grad_dtype": str(layer.dw_dtype).replace("torch.", ""),
+            "swiglu_inputs": ("kept by the forward (FP32 a, b); the backward recomputes h" if layer.keep_ab
+                              else "recomputed in the backward by the gate/up GEMMs"),
             "note": ("forward + FP8 backward (dgrad and wgrad in E4M3); no optimizer")}
 
 

@@ -103,8 +103,8 @@ _sig = {
     "moe_transpose_fp8_blocks": ([_I64, _I64, _I64, _P, _P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "moe_grouped_ffn_backward_workspace_bytes": ([_CFG, _I32, _I64], _SZ),
     "moe_grouped_ffn_fp8_backward": ([_CFG, _I32, _I64, _I64, _P, _P, _P, ctypes.c_int, _P, _P, _P,
-                                      _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
-                                      _P, _P, ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
+                                      _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int,
+                                      _P, _P, _P, ctypes.c_int, _P, _SZ, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _sig.items():
     _f = getattr(_lib, _name)
@@ -474,21 +474,22 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def moe_combine_backward(cfg: moe_config, dout: torch.Tensor, y_rows: torch.Tensor,
-                         row_of: torch.Tensor, topk_gate: torch.Tensor, dy: torch.Tensor = None,
-                         dgate: torch.Tensor = None, stream=None):
-    """-> (dy [T*(k+N_s), H] f32, dgate [T, k] f32) from dout [T, H] bf16."""
+                         row_of: torch.Tensor, topk_gate: torch.Tensor,
+                         row_gate: torch.Tensor = None, dgate: torch.Tensor = None, stream=None):
+    """-> (row_gate [T*(k+N_s)] f32, dgate [T, k] f32) from dout [T, H] bf16. The rows'
+    upstream gradient is row_gate[r] * dout[token(r)], formed by the FFN backward."""
     T, H = dout.shape
     k, S = cfg.top_k, cfg.n_shared
     dev = dout.device
-    dy = torch.empty((T * (k + S), H), dtype=torch.float32, device=dev) if dy is None else dy
+    row_gate = torch.empty((T * (k + S),), dtype=torch.float32, device=dev) if row_gate is None else row_gate
     dgate = torch.empty((T, k), dtype=torch.float32, device=dev) if dgate is None else dgate
     _check(_lib.moe_combine_backward(
         ctypes.byref(cfg), T, _dev(dout, torch.bfloat16, "dout", (T, cfg.hidden)),
         _dev(y_rows, y_rows.dtype, "y_rows", (T * (k + S), H)), _dt(y_rows),
         _dev(row_of, torch.int32, "row_of", (T, k)), _dev(topk_gate, torch.float32, "topk_gate", (T, k)),
-        _dev(dy, torch.float32, "dy", (T * (k + S), H)), _dev(dgate, torch.float32, "dgate", (T, k)),
+        _dev(row_gate, torch.float32, "row_gate", (T * (k + S),)), _dev(dgate, torch.float32, "dgate", (T, k)),
         _stream(stream)), "moe_combine_backward")
-    return dy, dgate
+    return row_gate, dgate
 
 
 def moe_route_backward_workspace_bytes(cfg: moe_config, T: int) -> int:
@@ -551,19 +552,22 @@ def moe_grouped_ffn_backward_workspace_bytes(cfg: moe_config, n_experts: int, n_
 
 
 def moe_grouped_ffn_fp8_backward(cfg: moe_config, n_experts: int, xq, xs, x, row_token, offsets,
-                                 w1, w1s, w3, w3s, w2t, w2ts, w13t, w13ts, dy,
+                                 w1, w1s, w3, w3s, w2t, w2ts, w13t, w13ts, dout,
+                                 row_gate: Optional[torch.Tensor] = None,
                                  dx_rows: torch.Tensor = None, dx_dtype=torch.float32,
                                  dw1: torch.Tensor = None, dw3: torch.Tensor = None,
                                  dw2: torch.Tensor = None, dw_dtype=torch.float32,
                                  ws: torch.Tensor = None, a_saved: torch.Tensor = None,
                                  b_saved: torch.Tensor = None, stream=None):
-    """-> (dx_rows [n_rows, H], dw1 [E, I, H], dw3 [E, I, H], dw2 [E, H, I]). ``a_saved``,
-    ``b_saved``: the SwiGLU inputs kept by moe_grouped_ffn_fp8_gate_up_train (both or
-    neither; without them they are recomputed from xq, xs)."""
-    n_rows = dy.shape[0]
-    T = xq.shape[0]
+    """-> (dx_rows [n_rows, H], dw1 [E, I, H], dw3 [E, I, H], dw2 [E, H, I]) for the rows'
+    upstream gradient dy_r = row_gate[r] * dout[row_token[r]] (dout [T, H] bf16; row_gate
+    None: every gate 1). ``a_saved``, ``b_saved``: the SwiGLU inputs kept by
+    moe_grouped_ffn_fp8_gate_up_train (both or neither; without them they are recomputed
+    from xq, xs)."""
+    n_rows = row_token.shape[0]
+    T = x.shape[0]
     H, I, E = cfg.hidden, cfg.inter, n_experts
-    dev = dy.device
+    dev = x.device
     if dx_rows is None:
         dx_rows = torch.empty((n_rows, H), dtype=dx_dtype, device=dev)
     dw1 = torch.empty((E, I, H), dtype=dw_dtype, device=dev) if dw1 is None else dw1
@@ -573,14 +577,15 @@ def moe_grouped_ffn_fp8_backward(cfg: moe_config, n_experts: int, xq, xs, x, row
         ws = torch.empty((max(moe_grouped_ffn_backward_workspace_bytes(cfg, E, n_rows), 1),),
                          dtype=torch.uint8, device=dev)
     _check(_lib.moe_grouped_ffn_fp8_backward(
-        ctypes.byref(cfg), E, n_rows, T, _dev(xq, torch.uint8, "xq", (T, H)),
-        _dev(xs, torch.float32, "xs", (T, H // 128)), _dev(x, x.dtype, "x", (T, H)), _dt(x),
+        ctypes.byref(cfg), E, n_rows, T, _opt(xq, torch.uint8, "xq", (T, H)),
+        _opt(xs, torch.float32, "xs", (T, H // 128)), _dev(x, x.dtype, "x", (T, H)), _dt(x),
         _dev(row_token, torch.int32, "row_token", (n_rows,)), _dev(offsets, torch.int32, "offsets", (E + 1,)),
         _dev(w1, torch.uint8, "w1"), _dev(w1s, torch.float32, "w1s"), _dev(w3, torch.uint8, "w3"),
         _dev(w3s, torch.float32, "w3s"), _dev(w2t, torch.uint8, "w2t"), _dev(w2ts, torch.float32, "w2ts"),
         _dev(w13t, torch.uint8, "w13t"), _dev(w13ts, torch.float32, "w13ts"),
         _opt(a_saved, torch.float32, "a_saved", (n_rows, I)), _opt(b_saved, torch.float32, "b_saved", (n_rows, I)),
-        _dev(dy, torch.float32, "dy", (n_rows, H)), _dev(dx_rows, dx_rows.dtype, "dx_rows", (n_rows, H)),
+        _dev(dout, torch.bfloat16, "dout", (T, H)), _opt(row_gate, torch.float32, "row_gate", (n_rows,)),
+        _dev(dx_rows, dx_rows.dtype, "dx_rows", (n_rows, H)),
         _dt(dx_rows), _dev(dw1, dw1.dtype, "dw1", (E, I, H)), _dev(dw3, dw1.dtype, "dw3", (E, I, H)),
         _dev(dw2, dw1.dtype, "dw2", (E, H, I)), _dt(dw1), _dev(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)), "moe_grouped_ffn_fp8_backward")

@@ -10,11 +10,12 @@
 //   selected experts times the scaling factor.
 //
 // Steps and launches:
-//   combine backward   dy rows (gate x dout, FP32) and the gates' gradient (dot products);
+//   combine backward   the gates' gradient (dot products) and each row's gate (dy of a row,
+//                      gate x dout, is formed where the FFN backward quantises it);
 //   router backward    gate gradient -> affinity -> logit gradient (FP32), then dx of the
 //                      router GEMM and dW_r summed per expert in segment order;
 //   FFN backward       per expert segment, on the forward's tile plan:
-//     dy  -> 1x128 along H                  (dgrad operand)
+//     dy = gate x dout -> 1x128 along H     (dgrad operand)
 //     a = xq W1^T, b = xq W3^T              (the SwiGLU inputs: kept by a training forward,
 //                                            else recomputed by the gate/up launch, FP32)
 //     dh = dy W2                            (FP8 grouped GEMM, K = H, FP32 out)
@@ -88,7 +89,9 @@ __device__ __forceinline__ void block_sum_slots(float (&v)[kMaxTopK], int k, flo
 }
 
 // ------------------------------------------------------------------------------------
-// Combine backward: one block per token.
+// Combine backward: one block per token. The rows' upstream gradient dy_r = gate_r dout_t is
+// not materialised: the block writes the gate of each of the token's rows (1 for the
+// shared rows), and the FFN backward forms the product where it quantises dy.
 // ------------------------------------------------------------------------------------
 template <typename YT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __restrict__ dout,
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ row_of,
                                                           const float* __restrict__ gate,
                                                           int64_t T, int H, int k, int S,
-                                                          int64_t n_rows, float* __restrict__ dy,
+                                                          int64_t n_rows, float* __restrict__ row_gate,
                                                           float* __restrict__ dgate) {
   __shared__ int32_t rows[kMaxTopK];
   __shared__ float g[kMaxTopK];
@@ -110,8 +113,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
       r = row_of[t * k + threadIdx.x];
       gv = gate[t * k + threadIdx.x];
     }
-    rows[threadIdx.x] = (r >= 0 && r < n_rows) ? r : -1;
+    r = (r >= 0 && r < n_rows) ? r : -1;
+    rows[threadIdx.x] = r;
     g[threadIdx.x] = gv;
+    if (r >= 0) row_gate[r] = gv;
+  } else if (threadIdx.x < kMaxTopK + S) {
+    row_gate[T * k + (threadIdx.x - kMaxTopK) * T + t] = 1.0f;
   }
   __syncthreads();
   float part[kMaxTopK];
@@ -122,19 +129,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
     float d[8];
     ld8(dout, t * H + c, d);
-    for (int s = 0; s < S; ++s) st8(dy, (T * k + s * T + t) * H + c, d);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k && rows[j] >= 0) {
-        const int64_t o = (int64_t)rows[j] * H + c;
-        float y[8], v[8];
-        ld8(y_rows, o, y);
+        float y[8];
+        ld8(y_rows, (int64_t)rows[j] * H + c, y);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          v[i] = g[j] * d[i];
-          part[j] = fmaf(d[i], y[i], part[j]);
-        }
-        st8(dy, o, v);
+        for (int i = 0; i < 8; ++i) part[j] = fmaf(d[i], y[i], part[j]);
       }
     }
   }
@@ -375,37 +376,56 @@ __device__ __forceinline__ void quant_tile_wave(float v0, float v1, float& s, ui
   c1 = e4m3_encode(__fdiv_rn(v1, s));
 }
 
-// dy [rows, H] FP32 -> codes [rows, H] and scales chunk-major [H/128][rows]; rows without
-// a token (row_token < 0) quantise as zeros. One workgroup per row; each wave takes every
-// fourth 128-wide tile, kQB tiles' loads in flight before any is quantised.
-constexpr int kQB = 8;
+// dy of the permuted rows, dy_r = fl32(row_gate[r] dout[row_token[r]]) (row_gate NULL: 1),
+// quantised 1x128 along H: codes [rows, H] and scales chunk-major [H/128][rows]; rows
+// without a token quantise as zeros. One workgroup per row; a thread takes 8 consecutive
+// values of every 2048 (16 lanes per 128-wide tile), all of its loads issued before any
+// tile is quantised.
+constexpr int kQRSteps = 8;   // 2048-wide steps: H <= 16384
 
-__global__ __launch_bounds__(256) void quant_rows_kernel(const float* __restrict__ v,
-                                                         const int32_t* __restrict__ row_token,
-                                                         int64_t n_rows, int C,
-                                                         uint8_t* __restrict__ q,
-                                                         float* __restrict__ s_cm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) void quant_dy_rows_kernel(const uint16_t* __restrict__ dout,
+                                                            const float* __restrict__ row_gate,
+                                                            const int32_t* __restrict__ row_token,
+                                                            int64_t n_tokens, int64_t n_rows, int C,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ s_cm) {
   const int64_t r = blockIdx.x;
-  const int nct = C / kTile;
-  const bool live = row_token == nullptr || row_token[r] >= 0;
-  for (int t0 = wave; t0 < nct; t0 += 4 * kQB) {
-    float2 x[kQB];
+  const int64_t t = row_token[r];
+  const bool live = t >= 0 && t < n_tokens;
+  const float gr = row_gate ? row_gate[r] : 1.0f;
+  float v[kQRSteps][8];
 #pragma unroll
-    for (int u = 0; u < kQB; ++u) {
-      const int ct = min(t0 + 4 * u, nct - 1);
-      x[u] = *reinterpret_cast<const float2*>(v + r * C + ct * kTile + 2 * lane);
+  for (int u = 0; u < kQRSteps; ++u) {
+    const int c = u * 2048 + threadIdx.x * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+    if (live && c < C) {
+      float d[8];
+      ld8(dout, t * C + c, d);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = gr * d[i];
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kQB; ++u) {
-      const int ct = t0 + 4 * u;
-      if (ct < nct) {
-        float s;
-        uint32_t c0, c1;
-        quant_tile_wave(live ? x[u].x : 0.0f, live ? x[u].y : 0.0f, s, c0, c1);
-        reinterpret_cast<uint16_t*>(q + r * C + ct * kTile)[lane] = (uint16_t)(c0 | (c1 << 8));
-        if (lane == 0) s_cm[(int64_t)ct * n_rows + r] = s;
-      }
+  for (int u = 0; u < kQRSteps; ++u) {
+    const int c = u * 2048 + threadIdx.x * 8;
+    if (u * 2048 >= C) break;
+    // amax over the tile's 16 lanes (lanes 16a .. 16a+15 hold one 128-wide tile)
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
+    m = fmaxf(m, __shfl_xor(m, 1, kWave));
+    m = fmaxf(m, __shfl_xor(m, 2, kWave));
+    m = fmaxf(m, __shfl_xor(m, 4, kWave));
+    m = fmaxf(m, __shfl_xor(m, 8, kWave));
+    if (c < C) {
+      const float sc = group_scale(m);
+      const uint32_t lo = e4m3_encode(__fdiv_rn(v[u][0], sc)) | (e4m3_encode(__fdiv_rn(v[u][1], sc)) << 8) |
+                          (e4m3_encode(__fdiv_rn(v[u][2], sc)) << 16) | (e4m3_encode(__fdiv_rn(v[u][3], sc)) << 24);
+      const uint32_t hi = e4m3_encode(__fdiv_rn(v[u][4], sc)) | (e4m3_encode(__fdiv_rn(v[u][5], sc)) << 8) |
+                          (e4m3_encode(__fdiv_rn(v[u][6], sc)) << 16) | (e4m3_encode(__fdiv_rn(v[u][7], sc)) << 24);
+      *reinterpret_cast<uint2*>(q + r * C + c) = make_uint2(lo, hi);
+      if ((threadIdx.x & 15) == 0) s_cm[(int64_t)(c / kTile) * n_rows + r] = sc;
     }
   }
 }
@@ -482,12 +502,17 @@ __global__ __launch_bounds__(1024) void pad_plan_kernel(const int32_t* __restric
 // Token-axis quantisation, transposed: for padded chunk g (128 padded rows of one expert)
 // and 64 columns, column c's 128 values (rows past the segment read zero) get the scale
 // s = fl32(amax / 448) and are stored as codes qt[c][128 g + i], scales s_cm[g][c].
-// Source rows: src[r] (MODE 0), src[row_token[r]] (MODE 1), or src[r] only where
-// row_token[r] >= 0 (MODE 2).
+// Source rows: src[r] (MODE 0), src[row_token[r]] (MODE 1), or src[row_token[r]] times
+// row_gate[r] in one FP32 rounding (MODE 3: dy from the upstream gradient; row_gate NULL
+// means 1).
+// Thread (q, rg) holds columns 4q .. 4q+3 of rows 8rg .. 8rg+7: one 8- or 16-byte load per
+// row (a wave's load covers four rows of 64 columns), all eight issued before any is used;
+// rows without a source are not read.
 template <typename T, int MODE>
 __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__ src, int64_t src_rows,
                                                            int64_t n_rows,
                                                            const int32_t* __restrict__ row_token,
+                                                           const float* __restrict__ row_gate,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ poff,
                                                            const int32_t* __restrict__ chunk_e,
@@ -496,66 +521,104 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__
                                                            float* __restrict__ s_cm) {
   __shared__ float amx[4][64];
   __shared__ int64_t srow[kTile];   // source row of each of the chunk's rows, -1: zero
-  __shared__ uint4 stg[64][8];      // codes of the 64 columns (128 bytes each), 16-byte
-                                    // segment q of column c at q ^ (c & 7)
+  __shared__ float grow[kTile];     // MODE 3: the row's gate
+  __shared__ uint2 stg[64][16];     // codes of the 64 columns (128 bytes each), 8-byte
+                                    // piece p of column c at p ^ ((c >> 2) & 15)
   const int64_t g = blockIdx.x;
   const int e = chunk_e[g];
   if (e < 0) return;
-  const int cg = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  const int c = blockIdx.y * 64 + cg;
+  const int q = threadIdx.x & 15, rg = threadIdx.x >> 4, wave = threadIdx.x >> 6;
+  const int c0 = blockIdx.y * 64 + 4 * q;           // first of this thread's four columns
   const int64_t first = offsets[e] + (g * kTile - poff[e]);   // permuted row of padded row 128 g
   const int64_t end = min((int64_t)offsets[e + 1], n_rows);
   if (threadIdx.x < kTile) {
     const int64_t r = first + threadIdx.x;
     int64_t sr = -1;
+    float gv = 1.0f;
     if (r < end) {
-      if (MODE == 1) {
+      if (MODE == 1 || MODE == 3) {
         const int64_t t = row_token[r];
         sr = (t >= 0 && t < src_rows) ? t : -1;
-      } else if (MODE == 2) {
-        sr = row_token[r] >= 0 ? r : -1;
+        if (MODE == 3 && row_gate) gv = row_gate[r];
       } else {
         sr = r;
       }
     }
     srow[threadIdx.x] = sr;
+    grow[threadIdx.x] = gv;
   }
   __syncthreads();
-  // all 32 loads of a thread are issued before any is used (rows without a source read
-  // row 0 and are dropped)
-  const int cc = min(c, C - 1);
-  float v[32];
+  const bool col_ok = c0 < C;   // C is a multiple of 128: all four columns or none
+  float v[8][4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int64_t sr = srow[rg * 32 + i];
-    v[i] = ld_val(src, (sr >= 0 ? sr : 0) * C + cc);
+  for (int i = 0; i < 8; ++i) {
+    const int64_t sr = srow[rg * 8 + i];
+    v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.0f;
+    if (sr >= 0 && col_ok) {
+      if constexpr (sizeof(T) == 2) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + sr * C + c0);
+        v[i][0] = __uint_as_float(raw.x << 16);
+        v[i][1] = __uint_as_float(raw.x & 0xffff0000u);
+        v[i][2] = __uint_as_float(raw.y << 16);
+        v[i][3] = __uint_as_float(raw.y & 0xffff0000u);
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + sr * C + c0);
+        v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+      }
+      if constexpr (MODE == 3) {
+        const float gv = grow[rg * 8 + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[i][j] = gv * v[i][j];
+      }
+    }
   }
-  float m = 0.0f;
+  // column maxima: this thread's 8 rows, the wave's 4 row groups (lanes 16 apart), then
+  // the 4 waves through LDS
+  float m[4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    v[i] = srow[rg * 32 + i] >= 0 ? v[i] : 0.0f;
-    m = fmaxf(m, fabsf(v[i]));
+  for (int j = 0; j < 4; ++j) {
+    m[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[j] = fmaxf(m[j], fabsf(v[i][j]));
+    m[j] = fmaxf(m[j], __shfl_xor(m[j], 16, kWave));
+    m[j] = fmaxf(m[j], __shfl_xor(m[j], 32, kWave));
   }
-  amx[rg][cg] = m;
-  __syncthreads();
-  const float amax = fmaxf(fmaxf(amx[0][cg], amx[1][cg]), fmaxf(amx[2][cg], amx[3][cg]));
-  const float s = group_scale(amax);
-  uint32_t w[8];
+  if ((threadIdx.x & 63) < 16) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    w[i] = e4m3_encode(__fdiv_rn(v[4 * i], s)) | (e4m3_encode(__fdiv_rn(v[4 * i + 1], s)) << 8) |
-           (e4m3_encode(__fdiv_rn(v[4 * i + 2], s)) << 16) | (e4m3_encode(__fdiv_rn(v[4 * i + 3], s)) << 24);
-  // through LDS, so that every store writes whole 128-byte rows of qt (8 lanes per row)
-  stg[cg][(2 * rg) ^ (cg & 7)] = make_uint4(w[0], w[1], w[2], w[3]);
-  stg[cg][(2 * rg + 1) ^ (cg & 7)] = make_uint4(w[4], w[5], w[6], w[7]);
-  if (rg == 0 && c < C) s_cm[g * C + c] = s;
+    for (int j = 0; j < 4; ++j) amx[wave][4 * q + j] = m[j];
+  }
   __syncthreads();
+  float sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cc = 4 * q + j;
+    sc[j] = group_scale(fmaxf(fmaxf(amx[0][cc], amx[1][cc]), fmaxf(amx[2][cc], amx[3][cc])));
+  }
+  // codes of column 4q + j, rows 8rg .. 8rg+7: bytes 8rg .. 8rg+7 of that column's 128
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cc = 4 * q + j;
+    const uint32_t lo = e4m3_encode(__fdiv_rn(v[0][j], sc[j])) | (e4m3_encode(__fdiv_rn(v[1][j], sc[j])) << 8) |
+                        (e4m3_encode(__fdiv_rn(v[2][j], sc[j])) << 16) | (e4m3_encode(__fdiv_rn(v[3][j], sc[j])) << 24);
+    const uint32_t hi = e4m3_encode(__fdiv_rn(v[4][j], sc[j])) | (e4m3_encode(__fdiv_rn(v[5][j], sc[j])) << 8) |
+                        (e4m3_encode(__fdiv_rn(v[6][j], sc[j])) << 16) | (e4m3_encode(__fdiv_rn(v[7][j], sc[j])) << 24);
+    stg[cc][rg ^ ((cc >> 2) & 15)] = make_uint2(lo, hi);
+  }
+  if (rg == 0 && col_ok) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_cm[g * C + c0 + j] = sc[j];
+  }
+  __syncthreads();
+  // whole 128-byte rows of qt (8 lanes per column, 16 bytes each)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int u = threadIdx.x + 256 * i, cc = u >> 3, q = u & 7;
+    const int u = threadIdx.x + 256 * i, cc = u >> 3, p = u & 7;
     const int col = blockIdx.y * 64 + cc;
-    if (col < C)
-      *reinterpret_cast<uint4*>(qt + (int64_t)col * pstride + g * kTile + q * 16) = stg[cc][q ^ (cc & 7)];
+    if (col < C) {
+      const uint2 a = stg[cc][(2 * p) ^ ((cc >> 2) & 15)];
+      const uint2 b = stg[cc][(2 * p + 1) ^ ((cc >> 2) & 15)];
+      *reinterpret_cast<uint4*>(qt + (int64_t)col * pstride + g * kTile + p * 16) = make_uint4(a.x, a.y, b.x, b.y);
+    }
   }
 }
 
@@ -755,24 +818,24 @@ using namespace moe;
 // ------------------------------------------------------------------------------------
 extern "C" moe_status moe_combine_backward(const moe_config* cfg, int64_t T, const uint16_t* dout,
                                            const void* y_rows, moe_dtype yt, const int32_t* row_of,
-                                           const float* topk_gate, float* dy, float* dgate,
+                                           const float* topk_gate, float* row_gate, float* dgate,
                                            void* stream) {
   const moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (T < 0 || T > 0x7fffffff) return MOE_ERR_SHAPE;
   if (yt != MOE_BF16 && yt != MOE_F32) return MOE_ERR_DTYPE;
   if (T == 0) return MOE_OK;
-  if (!dout || !y_rows || !row_of || !topk_gate || !dy || !dgate) return MOE_ERR_NULL;
+  if (!dout || !y_rows || !row_of || !topk_gate || !row_gate || !dgate) return MOE_ERR_NULL;
   const int64_t n_rows = T * (cfg->top_k + cfg->n_shared);
   hipStream_t s = as_stream(stream);
   if (yt == MOE_BF16)
     hipLaunchKernelGGL(combine_bwd_kernel<uint16_t>, dim3((unsigned)T), dim3(256), 0, s, dout,
                        static_cast<const uint16_t*>(y_rows), row_of, topk_gate, T, cfg->hidden,
-                       cfg->top_k, cfg->n_shared, n_rows, dy, dgate);
+                       cfg->top_k, cfg->n_shared, n_rows, row_gate, dgate);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3((unsigned)T), dim3(256), 0, s, dout,
                        static_cast<const float*>(y_rows), row_of, topk_gate, T, cfg->hidden,
-                       cfg->top_k, cfg->n_shared, n_rows, dy, dgate);
+                       cfg->top_k, cfg->n_shared, n_rows, row_gate, dgate);
   return launch_status();
 }
 
@@ -869,8 +932,9 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     const float* xs, const void* x, moe_dtype xt, const int32_t* row_token, const int32_t* offsets,
     const uint8_t* w1, const float* w1s, const uint8_t* w3, const float* w3s, const uint8_t* w2t,
     const float* w2ts, const uint8_t* w13t, const float* w13ts, const float* a_saved,
-    const float* b_saved, const float* dy, void* dx_rows, moe_dtype dxt, void* dw1, void* dw3,
-    void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes, void* stream) {
+    const float* b_saved, const uint16_t* dout, const float* row_gate, void* dx_rows,
+    moe_dtype dxt, void* dw1, void* dw3, void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes,
+    void* stream) {
   const moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->scale_mode != 0) return MOE_ERR_UNSUPPORTED;
@@ -889,12 +953,12 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     return MOE_ERR_UNSUPPORTED;
   if (!offsets || !dw1 || !dw3 || !dw2) return MOE_ERR_NULL;
   if (n_rows > 0 && (!row_token || !w1 || !w1s || !w3 || !w3s || !w2t || !w2ts || !w13t || !w13ts ||
-                     !dy || !dx_rows))
+                     !dx_rows))
     return MOE_ERR_NULL;
   // with the forward's SwiGLU inputs at hand, only h is recomputed (from them)
   const bool saved = a_saved != nullptr || b_saved != nullptr;
   if (saved && (!a_saved || !b_saved)) return MOE_ERR_NULL;
-  if (n_tokens > 0 && (!x || (!saved && (!xq || !xs)))) return MOE_ERR_NULL;
+  if (n_tokens > 0 && (!x || !dout || (!saved && (!xq || !xs)))) return MOE_ERR_NULL;
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -918,8 +982,8 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     if (r != MOE_OK) return r;
     // dgrad of the down projection and the recomputed gate/up inputs (K = H)
     const int64_t it = n_rows * (I / kTile);
-    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, dy, row_token,
-                       n_rows, (int)H, dyq, dys);
+    hipLaunchKernelGGL(quant_dy_rows_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, dout, row_gate,
+                       row_token, n_tokens, n_rows, (int)H, dyq, dys);
     if (!saved && (r = ffn_recompute_launch(plan, n_experts, n_rows, n_tokens, xq, xs, row_token, w1,
                                             w1s, w3, w3s, (int)H, (int)I, xgs, fa, fb, s)) != MOE_OK)
       return r;
@@ -946,22 +1010,22 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   float* uts = reinterpret_cast<float*>(base + L.uts);
   if (n_rows > 0) {
     const dim3 gh((unsigned)G, (unsigned)((H + 63) / 64)), gi((unsigned)G, (unsigned)((I + 63) / 64));
-    hipLaunchKernelGGL((quant_tokens_kernel<float, 2>), gh, dim3(256), 0, s, dy, n_rows, n_rows, row_token,
-                       offsets, poff, chunk_e, (int)H, P, dyt, dyts);
+    hipLaunchKernelGGL((quant_tokens_kernel<uint16_t, 3>), gh, dim3(256), 0, s, dout, n_tokens, n_rows,
+                       row_token, row_gate, offsets, poff, chunk_e, (int)H, P, dyt, dyts);
     if (xt == MOE_BF16)
       hipLaunchKernelGGL((quant_tokens_kernel<uint16_t, 1>), gh, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(x), n_tokens, n_rows, row_token, offsets, poff, chunk_e,
-                         (int)H, P, xtt, xts);
+                         static_cast<const uint16_t*>(x), n_tokens, n_rows, row_token, nullptr, offsets, poff,
+                         chunk_e, (int)H, P, xtt, xts);
     else
       hipLaunchKernelGGL((quant_tokens_kernel<float, 1>), gh, dim3(256), 0, s,
-                         static_cast<const float*>(x), n_tokens, n_rows, row_token, offsets, poff, chunk_e,
-                         (int)H, P, xtt, xts);
+                         static_cast<const float*>(x), n_tokens, n_rows, row_token, nullptr, offsets, poff,
+                         chunk_e, (int)H, P, xtt, xts);
     hipLaunchKernelGGL((quant_tokens_kernel<float, 0>), gi, dim3(256), 0, s, fdh, n_rows, n_rows, row_token,
-                       offsets, poff, chunk_e, (int)I, P, htt, hts);
+                       nullptr, offsets, poff, chunk_e, (int)I, P, htt, hts);
     hipLaunchKernelGGL((quant_tokens_kernel<float, 0>), gi, dim3(256), 0, s, fa, n_rows, n_rows, row_token,
-                       offsets, poff, chunk_e, (int)I, P, gtt, gts);
+                       nullptr, offsets, poff, chunk_e, (int)I, P, gtt, gts);
     hipLaunchKernelGGL((quant_tokens_kernel<float, 0>), gi, dim3(256), 0, s, fb, n_rows, n_rows, row_token,
-                       offsets, poff, chunk_e, (int)I, P, utt, uts);
+                       nullptr, offsets, poff, chunk_e, (int)I, P, utt, uts);
   }
   // wgrad GEMMs (every expert's gradient written; zero for an expert without rows)
   // grid: 8 XCDs x ceil(groups / 8) groups x tiles per group

@@ -248,7 +248,7 @@ class MoELayer:
         H, I, N, k, S = (cfg.hidden_size, cfg.moe_intermediate_size, cfg.num_experts,
                          cfg.num_experts_per_tok, cfg.num_shared_experts)
         EA, rows, f32 = N + S, T * (k + S), torch.float32
-        self.dy = torch.empty((rows, H), dtype=f32, device=d)
+        self.row_gate = torch.empty((rows,), dtype=f32, device=d)
         self.dgate = torch.empty((T, k), dtype=f32, device=d)
         self.dx_rows = torch.empty((rows, H), dtype=f32, device=d)
         self.dx_route = torch.empty((T, H), dtype=f32, device=d)
@@ -276,12 +276,13 @@ class MoELayer:
         EA = cfg.num_experts + cfg.num_shared_experts
         mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
         mark(0)
-        moe_combine_backward(c, dout, self.y_rows, self.row_of, self.topk_gate, dy=self.dy,
+        moe_combine_backward(c, dout, self.y_rows, self.row_of, self.topk_gate, row_gate=self.row_gate,
                              dgate=self.dgate)
         mark(1)
         moe_grouped_ffn_fp8_backward(c, EA, self.xq, self.xs, self.x, self.row_token, self.offsets,
                                      self.w1, self.w1s, self.w3, self.w3s, self.w2t, self.w2ts,
-                                     self.w13t, self.w13ts, self.dy, dx_rows=self.dx_rows,
+                                     self.w13t, self.w13ts, dout, row_gate=self.row_gate,
+                                     dx_rows=self.dx_rows,
                                      dw1=self.dw1, dw3=self.dw3, dw2=self.dw2, ws=self.bwd_ws,
                                      a_saved=self.a_saved if self.keep_ab else None,
                                      b_saved=self.b_saved if self.keep_ab else None)

@@ -424,16 +424,20 @@ moe_status moe_seq_balance(const moe_config* cfg, int64_t T, int64_t seq_len,
  *   dout      [T, H] bf16 bits: gradient of the layer output
  *   y_rows    [T*(k+N_s), H] (yt = MOE_BF16 or MOE_F32): the forward's expert output rows
  *   row_of, topk_gate: from the forward ([T, k] int32 / float)
- *   dy        [T*(k+N_s), H] float, output: gate_tj * dout_t (one FP32 rounding) on routed
- *             rows, dout_t on shared rows T*k + s*T + t; rows that no (token, slot) names
- *             are not written
+ *   row_gate  [T*(k+N_s)] float, output: the gate of every permuted row, gate_tj on row
+ *             row_of[t, j] and 1 on the shared rows T*k + s*T + t; rows that no (token,
+ *             slot) names are not written. The rows' upstream gradient is
+ *             dy_r = row_gate[r] * dout_{token(r)} (one FP32 rounding); it is never stored:
+ *             moe_grouped_ffn_fp8_backward forms it from dout and row_gate where it
+ *             quantises it.
  *   dgate     [T, k] float, output: sum_h dout_t[h] * y_row[h] (FP32, fixed order); 0 for a
  *             slot with row -1
  * Errors: NULL pointers (T > 0); invalid config; T < 0 or T >= 2^31; yt not BF16/F32.
  */
 moe_status moe_combine_backward(const moe_config* cfg, int64_t T, const uint16_t* dout,
                                 const void* y_rows, moe_dtype yt, const int32_t* row_of,
-                                const float* topk_gate, float* dy, float* dgate, void* stream);
+                                const float* topk_gate, float* row_gate, float* dgate,
+                                void* stream);
 
 /*
  * moe_route_backward — gradient of the gates through the router, in FP32 ([digest]
@@ -490,7 +494,8 @@ moe_status moe_transpose_fp8_blocks(int64_t E, int64_t R, int64_t C, const uint8
  *              (a_saved, b_saved from moe_grouped_ffn_fp8_gate_up_train), or, when both
  *              are NULL, recomputed by the FP8 fprop GEMMs on the forward's codes (the
  *              same launch, so the same values bit for bit).
- *   dgrad:     dh = dy W2 (dy in 1x128 tiles along H); dg = dh b silu'(a), du = dh silu(a)
+ *   dgrad:     dh = dy W2 with dy_r = fl32(row_gate[r] * dout[row_token[r]]) (dy in 1x128
+ *              tiles along H); dg = dh b silu'(a), du = dh silu(a)
  *              (FP32); dx_rows = dg W1 + du W3 ([dg | du] in 1x128 tiles along I, one
  *              GEMM over K = 2I with the packed [W1^T | W3^T]).
  *   wgrad:     dW2 = dy^T h, dW1 = dg^T x, dW3 = du^T x with h = silu(a) b (FP32) and x
@@ -504,7 +509,8 @@ moe_status moe_transpose_fp8_blocks(int64_t E, int64_t R, int64_t C, const uint8
  *                with scales [E, H/128, 2I/128] (moe_transpose_fp8_blocks, then
  *                moe_pack_fp8_weights)
  *   a_saved, b_saved  [n_rows, I] float each or both NULL: the forward's SwiGLU inputs
- *   dy           [n_rows, H] float (moe_combine_backward)
+ *   dout         [T, H] bf16 bits: the layer's upstream gradient (rows of dy are gated copies)
+ *   row_gate     [n_rows] float (moe_combine_backward) or NULL (every row's gate 1)
  *   dx_rows      [n_rows, H] output (dxt = BF16/F32)
  *   dw1, dw3     [E, I, H] and dw2 [E, H, I] outputs (dwt = BF16/F32): FP32-promoted
  *                sums, written for every expert (zero for an expert without rows)
@@ -521,8 +527,9 @@ moe_status moe_grouped_ffn_fp8_backward(
     const float* xs, const void* x, moe_dtype xt, const int32_t* row_token, const int32_t* offsets,
     const uint8_t* w1, const float* w1s, const uint8_t* w3, const float* w3s, const uint8_t* w2t,
     const float* w2ts, const uint8_t* w13t, const float* w13ts, const float* a_saved,
-    const float* b_saved, const float* dy, void* dx_rows, moe_dtype dxt, void* dw1, void* dw3,
-    void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes, void* stream);
+    const float* b_saved, const uint16_t* dout, const float* row_gate, void* dx_rows,
+    moe_dtype dxt, void* dw1, void* dw3, void* dw2, moe_dtype dwt, void* ws, size_t ws_bytes,
+    void* stream);
 
 #ifdef __cplusplus
 }

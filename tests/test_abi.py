@@ -174,9 +174,9 @@ def test_host_validation_status_codes():
     fb = L.moe_grouped_ffn_fp8_backward
     w10 = [fake] * 10   # row_token, offsets, w1, w1s, w3, w3s, w2t, w2ts, w13t, w13ts
 
-    def fbc(cfg, E, dxt, dx_rows, ws_bytes, ab=(None, None), xq=fake):
-        return fb(ctypes.byref(cfg), E, 100, 10, xq, fake, fake, 1, *w10, *ab, fake, dx_rows, dxt,
-                  fake, fake, fake, 0, fake, ws_bytes, None)
+    def fbc(cfg, E, dxt, dx_rows, ws_bytes, ab=(None, None), xq=fake, dout=fake):
+        return fb(ctypes.byref(cfg), E, 100, 10, xq, fake, fake, 1, *w10, *ab, dout, None, dx_rows,
+                  dxt, fake, fake, fake, 0, fake, ws_bytes, None)
     assert fbc(c, 4, 0, fake, need_fb - 1) == 6
     assert fbc(c, 0, 0, fake, need_fb) == 2
     assert fbc(c, 4, 5, fake, need_fb) == 3
@@ -185,6 +185,7 @@ def test_host_validation_status_codes():
     assert fbc(c, 4, 0, fake, need_fb, ab=(fake, None)) == 1
     assert fbc(c, 4, 0, fake, need_fb, ab=(None, fake)) == 1
     assert fbc(c, 4, 0, fake, need_fb, xq=None) == 1
+    assert fbc(c, 4, 0, fake, need_fb, dout=None) == 1
     p2 = _cfg(m, scale_mode=1)
     assert fbc(p2, 4, 0, fake, need_fb) == 4
     # the training gate/up: both outputs, FP32 group scales only

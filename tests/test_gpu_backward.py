@@ -1,6 +1,7 @@
 """Parity of the backward pass (HIP, through the C ABI) against the CPU oracle.
 
-Bit-exact: the weight transposition, dy (one FP32 product per element). Within stated
+Bit-exact: the weight transposition, the rows' gates and the dy formed from them (one
+FP32 product per element). Within stated
 tolerances: the gates' gradient and the router's gradients (FP32 sums against FP64), the
 FFN backward and the whole-layer gradients (FP8 GEMMs, normwise; see TOL).
 """
@@ -100,10 +101,23 @@ def test_combine_backward_matches_oracle(lib, T, H, N, k, S, ydt):
     gate = rng.uniform(0.05, 1.0, (T, k)).astype(np.float32)
     dout = oracle.round_bf16(rng.standard_normal((T, H)).astype(np.float32))
     say(f"combine_backward T={T} H={H} k={k} S={S} {ydt}")
-    dy, dgate = lib.moe_combine_backward(c, dev(dout, torch.bfloat16), dev(y, ydt), dev(row_of), dev(gate))
+    row_gate, dgate = lib.moe_combine_backward(c, dev(dout, torch.bfloat16), dev(y, ydt), dev(row_of),
+                                               dev(gate))
     torch.cuda.synchronize()
     rdy, rdg = oracle.combine_backward(dout, y, row_of, gate, S)
-    assert np.array_equal(host(dy).view(np.uint32), rdy.view(np.uint32))
+    # every row's gate (1 on the shared rows), and the rows' upstream gradient formed from it
+    # as the FFN backward forms it, one float32 product, bit-exact against the oracle's dy
+    g_rows = host(row_gate)
+    tok = np.empty(rows, np.int64)
+    for j in range(k):
+        tok[row_of[:, j]] = np.arange(T)
+        assert np.array_equal(g_rows[row_of[:, j]].view(np.uint32), gate[:, j].view(np.uint32))
+    for s_ in range(S):
+        tok[T * k + s_ * T:T * k + (s_ + 1) * T] = np.arange(T)
+    assert np.all(g_rows[T * k:] == 1.0)
+    dy = g_rows[:, None] * dout[tok]
+    assert dy.dtype == np.float32
+    assert np.array_equal(dy.view(np.uint32), rdy.view(np.uint32))
     # FP32 sum of H products against FP64: |err| <= ~H 2^-24 sum |terms|
     bound = H * 2.0 ** -24 * (np.abs(dout).astype(np.float64) @ np.abs(y).T.astype(np.float64)).max()
     assert np.max(np.abs(host(dgate) - rdg)) <= bound
@@ -216,13 +230,19 @@ def test_grouped_ffn_backward_matches_oracle(lib, H, I, loads, gaps, bf16):
     xs = (rng.uniform(0.5, 2.0, (T, H // 128)) * 2.0 ** -6).astype(np.float32)
     x = oracle.round_bf16(oracle.dequant_1x128(xq, xs).astype(np.float32)
                           * rng.uniform(0.9, 1.1, (T, H)).astype(np.float32))
-    dy = (rng.standard_normal((n_rows, H)) * 0.01).astype(np.float32)
+    # the rows' upstream gradient as the layer gives it: a gate per row times the token's
+    # bf16 gradient, one float32 product (no gates in the bf16-output case: all 1)
+    dout = oracle.round_bf16((rng.standard_normal((T, H)) * 0.01).astype(np.float32))
+    row_gate = None if bf16 else rng.uniform(0.05, 1.0, n_rows).astype(np.float32)
+    g_rows = np.ones(n_rows, np.float32) if row_gate is None else row_gate
+    dy = g_rows[:, None] * dout[np.where(row_token >= 0, row_token, 0)]
     ws = _expert_set(rng, E, H, I)
     say(f"ffn_backward H={H} I={I} loads={loads} gaps={gaps}")
     w = _device_weights(lib, ws, H, I)
     odt = torch.bfloat16 if bf16 else torch.float32
     dxr, dw1, dw3, dw2 = lib.moe_grouped_ffn_fp8_backward(
-        c, E, dev(xq), dev(xs), dev(x, torch.bfloat16), dev(row_token), dev(offsets), *w, dev(dy),
+        c, E, dev(xq), dev(xs), dev(x, torch.bfloat16), dev(row_token), dev(offsets), *w,
+        dev(dout, torch.bfloat16), row_gate=None if row_gate is None else dev(row_gate),
         dx_dtype=odt, dw_dtype=odt)
     assert dxr.dtype == odt and dw1.dtype == odt and dw2.dtype == odt
     torch.cuda.synchronize()
