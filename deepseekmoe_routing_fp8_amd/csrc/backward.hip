@@ -24,6 +24,8 @@
 //     dy, h, dg, du, x  -> 128-row tiles along the token axis, stored transposed
 //     dW2 = dy^T h; dW1 = dg^T x and dW3 = du^T x in one launch   (FP8 wgrad, K = tokens)
 //   unpermute-sum      dx_t = sum of its rows' dx (+ the router's dx), FP32, bf16 out.
+#include <algorithm>
+
 #include "common.h"
 #include "ffn_internal.h"
 
@@ -664,8 +666,8 @@ template <typename OT, int SHARE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wgrad_kernel(
     const uint8_t* __restrict__ at, const float* __restrict__ sa, const uint8_t* __restrict__ at2,
     const float* __restrict__ sa2, const uint8_t* __restrict__ bt, const float* __restrict__ sb,
-    const int32_t* __restrict__ poff, int n_experts, int NA, int NB, int64_t pstride,
-    OT* __restrict__ out, OT* __restrict__ out2) {
+    const int32_t* __restrict__ poff, const int32_t* __restrict__ offsets, int n_experts, int NA,
+    int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2) {
   // A group is the NB/128 tiles that share one 128-row block of A_T. Group q runs on XCD
   // q % 8, its tiles on consecutive slots there (the A rows stay in that L2), and each
   // expert's groups spread over all XCDs, so a long segment (a shared expert) is split
@@ -683,6 +685,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * (kWgM / 2);
   const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
   const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
+  // Operands are read through buffer descriptors (32-bit offsets; each array holds fewer
+  // than 2^31 bytes). A lane's 32 rows of a chunk past the segment's last row are padding,
+  // stored as zeros: the lane reads them at an offset outside the descriptor's range,
+  // which returns zeros without touching memory.
+  const int rows_e = max(offsets[e + 1] - offsets[e], 0);
+  const int range = (int)((int64_t)NA * pstride);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, range, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra2 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, range, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  auto frag = [&](__amdgpu_buffer_rsrc_t r, int64_t row, int64_t p, bool live) __attribute__((always_inline)) {
+    const int off = live ? (int)(row * pstride + p + lk) : (int)0x80000000;
+    const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
   // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v; acc2: the second gradient
   // (SHARE 1) or the columns 128 further on (SHARE 2)
@@ -692,24 +712,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 #pragma unroll
     for (int j = 0; j < kWJ; ++j) acc[i][j] = acc2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto load_a = [&](const uint8_t* aa, const float* ss, int64_t p, int64_t g, v8i (&A)[4],
-                    float (&san)[4]) __attribute__((always_inline)) {
+  auto load_a = [&](__amdgpu_buffer_rsrc_t r, const float* ss, int64_t p, int64_t g, bool live,
+                    v8i (&A)[4], float (&san)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4* pa = reinterpret_cast<const uint4*>(aa + (int64_t)(wn + 16 * i + lr) * pstride + p + lk);
-      const uint4 a0 = pa[0], a1 = pa[1];
-      A[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      A[i] = frag(r, wn + 16 * i + lr, p, live);
       san[i] = ss[g * NA + wn + 16 * i + lr];
     }
   };
-  auto load_b = [&](int mb, int64_t p, int64_t g, v8i (&B)[kWJ], float4 (&sbm)[kWJ])
+  auto load_b = [&](int mb, int64_t p, int64_t g, bool live, v8i (&B)[kWJ], float4 (&sbm)[kWJ])
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j) {
-      const uint4* pb = reinterpret_cast<const uint4*>(bt + (int64_t)(mb + 16 * j + lr) * pstride + p + lk);
-      const uint4 b0 = pb[0], b1 = pb[1];
-      B[j] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-    }
+    for (int j = 0; j < kWJ; ++j) B[j] = frag(rb, mb + 16 * j + lr, p, live);
 #pragma unroll
     for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + mb + 16 * j + 4 * lg);
   };
@@ -733,26 +747,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   for (int ch = 0; ch < nch; ++ch) {
     const int64_t p = p0 + (int64_t)ch * kTile;
     const int64_t g = p / kTile;
+    const bool live = lk < rows_e - ch * kTile;
     if constexpr (SHARE == 2) {
       v8i A[4];
       float san[4];
-      load_a(at, sa, p, g, A, san);
+      load_a(ra, sa, p, g, live, A, san);
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
         v8i B[kWJ];
         float4 sbm[kWJ];
-        load_b(wm + pass * kWgM, p, g, B, sbm);
+        load_b(wm + pass * kWgM, p, g, live, B, sbm);
         mma(A, san, B, sbm, pass ? acc2 : acc);
       }
     } else {
       v8i B[kWJ];
       float4 sbm[kWJ];
-      load_b(wm, p, g, B, sbm);
+      load_b(wm, p, g, live, B, sbm);
 #pragma unroll
       for (int pass = 0; pass < (SHARE == 1 ? 2 : 1); ++pass) {
         v8i A[4];
         float san[4];
-        load_a(pass ? at2 : at, pass ? sa2 : sa, p, g, A, san);
+        load_a(pass ? ra2 : ra, pass ? sa2 : sa, p, g, live, A, san);
         mma(A, san, B, sbm, pass ? acc2 : acc);
       }
     }
@@ -949,7 +964,7 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   // 32-bit offsets inside the grouped GEMM and the transposed operands
   if (n_rows * H >= ((int64_t)1 << 32) || n_rows * 2 * I >= ((int64_t)1 << 32) ||
       n_rows * (H / kTile) * 4 >= ((int64_t)1 << 31) || L.max_chunks >= ((int64_t)1 << 24) ||
-      H > 16384 || 2 * I > 16384)
+      H > 16384 || 2 * I > 16384 || std::max(H, I) * L.pstride >= ((int64_t)1 << 31))
     return MOE_ERR_UNSUPPORTED;
   if (!offsets || !dw1 || !dw3 || !dw2) return MOE_ERR_NULL;
   if (n_rows > 0 && (!row_token || !w1 || !w1s || !w3 || !w3s || !w2t || !w2ts || !w13t || !w13ts ||
@@ -1038,26 +1053,26 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   if (dwt == MOE_F32) {
     if (pair)
       hipLaunchKernelGGL((wgrad_kernel<float, 2>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts,
-                         nullptr, nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P,
+                         nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P,
                          static_cast<float*>(dw2), nullptr);
     else
       hipLaunchKernelGGL((wgrad_kernel<float, 0>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
-                         nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P, static_cast<float*>(dw2),
+                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, static_cast<float*>(dw2),
                          nullptr);
     hipLaunchKernelGGL((wgrad_kernel<float, 1>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts,
-                       xtt, xts, poff, n_experts, (int)I, (int)H, P, static_cast<float*>(dw1),
+                       xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, static_cast<float*>(dw1),
                        static_cast<float*>(dw3));
   } else {
     if (pair)
       hipLaunchKernelGGL((wgrad_kernel<uint16_t, 2>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts,
-                         nullptr, nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P,
+                         nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P,
                          static_cast<uint16_t*>(dw2), nullptr);
     else
       hipLaunchKernelGGL((wgrad_kernel<uint16_t, 0>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts,
-                         nullptr, nullptr, htt, hts, poff, n_experts, (int)H, (int)I, P,
+                         nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P,
                          static_cast<uint16_t*>(dw2), nullptr);
     hipLaunchKernelGGL((wgrad_kernel<uint16_t, 1>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts,
-                       xtt, xts, poff, n_experts, (int)I, (int)H, P, static_cast<uint16_t*>(dw1),
+                       xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, static_cast<uint16_t*>(dw1),
                        static_cast<uint16_t*>(dw3));
   }
   return launch_status();

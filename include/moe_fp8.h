@@ -518,7 +518,9 @@ moe_status moe_transpose_fp8_blocks(int64_t E, int64_t R, int64_t C, const uint8
  * Errors: NULL pointers (one of a_saved, b_saved NULL and the other not is NULL too);
  * invalid config; scale_mode != 0 (UNSUPPORTED); E outside 1..1024, n_rows or T out of
  * range (SHAPE); bad dtypes (DTYPE); workspace (WORKSPACE);
- * n_rows * H or n_rows * 2I >= 2^32, H or 2I > 16384 (UNSUPPORTED).
+ * n_rows * H or n_rows * 2I >= 2^32, H or 2I > 16384, or max(H, I) * (n_rows + 128 E)
+ * >= 2^31 (the token-axis operands' 32-bit offsets; about 266,000 rows at the V3 shape)
+ * (UNSUPPORTED).
  */
 size_t moe_grouped_ffn_backward_workspace_bytes(const moe_config* cfg, int32_t n_experts,
                                                 int64_t n_rows);
