@@ -4,8 +4,9 @@ Usage: python deepseekmoe_routing_fp8_amd/build.py [--tools]  (run as a file: im
 the package would first load the library being built).
 Objects go to <repo>/_build/, the library next to this file. ``--tools`` (build_tools())
 also builds the measurement drivers: bench/moe_counters, a native driver of one layer
-step for profiler counter runs, and bench/hbm_read, the plain streaming read that the
-HBM rooflines are compared with.
+step for profiler counter runs, bench/hbm_read, the plain streaming read that the HBM
+rooflines are compared with, and bench/hbm_write, the store patterns that the
+write-bound weight gradients are compared with.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoe_fp8.so")
 COUNTERS = os.path.join(PKG, "bench", "moe_counters")
 HBM_READ = os.path.join(PKG, "bench", "hbm_read")
+HBM_WRITE = os.path.join(PKG, "bench", "hbm_write")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -62,9 +64,10 @@ def build_tools() -> None:
     _run([HIPCC, *FLAGS, COUNTERS + ".hip", "-L" + PKG, "-lmoe_fp8", "-Wl,-rpath,$ORIGIN/..",
           "-o", tmp])
     os.replace(tmp, COUNTERS)
-    tmp = HBM_READ + ".tmp"
-    _run([HIPCC, *FLAGS, HBM_READ + ".hip", "-o", tmp])
-    os.replace(tmp, HBM_READ)
+    for tool in (HBM_READ, HBM_WRITE):
+        tmp = tool + ".tmp"
+        _run([HIPCC, *FLAGS, tool + ".hip", "-o", tmp])
+        os.replace(tmp, tool)
 
 
 if __name__ == "__main__":
