@@ -377,8 +377,8 @@ def test_kept_swiglu_inputs_match_recompute(lib):
         e_b = relerr(host(keep.b_saved[lo:hi]), u)
         say(f"  expert {e} ({hi - lo} rows): a {e_a:.2e}, b {e_b:.2e}")
         # FP32 promotion of per-chunk MFMA partial sums (each within ~2^-12 of its chunk's
-        # sum of |products|) against the FP64 products
-        assert e_a < 1e-3 and e_b < 1e-3
+        # sum of |products|) against the FP64 products; measured 1.4e-5
+        assert e_a < 1e-4 and e_b < 1e-4
     del keep, rec
     torch.cuda.empty_cache()
 

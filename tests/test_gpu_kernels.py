@@ -507,6 +507,53 @@ def test_grouped_ffn_halves_equal_fused_call(lib, ydt):
     assert torch.equal(y_fused.view(torch.uint8), y_split.view(torch.uint8))
 
 
+@pytest.mark.parametrize("H,I,loads", [
+    (512, 256, [5, 400, 0, 193, 64, 250]),     # 160-row tiles, ragged tails
+    (1024, 512, [380, 370, 200]),              # 192-row tiles (12 16-row tiles) beside shorter
+    (7168, 2048, [160, 137, 1]),               # the V3 expert shape
+])
+def test_gate_up_train_keeps_swiglu_inputs(lib, H, I, loads):
+    """The training gate/up launch leaves the same (hq, hs) as the plain one, bit for bit,
+    and its a = G, b = U (FP32 rows) are the FP64 products of the oracle within the FP32
+    promotion of the MFMA's partial sums (rows without a token: zeros)."""
+    import dataclasses
+    rng = np.random.default_rng(H + len(loads))
+    E, rows, T = len(loads), int(sum(loads)), 301
+    cfg = dataclasses.replace(synth.PRESETS["tiny"], hidden_size=H, moe_intermediate_size=I,
+                              num_experts=max(E, 4), num_experts_per_tok=1, tokens=T)
+    c = lib.make_config(cfg)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    xq, xs = oracle.quantize_1x128(x)
+    offsets = np.concatenate([[0], np.cumsum(loads)]).astype(np.int32)
+    row_token = rng.integers(0, T, rows).astype(np.int32)
+    row_token[rng.choice(rows, 3, replace=False)] = -1
+    w = _expert_set(rng, E, H, I)
+    wd = _device_weights(lib, w)
+    args = (dev(xq), dev(xs), dev(row_token), dev(offsets))
+    say(f"gate_up_train H={H} I={I} loads={loads}")
+    ws_plain = lib.moe_grouped_ffn_fp8_gate_up(c, E, rows, *args, *wd[:4])
+    ws_train, a, b = lib.moe_grouped_ffn_fp8_gate_up_train(c, E, rows, *args, *wd[:4])
+    torch.cuda.synchronize()
+    hq0, hs0 = lib.grouped_ffn_intermediate(c, E, rows, ws_plain)
+    hq1, hs1 = lib.grouped_ffn_intermediate(c, E, rows, ws_train)
+    assert torch.equal(hq0, hq1) and torch.equal(hs0, hs1)
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    dead = row_token < 0
+    assert not np.any(a[dead]) and not np.any(b[dead])
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        live = np.nonzero(~dead[lo:hi])[0] + lo
+        if len(live) == 0:
+            continue
+        act = oracle.dequant_1x128(xq[row_token[live]], xs[row_token[live]])
+        g = act @ oracle.dequant_128x128(w[0][e], w[1][e]).T
+        u = act @ oracle.dequant_128x128(w[2][e], w[3][e]).T
+        e_a, e_b = _relerr(a[live], g), _relerr(b[live], u)
+        say(f"  expert {e} ({len(live)} rows): a {e_a:.2e}, b {e_b:.2e}")
+        # measured 5.4-5.5e-5 with these random codes
+        assert e_a < 3e-4 and e_b < 3e-4, (e, e_a, e_b)
+
+
 def test_grouped_ffn_bf16_output_and_bad_tokens(lib):
     import dataclasses
     rng = np.random.default_rng(21)
