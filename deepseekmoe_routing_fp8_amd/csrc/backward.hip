@@ -35,23 +35,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <typename T>
-__device__ __forceinline__ float ld_val(const T* p, int64_t i) {
-  if constexpr (sizeof(T) == 2)
-    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);
-  else
-    return reinterpret_cast<const float*>(p)[i];
-}
-
-template <typename T>
-__device__ __forceinline__ void st_val(T* p, int64_t i, float v) {
-  if constexpr (sizeof(T) == 2)
-    reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
-  else
-    reinterpret_cast<float*>(p)[i] = v;
-}
-
-// 8 consecutive values at p[i..i+8) (i a multiple of 8) as floats / stored from floats.
+// 8 consecutive values at p[i..i+8) (i a multiple of 8) as floats.
 template <typename T>
 __device__ __forceinline__ void ld8(const T* p, int64_t i, float (&v)[8]) {
   if constexpr (sizeof(T) == 2) {
@@ -68,11 +52,6 @@ __device__ __forceinline__ void ld8(const T* p, int64_t i, float (&v)[8]) {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
-}
-
-__device__ __forceinline__ void st8(float* p, int64_t i, const float (&v)[8]) {
-  *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
 // Sum over the 256 threads of a block, one value per slot (k <= kMaxTopK slots), in a fixed
