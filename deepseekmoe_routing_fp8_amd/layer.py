@@ -63,7 +63,8 @@ class MoELayer:
         self._T = None
         self._graph = None
         self.backward_enabled = backward
-        self.keep_ab = backward and keep_swiglu_inputs
+        # (the backward runs on the FP32 group scales only)
+        self.keep_ab = backward and keep_swiglu_inputs and scale_mode == 0
         self.dw_dtype = dw_dtype
         if backward:
             # dgrad operands: W2^T [I, H] and [W1^T | W3^T] [H, 2I] per expert, packed
