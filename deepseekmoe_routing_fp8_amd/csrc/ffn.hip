@@ -234,8 +234,14 @@ inline int gate_up_nb_per(int64_t n_rows, int32_t n_experts, bool mx) {
 // n-blocks per down-projection workgroup: with a few rows per expert (decode) each
 // workgroup streams weights for little compute, and one block per workgroup balances the
 // launch better (measured 9% faster at 4.5 rows per expert, 2-8% slower from ~140 up).
-inline int down_nb_per(int64_t n_rows, int32_t n_experts) {
-  return n_rows < 32 * (int64_t)n_experts ? 1 : kNbPerWg2;
+// Fewer blocks per workgroup also when n_nb blocks leave under eight rounds of workgroups
+// for the chip (with at least n_rows / tile-rows tiles): with N = I (the backward's dh)
+// four blocks per workgroup left 2.2 rounds, the last one mostly idle.
+inline int down_nb_per(int64_t n_rows, int32_t n_experts, int n_nb) {
+  int nbp = n_rows < 32 * (int64_t)n_experts ? 1 : kNbPerWg2;
+  const int64_t tiles_lo = std::max<int64_t>(n_rows / tile_rows(n_rows, n_experts, false), 1);
+  while (nbp > 1 && tiles_lo * ((n_nb + nbp - 1) / nbp) < 8 * 256) nbp /= 2;
+  return nbp;
 }
 constexpr int kXcds = 8;
 constexpr int kMaxChunks = 128;                  // K <= 16384
@@ -965,7 +971,8 @@ moe_status ffn_down(const moe_config* cfg, int32_t n_experts, int64_t n_rows, co
   hipStream_t s = as_stream(stream);
   const int H = cfg->hidden, I = cfg->inter;
   FfnArgs a2{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, f.hq, f.hs, n_rows,
-             nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256, down_nb_per(n_rows, n_experts),
+             nullptr, w2, w2s, nullptr, nullptr, H, I, (H + 255) / 256,
+             down_nb_per(n_rows, n_experts, (H + 255) / 256),
              nullptr, nullptr, y};
   const dim3 grid((unsigned)ffn_grid(f.L.max_tiles, (a2.n_nb + a2.nb_per - 1) / a2.nb_per, n_rows));
   const bool mx = cfg->scale_mode == 1;
@@ -1021,7 +1028,7 @@ moe_status ffn_grouped_gemm_launch(const void* plan, int32_t n_experts, int64_t 
     return MOE_ERR_UNSUPPORTED;
   const int64_t max_tiles = (n_rows + kMTShort - 1) / kMTShort + n_experts;
   const int n_nb = (N + 255) / 256;
-  const int nbp = down_nb_per(n_rows, n_experts);
+  const int nbp = down_nb_per(n_rows, n_experts, n_nb);
   const int64_t nwg = (n_nb + nbp - 1) / nbp;
   if (ffn_grid(max_tiles, nwg, n_rows) * kFThreads >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   const Tile* tiles = static_cast<const Tile*>(plan);
