@@ -5,7 +5,11 @@
 //   wgrad     the weight-gradient kernel's pattern: a 256-thread workgroup writes a
 //             128 x 128 tile, each wave a 64 x 64 quarter, each store instruction 16 rows
 //             x 64 contiguous bytes (lane l: row l % 16, 16 bytes at column 4 (l / 16));
-//   rows      the same tiles written as two 512-byte row pieces per store instruction.
+//   rows      the same tiles written as two 512-byte row pieces per store instruction;
+//   pairs     the gate/up epilogue's pattern for its FP32 rows: a 512-thread workgroup
+//             writes 16 rows x 128 columns per step, wave w lane l 16 bytes at row l % 16,
+//             column 32 (w / 2) + 8 (l / 16) + 4 (w % 2), so the two halves of every
+//             32-byte piece come from two waves.
 // Prints the best time of three per pattern (event-timed).
 #include <hip/hip_runtime.h>
 
@@ -37,6 +41,14 @@ __global__ __launch_bounds__(256) void store_rows(float* __restrict__ out, float
   }
 }
 
+__global__ __launch_bounds__(512) void store_pairs(float* __restrict__ out, float v) {
+  const int tc = blockIdx.x % (kC / 128), tr = blockIdx.x / (kC / 128);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = tc * 128 + 32 * (wave >> 1) + 8 * (lane >> 4) + 4 * (wave & 1);
+  for (int ts = 0; ts < 8; ++ts)   // 128 rows per workgroup
+    *reinterpret_cast<v4f*>(out + (long)(tr * 128 + ts * 16 + (lane & 15)) * kC + col) = v4f{v, v, v, v};
+}
+
 int main() {
   const size_t bytes = (size_t)kR * kC * 4;
   float* out = nullptr;
@@ -47,14 +59,15 @@ int main() {
   hipEvent_t a, b;
   if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return 1;
   const int tiles = (kR / 128) * (kC / 128);
-  const char* names[3] = {"linear", "wgrad 16 rows x 64 B", "rows 2 x 512 B"};
-  for (int k = 0; k < 3; ++k) {
+  const char* names[4] = {"linear", "wgrad 16 rows x 64 B", "rows 2 x 512 B", "pairs 16 B halves"};
+  for (int k = 0; k < 4; ++k) {
     float best = 1e30f;
     for (int r = 0; r < 4; ++r) {   // the first run of each pattern is a warm-up
       hipEventRecord(a);
       if (k == 0) hipLaunchKernelGGL(store_linear, dim3(4096), dim3(256), 0, 0, out, (long)(bytes / 16), 1.0f);
       if (k == 1) hipLaunchKernelGGL(store_wgrad, dim3(tiles), dim3(256), 0, 0, out, 2.0f);
       if (k == 2) hipLaunchKernelGGL(store_rows, dim3(tiles), dim3(256), 0, 0, out, 3.0f);
+      if (k == 3) hipLaunchKernelGGL(store_pairs, dim3(tiles), dim3(512), 0, 0, out, 4.0f);
       hipEventRecord(b);
       if (hipEventSynchronize(b) != hipSuccess) return 1;
       float ms = 0.0f;
