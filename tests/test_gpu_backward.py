@@ -277,7 +277,7 @@ def _q3(w):
     return (*oracle.quantize_128x128(w[0]), *oracle.quantize_128x128(w[1]), *oracle.quantize_128x128(w[2]))
 
 
-@pytest.mark.parametrize("name,tokens", [("tiny", None), ("reduced", 512)])
+@pytest.mark.parametrize("name,tokens", [("tiny", None), ("tiny", 1), ("tiny", 17), ("reduced", 512)])
 def test_layer_backward_matches_oracle(lib, name, tokens):
     from deepseekmoe_routing_fp8_amd import MoELayer
     cfg = synth.PRESETS[name]
