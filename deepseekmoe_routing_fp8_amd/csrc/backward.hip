@@ -953,6 +953,8 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   const bool saved = a_saved != nullptr || b_saved != nullptr;
   if (saved && (!a_saved || !b_saved)) return MOE_ERR_NULL;
   if (n_tokens > 0 && (!x || !dout || (!saved && (!xq || !xs)))) return MOE_ERR_NULL;
+  // the token-axis quantisers read x and dout rows in 8- and 16-byte pieces
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dout)) & 15) return MOE_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);

@@ -503,13 +503,14 @@ moe_status moe_transpose_fp8_blocks(int64_t E, int64_t R, int64_t C, const uint8
  *   Rows with row_token < 0 count as zero rows (their dy is ignored).
  *   xq, xs       [T, H] u8 / [T, H/128] float: the forward's activation codes and scales
  *                (read only to recompute a and b; may be NULL with a_saved, b_saved)
- *   x            [T, H] (xt = BF16/F32): the layer input
+ *   x            [T, H] (xt = BF16/F32): the layer input, 16-byte aligned
  *   w1, w3 (+s)  the forward's packed weights; w2t (+s): packed W2^T [E, I, H] with
  *                scales [E, I/128, H/128]; w13t (+s): packed [W1^T | W3^T] [E, H, 2I]
  *                with scales [E, H/128, 2I/128] (moe_transpose_fp8_blocks, then
  *                moe_pack_fp8_weights)
  *   a_saved, b_saved  [n_rows, I] float each or both NULL: the forward's SwiGLU inputs
- *   dout         [T, H] bf16 bits: the layer's upstream gradient (rows of dy are gated copies)
+ *   dout         [T, H] bf16 bits, 16-byte aligned: the layer's upstream gradient (rows of dy
+ *                are gated copies)
  *   row_gate     [n_rows] float (moe_combine_backward) or NULL (every row's gate 1)
  *   dx_rows      [n_rows, H] output (dxt = BF16/F32)
  *   dw1, dw3     [E, I, H] and dw2 [E, H, I] outputs (dwt = BF16/F32): FP32-promoted
@@ -519,8 +520,8 @@ moe_status moe_transpose_fp8_blocks(int64_t E, int64_t R, int64_t C, const uint8
  * invalid config; scale_mode != 0 (UNSUPPORTED); E outside 1..1024, n_rows or T out of
  * range (SHAPE); bad dtypes (DTYPE); workspace (WORKSPACE);
  * n_rows * H or n_rows * 2I >= 2^32, H or 2I > 16384, or max(H, I) * (n_rows + 128 E)
- * >= 2^31 (the token-axis operands' 32-bit offsets; about 266,000 rows at the V3 shape)
- * (UNSUPPORTED).
+ * >= 2^31 (the token-axis operands' 32-bit offsets; about 266,000 rows at the V3 shape),
+ * or x or dout not 16-byte aligned (UNSUPPORTED).
  */
 size_t moe_grouped_ffn_backward_workspace_bytes(const moe_config* cfg, int32_t n_experts,
                                                 int64_t n_rows);

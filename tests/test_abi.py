@@ -186,6 +186,8 @@ def test_host_validation_status_codes():
     assert fbc(c, 4, 0, fake, need_fb, ab=(None, fake)) == 1
     assert fbc(c, 4, 0, fake, need_fb, xq=None) == 1
     assert fbc(c, 4, 0, fake, need_fb, dout=None) == 1
+    # the upstream gradient is read in 16-byte pieces
+    assert fbc(c, 4, 0, fake, need_fb, dout=P(0x1008)) == 4
     p2 = _cfg(m, scale_mode=1)
     assert fbc(p2, 4, 0, fake, need_fb) == 4
     # the training gate/up: both outputs, FP32 group scales only
