@@ -269,7 +269,9 @@ __global__ __launch_bounds__(256) void route_bwd_dw_kernel(const float* __restri
 
 // ------------------------------------------------------------------------------------
 // Unpermute-sum: dx_t = sum_s rows[T k + s T + t] + sum_j rows[row_of[t, j]] (+ extra_t),
-// FP32 in that order, one bf16 rounding.
+// FP32 in that order, one bf16 rounding. Block (token, 1024 columns), 4 columns per thread;
+// the slot rows and extra are loaded before anything is added, so a thread's loads are in
+// flight together.
 // ------------------------------------------------------------------------------------
 template <typename YT>
 __global__ __launch_bounds__(256) void unpermute_sum_kernel(const YT* __restrict__ rows,
@@ -286,33 +288,31 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(const YT* __restrict
     rs[threadIdx.x] = (r >= 0 && r < n_rows) ? r : -1;
   }
   __syncthreads();
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float v[8];
-    for (int s = 0; s < S; ++s) {
-      ld8(rows, (T * k + s * T + t) * H + c, v);
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  float v[kMaxTopK][4], ve[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-    for (int j = 0; j < k; ++j) {
-      if (rs[j] >= 0) {
-        ld8(rows, (int64_t)rs[j] * H + c, v);
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k && rs[j] >= 0) ld4(rows, (int64_t)rs[j] * H + c, v[j]);
+  if (extra) ld4(extra, t * H + c, ve);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    float u[4];
+    ld4(rows, (T * k + s * T + t) * H + c, u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
-      }
-    }
-    if (extra) {
-      ld8(extra, t * H + c, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(out + t * H + c) = o;
+    for (int i = 0; i < 4; ++i) acc[i] += u[i];
   }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k && rs[j] >= 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += v[j][i];
+    }
+  if (extra) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += ve[i];
+  }
+  *reinterpret_cast<uint2*>(out + t * H + c) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
 }
 
 // ------------------------------------------------------------------------------------
@@ -361,9 +361,9 @@ __device__ __forceinline__ void quant_tile_wave(float v0, float v1, float& s, ui
 // quantised 1x128 along H: codes [rows, H] and scales chunk-major [H/128][rows]; rows
 // without a token quantise as zeros. One workgroup per row; a thread takes 8 consecutive
 // values of every 2048 (16 lanes per 128-wide tile), all of its loads issued before any
-// tile is quantised.
-constexpr int kQRSteps = 8;   // 2048-wide steps: H <= 16384
-
+// tile is quantised. STEPS = ceil(H / 2048) (at most 8: H <= 16384), so a thread holds only
+// the values it quantises.
+template <int STEPS>
 __global__ __launch_bounds__(256) void quant_dy_rows_kernel(const uint16_t* __restrict__ dout,
                                                             const float* __restrict__ row_gate,
                                                             const int32_t* __restrict__ row_token,
@@ -374,9 +374,9 @@ __global__ __launch_bounds__(256) void quant_dy_rows_kernel(const uint16_t* __re
   const int64_t t = row_token[r];
   const bool live = t >= 0 && t < n_tokens;
   const float gr = row_gate ? row_gate[r] : 1.0f;
-  float v[kQRSteps][8];
+  float v[STEPS][8];
 #pragma unroll
-  for (int u = 0; u < kQRSteps; ++u) {
+  for (int u = 0; u < STEPS; ++u) {
     const int c = u * 2048 + threadIdx.x * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void quant_dy_rows_kernel(const uint16_t* __re
     }
   }
 #pragma unroll
-  for (int u = 0; u < kQRSteps; ++u) {
+  for (int u = 0; u < STEPS; ++u) {
     const int c = u * 2048 + threadIdx.x * 8;
     if (u * 2048 >= C) break;
     // amax over the tile's 16 lanes (lanes 16a .. 16a+15 hold one 128-wide tile)
@@ -886,12 +886,13 @@ extern "C" moe_status moe_unpermute_sum(const moe_config* cfg, int64_t T, const 
   if (!rows || !row_of || !out) return MOE_ERR_NULL;
   const int64_t n_rows = T * (cfg->top_k + cfg->n_shared);
   hipStream_t s = as_stream(stream);
+  const dim3 grid((unsigned)T, (unsigned)((cfg->hidden + 1023) / 1024));
   if (rt == MOE_BF16)
-    hipLaunchKernelGGL(unpermute_sum_kernel<uint16_t>, dim3((unsigned)T), dim3(256), 0, s,
+    hipLaunchKernelGGL(unpermute_sum_kernel<uint16_t>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(rows), row_of, extra, T, cfg->hidden, cfg->top_k,
                        cfg->n_shared, n_rows, out);
   else
-    hipLaunchKernelGGL(unpermute_sum_kernel<float>, dim3((unsigned)T), dim3(256), 0, s,
+    hipLaunchKernelGGL(unpermute_sum_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(rows), row_of, extra, T, cfg->hidden, cfg->top_k,
                        cfg->n_shared, n_rows, out);
   return launch_status();
@@ -978,8 +979,17 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     if (r != MOE_OK) return r;
     // dgrad of the down projection and the recomputed gate/up inputs (K = H)
     const int64_t it = n_rows * (I / kTile);
-    hipLaunchKernelGGL(quant_dy_rows_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, dout, row_gate,
-                       row_token, n_tokens, n_rows, (int)H, dyq, dys);
+    const dim3 gq((unsigned)n_rows);
+    switch ((H + 2047) / 2048) {
+#define MOE_QDY(n)                                                                                  \
+  case n:                                                                                          \
+    hipLaunchKernelGGL(quant_dy_rows_kernel<n>, gq, dim3(256), 0, s, dout, row_gate, row_token, \
+                       n_tokens, n_rows, (int)H, dyq, dys);                                        \
+    break;
+      MOE_QDY(1) MOE_QDY(2) MOE_QDY(3) MOE_QDY(4) MOE_QDY(5) MOE_QDY(6) MOE_QDY(7) MOE_QDY(8)
+#undef MOE_QDY
+      default: return MOE_ERR_UNSUPPORTED;
+    }
     if (!saved && (r = ffn_recompute_launch(plan, n_experts, n_rows, n_tokens, xq, xs, row_token, w1,
                                             w1s, w3, w3s, (int)H, (int)I, xgs, fa, fb, s)) != MOE_OK)
       return r;

@@ -151,25 +151,51 @@ def test_route_backward_matches_oracle(lib, T, H, N, k):
 # ---------------------------------------------------------------------------------------
 # Unpermute-sum
 # ---------------------------------------------------------------------------------------
-def test_unpermute_sum(lib):
-    rng = np.random.default_rng(3)
-    T, H, N, k, S = 100, 512, 32, 4, 2
+def _bf16_rne(a32):
+    """float32 -> the nearest bf16 value (ties to even), as float32."""
+    u = np.ascontiguousarray(a32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("T,H,k,S,rdt,drop", [(100, 512, 4, 2, "f32", False),
+                                               (37, 1152, 8, 1, "bf16", True),
+                                               (5, 7168, 8, 1, "f32", True)])
+def test_unpermute_sum(lib, T, H, k, S, rdt, drop):
+    rng = np.random.default_rng(3 + T)
+    N = 32
     cfg = _cfg(tokens=T, hidden_size=H, num_experts=N, num_experts_per_tok=k, num_shared_experts=S)
     c = lib.make_config(cfg)
     idx = np.stack([rng.choice(N, k, replace=False) for _ in range(T)]).astype(np.int32)
     _, _, row_of = oracle.permute(idx, N)
+    row_of = row_of.astype(np.int32)
+    if drop:   # slots without a row contribute nothing
+        row_of[rng.random(row_of.shape) < 0.2] = -1
     rows = rng.standard_normal((T * (k + S), H)).astype(np.float32)
+    if rdt == "bf16":
+        rows = _bf16_rne(rows)
     extra = rng.standard_normal((T, H)).astype(np.float32)
-    say("unpermute_sum")
-    out = lib.moe_unpermute_sum(c, dev(rows), dev(row_of), extra=dev(extra))
+    say(f"unpermute_sum T={T} H={H} k={k} S={S} rows {rdt} drop={drop}")
+    out = lib.moe_unpermute_sum(c, dev(rows, torch.bfloat16 if rdt == "bf16" else torch.float32),
+                                dev(row_of), extra=dev(extra))
     torch.cuda.synchronize()
+    got = host(out)
+    valid = row_of >= 0
     ref = extra.astype(np.float64) + sum(rows[T * k + s * T:T * k + (s + 1) * T].astype(np.float64)
                                          for s in range(S))
     for j in range(k):
-        ref = ref + rows[row_of[:, j]]
+        ref = ref + np.where(valid[:, j:j + 1], rows[np.maximum(row_of[:, j], 0)], 0.0)
     # one bf16 rounding of an FP32 sum of k + S + 1 terms
     bound = np.abs(ref) * 2.0 ** -8 + 1e-6 * (k + S + 1) * 4
-    assert np.all(np.abs(host(out) - ref) <= bound)
+    assert np.all(np.abs(got - ref) <= bound)
+    # the stated order, exactly: shared rows, then slots in order, then extra, FP32, bf16 RNE
+    acc = np.zeros((T, H), np.float32)
+    for s in range(S):
+        acc = acc + rows[T * k + s * T:T * k + (s + 1) * T]
+    for j in range(k):
+        acc = np.where(valid[:, j:j + 1], acc + rows[np.maximum(row_of[:, j], 0)], acc)
+    acc = acc + extra
+    assert np.array_equal(got.astype(np.float32), _bf16_rne(acc))
 
 
 # ---------------------------------------------------------------------------------------
