@@ -25,6 +25,7 @@
 //     dW2 = dy^T h; dW1 = dg^T x and dW3 = du^T x in one launch   (FP8 wgrad, K = tokens)
 //   unpermute-sum      dx_t = sum of its rows' dx (+ the router's dx), FP32, bf16 out.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "ffn_internal.h"
@@ -456,21 +457,26 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* a, const f
 
 // Padded segment layout for the token-axis operands: expert e's rows occupy padded rows
 // [poff[e], poff[e] + 128 ceil(M_e / 128)); chunk_e[g] names the expert of padded chunk g
-// (-1 past the last). One workgroup.
+// (-1 past the last); elong = {count, experts of more than long_ch chunks in ascending
+// order}. One workgroup.
 __global__ __launch_bounds__(1024) void pad_plan_kernel(const int32_t* __restrict__ offsets,
-                                                        int n_experts, int max_chunks,
+                                                        int n_experts, int max_chunks, int long_ch,
                                                         int32_t* __restrict__ poff,
-                                                        int32_t* __restrict__ chunk_e) {
+                                                        int32_t* __restrict__ chunk_e,
+                                                        int32_t* __restrict__ elong) {
   __shared__ int32_t cs[1025];
   const int tid = threadIdx.x;
   if (tid == 0) {
-    int run = 0;
+    int run = 0, nl = 0;
     for (int e = 0; e < n_experts; ++e) {
       cs[e] = run;
       const int m = max(offsets[e + 1] - offsets[e], 0);
-      run += (m + kTile - 1) / kTile;
+      const int nch = (m + kTile - 1) / kTile;
+      run += nch;
+      if (nch > long_ch) elong[1 + nl++] = e;
     }
     cs[n_experts] = min(run, max_chunks);
+    elong[0] = nl;
   }
   __syncthreads();
   for (int e = tid; e <= n_experts; e += 1024) poff[e] = min(cs[e], max_chunks) * kTile;
@@ -616,6 +622,18 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__
 constexpr int kWJ = 4;              // 16-column blocks per wave
 constexpr int kWgM = 32 * kWJ;      // output columns per workgroup
 
+// Stores one lane's 4 consecutive m of one n.
+template <typename OT>
+__device__ __forceinline__ void wgrad_store1(OT* o, const v4f& v) {
+  if constexpr (sizeof(OT) == 4) {
+    *reinterpret_cast<v4f*>(o) = v;
+  } else {
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    const v2u pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<v2u*>(o) = pk;
+  }
+}
+
 // Stores one wave's 64 x 64 result: lane values are 4 consecutive m of one n.
 template <typename OT>
 __device__ __forceinline__ void wgrad_store(OT* o, int NB, int wn, int wm, int lr, int lg,
@@ -641,127 +659,320 @@ __device__ __forceinline__ void wgrad_store(OT* o, int NB, int wn, int wm, int l
 // 7.8 ms for the pair at the V3 shape against 2 x 5.0 ms for two launches).
 // SHARE 2: one gradient, two adjacent 128-column tiles per workgroup sharing the A
 // fragments (out2 unused; the second tile's columns start 128 after the first's).
-template <typename OT, int SHARE>
+template <typename OT, int SHARE, bool LIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wgrad_kernel(
     const uint8_t* __restrict__ at, const float* __restrict__ sa, const uint8_t* __restrict__ at2,
     const float* __restrict__ sa2, const uint8_t* __restrict__ bt, const float* __restrict__ sb,
     const int32_t* __restrict__ poff, const int32_t* __restrict__ offsets, int n_experts, int NA,
-    int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2) {
+    int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2,
+    const int32_t* __restrict__ elist) {
   // A group is the NB/128 tiles that share one 128-row block of A_T. Group q runs on XCD
   // q % 8, its tiles on consecutive slots there (the A rows stay in that L2), and each
   // expert's groups spread over all XCDs, so a long segment (a shared expert) is split
-  // evenly instead of loading one XCD.
+  // evenly instead of loading one XCD. Work item L is workgroup L; with LIST, the experts
+  // of elist = {count, experts...} only (the long segments beside wgrad_strip_kernel), over
+  // a persistent grid (a multiple of 8 workgroups).
   constexpr int kSpan = SHARE == 2 ? 2 * kWgM : kWgM;   // output columns per workgroup
   const int ga = NA / kTile, tg = NB / kSpan;
-  const int64_t groups = (int64_t)ga * n_experts;
-  const int64_t L = blockIdx.x;
-  const int64_t slot = L / 8;
-  const int64_t q = (L % 8) + 8 * (slot / tg);
-  if (q >= groups) return;
-  const int e = (int)(q / ga);
-  const int n0 = (int)(q % ga) * kTile, m0 = (int)(slot % tg) * kSpan;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * (kWgM / 2);
-  const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
-  const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
-  // Operands are read through buffer descriptors (32-bit offsets; each array holds fewer
-  // than 2^31 bytes). A lane's 32 rows of a chunk past the segment's last row are padding,
-  // stored as zeros: the lane reads them at an offset outside the descriptor's range,
-  // which returns zeros without touching memory.
-  const int rows_e = max(offsets[e + 1] - offsets[e], 0);
-  const int range = (int)((int64_t)NA * pstride);
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, range, 0x00020000);
-  const __amdgpu_buffer_rsrc_t ra2 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, range, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
-  typedef int v4i __attribute__((ext_vector_type(4)));
-  auto frag = [&](__amdgpu_buffer_rsrc_t r, int64_t row, int64_t p, bool live) __attribute__((always_inline)) {
-    const int off = live ? (int)(row * pstride + p + lk) : (int)0x80000000;
-    const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
+  const int ne = LIST ? min(elist[0], n_experts) : n_experts;
+  const int64_t groups = (int64_t)ga * ne;
+  auto item = [&](int64_t L) __attribute__((always_inline)) {
+    const int64_t slot = L / 8;
+    const int64_t q = (L % 8) + 8 * (slot / tg);
+    if (q >= groups) return;
+    const int e = LIST ? elist[1 + q / ga] : (int)(q / ga);
+    const int n0 = (int)(q % ga) * kTile, m0 = (int)(slot % tg) * kSpan;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * (kWgM / 2);
+    const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
+    const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
+    // Operands are read through buffer descriptors (32-bit offsets; each array holds fewer
+    // than 2^31 bytes). A lane's 32 rows of a chunk past the segment's last row are padding,
+    // stored as zeros: the lane reads them at an offset outside the descriptor's range,
+    // which returns zeros without touching memory.
+    const int rows_e = max(offsets[e + 1] - offsets[e], 0);
+    const int range = (int)((int64_t)NA * pstride);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, range, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra2 =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, range, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    auto frag = [&](__amdgpu_buffer_rsrc_t r, int64_t row, int64_t p, bool live) __attribute__((always_inline)) {
+      const int off = live ? (int)(row * pstride + p + lk) : (int)0x80000000;
+      const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+      const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 
-  // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v; acc2: the second gradient
-  // (SHARE 1) or the columns 128 further on (SHARE 2)
-  v4f acc[4][kWJ], acc2[4][kWJ];
+    // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v; acc2: the second gradient
+    // (SHARE 1) or the columns 128 further on (SHARE 2)
+    v4f acc[4][kWJ], acc2[4][kWJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j) acc[i][j] = acc2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kWJ; ++j) acc[i][j] = acc2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto load_a = [&](__amdgpu_buffer_rsrc_t r, const float* ss, int64_t p, int64_t g, bool live,
-                    v8i (&A)[4], float (&san)[4]) __attribute__((always_inline)) {
+    auto load_a = [&](__amdgpu_buffer_rsrc_t r, const float* ss, int64_t p, int64_t g, bool live,
+                      v8i (&A)[4], float (&san)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      A[i] = frag(r, wn + 16 * i + lr, p, live);
-      san[i] = ss[g * NA + wn + 16 * i + lr];
-    }
-  };
-  auto load_b = [&](int mb, int64_t p, int64_t g, bool live, v8i (&B)[kWJ], float4 (&sbm)[kWJ])
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < kWJ; ++j) B[j] = frag(rb, mb + 16 * j + lr, p, live);
-#pragma unroll
-    for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + mb + 16 * j + 4 * lg);
-  };
-  auto mma = [&](const v8i (&A)[4], const float (&san)[4], const v8i (&B)[kWJ],
-                 const float4 (&sbm)[kWJ], v4f (&ac)[4][kWJ]) __attribute__((always_inline)) {
-    const v4f z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < kWJ; ++j) {
-        // rows of the result: m (from B_T), columns: n (from A_T)
-        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[j], A[i], z, 0, 0, 0, 127, 0, 127);
-        ac[i][j][0] = fmaf(d[0], san[i] * sbm[j].x, ac[i][j][0]);
-        ac[i][j][1] = fmaf(d[1], san[i] * sbm[j].y, ac[i][j][1]);
-        ac[i][j][2] = fmaf(d[2], san[i] * sbm[j].z, ac[i][j][2]);
-        ac[i][j][3] = fmaf(d[3], san[i] * sbm[j].w, ac[i][j][3]);
+      for (int i = 0; i < 4; ++i) {
+        A[i] = frag(r, wn + 16 * i + lr, p, live);
+        san[i] = ss[g * NA + wn + 16 * i + lr];
       }
-    }
-  };
-
-  for (int ch = 0; ch < nch; ++ch) {
-    const int64_t p = p0 + (int64_t)ch * kTile;
-    const int64_t g = p / kTile;
-    const bool live = lk < rows_e - ch * kTile;
-    if constexpr (SHARE == 2) {
-      v8i A[4];
-      float san[4];
-      load_a(ra, sa, p, g, live, A, san);
+    };
+    auto load_b = [&](int mb, int64_t p, int64_t g, bool live, v8i (&B)[kWJ], float4 (&sbm)[kWJ])
+        __attribute__((always_inline)) {
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        v8i B[kWJ];
-        float4 sbm[kWJ];
-        load_b(wm + pass * kWgM, p, g, live, B, sbm);
-        mma(A, san, B, sbm, pass ? acc2 : acc);
+      for (int j = 0; j < kWJ; ++j) B[j] = frag(rb, mb + 16 * j + lr, p, live);
+#pragma unroll
+      for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + mb + 16 * j + 4 * lg);
+    };
+    auto mma = [&](const v8i (&A)[4], const float (&san)[4], const v8i (&B)[kWJ],
+                   const float4 (&sbm)[kWJ], v4f (&ac)[4][kWJ]) __attribute__((always_inline)) {
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < kWJ; ++j) {
+          // rows of the result: m (from B_T), columns: n (from A_T)
+          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[j], A[i], z, 0, 0, 0, 127, 0, 127);
+          ac[i][j][0] = fmaf(d[0], san[i] * sbm[j].x, ac[i][j][0]);
+          ac[i][j][1] = fmaf(d[1], san[i] * sbm[j].y, ac[i][j][1]);
+          ac[i][j][2] = fmaf(d[2], san[i] * sbm[j].z, ac[i][j][2]);
+          ac[i][j][3] = fmaf(d[3], san[i] * sbm[j].w, ac[i][j][3]);
+        }
       }
-    } else {
-      v8i B[kWJ];
-      float4 sbm[kWJ];
-      load_b(wm, p, g, live, B, sbm);
-#pragma unroll
-      for (int pass = 0; pass < (SHARE == 1 ? 2 : 1); ++pass) {
+    };
+
+    for (int ch = 0; ch < nch; ++ch) {
+      const int64_t p = p0 + (int64_t)ch * kTile;
+      const int64_t g = p / kTile;
+      const bool live = lk < rows_e - ch * kTile;
+      if constexpr (SHARE == 2) {
         v8i A[4];
         float san[4];
-        load_a(pass ? ra2 : ra, pass ? sa2 : sa, p, g, live, A, san);
-        mma(A, san, B, sbm, pass ? acc2 : acc);
+        load_a(ra, sa, p, g, live, A, san);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          v8i B[kWJ];
+          float4 sbm[kWJ];
+          load_b(wm + pass * kWgM, p, g, live, B, sbm);
+          mma(A, san, B, sbm, pass ? acc2 : acc);
+        }
+      } else {
+        v8i B[kWJ];
+        float4 sbm[kWJ];
+        load_b(wm, p, g, live, B, sbm);
+#pragma unroll
+        for (int pass = 0; pass < (SHARE == 1 ? 2 : 1); ++pass) {
+          v8i A[4];
+          float san[4];
+          load_a(pass ? ra2 : ra, pass ? sa2 : sa, p, g, live, A, san);
+          mma(A, san, B, sbm, pass ? acc2 : acc);
+        }
       }
     }
+    wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc);
+    if constexpr (SHARE == 1) wgrad_store(out2 + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc2);
+    if constexpr (SHARE == 2) wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm + kWgM, lr, lg, acc2);
+  };
+  if constexpr (LIST) {
+    const int64_t items = 8 * ((groups + 7) / 8) * tg;
+    for (int64_t L = blockIdx.x; L < items; L += gridDim.x) item(L);
+  } else {
+    item(blockIdx.x);
   }
-  wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc);
-  if constexpr (SHARE == 1) wgrad_store(out2 + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc2);
-  if constexpr (SHARE == 2) wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm + kWgM, lr, lg, acc2);
+}
+
+// ------------------------------------------------------------------------------------
+// wgrad of short segments (at most kStripCh token chunks, as every routed expert has at a
+// few thousand tokens): a workgroup keeps the expert's 128-row strip of A_T (and of A2_T),
+// all of its chunks, in LDS and walks kStripMR consecutive 128-column output tiles, so per
+// tile it loads only the B_T fragments and their scales. A wave's memory operations
+// complete in issue order, and the loads of tile j+1 are issued before the stores of tile
+// j, so the wait for them is not a wait for the stores. Same products and FP32 order as
+// wgrad_kernel (SHARE 0 or 1), so the same results bit for bit.
+// ------------------------------------------------------------------------------------
+constexpr int kStripCh = 2;                  // chunks of a short segment
+constexpr int kStripRow = kStripCh * kTile;  // LDS bytes of one strip row (16 pieces of 16)
+constexpr int kStripMR = 8;                  // output tiles per workgroup
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding and every LDS
+// operation done (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in
+// bits 15:14).
+constexpr int wait_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0070; }
+
+template <typename OT, int SHARE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wgrad_strip_kernel(
+    const uint8_t* __restrict__ at, const float* __restrict__ sa, const uint8_t* __restrict__ at2,
+    const float* __restrict__ sa2, const uint8_t* __restrict__ bt, const float* __restrict__ sb,
+    const int32_t* __restrict__ poff, const int32_t* __restrict__ offsets, int n_experts, int NA,
+    int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2) {
+  static_assert(SHARE == 0 || SHARE == 1, "one or two A strips");
+  constexpr int NS = SHARE == 1 ? 2 : 1;     // A strips, one output each
+  constexpr int kStores = NS * 16;           // store instructions per wave and tile
+  // strip rows of A_T: 16-byte piece s of row r holds K piece s ^ (r & 15)
+  __shared__ __attribute__((aligned(16))) uint8_t lda[NS][kTile * kStripRow];
+  __shared__ __attribute__((aligned(16))) float lsa[NS][kStripCh][kTile];   // A scales
+  __shared__ __attribute__((aligned(16))) float lsb[2][kStripCh][kTile];    // B scales, by tile parity
+  // work item: expert e (on XCD e % 8, so its B_T rows stay in one L2), strip of 128 rows
+  // of A_T, range of kStripMR column tiles
+  const int ga = NA / kTile, tiles = NB / kWgM;
+  const int nmr = (tiles + kStripMR - 1) / kStripMR, per_e = ga * nmr;
+  const int64_t L = blockIdx.x, slot = L / 8;
+  const int64_t ee = L % 8 + 8 * (slot / per_e);
+  if (ee >= n_experts) return;
+  const int e = (int)ee;
+  const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
+  if (nch > kStripCh) return;   // a long segment: wgrad_kernel
+  const int it = (int)(slot % per_e);
+  const int n0 = (it / nmr) * kTile;
+  const int j0 = (it % nmr) * kStripMR, j1 = min(j0 + kStripMR, tiles);
+  const int g0 = p0 / kTile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
+  const int wml = wave * 32;   // the wave's 32 columns of the tile, against all 128 rows
+  const int rows_e = max(offsets[e + 1] - offsets[e], 0);
+  constexpr int kOut = (int)0x80000000;   // an offset past every range: reads zeros
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, (int)((int64_t)NA * pstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, (int)((int64_t)NA * pstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sa), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(SHARE == 1 ? sa2 : sa), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sb), 0, 0x7fffffff, 0x00020000);
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) const v4i lds_v4i;
+
+  // B_T fragments of one tile (this wave's 32 columns), every chunk of the segment, and the
+  // tile's B scales (all 4 waves: 2 x 128 floats) into lsb[buf]
+  constexpr int kSJ = 2;   // 16-column blocks per wave
+  v8i B[kStripCh][kSJ];
+  auto issue_b = [&](int j, int buf) __attribute__((always_inline)) {
+    {
+      const int v = wave * kWave + lane, ch = v >> 7, mm = v & (kTile - 1);
+      const int off = ch < nch ? (int)(((int64_t)(g0 + ch) * NB + j * kWgM + mm) * 4) : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_u8*)&lsb[buf][0][0] + wave * kWave * 4, 4, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ch = 0; ch < kStripCh; ++ch) {
+      if (ch < nch) {
+        const bool live = lk < rows_e - ch * kTile;
+#pragma unroll
+        for (int jj = 0; jj < kSJ; ++jj) {
+          const int64_t row = j * kWgM + wml + 16 * jj + lr;
+          int off = live ? (int)(row * pstride + p0 + ch * kTile + lk) : kOut;
+          // one load for both cases (split into two, the loads' registers would make the
+          // compiler wait for every earlier store)
+          asm volatile("" : "+v"(off));
+          const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+          const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, off + 16, 0, 0));
+          B[ch][jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+    }
+  };
+
+  // prologue: the strips and their scales (rows past the segment are stored zeros; chunks
+  // past it read zeros), then the first tile's B
+#pragma unroll
+  for (int w = 0; w < NS; ++w) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int u = (q * 4 + wave) * kWave + lane;   // 16-byte unit of lda[w]
+      const int rr = u >> 4, kp = (u & 15) ^ (rr & 15), ch = kp >> 3;
+      const int off = ch < nch ? (int)((int64_t)(n0 + rr) * pstride + p0 + ch * kTile + (kp & 7) * 16) : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w ? ra2 : ra, (lds_u8*)&lda[w][0] + (q * 4 + wave) * kWave * 16, 16,
+                                               off, 0, 0, 0);
+    }
+    {
+      const int v = wave * kWave + lane, ch = v >> 7, rr = v & (kTile - 1);
+      const int off = ch < nch ? (int)(((int64_t)(g0 + ch) * NA + n0 + rr) * 4) : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w ? rsa2 : rsa, (lds_u8*)&lsa[w][0][0] + wave * kWave * 4, 4, off,
+                                               0, 0, 0);
+    }
+  }
+  issue_b(j0, 0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // acc[w][i][jj]: n = n0 + 16 i + lr, m = 128 j + wml + 16 jj + 4 lg + v
+  v4f acc[NS][8][kSJ];
+  for (int j = j0; j < j1; ++j) {
+    const int buf = (j - j0) & 1;
+#pragma unroll
+    for (int w = 0; w < NS; ++w)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jj = 0; jj < kSJ; ++jj) acc[w][i][jj] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < kStripCh; ++ch) {
+      if (ch < nch) {
+        float4 sbm[kSJ];
+#pragma unroll
+        for (int jj = 0; jj < kSJ; ++jj)
+          sbm[jj] = *reinterpret_cast<const float4*>(&lsb[buf][ch][wml + 16 * jj + 4 * lg]);
+#pragma unroll
+        for (int w = 0; w < NS; ++w) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int row = 16 * i + lr;   // row & 15 == lr
+            const int kp = ch * 8 + lg * 2;
+            const lds_u8* rp = (const lds_u8*)&lda[w][0] + row * kStripRow;
+            const v4i lo = *reinterpret_cast<lds_v4i*>(rp + ((kp ^ lr) << 4));
+            const v4i hi = *reinterpret_cast<lds_v4i*>(rp + (((kp + 1) ^ lr) << 4));
+            const v8i A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const float san = lsa[w][ch][row];
+            const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < kSJ; ++jj) {
+              const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[ch][jj], A, z, 0, 0, 0, 127, 0, 127);
+              acc[w][i][jj][0] = fmaf(d[0], san * sbm[jj].x, acc[w][i][jj][0]);
+              acc[w][i][jj][1] = fmaf(d[1], san * sbm[jj].y, acc[w][i][jj][1]);
+              acc[w][i][jj][2] = fmaf(d[2], san * sbm[jj].z, acc[w][i][jj][2]);
+              acc[w][i][jj][3] = fmaf(d[3], san * sbm[jj].w, acc[w][i][jj][3]);
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < j1) issue_b(j + 1, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int w = 0; w < NS; ++w) {
+      OT* o = (w ? out2 : out) + (int64_t)e * NA * NB;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jj = 0; jj < kSJ; ++jj)
+          wgrad_store1(o + (int64_t)(n0 + 16 * i + lr) * NB + j * kWgM + wml + 16 * jj + 4 * lg, acc[w][i][jj]);
+    }
+    if (j + 1 < j1) {
+      // the next tile's B (and every wave's scale copies) arrived; the stores stay in flight
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kStores));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+  }
 }
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace of the FFN backward.
 struct BwdLayout {
-  size_t plan, dyq, dys, xgs, fa, fb, fdh, q3, s3, poff, chunk_e, dyt, dyts, xt, xts, ht, hts,
-      gt, gts, ut, uts, total;
+  size_t plan, dyq, dys, xgs, fa, fb, fdh, q3, s3, poff, chunk_e, elong, dyt, dyts, xt, xts, ht,
+      hts, gt, gts, ut, uts, total;
   int64_t max_chunks, pstride;
 };
 
@@ -788,6 +999,7 @@ inline BwdLayout bwd_layout(const moe_config* c, int32_t E, int64_t n_rows) {
   L.s3 = take((size_t)n_rows * (2 * I / kTile) * 4);
   L.poff = take((size_t)(E + 1) * 4);
   L.chunk_e = take((size_t)G * 4);
+  L.elong = take((size_t)(E + 1) * 4);
   L.dyt = take((size_t)H * P);
   L.dyts = take((size_t)G * H * 4);
   L.xt = take((size_t)H * P);
@@ -970,10 +1182,11 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   float* s3 = reinterpret_cast<float*>(base + L.s3);
   int32_t* poff = reinterpret_cast<int32_t*>(base + L.poff);
   int32_t* chunk_e = reinterpret_cast<int32_t*>(base + L.chunk_e);
+  int32_t* elong = reinterpret_cast<int32_t*>(base + L.elong);
   const int64_t P = L.pstride, G = L.max_chunks;
   moe_status r;
-  hipLaunchKernelGGL(pad_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, n_experts, (int)G, poff,
-                     chunk_e);
+  hipLaunchKernelGGL(pad_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, n_experts, (int)G, kStripCh, poff,
+                     chunk_e, elong);
   if (n_rows > 0) {
     r = ffn_plan_launch(offsets, n_experts, n_rows, plan, s);
     if (r != MOE_OK) return r;
@@ -1039,32 +1252,53 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     const int64_t groups = (NA / kTile) * n_experts;
     return dim3((unsigned)(8 * ((groups + 7) / 8) * (NB / span)));
   };
+  // strip grid: 8 XCDs x ceil(E / 8) experts x strips x ranges of kStripMR tiles
+  auto sgrid = [&](int64_t NA, int64_t NB) {
+    const int64_t nmr = (NB / kWgM + kStripMR - 1) / kStripMR;
+    return dim3((unsigned)(8 * (((int64_t)n_experts + 7) / 8) * (NA / kTile) * nmr));
+  };
   // dW2 pairs adjacent column tiles when I allows (I % 256 == 0)
   const bool pair = I % (2 * kWgM) == 0;
-  if (dwt == MOE_F32) {
-    if (pair)
-      hipLaunchKernelGGL((wgrad_kernel<float, 2>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts,
-                         nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P,
-                         static_cast<float*>(dw2), nullptr);
-    else
-      hipLaunchKernelGGL((wgrad_kernel<float, 0>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
-                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, static_cast<float*>(dw2),
-                         nullptr);
-    hipLaunchKernelGGL((wgrad_kernel<float, 1>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts,
-                       xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, static_cast<float*>(dw1),
-                       static_cast<float*>(dw3));
-  } else {
-    if (pair)
-      hipLaunchKernelGGL((wgrad_kernel<uint16_t, 2>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts,
-                         nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P,
-                         static_cast<uint16_t*>(dw2), nullptr);
-    else
-      hipLaunchKernelGGL((wgrad_kernel<uint16_t, 0>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts,
-                         nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P,
-                         static_cast<uint16_t*>(dw2), nullptr);
-    hipLaunchKernelGGL((wgrad_kernel<uint16_t, 1>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts,
-                       xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, static_cast<uint16_t*>(dw1),
-                       static_cast<uint16_t*>(dw3));
-  }
+  // With short segments on average (at most kStripCh chunks), those go by strips and the
+  // long ones (the shared experts, hot routed ones) by tiles over a persistent grid of two
+  // workgroups per CU; otherwise every segment by tiles.
+  const bool strips = n_rows <= (int64_t)n_experts * kStripCh * kTile;
+  auto run = [&](auto* o1, auto* o3, auto* o2) {
+    using OT = std::remove_pointer_t<decltype(o1)>;
+    auto persistent = [](dim3 g) { return dim3(std::min(g.x, 2u * 256u)); };
+    // dW2 = dy^T h
+    if (strips) {
+      hipLaunchKernelGGL((wgrad_strip_kernel<OT, 0>), sgrid(H, I), dim3(256), 0, s, dyt, dyts, nullptr, nullptr,
+                         htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
+      if (pair)
+        hipLaunchKernelGGL((wgrad_kernel<OT, 2, true>), persistent(wgrid(H, I, 2 * kWgM)), dim3(256), 0, s, dyt,
+                           dyts, nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2,
+                           nullptr, elong);
+      else
+        hipLaunchKernelGGL((wgrad_kernel<OT, 0, true>), persistent(wgrid(H, I, kWgM)), dim3(256), 0, s, dyt, dyts,
+                           nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr,
+                           elong);
+    } else if (pair) {
+      hipLaunchKernelGGL((wgrad_kernel<OT, 2, false>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
+                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr, nullptr);
+    } else {
+      hipLaunchKernelGGL((wgrad_kernel<OT, 0, false>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
+                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr, nullptr);
+    }
+    // dW1 = dg^T x and dW3 = du^T x, sharing x
+    if (strips) {
+      hipLaunchKernelGGL((wgrad_strip_kernel<OT, 1>), sgrid(I, H), dim3(256), 0, s, gtt, gts, utt, uts, xtt,
+                         xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3);
+      hipLaunchKernelGGL((wgrad_kernel<OT, 1, true>), persistent(wgrid(I, H, kWgM)), dim3(256), 0, s, gtt, gts,
+                         utt, uts, xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3, elong);
+    } else {
+      hipLaunchKernelGGL((wgrad_kernel<OT, 1, false>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts, xtt,
+                         xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3, nullptr);
+    }
+  };
+  if (dwt == MOE_F32)
+    run(static_cast<float*>(dw1), static_cast<float*>(dw3), static_cast<float*>(dw2));
+  else
+    run(static_cast<uint16_t*>(dw1), static_cast<uint16_t*>(dw3), static_cast<uint16_t*>(dw2));
   return launch_status();
 }
