@@ -34,6 +34,7 @@ namespace moe {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // 8 consecutive values at p[i..i+8) (i a multiple of 8) as floats.
@@ -659,130 +660,118 @@ __device__ __forceinline__ void wgrad_store(OT* o, int NB, int wn, int wm, int l
 // 7.8 ms for the pair at the V3 shape against 2 x 5.0 ms for two launches).
 // SHARE 2: one gradient, two adjacent 128-column tiles per workgroup sharing the A
 // fragments (out2 unused; the second tile's columns start 128 after the first's).
-template <typename OT, int SHARE, bool LIST>
+template <typename OT, int SHARE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wgrad_kernel(
     const uint8_t* __restrict__ at, const float* __restrict__ sa, const uint8_t* __restrict__ at2,
     const float* __restrict__ sa2, const uint8_t* __restrict__ bt, const float* __restrict__ sb,
     const int32_t* __restrict__ poff, const int32_t* __restrict__ offsets, int n_experts, int NA,
-    int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2,
-    const int32_t* __restrict__ elist) {
+    int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2) {
   // A group is the NB/128 tiles that share one 128-row block of A_T. Group q runs on XCD
   // q % 8, its tiles on consecutive slots there (the A rows stay in that L2), and each
   // expert's groups spread over all XCDs, so a long segment (a shared expert) is split
-  // evenly instead of loading one XCD. Work item L is workgroup L; with LIST, the experts
-  // of elist = {count, experts...} only (the long segments beside wgrad_strip_kernel), over
-  // a persistent grid (a multiple of 8 workgroups).
+  // evenly instead of loading one XCD.
   constexpr int kSpan = SHARE == 2 ? 2 * kWgM : kWgM;   // output columns per workgroup
   const int ga = NA / kTile, tg = NB / kSpan;
-  const int ne = LIST ? min(elist[0], n_experts) : n_experts;
-  const int64_t groups = (int64_t)ga * ne;
-  auto item = [&](int64_t L) __attribute__((always_inline)) {
-    const int64_t slot = L / 8;
-    const int64_t q = (L % 8) + 8 * (slot / tg);
-    if (q >= groups) return;
-    const int e = LIST ? elist[1 + q / ga] : (int)(q / ga);
-    const int n0 = (int)(q % ga) * kTile, m0 = (int)(slot % tg) * kSpan;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * (kWgM / 2);
-    const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
-    const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
-    // Operands are read through buffer descriptors (32-bit offsets; each array holds fewer
-    // than 2^31 bytes). A lane's 32 rows of a chunk past the segment's last row are padding,
-    // stored as zeros: the lane reads them at an offset outside the descriptor's range,
-    // which returns zeros without touching memory.
-    const int rows_e = max(offsets[e + 1] - offsets[e], 0);
-    const int range = (int)((int64_t)NA * pstride);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, range, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ra2 =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, range, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
-    typedef int v4i __attribute__((ext_vector_type(4)));
+  const int64_t groups = (int64_t)ga * n_experts;
+  const int64_t L = blockIdx.x;
+  const int64_t slot = L / 8;
+  const int64_t q = (L % 8) + 8 * (slot / tg);
+  if (q >= groups) return;
+  const int e = (int)(q / ga);
+  const int n0 = (int)(q % ga) * kTile, m0 = (int)(slot % tg) * kSpan;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * (kWgM / 2);
+  const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
+  const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
+  // Operands are read through buffer descriptors (32-bit offsets; each array holds fewer
+  // than 2^31 bytes). A lane's 32 rows of a chunk past the segment's last row are padding,
+  // stored as zeros: the lane reads them at an offset outside the descriptor's range,
+  // which returns zeros without touching memory.
+  const int rows_e = max(offsets[e + 1] - offsets[e], 0);
+  const int range = (int)((int64_t)NA * pstride);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, range, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra2 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, range, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
     auto frag = [&](__amdgpu_buffer_rsrc_t r, int64_t row, int64_t p, bool live) __attribute__((always_inline)) {
-      const int off = live ? (int)(row * pstride + p + lk) : (int)0x80000000;
-      const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-      const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
+    const int off = live ? (int)(row * pstride + p + lk) : (int)0x80000000;
+    const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
-    // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v; acc2: the second gradient
-    // (SHARE 1) or the columns 128 further on (SHARE 2)
-    v4f acc[4][kWJ], acc2[4][kWJ];
+  // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v; acc2: the second gradient
+  // (SHARE 1) or the columns 128 further on (SHARE 2)
+  v4f acc[4][kWJ], acc2[4][kWJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < kWJ; ++j) acc[i][j] = acc2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kWJ; ++j) acc[i][j] = acc2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    auto load_a = [&](__amdgpu_buffer_rsrc_t r, const float* ss, int64_t p, int64_t g, bool live,
-                      v8i (&A)[4], float (&san)[4]) __attribute__((always_inline)) {
+  auto load_a = [&](__amdgpu_buffer_rsrc_t r, const float* ss, int64_t p, int64_t g, bool live,
+                    v8i (&A)[4], float (&san)[4]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        A[i] = frag(r, wn + 16 * i + lr, p, live);
-        san[i] = ss[g * NA + wn + 16 * i + lr];
-      }
-    };
-    auto load_b = [&](int mb, int64_t p, int64_t g, bool live, v8i (&B)[kWJ], float4 (&sbm)[kWJ])
-        __attribute__((always_inline)) {
+    for (int i = 0; i < 4; ++i) {
+      A[i] = frag(r, wn + 16 * i + lr, p, live);
+      san[i] = ss[g * NA + wn + 16 * i + lr];
+    }
+  };
+  auto load_b = [&](int mb, int64_t p, int64_t g, bool live, v8i (&B)[kWJ], float4 (&sbm)[kWJ])
+      __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < kWJ; ++j) B[j] = frag(rb, mb + 16 * j + lr, p, live);
+    for (int j = 0; j < kWJ; ++j) B[j] = frag(rb, mb + 16 * j + lr, p, live);
 #pragma unroll
-      for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + mb + 16 * j + 4 * lg);
-    };
-    auto mma = [&](const v8i (&A)[4], const float (&san)[4], const v8i (&B)[kWJ],
-                   const float4 (&sbm)[kWJ], v4f (&ac)[4][kWJ]) __attribute__((always_inline)) {
-      const v4f z = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + mb + 16 * j + 4 * lg);
+  };
+  auto mma = [&](const v8i (&A)[4], const float (&san)[4], const v8i (&B)[kWJ],
+                 const float4 (&sbm)[kWJ], v4f (&ac)[4][kWJ]) __attribute__((always_inline)) {
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < kWJ; ++j) {
-          // rows of the result: m (from B_T), columns: n (from A_T)
-          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[j], A[i], z, 0, 0, 0, 127, 0, 127);
-          ac[i][j][0] = fmaf(d[0], san[i] * sbm[j].x, ac[i][j][0]);
-          ac[i][j][1] = fmaf(d[1], san[i] * sbm[j].y, ac[i][j][1]);
-          ac[i][j][2] = fmaf(d[2], san[i] * sbm[j].z, ac[i][j][2]);
-          ac[i][j][3] = fmaf(d[3], san[i] * sbm[j].w, ac[i][j][3]);
-        }
-      }
-    };
-
-    for (int ch = 0; ch < nch; ++ch) {
-      const int64_t p = p0 + (int64_t)ch * kTile;
-      const int64_t g = p / kTile;
-      const bool live = lk < rows_e - ch * kTile;
-      if constexpr (SHARE == 2) {
-        v8i A[4];
-        float san[4];
-        load_a(ra, sa, p, g, live, A, san);
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-          v8i B[kWJ];
-          float4 sbm[kWJ];
-          load_b(wm + pass * kWgM, p, g, live, B, sbm);
-          mma(A, san, B, sbm, pass ? acc2 : acc);
-        }
-      } else {
-        v8i B[kWJ];
-        float4 sbm[kWJ];
-        load_b(wm, p, g, live, B, sbm);
-#pragma unroll
-        for (int pass = 0; pass < (SHARE == 1 ? 2 : 1); ++pass) {
-          v8i A[4];
-          float san[4];
-          load_a(pass ? ra2 : ra, pass ? sa2 : sa, p, g, live, A, san);
-          mma(A, san, B, sbm, pass ? acc2 : acc);
-        }
+      for (int j = 0; j < kWJ; ++j) {
+        // rows of the result: m (from B_T), columns: n (from A_T)
+        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[j], A[i], z, 0, 0, 0, 127, 0, 127);
+        ac[i][j][0] = fmaf(d[0], san[i] * sbm[j].x, ac[i][j][0]);
+        ac[i][j][1] = fmaf(d[1], san[i] * sbm[j].y, ac[i][j][1]);
+        ac[i][j][2] = fmaf(d[2], san[i] * sbm[j].z, ac[i][j][2]);
+        ac[i][j][3] = fmaf(d[3], san[i] * sbm[j].w, ac[i][j][3]);
       }
     }
-    wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc);
-    if constexpr (SHARE == 1) wgrad_store(out2 + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc2);
-    if constexpr (SHARE == 2) wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm + kWgM, lr, lg, acc2);
   };
-  if constexpr (LIST) {
-    const int64_t items = 8 * ((groups + 7) / 8) * tg;
-    for (int64_t L = blockIdx.x; L < items; L += gridDim.x) item(L);
-  } else {
-    item(blockIdx.x);
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int64_t p = p0 + (int64_t)ch * kTile;
+    const int64_t g = p / kTile;
+    const bool live = lk < rows_e - ch * kTile;
+    if constexpr (SHARE == 2) {
+      v8i A[4];
+      float san[4];
+      load_a(ra, sa, p, g, live, A, san);
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        v8i B[kWJ];
+        float4 sbm[kWJ];
+        load_b(wm + pass * kWgM, p, g, live, B, sbm);
+        mma(A, san, B, sbm, pass ? acc2 : acc);
+      }
+    } else {
+      v8i B[kWJ];
+      float4 sbm[kWJ];
+      load_b(wm, p, g, live, B, sbm);
+#pragma unroll
+      for (int pass = 0; pass < (SHARE == 1 ? 2 : 1); ++pass) {
+        v8i A[4];
+        float san[4];
+        load_a(pass ? ra2 : ra, pass ? sa2 : sa, p, g, live, A, san);
+        mma(A, san, B, sbm, pass ? acc2 : acc);
+      }
+    }
   }
+  wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc);
+  if constexpr (SHARE == 1) wgrad_store(out2 + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc2);
+  if constexpr (SHARE == 2) wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm + kWgM, lr, lg, acc2);
 }
 
 // ------------------------------------------------------------------------------------
@@ -796,9 +785,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 // ------------------------------------------------------------------------------------
 constexpr int kStripCh = 2;                  // chunks of a short segment
 constexpr int kStripRow = kStripCh * kTile;  // LDS bytes of one strip row (16 pieces of 16)
-constexpr int kStripMR = 8;                  // output tiles per workgroup
+constexpr int kStripMR = 4;                  // output tiles per workgroup (2, 3, 6, 8 and 16 measured slower)
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding and every LDS
 // operation done (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in
@@ -847,8 +837,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   const __amdgpu_buffer_rsrc_t rsa2 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(SHARE == 1 ? sa2 : sa), 0, 0x7fffffff, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sb), 0, 0x7fffffff, 0x00020000);
-  typedef int v4i __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) const v4i lds_v4i;
 
   // B_T fragments of one tile (this wave's 32 columns), every chunk of the segment, and the
   // tile's B scales (all 4 waves: 2 x 128 floats) into lsb[buf]
@@ -965,6 +953,243 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       asm volatile("" ::: "memory");
     }
   }
+}
+
+// ------------------------------------------------------------------------------------
+// wgrad of long segments (more than kStripCh chunks: the shared experts, hot routed
+// ones): one persistent workgroup of 8 waves per CU walks 128 x 128 output tiles of the
+// experts of elist = {count, experts...} and streams each tile's token chunks through an
+// LDS ring of three slots (the chunk's A_T and A2_T rows, its B_T rows and their scales,
+// copied by direct buffer->LDS loads two chunks ahead, across tile boundaries). Wave w
+// computes rows 64 (w >> 2) .. +64 by columns 32 (w & 3) .. +32 of the tile. A wave's
+// memory operations complete in issue order; every wait counts the copies and stores
+// issued after the chunk it needs, so it never waits for a finished tile's stores. Same
+// products and FP32 order as wgrad_kernel (SHARE 0 or 1).
+// ------------------------------------------------------------------------------------
+constexpr int kLongWaves = 8;
+
+template <int NS>
+struct LongSlot {
+  uint8_t blk[NS + 1][kTile * kTile];   // A_T (and A2_T) rows, then B_T rows: 16-byte piece p
+                                        // of row r at p ^ (r & 7)
+  float sc[NS + 1][kTile];              // their scales
+  float junk[kWave];                    // landing area of the waves with no scale copy
+};
+
+template <typename OT, int SHARE>
+__global__ __launch_bounds__(kLongWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void wgrad_long_kernel(
+    const uint8_t* __restrict__ at, const float* __restrict__ sa, const uint8_t* __restrict__ at2,
+    const float* __restrict__ sa2, const uint8_t* __restrict__ bt, const float* __restrict__ sb,
+    const int32_t* __restrict__ poff, const int32_t* __restrict__ offsets, int n_experts, int NA,
+    int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2,
+    const int32_t* __restrict__ elist) {
+  static_assert(SHARE == 0 || SHARE == 1, "one or two outputs");
+  constexpr int NS = SHARE == 1 ? 2 : 1;
+  constexpr int kBlkCopies = kTile * kTile / (kLongWaves * kWave * 16);   // per wave per block: 2
+  constexpr int kOps = (NS + 1) * kBlkCopies + 1;   // copies per wave per chunk
+  constexpr int kStores = NS * 8;                   // stores per wave per tile
+  static_assert(kOps + 2 * kStores <= 63, "vmcnt range");
+  // three slots, used in a loop unrolled by three; each step reads one slot and fills
+  // another through restrict pointers, so the compiler can see that the reads never touch
+  // the copies just issued (without that it waits for them before every read)
+  __shared__ __attribute__((aligned(16))) LongSlot<NS> slot0, slot1, slot2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: descriptors and LDS bases
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wrow = (wave >> 2) * 64, wcol = (wave & 3) * 32;
+  const int ga = NA / kTile, tg = NB / kWgM;
+  const int ne = min(elist[0], n_experts);
+  const int64_t groups = (int64_t)ga * ne;
+  const int64_t items = 8 * ((groups + 7) / 8) * tg;
+  constexpr int kOut = (int)0x80000000;   // an offset past every range: reads zeros
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, (int)((int64_t)NA * pstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, (int)((int64_t)NA * pstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sa), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(SHARE == 1 ? sa2 : sa), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sb), 0, 0x7fffffff, 0x00020000);
+
+  // A tile of the stream: expert, first row of A_T, first row of B_T, padded-row offset
+  // and chunk count (0 for the slots past the last group).
+  struct Tl {
+    int e, n0, m0, p0, nch;
+  };
+  auto tile_of = [&](int64_t L) __attribute__((always_inline)) {
+    Tl t{0, 0, 0, 0, 0};
+    if (L >= items) return t;
+    const int64_t slot = L / 8;
+    const int64_t q = (L % 8) + 8 * (slot / tg);
+    if (q >= groups) return t;
+    t.e = elist[1 + q / ga];
+    t.n0 = (int)(q % ga) * kTile;
+    t.m0 = (int)(slot % tg) * kWgM;
+    t.p0 = poff[t.e];
+    t.nch = (poff[t.e + 1] - t.p0) / kTile;
+    return t;
+  };
+  // next tile of this workgroup with at least one chunk, from L on (L >= items: none)
+  auto next_tile = [&](int64_t& L, Tl& t) __attribute__((always_inline)) {
+    for (; L < items; L += gridDim.x) {
+      t = tile_of(L);
+      if (t.nch > 0) return;
+    }
+    t = Tl{0, 0, 0, 0, 0};
+  };
+
+  // copies of chunk c of tile t into slot S (every wave: kOps copies)
+  auto issue = [&](const Tl& t, int c, LongSlot<NS>* __restrict__ Sp) __attribute__((always_inline)) {
+    LongSlot<NS>& S = *Sp;
+    const int64_t pc = t.p0 + (int64_t)c * kTile;
+#pragma unroll
+    for (int b = 0; b <= NS; ++b) {
+#pragma unroll
+      for (int k = 0; k < kBlkCopies; ++k) {
+        const int u = (k * kLongWaves + wave) * kWave + lane;   // 16-byte unit of the block
+        const int r = u >> 3, kp = (u & 7) ^ (r & 7);
+        const int64_t row = (b < NS ? t.n0 : t.m0) + r;
+        const int off = (int)(row * pstride + pc + kp * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b == NS ? rb : (b ? ra2 : ra),
+                                                 (lds_u8*)&S.blk[b][0] + (k * kLongWaves + wave) * kWave * 16, 16,
+                                                 off, 0, 0, 0);
+      }
+    }
+    // scales: 2 (NS + 1) copies of 64 floats, by the first waves; the others copy zeros
+    // into the junk area (every wave issues kOps copies)
+    const int g = (int)(pc / kTile);
+    const int b = wave >> 1, half = wave & 1;   // uniform
+    const int idx = half * kWave + lane;
+    lds_u8* const sc0 = (lds_u8*)&S.sc[0][0] + (b * kTile + half * kWave) * 4;
+    if (b < NS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b == 0 ? rsa : rsa2, sc0, 4, (int)(((int64_t)g * NA + t.n0 + idx) * 4), 0,
+                                               0, 0);
+    else if (b == NS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, sc0, 4, (int)(((int64_t)g * NB + t.m0 + idx) * 4), 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_u8*)&S.junk[0], 4, kOut, 0, 0, 0);
+  };
+
+  // stream state: the tile and chunk being computed, and the ones being copied (two ahead)
+  int64_t Lc = blockIdx.x, Ll;
+  Tl tc, tl;
+  next_tile(Lc, tc);
+  if (tc.nch == 0) return;
+  Ll = Lc;
+  tl = tc;
+  int cl = 0;   // chunk of tl to copy next
+  auto advance_load = [&]() __attribute__((always_inline)) {
+    if (++cl == tl.nch) {
+      cl = 0;
+      Ll += gridDim.x;
+      next_tile(Ll, tl);
+    }
+  };
+  bool more;   // a copied chunk after the one computed next
+  auto prime = [&](LongSlot<NS>* __restrict__ S0, LongSlot<NS>* __restrict__ S1) __attribute__((always_inline)) {
+    issue(tl, cl, S0);
+    advance_load();
+    more = tl.nch > 0;
+    if (more) {
+      issue(tl, cl, S1);
+      advance_load();
+    }
+  };
+  prime(&slot0, &slot1);
+
+  v4f acc[NS][4][2];
+#pragma unroll
+  for (int w = 0; w < NS; ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[w][i][0] = acc[w][i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  int cc = 0;
+  int s1 = 0, s2 = 0;   // stores issued one and two steps back (per wave)
+  // one chunk: compute from Sc, copy two chunks ahead into Sl; false when the stream ends
+  auto step = [&](const LongSlot<NS>* __restrict__ Scp, LongSlot<NS>* __restrict__ Sl)
+                  __attribute__((always_inline)) {
+    const LongSlot<NS>& Sc = *Scp;
+    // the copies of the next chunk (if any) and the stores of the last two steps were
+    // issued after this chunk's copies
+    const bool next_exists = more;
+    const int after = s1 + s2;
+    asm volatile("" ::: "memory");
+    if (!next_exists) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    else if (after == 0) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kOps));
+    else if (after == kStores) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kOps + kStores));
+    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kOps + 2 * kStores));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // copies two chunks ahead, into the slot every wave finished with last step
+    more = tl.nch > 0;
+    if (more) {
+      issue(tl, cl, Sl);
+      advance_load();
+    }
+    {
+      float4 sbm[2];
+      v8i B[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int row = wcol + 16 * jj + lr;
+        const lds_u8* rp = (const lds_u8*)&Sc.blk[NS][0] + row * kTile;
+        const v4i lo = *reinterpret_cast<lds_v4i*>(rp + (((2 * lg) ^ (row & 7)) << 4));
+        const v4i hi = *reinterpret_cast<lds_v4i*>(rp + (((2 * lg + 1) ^ (row & 7)) << 4));
+        B[jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        sbm[jj] = *reinterpret_cast<const float4*>(&Sc.sc[NS][wcol + 16 * jj + 4 * lg]);
+      }
+#pragma unroll
+      for (int w = 0; w < NS; ++w) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wrow + 16 * i + lr;
+          const lds_u8* rp = (const lds_u8*)&Sc.blk[w][0] + row * kTile;
+          const v4i lo = *reinterpret_cast<lds_v4i*>(rp + (((2 * lg) ^ (row & 7)) << 4));
+          const v4i hi = *reinterpret_cast<lds_v4i*>(rp + (((2 * lg + 1) ^ (row & 7)) << 4));
+          const v8i A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const float san = Sc.sc[w][row];
+          const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[jj], A, z, 0, 0, 0, 127, 0, 127);
+            acc[w][i][jj][0] = fmaf(d[0], san * sbm[jj].x, acc[w][i][jj][0]);
+            acc[w][i][jj][1] = fmaf(d[1], san * sbm[jj].y, acc[w][i][jj][1]);
+            acc[w][i][jj][2] = fmaf(d[2], san * sbm[jj].z, acc[w][i][jj][2]);
+            acc[w][i][jj][3] = fmaf(d[3], san * sbm[jj].w, acc[w][i][jj][3]);
+          }
+        }
+      }
+    }
+    s2 = s1;
+    s1 = 0;
+    if (++cc == tc.nch) {
+      // the tile is done: store it, start the next one
+#pragma unroll
+      for (int w = 0; w < NS; ++w) {
+        OT* o = (w ? out2 : out) + (int64_t)tc.e * NA * NB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            wgrad_store1(o + (int64_t)(tc.n0 + wrow + 16 * i + lr) * NB + tc.m0 + wcol + 16 * jj + 4 * lg,
+                         acc[w][i][jj]);
+            acc[w][i][jj] = v4f{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+      s1 = kStores;
+      if (!next_exists) return false;
+      cc = 0;
+      Lc += gridDim.x;
+      next_tile(Lc, tc);
+    }
+    return true;
+  };
+  // the first three steps are peeled: entering the loop from the prologue, the compiler's
+  // wait analysis cannot tell the slots apart and waits for every copy in flight
+  if (step(&slot0, &slot2) && step(&slot1, &slot0) && step(&slot2, &slot1))
+    while (step(&slot0, &slot2) && step(&slot1, &slot0) && step(&slot2, &slot1)) {
+    }
 }
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1265,35 +1490,28 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   const bool strips = n_rows <= (int64_t)n_experts * kStripCh * kTile;
   auto run = [&](auto* o1, auto* o3, auto* o2) {
     using OT = std::remove_pointer_t<decltype(o1)>;
-    auto persistent = [](dim3 g) { return dim3(std::min(g.x, 2u * 256u)); };
     // dW2 = dy^T h
     if (strips) {
       hipLaunchKernelGGL((wgrad_strip_kernel<OT, 0>), sgrid(H, I), dim3(256), 0, s, dyt, dyts, nullptr, nullptr,
                          htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
-      if (pair)
-        hipLaunchKernelGGL((wgrad_kernel<OT, 2, true>), persistent(wgrid(H, I, 2 * kWgM)), dim3(256), 0, s, dyt,
-                           dyts, nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2,
-                           nullptr, elong);
-      else
-        hipLaunchKernelGGL((wgrad_kernel<OT, 0, true>), persistent(wgrid(H, I, kWgM)), dim3(256), 0, s, dyt, dyts,
-                           nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr,
-                           elong);
+      hipLaunchKernelGGL((wgrad_long_kernel<OT, 0>), dim3(256), dim3(kLongWaves * kWave), 0, s, dyt, dyts, nullptr,
+                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr, elong);
     } else if (pair) {
-      hipLaunchKernelGGL((wgrad_kernel<OT, 2, false>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
-                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr, nullptr);
+      hipLaunchKernelGGL((wgrad_kernel<OT, 2>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
+                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
     } else {
-      hipLaunchKernelGGL((wgrad_kernel<OT, 0, false>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
-                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr, nullptr);
+      hipLaunchKernelGGL((wgrad_kernel<OT, 0>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
+                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
     }
     // dW1 = dg^T x and dW3 = du^T x, sharing x
     if (strips) {
       hipLaunchKernelGGL((wgrad_strip_kernel<OT, 1>), sgrid(I, H), dim3(256), 0, s, gtt, gts, utt, uts, xtt,
                          xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3);
-      hipLaunchKernelGGL((wgrad_kernel<OT, 1, true>), persistent(wgrid(I, H, kWgM)), dim3(256), 0, s, gtt, gts,
-                         utt, uts, xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3, elong);
+      hipLaunchKernelGGL((wgrad_long_kernel<OT, 1>), dim3(256), dim3(kLongWaves * kWave), 0, s, gtt, gts, utt, uts,
+                         xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3, elong);
     } else {
-      hipLaunchKernelGGL((wgrad_kernel<OT, 1, false>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts, xtt,
-                         xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3, nullptr);
+      hipLaunchKernelGGL((wgrad_kernel<OT, 1>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts, xtt,
+                         xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3);
     }
   };
   if (dwt == MOE_F32)
