@@ -613,15 +613,14 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const T* __restrict__
 // ------------------------------------------------------------------------------------
 // wgrad: out_e[n][m] = sum over expert e's padded rows p of A_T[n][p] B_T[m][p], FP8 E4M3
 // operands in 128-row tiles along p with scales chunk-major (sa[g][n], sb[g][m]); each
-// 128-row chunk is one MFMA per 16x16 block, promoted in FP32 by sa[n] sb[m]. A 256-thread
-// workgroup computes a 128 x kWgM output tile, each wave 64 x kWgM/2 (4 x kWJ blocks; at
-// 128 x 64 with four waves per SIMD it measured 7% slower: twice the A loads). The
-// MFMA takes B_T as its first operand, so a lane's four results are four consecutive m of
-// one n: one 16-byte store each (plain stores: measured non-temporal ones of this pattern,
-// half cache lines per row, at 60% of the plain rate).
+// 128-row chunk is one MFMA per 16x16 block, promoted in FP32 by sa[n] sb[m], chunks in
+// order. Output tiles are 128 x 128. The MFMA takes B_T as its first operand, so a lane's
+// four results are four consecutive m of one n: one 16-byte store each (plain stores:
+// measured non-temporal ones of this pattern, half cache lines per row, at 60% of the
+// plain rate). Two kernels split the experts by segment length: wgrad_strip_kernel (at
+// most kStripCh chunks) and wgrad_long_kernel (the rest).
 // ------------------------------------------------------------------------------------
-constexpr int kWJ = 4;              // 16-column blocks per wave
-constexpr int kWgM = 32 * kWJ;      // output columns per workgroup
+constexpr int kWgM = 128;   // output columns per tile
 
 // Stores one lane's 4 consecutive m of one n.
 template <typename OT>
@@ -635,153 +634,14 @@ __device__ __forceinline__ void wgrad_store1(OT* o, const v4f& v) {
   }
 }
 
-// Stores one wave's 64 x 64 result: lane values are 4 consecutive m of one n.
-template <typename OT>
-__device__ __forceinline__ void wgrad_store(OT* o, int NB, int wn, int wm, int lr, int lg,
-                                            const v4f (&acc)[4][kWJ]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < kWJ; ++j) {
-      const int64_t off = (int64_t)(wn + 16 * i + lr) * NB + wm + 16 * j + 4 * lg;
-      if constexpr (sizeof(OT) == 4) {
-        *reinterpret_cast<v4f*>(o + off) = acc[i][j];
-      } else {
-        typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-        const v2u pk = {pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
-        *reinterpret_cast<v2u*>(o + off) = pk;
-      }
-    }
-  }
-}
-
-// SHARE 1: two gradients that share B_T (dW1 = dg^T x and dW3 = du^T x) in one launch: each
-// workgroup loads the B fragments once and runs both A operands against them (measured
-// 7.8 ms for the pair at the V3 shape against 2 x 5.0 ms for two launches).
-// SHARE 2: one gradient, two adjacent 128-column tiles per workgroup sharing the A
-// fragments (out2 unused; the second tile's columns start 128 after the first's).
-template <typename OT, int SHARE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wgrad_kernel(
-    const uint8_t* __restrict__ at, const float* __restrict__ sa, const uint8_t* __restrict__ at2,
-    const float* __restrict__ sa2, const uint8_t* __restrict__ bt, const float* __restrict__ sb,
-    const int32_t* __restrict__ poff, const int32_t* __restrict__ offsets, int n_experts, int NA,
-    int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2) {
-  // A group is the NB/128 tiles that share one 128-row block of A_T. Group q runs on XCD
-  // q % 8, its tiles on consecutive slots there (the A rows stay in that L2), and each
-  // expert's groups spread over all XCDs, so a long segment (a shared expert) is split
-  // evenly instead of loading one XCD.
-  constexpr int kSpan = SHARE == 2 ? 2 * kWgM : kWgM;   // output columns per workgroup
-  const int ga = NA / kTile, tg = NB / kSpan;
-  const int64_t groups = (int64_t)ga * n_experts;
-  const int64_t L = blockIdx.x;
-  const int64_t slot = L / 8;
-  const int64_t q = (L % 8) + 8 * (slot / tg);
-  if (q >= groups) return;
-  const int e = (int)(q / ga);
-  const int n0 = (int)(q % ga) * kTile, m0 = (int)(slot % tg) * kSpan;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = n0 + (wave >> 1) * 64, wm = m0 + (wave & 1) * (kWgM / 2);
-  const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
-  const int lr = lane & 15, lg = lane >> 4, lk = lg * 32;
-  // Operands are read through buffer descriptors (32-bit offsets; each array holds fewer
-  // than 2^31 bytes). A lane's 32 rows of a chunk past the segment's last row are padding,
-  // stored as zeros: the lane reads them at an offset outside the descriptor's range,
-  // which returns zeros without touching memory.
-  const int rows_e = max(offsets[e + 1] - offsets[e], 0);
-  const int range = (int)((int64_t)NA * pstride);
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, range, 0x00020000);
-  const __amdgpu_buffer_rsrc_t ra2 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, range, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
-    auto frag = [&](__amdgpu_buffer_rsrc_t r, int64_t row, int64_t p, bool live) __attribute__((always_inline)) {
-    const int off = live ? (int)(row * pstride + p + lk) : (int)0x80000000;
-    const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-
-  // acc[i][j]: n = wn + 16 i + lr, m = wm + 16 j + 4 lg + v; acc2: the second gradient
-  // (SHARE 1) or the columns 128 further on (SHARE 2)
-  v4f acc[4][kWJ], acc2[4][kWJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < kWJ; ++j) acc[i][j] = acc2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  auto load_a = [&](__amdgpu_buffer_rsrc_t r, const float* ss, int64_t p, int64_t g, bool live,
-                    v8i (&A)[4], float (&san)[4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      A[i] = frag(r, wn + 16 * i + lr, p, live);
-      san[i] = ss[g * NA + wn + 16 * i + lr];
-    }
-  };
-  auto load_b = [&](int mb, int64_t p, int64_t g, bool live, v8i (&B)[kWJ], float4 (&sbm)[kWJ])
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < kWJ; ++j) B[j] = frag(rb, mb + 16 * j + lr, p, live);
-#pragma unroll
-    for (int j = 0; j < kWJ; ++j) sbm[j] = *reinterpret_cast<const float4*>(sb + g * NB + mb + 16 * j + 4 * lg);
-  };
-  auto mma = [&](const v8i (&A)[4], const float (&san)[4], const v8i (&B)[kWJ],
-                 const float4 (&sbm)[kWJ], v4f (&ac)[4][kWJ]) __attribute__((always_inline)) {
-    const v4f z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < kWJ; ++j) {
-        // rows of the result: m (from B_T), columns: n (from A_T)
-        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(B[j], A[i], z, 0, 0, 0, 127, 0, 127);
-        ac[i][j][0] = fmaf(d[0], san[i] * sbm[j].x, ac[i][j][0]);
-        ac[i][j][1] = fmaf(d[1], san[i] * sbm[j].y, ac[i][j][1]);
-        ac[i][j][2] = fmaf(d[2], san[i] * sbm[j].z, ac[i][j][2]);
-        ac[i][j][3] = fmaf(d[3], san[i] * sbm[j].w, ac[i][j][3]);
-      }
-    }
-  };
-
-  for (int ch = 0; ch < nch; ++ch) {
-    const int64_t p = p0 + (int64_t)ch * kTile;
-    const int64_t g = p / kTile;
-    const bool live = lk < rows_e - ch * kTile;
-    if constexpr (SHARE == 2) {
-      v8i A[4];
-      float san[4];
-      load_a(ra, sa, p, g, live, A, san);
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        v8i B[kWJ];
-        float4 sbm[kWJ];
-        load_b(wm + pass * kWgM, p, g, live, B, sbm);
-        mma(A, san, B, sbm, pass ? acc2 : acc);
-      }
-    } else {
-      v8i B[kWJ];
-      float4 sbm[kWJ];
-      load_b(wm, p, g, live, B, sbm);
-#pragma unroll
-      for (int pass = 0; pass < (SHARE == 1 ? 2 : 1); ++pass) {
-        v8i A[4];
-        float san[4];
-        load_a(pass ? ra2 : ra, pass ? sa2 : sa, p, g, live, A, san);
-        mma(A, san, B, sbm, pass ? acc2 : acc);
-      }
-    }
-  }
-  wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc);
-  if constexpr (SHARE == 1) wgrad_store(out2 + (int64_t)e * NA * NB, NB, wn, wm, lr, lg, acc2);
-  if constexpr (SHARE == 2) wgrad_store(out + (int64_t)e * NA * NB, NB, wn, wm + kWgM, lr, lg, acc2);
-}
-
 // ------------------------------------------------------------------------------------
 // wgrad of short segments (at most kStripCh token chunks, as every routed expert has at a
 // few thousand tokens): a workgroup keeps the expert's 128-row strip of A_T (and of A2_T),
 // all of its chunks, in LDS and walks kStripMR consecutive 128-column output tiles, so per
 // tile it loads only the B_T fragments and their scales. A wave's memory operations
 // complete in issue order, and the loads of tile j+1 are issued before the stores of tile
-// j, so the wait for them is not a wait for the stores. Same products and FP32 order as
-// wgrad_kernel (SHARE 0 or 1), so the same results bit for bit.
+// j, so the wait for them is not a wait for the stores. SHARE 1: two A strips (dW1 and dW3
+// share B = x); SHARE 0: one. A wave computes all 128 rows by 32 columns of a tile.
 // ------------------------------------------------------------------------------------
 constexpr int kStripCh = 2;                  // chunks of a short segment
 constexpr int kStripRow = kStripCh * kTile;  // LDS bytes of one strip row (16 pieces of 16)
@@ -817,7 +677,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   if (ee >= n_experts) return;
   const int e = (int)ee;
   const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
-  if (nch > kStripCh) return;   // a long segment: wgrad_kernel
+  if (nch > kStripCh) return;   // a long segment: wgrad_long_kernel
   const int it = (int)(slot % per_e);
   const int n0 = (it / nmr) * kTile;
   const int j0 = (it % nmr) * kStripMR, j1 = min(j0 + kStripMR, tiles);
@@ -964,9 +824,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 // computes rows 64 (w >> 2) .. +64 by columns 32 (w & 3) .. +32 of the tile. A wave's
 // memory operations complete in issue order; every wait counts the copies and stores
 // issued after the chunk it needs, so it never waits for a finished tile's stores. Same
-// products and FP32 order as wgrad_kernel (SHARE 0 or 1).
+// products and FP32 order as wgrad_strip_kernel (SHARE 0 or 1).
 // ------------------------------------------------------------------------------------
 constexpr int kLongWaves = 8;
+constexpr int kLongGrid = 256;   // one workgroup per CU (the ring takes 100-150 KB of LDS)
 
 template <int NS>
 struct LongSlot {
@@ -1471,48 +1332,26 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
     hipLaunchKernelGGL((quant_tokens_kernel<float, 0>), gi, dim3(256), 0, s, fb, n_rows, n_rows, row_token,
                        nullptr, offsets, poff, chunk_e, (int)I, P, utt, uts);
   }
-  // wgrad GEMMs (every expert's gradient written; zero for an expert without rows)
-  // grid: 8 XCDs x ceil(groups / 8) groups x tiles per group
-  auto wgrid = [&](int64_t NA, int64_t NB, int64_t span) {
-    const int64_t groups = (NA / kTile) * n_experts;
-    return dim3((unsigned)(8 * ((groups + 7) / 8) * (NB / span)));
-  };
+  // wgrad GEMMs (every expert's gradient written; zero for an expert without rows): short
+  // segments (at most kStripCh chunks, every expert without rows included) by strips, the
+  // others (listed in elong) by the persistent long-segment kernel, one workgroup per CU
   // strip grid: 8 XCDs x ceil(E / 8) experts x strips x ranges of kStripMR tiles
   auto sgrid = [&](int64_t NA, int64_t NB) {
     const int64_t nmr = (NB / kWgM + kStripMR - 1) / kStripMR;
     return dim3((unsigned)(8 * (((int64_t)n_experts + 7) / 8) * (NA / kTile) * nmr));
   };
-  // dW2 pairs adjacent column tiles when I allows (I % 256 == 0)
-  const bool pair = I % (2 * kWgM) == 0;
-  // With short segments on average (at most kStripCh chunks), those go by strips and the
-  // long ones (the shared experts, hot routed ones) by tiles over a persistent grid of two
-  // workgroups per CU; otherwise every segment by tiles.
-  const bool strips = n_rows <= (int64_t)n_experts * kStripCh * kTile;
   auto run = [&](auto* o1, auto* o3, auto* o2) {
     using OT = std::remove_pointer_t<decltype(o1)>;
     // dW2 = dy^T h
-    if (strips) {
-      hipLaunchKernelGGL((wgrad_strip_kernel<OT, 0>), sgrid(H, I), dim3(256), 0, s, dyt, dyts, nullptr, nullptr,
-                         htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
-      hipLaunchKernelGGL((wgrad_long_kernel<OT, 0>), dim3(256), dim3(kLongWaves * kWave), 0, s, dyt, dyts, nullptr,
-                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr, elong);
-    } else if (pair) {
-      hipLaunchKernelGGL((wgrad_kernel<OT, 2>), wgrid(H, I, 2 * kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
-                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
-    } else {
-      hipLaunchKernelGGL((wgrad_kernel<OT, 0>), wgrid(H, I, kWgM), dim3(256), 0, s, dyt, dyts, nullptr,
-                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
-    }
+    hipLaunchKernelGGL((wgrad_strip_kernel<OT, 0>), sgrid(H, I), dim3(256), 0, s, dyt, dyts, nullptr, nullptr, htt,
+                       hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
+    hipLaunchKernelGGL((wgrad_long_kernel<OT, 0>), dim3(kLongGrid), dim3(kLongWaves * kWave), 0, s, dyt, dyts,
+                       nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr, elong);
     // dW1 = dg^T x and dW3 = du^T x, sharing x
-    if (strips) {
-      hipLaunchKernelGGL((wgrad_strip_kernel<OT, 1>), sgrid(I, H), dim3(256), 0, s, gtt, gts, utt, uts, xtt,
-                         xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3);
-      hipLaunchKernelGGL((wgrad_long_kernel<OT, 1>), dim3(256), dim3(kLongWaves * kWave), 0, s, gtt, gts, utt, uts,
-                         xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3, elong);
-    } else {
-      hipLaunchKernelGGL((wgrad_kernel<OT, 1>), wgrid(I, H, kWgM), dim3(256), 0, s, gtt, gts, utt, uts, xtt,
-                         xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3);
-    }
+    hipLaunchKernelGGL((wgrad_strip_kernel<OT, 1>), sgrid(I, H), dim3(256), 0, s, gtt, gts, utt, uts, xtt, xts,
+                       poff, offsets, n_experts, (int)I, (int)H, P, o1, o3);
+    hipLaunchKernelGGL((wgrad_long_kernel<OT, 1>), dim3(kLongGrid), dim3(kLongWaves * kWave), 0, s, gtt, gts, utt,
+                       uts, xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3, elong);
   };
   if (dwt == MOE_F32)
     run(static_cast<float*>(dw1), static_cast<float*>(dw3), static_cast<float*>(dw2));

@@ -240,7 +240,7 @@ def _device_weights(lib, ws, H, I):
     (7168, 2048, [256, 37, 140], 0, False),
     (384, 256, [130, 0, 61], 3, True),      # bf16 dx rows and weight gradients
     (384, 256, [700, 20, 0], 2, True),      # a long segment (6 chunks) beside short ones, bf16
-    (512, 256, [600, 300, 129], 0, False),  # over 2 chunks per segment on average: tiles only
+    (512, 256, [600, 300, 129], 0, False),  # long segments of 5 and 3 chunks beside a short one
 ])
 def test_grouped_ffn_backward_matches_oracle(lib, H, I, loads, gaps, bf16):
     rng = np.random.default_rng(H + sum(loads))
