@@ -640,8 +640,10 @@ __device__ __forceinline__ void wgrad_store1(OT* o, const v4f& v) {
 // all of its chunks, in LDS and walks kStripMR consecutive 128-column output tiles, so per
 // tile it loads only the B_T fragments and their scales. A wave's memory operations
 // complete in issue order, and the loads of tile j+1 are issued before the stores of tile
-// j, so the wait for them is not a wait for the stores. SHARE 1: two A strips (dW1 and dW3
-// share B = x); SHARE 0: one. A wave computes all 128 rows by 32 columns of a tile.
+// j, so the wait for them is not a wait for the stores. SHARE 1: two A strips, the same
+// rows of two matrices (dW1 and dW3 share B = x); SHARE 2: two consecutive 128-row strips
+// of one matrix (dW2); SHARE 0: one strip. Either way of pairing, each B load serves two
+// output tiles. A wave computes all 128 rows by 32 columns of a tile.
 // ------------------------------------------------------------------------------------
 constexpr int kStripCh = 2;                  // chunks of a short segment
 constexpr int kStripRow = kStripCh * kTile;  // LDS bytes of one strip row (16 pieces of 16)
@@ -661,16 +663,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const float* __restrict__ sa2, const uint8_t* __restrict__ bt, const float* __restrict__ sb,
     const int32_t* __restrict__ poff, const int32_t* __restrict__ offsets, int n_experts, int NA,
     int NB, int64_t pstride, OT* __restrict__ out, OT* __restrict__ out2) {
-  static_assert(SHARE == 0 || SHARE == 1, "one or two A strips");
-  constexpr int NS = SHARE == 1 ? 2 : 1;     // A strips, one output each
+  static_assert(SHARE >= 0 && SHARE <= 2, "one or two A strips");
+  constexpr int NS = SHARE ? 2 : 1;          // A strips, one output tile each
+  constexpr int kSpanA = SHARE == 2 ? 2 * kTile : kTile;   // rows of A_T per work item
   constexpr int kStores = NS * 16;           // store instructions per wave and tile
   // strip rows of A_T: 16-byte piece s of row r holds K piece s ^ (r & 15)
   __shared__ __attribute__((aligned(16))) uint8_t lda[NS][kTile * kStripRow];
   __shared__ __attribute__((aligned(16))) float lsa[NS][kStripCh][kTile];   // A scales
   __shared__ __attribute__((aligned(16))) float lsb[2][kStripCh][kTile];    // B scales, by tile parity
-  // work item: expert e (on XCD e % 8, so its B_T rows stay in one L2), strip of 128 rows
-  // of A_T, range of kStripMR column tiles
-  const int ga = NA / kTile, tiles = NB / kWgM;
+  // work item: expert e (on XCD e % 8, so its B_T rows stay in one L2), kSpanA rows of A_T,
+  // range of kStripMR column tiles
+  const int ga = NA / kSpanA, tiles = NB / kWgM;
   const int nmr = (tiles + kStripMR - 1) / kStripMR, per_e = ga * nmr;
   const int64_t L = blockIdx.x, slot = L / 8;
   const int64_t ee = L % 8 + 8 * (slot / per_e);
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   const int p0 = poff[e], nch = (poff[e + 1] - p0) / kTile;
   if (nch > kStripCh) return;   // a long segment: wgrad_long_kernel
   const int it = (int)(slot % per_e);
-  const int n0 = (it / nmr) * kTile;
+  const int n0 = (it / nmr) * kSpanA;
   const int j0 = (it % nmr) * kStripMR, j1 = min(j0 + kStripMR, tiles);
   const int g0 = p0 / kTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -691,6 +694,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(at), 0, (int)((int64_t)NA * pstride), 0x00020000);
   const __amdgpu_buffer_rsrc_t ra2 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(SHARE == 1 ? at2 : at), 0, (int)((int64_t)NA * pstride), 0x00020000);
+  // strip w: rows n0 + sw * w of A (SHARE 2: the second strip is the next 128 rows of the
+  // same matrix and output; SHARE 1: the same rows of the second matrix and output)
+  constexpr int sw = SHARE == 2 ? kTile : 0;
   const __amdgpu_buffer_rsrc_t rb =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bt), 0, (int)((int64_t)NB * pstride), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sa), 0, 0x7fffffff, 0x00020000);
@@ -735,13 +741,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     for (int q = 0; q < 8; ++q) {
       const int u = (q * 4 + wave) * kWave + lane;   // 16-byte unit of lda[w]
       const int rr = u >> 4, kp = (u & 15) ^ (rr & 15), ch = kp >> 3;
-      const int off = ch < nch ? (int)((int64_t)(n0 + rr) * pstride + p0 + ch * kTile + (kp & 7) * 16) : kOut;
+      const int off =
+          ch < nch ? (int)((int64_t)(n0 + sw * w + rr) * pstride + p0 + ch * kTile + (kp & 7) * 16) : kOut;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w ? ra2 : ra, (lds_u8*)&lda[w][0] + (q * 4 + wave) * kWave * 16, 16,
                                                off, 0, 0, 0);
     }
     {
       const int v = wave * kWave + lane, ch = v >> 7, rr = v & (kTile - 1);
-      const int off = ch < nch ? (int)(((int64_t)(g0 + ch) * NA + n0 + rr) * 4) : kOut;
+      const int off = ch < nch ? (int)(((int64_t)(g0 + ch) * NA + n0 + sw * w + rr) * 4) : kOut;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w ? rsa2 : rsa, (lds_u8*)&lsa[w][0][0] + wave * kWave * 4, 4, off,
                                                0, 0, 0);
     }
@@ -798,7 +805,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int w = 0; w < NS; ++w) {
-      OT* o = (w ? out2 : out) + (int64_t)e * NA * NB;
+      OT* o = (SHARE == 1 && w ? out2 : out) + ((int64_t)e * NA + sw * w) * NB;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -1336,19 +1343,24 @@ extern "C" moe_status moe_grouped_ffn_fp8_backward(
   // segments (at most kStripCh chunks, every expert without rows included) by strips, the
   // others (listed in elong) by the persistent long-segment kernel, one workgroup per CU
   // strip grid: 8 XCDs x ceil(E / 8) experts x strips x ranges of kStripMR tiles
-  auto sgrid = [&](int64_t NA, int64_t NB) {
+  auto sgrid = [&](int64_t NA, int64_t NB, int64_t span) {
     const int64_t nmr = (NB / kWgM + kStripMR - 1) / kStripMR;
-    return dim3((unsigned)(8 * (((int64_t)n_experts + 7) / 8) * (NA / kTile) * nmr));
+    return dim3((unsigned)(8 * (((int64_t)n_experts + 7) / 8) * (NA / span) * nmr));
   };
   auto run = [&](auto* o1, auto* o3, auto* o2) {
     using OT = std::remove_pointer_t<decltype(o1)>;
-    // dW2 = dy^T h
-    hipLaunchKernelGGL((wgrad_strip_kernel<OT, 0>), sgrid(H, I), dim3(256), 0, s, dyt, dyts, nullptr, nullptr, htt,
-                       hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
+    // dW2 = dy^T h: two 128-row strips of dy_T per work item where H allows (each B load
+    // then serves two output tiles, as for dW1 and dW3 below)
+    if (H % (2 * kTile) == 0)
+      hipLaunchKernelGGL((wgrad_strip_kernel<OT, 2>), sgrid(H, I, 2 * kTile), dim3(256), 0, s, dyt, dyts, nullptr,
+                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
+    else
+      hipLaunchKernelGGL((wgrad_strip_kernel<OT, 0>), sgrid(H, I, kTile), dim3(256), 0, s, dyt, dyts, nullptr,
+                         nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr);
     hipLaunchKernelGGL((wgrad_long_kernel<OT, 0>), dim3(kLongGrid), dim3(kLongWaves * kWave), 0, s, dyt, dyts,
                        nullptr, nullptr, htt, hts, poff, offsets, n_experts, (int)H, (int)I, P, o2, nullptr, elong);
     // dW1 = dg^T x and dW3 = du^T x, sharing x
-    hipLaunchKernelGGL((wgrad_strip_kernel<OT, 1>), sgrid(I, H), dim3(256), 0, s, gtt, gts, utt, uts, xtt, xts,
+    hipLaunchKernelGGL((wgrad_strip_kernel<OT, 1>), sgrid(I, H, kTile), dim3(256), 0, s, gtt, gts, utt, uts, xtt, xts,
                        poff, offsets, n_experts, (int)I, (int)H, P, o1, o3);
     hipLaunchKernelGGL((wgrad_long_kernel<OT, 1>), dim3(kLongGrid), dim3(kLongWaves * kWave), 0, s, gtt, gts, utt,
                        uts, xtt, xts, poff, offsets, n_experts, (int)I, (int)H, P, o1, o3, elong);
