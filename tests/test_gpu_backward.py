@@ -234,6 +234,42 @@ def _device_weights(lib, ws, H, I):
     return (w1, s1, w3, s3, lib.moe_pack_fp8_weights(t2), t2s, lib.moe_pack_fp8_weights(t13), t13s)
 
 
+def test_wgrad_strip_and_long_paths_agree(lib):
+    """The weight gradients of a segment of two token chunks (strip kernel) equal those of
+    the same segment grown to three chunks by rows without a token (long-segment kernel)
+    bit for bit: both sum the same per-chunk products in the same FP32 order, and the added
+    rows quantise to zero codes. The other outputs are per row and must agree as well."""
+    rng = np.random.default_rng(11)
+    H, I, T = 256, 128, 64
+    cfg = _cfg(tokens=T, hidden_size=H, moe_intermediate_size=I, num_experts=4,
+               num_experts_per_tok=4, num_shared_experts=0)
+    c = lib.make_config(cfg)
+    xq = _rand_codes(rng, (T, H))
+    xs = (rng.uniform(0.5, 2.0, (T, H // 128)) * 2.0 ** -6).astype(np.float32)
+    x = oracle.round_bf16(oracle.dequant_1x128(xq, xs).astype(np.float32))
+    dout = oracle.round_bf16((rng.standard_normal((T, H)) * 0.01).astype(np.float32))
+    ws = _expert_set(rng, 2, H, I)
+    w = _device_weights(lib, ws, H, I)
+    tok0 = rng.integers(0, T, 200).astype(np.int32)   # expert 0: 200 rows (two chunks)
+    tok1 = rng.integers(0, T, 50).astype(np.int32)    # expert 1: 50 rows
+    gate0, gate1 = (rng.uniform(0.05, 1.0, n).astype(np.float32) for n in (200, 50))
+    outs = []
+    for pad in (0, 57):   # 57 rows without a token make expert 0 three chunks long
+        row_token = np.concatenate([tok0, np.full(pad, -1, np.int32), tok1])
+        row_gate = np.concatenate([gate0, np.ones(pad, np.float32), gate1])
+        offsets = np.array([0, 200 + pad, 250 + pad], np.int32)
+        say(f"wgrad paths: expert 0 with {200 + pad} rows")
+        r = lib.moe_grouped_ffn_fp8_backward(
+            c, 2, dev(xq), dev(xs), dev(x, torch.bfloat16), dev(row_token), dev(offsets), *w,
+            dev(dout, torch.bfloat16), row_gate=dev(row_gate))
+        torch.cuda.synchronize()
+        dxr, dw1, dw3, dw2 = (host(t) for t in r)
+        keep = np.concatenate([np.arange(200), np.arange(200 + pad, 250 + pad)])
+        outs.append((dxr[keep], dw1, dw3, dw2))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("H,I,loads,gaps,bf16", [
     (256, 128, [0, 17, 200, 3], 0, False),
     (512, 256, [300, 1, 129, 128], 5, False),
