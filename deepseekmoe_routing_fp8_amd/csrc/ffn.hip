@@ -226,9 +226,16 @@ constexpr int kNbPerWg1 = 2, kNbPerWg2 = 4;      // gate/up (16 blocks at I = 20
 
 // n-blocks per gate/up workgroup: one with tall tiles (measured 1.7% faster on the V3
 // gate/up at 16384 skewed tokens: twice the workgroups balance the long launch better),
-// else two (the same at 4096 tokens; four measured 2-4% slower everywhere).
-inline int gate_up_nb_per(int64_t n_rows, int32_t n_experts, bool mx) {
-  return tile_rows(n_rows, n_experts, mx) == kMT ? 1 : kNbPerWg1;
+// else two (the same at 4096 tokens; four measured 2-4% slower everywhere), and one again
+// when two would leave under four rounds of workgroups for the chip (2048 tokens at width
+// 2048, 64 + 2 experts: 2.4 rounds with two, gate/up 160 -> 152 us with one; at the V3
+// prefill, 8.8 rounds, one measured 2.5% slower). Tiles: at least n_rows / tile-rows, and
+// about one per expert when the rows spread over all of them.
+inline int gate_up_nb_per(int64_t n_rows, int32_t n_experts, bool mx, int n_nb) {
+  const int rows = tile_rows(n_rows, n_experts, mx);
+  if (rows == kMT) return 1;
+  const int64_t tiles = std::max<int64_t>(n_rows / rows, std::min<int64_t>(n_rows, n_experts));
+  return tiles * ((n_nb + kNbPerWg1 - 1) / kNbPerWg1) < 4 * 256 ? 1 : kNbPerWg1;
 }
 
 // n-blocks per down-projection workgroup: with a few rows per expert (decode) each
@@ -948,7 +955,7 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
                        row_token, H / kTile, f.xsp);
   FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, f.xsp, n_tokens,
              row_token, w1, w1s, w3, w3s, H, I, I / kTile,
-             gate_up_nb_per(n_rows, n_experts, cfg->scale_mode == 1), f.hq, f.hs, a_out, b_out};
+             gate_up_nb_per(n_rows, n_experts, cfg->scale_mode == 1, I / kTile), f.hq, f.hs, a_out, b_out};
   const dim3 grid((unsigned)ffn_grid(f.L.max_tiles, (a1.n_nb + a1.nb_per - 1) / a1.nb_per, n_rows));
   if (save)
     hipLaunchKernelGGL((ffn_kernel<4, uint16_t, false>), grid, dim3(kFThreads), 0, s, a1);
