@@ -364,18 +364,20 @@ def other_configs(layer, warmup: int, decode_steps: int, args_skewed_steps: int 
         res["decode"] = measure(layer, cfg, xd, decode_steps, warmup)
         res["decode"]["graph"] = measure_graph(layer, xd[0], decode_steps, warmup)
         cfg = synth.PRESETS["v3_skewed"]
-        log(f"[bench] skewed: T={cfg.tokens}, generating {args_skewed_steps} fresh clustered batches")
-        xs = device_batches(cfg, args_skewed_steps)
-        log(f"[bench] skewed: {args_skewed_steps} steps, bias from 0, updated every step")
-        layer.bias.zero_()
-        res["skewed"] = measure(layer, cfg, xs, args_skewed_steps, 0, reset_bias=False)
-        xs_p2 = xs[:20]   # the power-of-two variant is compared on the first 20 batches
-        del xs
-        layer.bias.zero_()
-        skewed_default_20 = measure(layer, cfg, xs_p2, len(xs_p2), 0, reset_bias=False)
-        # per-sequence balance loss / allocation entropy of the last skewed step's routing
-        # (4 sequences of 4096 tokens); timed on its own, it is not part of the forward step
-        res["seq_balance"] = time_seq_balance(layer, cfg, 4096)
+        xs_p2 = []
+        if args_skewed_steps > 0:
+            log(f"[bench] skewed: T={cfg.tokens}, generating {args_skewed_steps} fresh clustered batches")
+            xs = device_batches(cfg, args_skewed_steps)
+            log(f"[bench] skewed: {args_skewed_steps} steps, bias from 0, updated every step")
+            layer.bias.zero_()
+            res["skewed"] = measure(layer, cfg, xs, args_skewed_steps, 0, reset_bias=False)
+            xs_p2 = xs[:20]   # the power-of-two variant is compared on the first 20 batches
+            del xs
+            layer.bias.zero_()
+            skewed_default_20 = measure(layer, cfg, xs_p2, len(xs_p2), 0, reset_bias=False)
+            # per-sequence balance loss / allocation entropy of the last skewed step's routing
+            # (4 sequences of 4096 tokens); timed on its own, it is not part of the forward step
+            res["seq_balance"] = time_seq_balance(layer, cfg, 4096)
         cfg = synth.PRESETS["reduced"]
         log("[bench] reduced layer: weights on the device")
         small = MoELayer(cfg)
@@ -393,14 +395,15 @@ def other_configs(layer, warmup: int, decode_steps: int, args_skewed_steps: int 
         # the same variant where compute matters: the skewed T=16384 step, 20 fresh batches
         # from bias 0, beside the default path on the same batches
         cs = synth.PRESETS["v3_skewed"]
-        p2.bias.zero_()
-        r2 = measure(p2, cs, xs_p2, len(xs_p2), 0, reset_bias=False)
-        res["pow2_scales_skewed"] = {
-            "steps": len(xs_p2), "pow2_ms_per_step": r2["ms_per_step"],
-            "default_ms_per_step": skewed_default_20["ms_per_step"],
-            "pow2_ffn_ms": r2["ffn_ms"], "default_ffn_ms": skewed_default_20["ffn_ms"],
-            "pow2_tflops_fp8": r2["tflops_fp8"], "default_tflops_fp8": skewed_default_20["tflops_fp8"],
-            "note": "first 20 fresh skewed batches, bias from 0 updated every step, both paths"}
+        if xs_p2:
+            p2.bias.zero_()
+            r2 = measure(p2, cs, xs_p2, len(xs_p2), 0, reset_bias=False)
+            res["pow2_scales_skewed"] = {
+                "steps": len(xs_p2), "pow2_ms_per_step": r2["ms_per_step"],
+                "default_ms_per_step": skewed_default_20["ms_per_step"],
+                "pow2_ffn_ms": r2["ffn_ms"], "default_ffn_ms": skewed_default_20["ffn_ms"],
+                "pow2_tflops_fp8": r2["tflops_fp8"], "default_tflops_fp8": skewed_default_20["tflops_fp8"],
+                "note": f"first {len(xs_p2)} fresh skewed batches, bias from 0 updated every step, both paths"}
         del p2, xs_p2
         # forward + FP8 backward on the headline workload (its own layer with the dgrad
         # operands and FP32 weight-gradient buffers)
@@ -433,7 +436,7 @@ def main():
                          "skewed and reduced workloads follow it (0: skip all three)")
     ap.add_argument("--skewed-steps", type=int, default=100,
                     help="forward + bias-update steps of the skewed T=16384 workload, each on a "
-                         "fresh clustered batch generated before the timed region")
+                         "fresh clustered batch generated before the timed region (0: skip it)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -80,12 +80,11 @@ __device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& a, const v8i& b, const
 // count; n_tiles[1], with tall tiles only, the tiles of experts with two or more (they
 // come first), which the GEMM kernels schedule so that an expert's tiles share its weight
 // stream (wg_work).
-__global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
-                                                               int n_experts, int n_rows, int mt,
-                                                               int max_tiles,
-                                                               Tile* __restrict__ tiles,
-                                                               int32_t* __restrict__ n_tiles) {
-  __shared__ int len_s[kMaxExperts];
+// One block of kMaxExperts threads, thread e for expert e.
+__device__ __forceinline__ void plan_tiles(const int32_t* __restrict__ offsets, int n_experts,
+                                           int n_rows, int mt, int max_tiles,
+                                           Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ __attribute__((aligned(16))) int len_s[kMaxExperts];
   __shared__ int nt_r[kMaxExperts];
   __shared__ int start_r[kMaxExperts];
   __shared__ int wsum[kMaxExperts / kWave];
@@ -104,9 +103,18 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __
   if (nt >= 2) atomicAdd(&multi_s, nt);
   int rank = 0;
   if (e < n_experts) {
-    for (int j = 0; j < n_experts; ++j) {
-      const int mj = len_s[j];
-      rank += (mj > m) || (mj == m && j < e);
+    // four lengths per LDS read; entries past n_experts hold 0 and never count (0 > m is
+    // false for m >= 0, and their index is above e)
+    const int4* l4 = reinterpret_cast<const int4*>(len_s);
+    const int nq = (n_experts + 3) >> 2;
+#pragma unroll 8
+    for (int q = 0; q < nq; ++q) {
+      const int4 v = l4[q];
+      const int j = 4 * q;
+      rank += (v.x > m) || (v.x == m && j < e);
+      rank += (v.y > m) || (v.y == m && j + 1 < e);
+      rank += (v.z > m) || (v.z == m && j + 2 < e);
+      rank += (v.w > m) || (v.w == m && j + 3 < e);
     }
     nt_r[rank] = nt;   // ranks are a permutation of [0, n_experts)
   }
@@ -146,6 +154,14 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __
   }
 }
 
+__global__ __launch_bounds__(kMaxExperts) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
+                                                               int n_experts, int n_rows, int mt,
+                                                               int max_tiles,
+                                                               Tile* __restrict__ tiles,
+                                                               int32_t* __restrict__ n_tiles) {
+  plan_tiles(offsets, n_experts, n_rows, mt, max_tiles, tiles, n_tiles);
+}
+
 // Activation scales of the permuted rows, chunk-major ([H/128][n_rows]): the scales of one
 // K chunk for a tile's rows are then one contiguous run, copied per chunk as a few cache
 // lines instead of one line per row. Rows that name no token get scale 0 (their codes are
@@ -174,6 +190,47 @@ __global__ __launch_bounds__(kMT) void ffn_gather_scales_kernel(const Tile* __re
 #pragma unroll
   for (int u = 0; u < kGatherChunks; ++u)
     if (c0 + u < nkc) xsp[(int64_t)(c0 + u) * n_rows + tl.m0 + r] = v[u];
+}
+
+// Tile plan and scale gather of a gate/up call in one launch. Block 0 plans the tiles
+// (plan_tiles); blocks 1.. gather the scales of kMaxExperts permuted rows x kGatherChunks
+// K chunks each, chunk-major as ffn_gather_scales_kernel. The gather needs no plan: a
+// row's token is row_token[r] or, without row_token, its index inside the segment that
+// holds it (segments clamped as by the plan). Rows of no segment or without a token get
+// scale 0.
+__global__ __launch_bounds__(kMaxExperts) void ffn_prep_kernel(
+    const int32_t* __restrict__ offsets, int n_experts, int n_rows, int mt, int max_tiles,
+    Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles, const float* __restrict__ xs,
+    int64_t n_tokens, const int32_t* __restrict__ row_token, int nkc, float* __restrict__ xsp) {
+  if (blockIdx.x == 0) {
+    plan_tiles(offsets, n_experts, n_rows, mt, max_tiles, tiles, n_tiles);
+    return;
+  }
+  const int ncg = (nkc + kGatherChunks - 1) / kGatherChunks;
+  const int b = blockIdx.x - 1;
+  const int c0 = (b % ncg) * kGatherChunks;
+  const int64_t r = (int64_t)(b / ncg) * kMaxExperts + threadIdx.x;
+  if (r >= n_rows) return;
+  int64_t t;
+  if (row_token) {
+    t = row_token[r];
+  } else {
+    auto start = [&](int e) { return min(max(offsets[e], 0), n_rows); };
+    int lo_e = 0, hi_e = n_experts;   // the last segment that starts at or before r
+    while (hi_e - lo_e > 1) {
+      const int mid = (lo_e + hi_e) >> 1;
+      if (start(mid) <= r) lo_e = mid; else hi_e = mid;
+    }
+    const int lo = start(lo_e), hi = min(max(offsets[lo_e + 1], lo), n_rows);
+    t = r >= lo && r < hi ? r - lo : -1;
+  }
+  const bool ok = t >= 0 && t < n_tokens;
+  float v[kGatherChunks];
+#pragma unroll
+  for (int u = 0; u < kGatherChunks; ++u) v[u] = (ok && c0 + u < nkc) ? xs[t * nkc + c0 + u] : 0.0f;
+#pragma unroll
+  for (int u = 0; u < kGatherChunks; ++u)
+    if (c0 + u < nkc) xsp[(int64_t)(c0 + u) * n_rows + r] = v[u];
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
@@ -944,15 +1001,14 @@ moe_status ffn_gate_up(const moe_config* cfg, int32_t n_experts, int64_t n_rows,
   if (save && (!a_out || !b_out)) return MOE_ERR_NULL;
   hipStream_t s = as_stream(stream);
   const int H = cfg->hidden, I = cfg->inter;
-  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, n_experts,
-                     (int)n_rows, tile_rows(n_rows, n_experts, cfg->scale_mode == 1),
-                     (int)f.L.max_tiles, f.tiles, f.ntiles);
-  // also without tokens: every row's scale is then written as 0, never left undefined
-  hipLaunchKernelGGL(ffn_gather_scales_kernel,
-                       dim3((unsigned)f.L.max_tiles, (unsigned)((H / kTile + kGatherChunks - 1) / kGatherChunks)),
-                       dim3(kMT), 0, s,
-                       f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xs, n_tokens,
-                       row_token, H / kTile, f.xsp);
+  // plan and scale gather in one launch; also without tokens: every row's scale is then
+  // written as 0, never left undefined
+  const int64_t prep_blocks =
+      1 + (n_rows + kMaxExperts - 1) / kMaxExperts * ((H / kTile + kGatherChunks - 1) / kGatherChunks);
+  hipLaunchKernelGGL(ffn_prep_kernel, dim3((unsigned)prep_blocks), dim3(kMaxExperts), 0, s, offsets,
+                     n_experts, (int)n_rows, tile_rows(n_rows, n_experts, cfg->scale_mode == 1),
+                     (int)f.L.max_tiles, f.tiles, f.ntiles, xs, n_tokens, row_token, H / kTile,
+                     f.xsp);
   FfnArgs a1{f.tiles, f.ntiles, (int)f.L.max_tiles, n_experts, (int)n_rows, xq, f.xsp, n_tokens,
              row_token, w1, w1s, w3, w3s, H, I, I / kTile,
              gate_up_nb_per(n_rows, n_experts, cfg->scale_mode == 1, I / kTile), f.hq, f.hs, a_out, b_out};
