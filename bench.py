@@ -243,22 +243,29 @@ def measure(layer, cfg, xs, steps: int, warmup: int, reset_bias: bool = True):
 
 def measure_graph(layer, x, steps: int, warmup: int):
     """The same step (bias update included) captured once into a HIP graph and replayed
-    ``steps`` times: the launches' host overhead leaves the timed region."""
+    ``steps`` times: the launches' host overhead leaves the timed region. As in the eager
+    loop, the configured bias is restored (a 1 KB device copy) before every replay, so both
+    route the same workload."""
     import torch
+    b0 = layer.bias.clone()
     layer.capture(x, update_bias=True)
     for _ in range(warmup):
+        layer.bias.copy_(b0)
         layer.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
+        layer.bias.copy_(b0)
         layer.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     layer._graph = None
+    layer.bias.copy_(b0)
     T = x.shape[0]
     return {"ms_per_step": round(wall * 1e3 / steps, 4), "tokens_per_s": round(T * steps / wall, 1),
             "steps": steps, "note": "MoELayer.capture / replay: one HIP graph per step (bias update "
-                                    "inside the graph, so the bias moves across replays)"}
+                                    "inside the graph; the configured bias restored before each "
+                                    "replay, as in the eager loop)"}
 
 
 def device_batches(cfg, n: int):

@@ -495,16 +495,23 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
       return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     if constexpr (MX) {
-      // each tile's operands are read and multiplied into its accumulators in turn (the
-      // other wave on the SIMD covers the LDS latency)
+      // the MFMA applies the scales and accumulates, so nothing is promoted; the operands of
+      // tile t+1 are read while tile t multiplies
       const int e0 = e8m0_of(s0), e1 = e8m0_of(s1);
+      v8i mq[2];
+      float ms[2];
+      mq[0] = frag(0);
+      ms[0] = *reinterpret_cast<lds_f32*>(bs);
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts) {
-        const v8i bq = frag(ts);
-        const int ea = e8m0_of(*reinterpret_cast<lds_f32*>(bs + ts * 64));
-        acc0[ts] = mfma_fp8_scaled(A0, bq, acc0[ts], e0, ea);
-        acc1[ts] = mfma_fp8_scaled(A1, bq, acc1[ts], e1, ea);
-        __builtin_amdgcn_sched_barrier(0);   // one tile's operands at a time
+        if (ts + 1 < NT) {
+          mq[(ts + 1) & 1] = frag(ts + 1);
+          ms[(ts + 1) & 1] = *reinterpret_cast<lds_f32*>(bs + (ts + 1) * 64);
+        }
+        const int ea = e8m0_of(ms[ts & 1]);
+        acc0[ts] = mfma_fp8_scaled(A0, mq[ts & 1], acc0[ts], e0, ea);
+        acc1[ts] = mfma_fp8_scaled(A1, mq[ts & 1], acc1[ts], e1, ea);
+        __builtin_amdgcn_sched_barrier(0);   // bound the live operands to two tiles
       }
       return;
     }
