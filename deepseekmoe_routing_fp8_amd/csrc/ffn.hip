@@ -286,9 +286,10 @@ constexpr int kNbPerWg1 = 2, kNbPerWg2 = 4;      // gate/up (16 blocks at I = 20
 // gate/up at 16384 skewed tokens: twice the workgroups balance the long launch better),
 // else two (the same at 4096 tokens; four measured 2-4% slower everywhere), and one again
 // when two would leave under four rounds of workgroups for the chip (2048 tokens at width
-// 2048, 64 + 2 experts: 2.4 rounds with two, gate/up 160 -> 152 us with one; at the V3
-// prefill, 8.8 rounds, one measured 2.5% slower). Tiles: at least n_rows / tile-rows, and
-// about one per expert when the rows spread over all of them.
+// 2048, 64 + 2 experts, when that layer ran 160-row tiles: 2.4 rounds with two, gate/up
+// 160 -> 152 us with one; at the V3 prefill, 8.8 rounds, one measured 2.5% slower).
+// Tiles: at least n_rows / tile-rows, and about one per expert when the rows spread over
+// all of them.
 inline int gate_up_nb_per(int64_t n_rows, int32_t n_experts, bool mx, int n_nb) {
   const int rows = tile_rows(n_rows, n_experts, mx);
   if (rows == kMT) return 1;
