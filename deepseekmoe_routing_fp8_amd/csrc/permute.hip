@@ -3,7 +3,7 @@
 // and none is dropped). On one GPU the dispatch becomes a stable counting sort of the
 // (token, slot) pairs by expert, so that each expert's rows are one contiguous segment.
 //
-// Three launches over blocks of kPB tokens:
+// Three launches over blocks of kPB tokens (one, perm_single_kernel, for a single block):
 //   count   - per block, the expert histogram of its pairs (LDS atomics) -> ws[b][e];
 //   scan    - one workgroup: per expert, the exclusive prefix over blocks, then the
 //             exclusive prefix over experts (offsets, a wave-parallel scan); ws[b][e]
@@ -154,6 +154,98 @@ __global__ __launch_bounds__(kPB) void perm_scatter_kernel(const int32_t* __rest
     row_token[pairs + r] = (int32_t)(r % T);
 }
 
+// A batch of at most kPB tokens (one block: decode): the three steps in one workgroup and
+// one launch instead of three, with the same results. The pairs' histogram (LDS atomics,
+// as perm_count_kernel), the exclusive prefix over experts (perm_scan_kernel with one
+// block, whose per-block prefix is 0), and the stable scatter (perm_scatter_kernel).
+__global__ __launch_bounds__(kPB) void perm_single_kernel(const int32_t* __restrict__ idx,
+                                                          int64_t T, int k, int N, int S,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ row_token,
+                                                          int32_t* __restrict__ row_of) {
+  constexpr int kPer = kMaxRouted / kPB;   // experts per thread in the prefix
+  static_assert(kMaxRouted % kPB == 0, "experts per thread");
+  __shared__ unsigned long long mask[kPWaves][kMaxRouted];
+  __shared__ int before[kPWaves][kMaxRouted];
+  __shared__ int cnt[kMaxRouted];
+  __shared__ int base[kMaxRouted + 1];
+  __shared__ int wtot[kPWaves];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t pairs = T * k;
+  for (int i = tid; i < kPWaves * N; i += kPB) mask[i / N][i % N] = 0ull;
+  for (int i = tid; i < N; i += kPB) cnt[i] = 0;
+  __syncthreads();
+  const bool live = tid < T;
+  int ej[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    ej[j] = -1;
+    if (j < k && live) {
+      const int e = idx[(int64_t)tid * k + j];
+      if (e >= 0 && e < N) {
+        ej[j] = e;
+        atomicAdd(&cnt[e], 1);
+        atomicOr(&mask[wave][e], 1ull << lane);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += kPB) {
+    int run = 0;
+    for (int w = 0; w < kPWaves; ++w) {
+      before[w][e] = run;
+      run += __popcll(mask[w][e]);
+    }
+  }
+  {
+    // exclusive prefix of the counts: thread t owns experts kPer*t .. kPer*t + kPer - 1
+    int c[kPer], sum = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = kPer * tid + u;
+      c[u] = e < N ? cnt[e] : 0;
+      sum += c[u];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(inc, d, kWave);
+      if (lane >= d) inc += v;
+    }
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    int bef = 0;
+    for (int i = 0; i < wave; ++i) bef += wtot[i];
+    int ex = bef + inc - sum;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = kPer * tid + u;
+      if (e < N) base[e] = ex;
+      ex += c[u];
+    }
+    if (tid == kPB - 1) base[N] = bef + inc;   // the total (experts past N add 0)
+  }
+  __syncthreads();
+  for (int i = tid; i <= N; i += kPB) offsets[i] = base[i];
+  for (int s = tid; s < S; s += kPB) offsets[N + 1 + s] = (int32_t)(pairs + (s + 1) * T);
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k && live) {
+      const int e = ej[j];
+      int32_t r = -1;
+      if (e >= 0) {
+        r = base[e] + before[wave][e] + __popcll(mask[wave][e] & lt);
+        if (r < pairs) row_token[r] = tid;
+      }
+      row_of[(int64_t)tid * k + j] = r;
+    }
+  }
+  // rows past the routed ones: gap rows carry -1, shared segments the token index
+  for (int64_t r = base[N] + tid; r < pairs; r += kPB) row_token[r] = -1;
+  for (int64_t r = tid; r < S * T; r += kPB) row_token[pairs + r] = (int32_t)(r % T);
+}
+
 inline int64_t perm_blocks(int64_t T) { return (T + kPB - 1) / kPB; }
 
 }  // namespace
@@ -180,6 +272,11 @@ extern "C" moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_
   hipStream_t s = as_stream(stream);
   const int N = cfg->n_routed, k = cfg->top_k, S = cfg->n_shared;
   int32_t* hist = static_cast<int32_t*>(ws);
+  if (T > 0 && T <= kPB) {
+    hipLaunchKernelGGL(perm_single_kernel, dim3(1), dim3(kPB), 0, s, topk_idx, T, k, N, S, offsets,
+                       row_token, row_of);
+    return launch_status();
+  }
   if (T > 0)
     hipLaunchKernelGGL(perm_count_kernel, dim3((unsigned)nblk), dim3(kPB), 0, s, topk_idx, T, k, N,
                        hist);

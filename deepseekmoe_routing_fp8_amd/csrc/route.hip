@@ -147,10 +147,14 @@ __device__ __forceinline__ v8bf lds_frag(const uint8_t* p) {
 }
 
 // XP = bf16 pieces per activation: 1 (bf16 x) or 3 (FP32 x, pre-split into planes).
+// Workgroup 0 also zeroes the N load counters, which the launches after this one add to
+// (one launch fewer than a separate fill).
 template <int XP>
 __global__ __launch_bounds__(kLThreads) void router_logits_kernel(
     const uint16_t* __restrict__ xp, int64_t T, int H, const uint16_t* __restrict__ wpk, int N,
-    int nb16, RouteGeom g, double* __restrict__ part) {
+    int nb16, RouteGeom g, double* __restrict__ part, int32_t* __restrict__ counts) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < N; i += kLThreads) counts[i] = 0;
   constexpr int kXB = XP * 8 * kFragBytesR;   // x fragments per step: XP planes x 8 token blocks
   constexpr int kStage = kXB + 3 * 8 * kFragBytesR;
   constexpr int NST = XP == 1 ? 4 : 2;        // ring depth (steps in flight: NST - 1)
@@ -559,8 +563,10 @@ extern "C" moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype 
   if (T > 0 && (!ws || ws_bytes < W.total)) return MOE_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   const int N = cfg->n_routed, H = cfg->hidden;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((N + 255) / 256), dim3(256), 0, s, counts, N, 0);
-  if (T == 0) return launch_status();
+  if (T == 0) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((N + 255) / 256), dim3(256), 0, s, counts, N, 0);
+    return launch_status();
+  }
   const RouteGeom g = route_geom(T, N, H);
   if (g.grid > 0x7fffffff || (T * N + 255) / 256 > 0x7fffffff) return MOE_ERR_SHAPE;
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -568,14 +574,15 @@ extern "C" moe_status moe_route(const moe_config* cfg, const void* x, moe_dtype 
   const int nb16 = (N + 15) / 16;
   if (xt == MOE_BF16) {
     hipLaunchKernelGGL(router_logits_kernel<1>, dim3((unsigned)g.grid), dim3(kLThreads), 0, s,
-                       static_cast<const uint16_t*>(x), T, H, w_router_split, N, nb16, g, part);
+                       static_cast<const uint16_t*>(x), T, H, w_router_split, N, nb16, g, part,
+                       counts);
   } else {
     uint16_t* xs3 = reinterpret_cast<uint16_t*>(base + W.xsplit);
     const int64_t n = T * H;
     hipLaunchKernelGGL(x_split_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
                        static_cast<const float*>(x), n, xs3);
     hipLaunchKernelGGL(router_logits_kernel<3>, dim3((unsigned)g.grid), dim3(kLThreads), 0, s,
-                       xs3, T, H, w_router_split, N, nb16, g, part);
+                       xs3, T, H, w_router_split, N, nb16, g, part, counts);
   }
   // few tokens: many K ranges, summed by one thread per (token, expert) first
   const bool fused = g.S <= kFusedSplits;

@@ -321,7 +321,11 @@ def _check_permute(idx, N, S, off, rt, ro):
 
 @pytest.mark.parametrize("T,N,k,skew,S", [(64, 16, 4, None, 1), (4096, 256, 8, None, 1),
                                           (16384, 256, 8, 1.1, 1), (1, 256, 8, None, 1),
-                                          (1500, 512, 16, None, 0), (3000, 64, 6, 2.0, 2)])
+                                          (1500, 512, 16, None, 0), (3000, 64, 6, 2.0, 2),
+                                          # one block of tokens (the one-launch path)
+                                          (128, 256, 8, None, 1), (256, 512, 16, None, 2),
+                                          (200, 256, 8, 1.1, 1), (256, 64, 6, 2.0, 0),
+                                          (257, 256, 8, None, 1)])
 def test_permute_matches_oracle(lib, T, N, k, skew, S):
     import dataclasses
     cfg = dataclasses.replace(synth.PRESETS["tiny"], num_experts=N, num_experts_per_tok=k, tokens=T,
@@ -334,17 +338,19 @@ def test_permute_matches_oracle(lib, T, N, k, skew, S):
     _check_permute(idx, N, S, off, rt, ro)
 
 
-def test_permute_invalid_entries(lib):
-    """Entries naming no routed expert are skipped; the rows they leave free read token -1."""
+@pytest.mark.parametrize("T", [500, 200])
+def test_permute_invalid_entries(lib, T):
+    """Entries naming no routed expert are skipped; the rows they leave free read token -1
+    (T = 200: the one-launch path of a single token block)."""
     import dataclasses
-    T, N, k, S = 500, 64, 6, 2
+    N, k, S = 64, 6, 2
     cfg = dataclasses.replace(synth.PRESETS["tiny"], num_experts=N, num_experts_per_tok=k, tokens=T,
                               num_shared_experts=S)
     rng = np.random.default_rng(5)
     idx = _idx(rng, T, N, k)
     idx[rng.random((T, k)) < 0.05] = -1
     idx[7, 2] = N + 3
-    say("permute with invalid entries")
+    say(f"permute with invalid entries T={T}")
     off, rt, ro = lib.moe_permute(lib.make_config(cfg), dev(idx))
     torch.cuda.synchronize()
     off, rt, ro = _check_permute(idx, N, S, off, rt, ro)
@@ -369,6 +375,11 @@ def test_permute_collapse_and_empty(lib):
     off, _, _ = _check_permute(idx, 256, 1, off, rt, ro)
     cnt = np.diff(off[:257])
     assert np.all(cnt[200:208] == 2048) and cnt.sum() == 2048 * 8
+    say("permute collapse, one token block")
+    off, rt, ro = lib.moe_permute(lib.make_config(dataclasses.replace(cfg, tokens=256)), dev(idx[:256]))
+    torch.cuda.synchronize()
+    off, _, _ = _check_permute(idx[:256], 256, 1, off, rt, ro)
+    assert np.all(np.diff(off[:257])[200:208] == 256)
     say("permute T=0")
     off, rt, ro = lib.moe_permute(c, torch.empty((0, 8), dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
