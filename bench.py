@@ -530,7 +530,7 @@ def main():
         "frac_fp8_mfma_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
         "roofline": {
             "kernel": "ffn_kernel<1> (moe_grouped_ffn_fp8_gate_up: routed + shared experts, "
-                      "gate/up GEMMs, SwiGLU, 1x128 re-quantisation; includes the 1-block tile plan)",
+                      "gate/up GEMMs, SwiGLU, 1x128 re-quantisation; includes the tile-plan and scale-gather launch)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "algorithmic_bytes": ab["gate_up"], "experts_touched": ab["experts"],
