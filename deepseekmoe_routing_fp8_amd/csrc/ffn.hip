@@ -351,8 +351,8 @@ struct FfnLds {
   uint8_t* ast[kMaxRing];   // ring slots (kAStage bytes each, 128-byte aligned); the
                             // last one, never a ring slot, stages phase-1 h codes
   uint8_t* junk;            // kJunk bytes
-  const int* tok_s;         // source row of every tile row (-1: none)
-  const float* wsc;         // [n-block][2][kMaxChunks + kMaxRing] weight-block scales
+  int* tok_s;               // source row of every tile row (-1: none)
+  float* wsc;               // [n-block][2][kMaxChunks + kMaxRing] weight-block scales
   float* red;               // [kFWaves][kMT] phase-1 amax partials
   uint8_t* ystage;          // phase 2, bf16 output: [kMT/2][512 bytes] block rows (the
                             // last slot, enlarged)
@@ -375,6 +375,18 @@ __device__ __forceinline__ v8i buf_wfrag(__amdgpu_buffer_rsrc_t d, int voff) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// A workgroup's set-up values, loaded into registers by ffn_kernel: the source row of
+// tile row tid (a token in phase 1, a permuted row in phase 2; -1: none) and this
+// thread's share of the weight-block scales of its n-blocks (entry c = tid + u * threads
+// of the [n-block][2][kWscRow] table). ffn_main stores them to LDS after it has issued
+// the first chunk's weight loads, so the two latencies overlap.
+constexpr int kWscRowAll = kMaxChunks + kMaxRing;
+constexpr int kWscPer = (kMaxNbPerWg * 2 * kWscRowAll + kFThreads - 1) / kFThreads;
+struct Setup {
+  int tok;
+  float w[kWscPer];
+};
+
 // ------------------------------------------------------------------------------------
 // Main loop and epilogue of one workgroup, for NT 16-row tiles (a compile-time count:
 // the tile's rows rounded up to 16 or more; rows past the tile are computed on a clamped
@@ -385,7 +397,7 @@ __device__ __forceinline__ v8i buf_wfrag(__amdgpu_buffer_rsrc_t d, int voff) {
 // ------------------------------------------------------------------------------------
 template <int PHASE, typename YT, int NT, int RING, bool MX>
 __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int nb0, int nbn,
-                                         int wave, int lane, const FfnLds& sh) {
+                                         int wave, int lane, const FfnLds& sh, const Setup& su) {
   static_assert(RING >= 3 && RING <= kMaxRing, "ring depth");
   static_assert(NT * 16 <= kMT, "tile rows");
   constexpr bool GU = PHASE != 2;   // phases 1, 3 and 4: the gate/up GEMMs (W1 and W3)
@@ -404,18 +416,7 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.aq), 0, (int)(uint32_t)(a.n_tokens * K), 0x00020000);
   const __amdgpu_buffer_rsrc_t sdesc =
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.as), 0, (int)(uint32_t)((int64_t)a.n_rows * nkc * 4), 0x00020000);
-  int aoff[kDma];
-#pragma unroll
-  for (int j = 0; j < kDma; ++j) {
-    const int unit = min((j * kActRound + wave * 1024 + lane * 16) / 16, kActBytes / 16 - 1);
-    const int r = unit >> 3, seg = (unit & 7) ^ (r & 7);
-    // rows past the tile and rows without a token read zeros (an offset at the end of
-    // the range), so the padding of the last 16-row tile costs the matrix cores no
-    // switching power
-    const int src = sh.tok_s[r];
-    aoff[j] = (int)(src >= 0 ? (uint32_t)src * (uint32_t)K + (uint32_t)(seg * 16)
-                             : (uint32_t)(a.n_tokens * K));
-  }
+  int aoff[kDma];   // set once the tile's source rows are in LDS (prologue)
   const int soff = (tl.m0 + min(tid, tl.mlen - 1)) * 4;   // permuted row of this lane's scale
 
   // This wave's two fragments of n-block nb: one descriptor per fragment row, formed per
@@ -566,6 +567,28 @@ __device__ __forceinline__ void ffn_main(const FfnArgs& a, const Tile& tl, int n
   // compiler's own waits for the weight registers never ask for more than these.
   static_assert(RING == 4, "pairs of steps over a 4-slot ring");
   issue_w(0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // The set-up values were loaded before these weights, so they arrive first; they go to
+  // LDS while the weights are in flight (an LDS-only barrier leaves the loads pending).
+  // From here on the issue order is the one the waits below count.
+  if (tid < kMT) sh.tok_s[tid] = su.tok;
+#pragma unroll
+  for (int u = 0; u < kWscPer; ++u) {
+    const int c = tid + u * kFThreads;
+    if (c < nbn * 2 * kWscRow) sh.wsc[c] = su.w[u];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < kDma; ++j) {
+    const int unit = min((j * kActRound + wave * 1024 + lane * 16) / 16, kActBytes / 16 - 1);
+    const int r = unit >> 3, seg = (unit & 7) ^ (r & 7);
+    // rows past the tile and rows without a token read zeros (an offset at the end of
+    // the range), so the padding of the last 16-row tile costs the matrix cores no
+    // switching power
+    const int src = sh.tok_s[r];
+    aoff[j] = (int)(src >= 0 ? (uint32_t)src * (uint32_t)K + (uint32_t)(seg * 16)
+                             : (uint32_t)(a.n_tokens * K));
+  }
   __builtin_amdgcn_sched_barrier(0);
   issue_a(0, sh.ast[0]);
   issue_a(1, sh.ast[1]);
@@ -863,36 +886,37 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   const int K = GU ? a.H : a.I;
   const int nkc = K / kTile;
 
-  // source row of every tile row: a token (phase 1) or a permuted row (phase 2)
-  for (int r = tid; r < kMT; r += kFThreads) {
-    int t = -1;
-    if (r < tl.mlen) {
-      if (GU) {
-        const int64_t v = a.row_token ? (int64_t)a.row_token[tl.m0 + r] : (int64_t)(tl.m0 + r - tl.lo);
-        t = (v >= 0 && v < a.n_tokens) ? (int)v : -1;
-      } else {
-        t = tl.m0 + r;
-      }
+  // set-up values (stored to LDS by ffn_main): the source row of tile row tid, a token
+  // (phase 1) or a permuted row (phase 2), and this thread's entries of the weight-block
+  // scales for every K chunk (0 past the last one) of each n-block: phase 1 (W1, W3) of
+  // row block nb; phase 2 the two W2 row blocks of the block's 256 rows
+  static_assert(kMT <= kFThreads && kWscRow == kWscRowAll, "one tile row per thread");
+  Setup su;
+  su.tok = -1;
+  if (tid < tl.mlen) {
+    if (GU) {
+      const int64_t v = a.row_token ? (int64_t)a.row_token[tl.m0 + tid] : (int64_t)(tl.m0 + tid - tl.lo);
+      su.tok = (v >= 0 && v < a.n_tokens) ? (int)v : -1;
+    } else {
+      su.tok = tl.m0 + tid;
     }
-    tok_s[r] = t;
   }
-  // weight-block scales for every K chunk (0 past the last one) of each n-block: phase 1
-  // (W1, W3) of row block nb; phase 2 the two W2 row blocks of the block's 256 rows
   const int64_t nrb = (GU ? a.I : a.H) / kTile;
-  for (int c = tid; c < nbn * 2 * kWscRow; c += kFThreads) {
+#pragma unroll
+  for (int u = 0; u < kWscPer; ++u) {
+    const int c = tid + u * kFThreads;
     const int it = c / (2 * kWscRow), which = (c / kWscRow) & 1, kc = c % kWscRow;
     const int nb = nb0 + it;
     float v = 0.0f;
-    if (kc >= nkc) {
+    if (c >= nbn * 2 * kWscRow || kc >= nkc) {
     } else if (GU) {
       v = (which == 0 ? a.wsa : a.wsb)[((int64_t)tl.e * nrb + nb) * nkc + kc];
     } else {
       const int64_t rb = min((int64_t)nb * 2 + which, nrb - 1);
       v = a.wsa[((int64_t)tl.e * nrb + rb) * nkc + kc];
     }
-    wsc[it * 2 + which][kc] = v;
+    su.w[u] = v;
   }
-  __syncthreads();
 
   const FfnLds sh{{ast0, ast1, ast2, ast3, ast4}, junk, tok_s, &wsc[0][0], red, ast4};
   // Ring depth 4: three chunks (96 KB of weights per CU) in flight cover the loaded HBM
@@ -903,14 +927,14 @@ __global__ __launch_bounds__(kFThreads) void ffn_kernel(const FfnArgs a) {
   // V3 prefill gate/up: its 60 padded steps per block cost more than the depth gained.)
   constexpr int R = 4;
   switch ((tl.mlen + 15) >> 4) {
-    case 1: case 2: ffn_main<PHASE, YT, 2, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 3: case 4: ffn_main<PHASE, YT, 4, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 5: case 6: ffn_main<PHASE, YT, 6, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 7: case 8: ffn_main<PHASE, YT, 8, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 9: ffn_main<PHASE, YT, 9, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
-    case 10: ffn_main<PHASE, YT, 10, R, MX>(a, tl, nb0, nbn, wave, lane, sh); break;
+    case 1: case 2: ffn_main<PHASE, YT, 2, R, MX>(a, tl, nb0, nbn, wave, lane, sh, su); break;
+    case 3: case 4: ffn_main<PHASE, YT, 4, R, MX>(a, tl, nb0, nbn, wave, lane, sh, su); break;
+    case 5: case 6: ffn_main<PHASE, YT, 6, R, MX>(a, tl, nb0, nbn, wave, lane, sh, su); break;
+    case 7: case 8: ffn_main<PHASE, YT, 8, R, MX>(a, tl, nb0, nbn, wave, lane, sh, su); break;
+    case 9: ffn_main<PHASE, YT, 9, R, MX>(a, tl, nb0, nbn, wave, lane, sh, su); break;
+    case 10: ffn_main<PHASE, YT, 10, R, MX>(a, tl, nb0, nbn, wave, lane, sh, su); break;
     default:
-      if constexpr (!MX) ffn_main<PHASE, YT, 12, R, MX>(a, tl, nb0, nbn, wave, lane, sh);
+      if constexpr (!MX) ffn_main<PHASE, YT, 12, R, MX>(a, tl, nb0, nbn, wave, lane, sh, su);
       break;
   }
 }
