@@ -440,6 +440,9 @@ def _relerr(a, b):
     (256, 128, 4, [0, 17, 64, 3], False),
     (512, 256, 3, [193, 1, 400], False),          # several M tiles, tiny tail
     (384, 256, 2, [16, 33], True),                 # identity token map, H % 256 == 128
+    # identity token map over many segments, empty ones first, last and between: each
+    # row's token comes from the segment that holds it, found without the tile plan
+    (256, 128, 12, [0, 5, 17, 0, 33, 1, 0, 0, 64, 3, 160, 0], True),
     (1024, 512, 5, [130, 0, 0, 7, 250], False),
     # every tile height the kernel specialises (2, 4, 6, 8, 9, 10 16-row tiles) on both
     # sides of its boundary, and the 160-row split into two tiles
