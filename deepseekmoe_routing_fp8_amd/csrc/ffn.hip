@@ -227,8 +227,17 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_prep_kernel(
   }
   const bool ok = t >= 0 && t < n_tokens;
   float v[kGatherChunks];
+  static_assert(kGatherChunks == 8, "two 16-byte loads");
+  if (ok && (nkc & 3) == 0 && c0 + kGatherChunks <= nkc && ((uintptr_t)xs & 15) == 0) {
+    // the token's eight scales as two 16-byte loads (t * nkc + c0 is a multiple of 4)
+    const float4* p = reinterpret_cast<const float4*>(xs + t * nkc + c0);
+    const float4 x0 = p[0], x1 = p[1];
+    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+  } else {
 #pragma unroll
-  for (int u = 0; u < kGatherChunks; ++u) v[u] = (ok && c0 + u < nkc) ? xs[t * nkc + c0 + u] : 0.0f;
+    for (int u = 0; u < kGatherChunks; ++u) v[u] = (ok && c0 + u < nkc) ? xs[t * nkc + c0 + u] : 0.0f;
+  }
 #pragma unroll
   for (int u = 0; u < kGatherChunks; ++u)
     if (c0 + u < nkc) xsp[(int64_t)(c0 + u) * n_rows + r] = v[u];
